@@ -1,0 +1,212 @@
+"""CPU oracle for C = ReLU(A @ B) on binary16 inputs -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The GPU library never routes through it:
+the oracle and the HIP path share no code, header, table or helper; the only
+thing both sides see is the seeded input generator in ``tgemm_workloads``.
+
+The arithmetic lives in ``tgemm_ref.c`` (plain C11 + OpenMP, built by gcc into
+``liboracle_tgemm.so`` next to this file). It follows the plain definition of the
+contraction in "Writing High-Performance Kernels in TileLang, from GEMM to MLA"
+(atlascloud.ai), section "Let's write a GEMM" (C = ReLU(A @ B), float16 operands,
+float accumulator, max(., 0) epilogue) and "TileLang-MUSA operator development"
+(7yue.com), section 3 (the same GEMM without ReLU, checked against an fp32 product):
+inputs are decoded exactly to float64, summed over k ascending in float64, and ReLU
+is ``x > 0 ? x : +0``.
+
+Pins (tests/test_oracle_*.py, all CPU): exact rational brute force, the closed forms
+ones @ ones = K and A @ I = A, the ReLU sign invariants, transpose and thread-count
+invariance, and numpy's binary16 codec over all 65536 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "tgemm_ref.c")
+LIBRARY = os.path.join(_HERE, "liboracle_tgemm.so")
+
+
+def build(src: str = SOURCE, out: str = LIBRARY, verbose: bool = False) -> str:
+    """Compile the oracle's C source with gcc (portable -O2, OpenMP). Always recompiles."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+           "-o", tmp, src, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _as_u16(x: np.ndarray) -> np.ndarray:
+    """View a float16 / uint16 array as its uint16 bit patterns (no value conversion)."""
+    x = np.asarray(x)
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    if x.dtype != np.uint16:
+        raise TypeError(f"expected float16 or uint16 bits, got {x.dtype}")
+    return x
+
+
+def _rowmajor_2d(x: np.ndarray):
+    """Return (array, leading dimension in elements) for a 2-D row-major view."""
+    if x.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    if x.shape[0] > 0 and x.shape[1] > 0 and x.strides[1] != x.itemsize:
+        x = np.ascontiguousarray(x)
+    if x.shape[0] > 1 and x.strides[0] % x.itemsize == 0 and x.strides[0] >= x.shape[1] * x.itemsize:
+        ld = x.strides[0] // x.itemsize
+    else:
+        x = np.ascontiguousarray(x)
+        ld = max(1, x.shape[1])
+    return x, ld
+
+
+class Oracle:
+    """One loaded build of the oracle library (the default one, or a test build)."""
+
+    def __init__(self, path: str = LIBRARY):
+        lib = ctypes.CDLL(path)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_f16_decode.restype = ctypes.c_double
+        lib.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_encode_rne.restype = ctypes.c_uint16
+        lib.oracle_f16_encode_rne.argtypes = [ctypes.c_double]
+        lib.oracle_f16_decode_array.argtypes = [p, p, i64]
+        lib.oracle_f16_encode_array.argtypes = [p, p, i64]
+        lib.oracle_gemm_f16.restype = ctypes.c_int
+        lib.oracle_gemm_f16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64,
+                                        ctypes.c_int, ctypes.c_int]
+        lib.oracle_gemm_f16_entries.restype = None
+        lib.oracle_gemm_f16_entries.argtypes = [i64, p, i64, p, i64, i64, p, p, p,
+                                                ctypes.c_int, ctypes.c_int]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def f16_decode(self, bits: np.ndarray) -> np.ndarray:
+        """Exact binary16 -> float64 decode of every element (the oracle's own codec)."""
+        b = np.ascontiguousarray(_as_u16(bits))
+        out = np.empty(b.shape, dtype=np.float64)
+        self.lib.oracle_f16_decode_array(b.ctypes.data, out.ctypes.data, b.size)
+        return out
+
+    def f16_encode(self, x: np.ndarray) -> np.ndarray:
+        """float64 -> binary16 bits, round to nearest even (the oracle's own codec)."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.oracle_f16_encode_array(x.ctypes.data, out.ctypes.data, x.size)
+        return out
+
+    def gemm(self, A: np.ndarray, B: np.ndarray, relu: bool, nthreads: int = 0) -> np.ndarray:
+        """Full product ReLU?(A @ B) in float64 from binary16 A (M x K) and B (K x N)."""
+        A, lda = _rowmajor_2d(_as_u16(A))
+        B, ldb = _rowmajor_2d(_as_u16(B))
+        M, K = A.shape
+        K2, N = B.shape
+        if K != K2:
+            raise ValueError(f"inner dimensions differ: {A.shape} @ {B.shape}")
+        C = np.empty((M, N), dtype=np.float64)
+        if M == 0 or N == 0:
+            return C
+        rc = self.lib.oracle_gemm_f16(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                                      C.ctypes.data, N, int(bool(relu)), int(nthreads))
+        if rc != 0:
+            raise MemoryError("oracle could not allocate its decode buffer")
+        return C
+
+    def gemm_entries(self, A: np.ndarray, B: np.ndarray, rows, cols, relu: bool,
+                     nthreads: int = 0) -> np.ndarray:
+        """Entries (rows[t], cols[t]) of ReLU?(A @ B), one by one, bitwise equal to gemm()."""
+        A, lda = _rowmajor_2d(_as_u16(A))
+        B, ldb = _rowmajor_2d(_as_u16(B))
+        M, K = A.shape
+        K2, N = B.shape
+        if K != K2:
+            raise ValueError(f"inner dimensions differ: {A.shape} @ {B.shape}")
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+        if rows.shape != cols.shape:
+            raise ValueError("rows and cols differ in shape")
+        if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+            raise IndexError("entry index out of range")
+        out = np.empty(rows.shape, dtype=np.float64)
+        self.lib.oracle_gemm_f16_entries(K, A.ctypes.data, lda, B.ctypes.data, ldb, rows.size,
+                                         rows.ctypes.data, cols.ctypes.data, out.ctypes.data,
+                                         int(bool(relu)), int(nthreads))
+        return out
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from tgemm_ref.c (compiled on first use if missing or stale)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def f16_decode(bits):
+    return default().f16_decode(bits)
+
+
+def f16_encode(x):
+    return default().f16_encode(x)
+
+
+def gemm(A, B, relu, nthreads=0):
+    return default().gemm(A, B, relu, nthreads)
+
+
+def gemm_entries(A, B, rows, cols, relu, nthreads=0):
+    return default().gemm_entries(A, B, rows, cols, relu, nthreads)
+
+
+def max_threads() -> int:
+    return default().max_threads()
+
+
+# --------------------------------------------------------------------------------------
+# Tolerance: |c - ref| <= 4e-3 * |ref| + 1e-3 * sqrt(K), elementwise, with c the decoded
+# binary16 GPU output and ref the oracle's unrounded float64 value. The relative term
+# covers the final rounding to binary16 (at most 2^-11 relative); the absolute term covers
+# float32 accumulation in any order. A second, scale-aware form replaces sqrt(K) by
+# sigma_A * sigma_B * sqrt(K) for inputs drawn with a standard deviation other than 1.
+# --------------------------------------------------------------------------------------
+REL_TOL = 4e-3
+ABS_TOL_PER_SQRT_K = 1e-3
+
+
+def tolerance(ref: np.ndarray, K: int, scale: float = 1.0) -> np.ndarray:
+    return REL_TOL * np.abs(ref) + ABS_TOL_PER_SQRT_K * scale * math.sqrt(max(K, 1))
+
+
+def compare(c_bits: np.ndarray, ref: np.ndarray, K: int, scale: float = 1.0) -> dict:
+    """Compare binary16 output bits against the float64 reference; returns a report."""
+    c = f16_decode(c_bits)
+    if c.shape != ref.shape:
+        raise ValueError(f"shape mismatch {c.shape} vs {ref.shape}")
+    err = np.abs(c - ref)
+    tol = tolerance(ref, K, scale)
+    bad = ~(err <= tol)  # NaN counts as a failure
+    ratio = np.where(tol > 0, err / tol, np.inf)
+    return {
+        "n": int(c.size),
+        "fails": int(bad.sum()),
+        "max_abs_err": float(err.max()) if c.size else 0.0,
+        "max_ratio": float(np.nanmax(ratio)) if c.size else 0.0,
+        "first_fail": (tuple(int(v) for v in np.argwhere(bad)[0]) if bad.any() else None),
+    }

@@ -1,0 +1,90 @@
+"""Seeded synthetic inputs for the fp16 GEMM(+ReLU) workloads.
+
+This module holds no arithmetic of the method: it only draws random binary16
+matrices from a seed, so the GPU path and the CPU oracle read the very same bytes.
+
+Recipe (fixed): numpy ``default_rng(seed)`` (PCG64); A (M x K) is drawn before B
+(K x N) from the one generator; values are drawn in float32 and rounded to binary16
+with numpy's round-to-nearest-even cast. Distributions:
+  * ``normal``  : standard normal times ``std``;
+  * ``uniform`` : uniform on [-1, 1) (float32 ``random()`` * 2 - 1).
+
+The workloads mirror the pages' synthetic ``randn`` float16 inputs: the 1024^3
+example of "Writing High-Performance Kernels in TileLang, from GEMM to MLA"
+(atlascloud.ai), section "Let's write a GEMM", and the 4096^3 fp16 benchmark of the
+nxmr.cn TileLang-on-A100 write-up, section 2.2.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    relu: bool
+    dist: str       # "normal" or "uniform"
+    std: float      # standard deviation for "normal" (ignored for "uniform")
+    seed: int
+
+    @property
+    def flop(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def scale(self) -> float:
+        """sigma_A * sigma_B of the input distribution (1 for N(0,1))."""
+        s = self.std if self.dist == "normal" else 1.0 / math.sqrt(3.0)
+        return s * s
+
+    def inputs(self):
+        return make_inputs(self.M, self.N, self.K, self.dist, self.std, self.seed)
+
+
+# The five measured configurations (seed = position, A drawn before B).
+WORKLOADS = {
+    "relu_1024": Workload("relu_1024", 1024, 1024, 1024, True, "normal", 1.0, 1),
+    "plain_4096": Workload("plain_4096", 4096, 4096, 4096, False, "normal", 1.0, 2),
+    "relu_edge_4095x3000x1000": Workload("relu_edge_4095x3000x1000", 4095, 3000, 1000, True,
+                                         "uniform", 1.0, 3),
+    "relu_8192": Workload("relu_8192", 8192, 8192, 8192, True, "normal", 1.0 / math.sqrt(8192.0), 4),
+    "relu_tall_16384x512x4096": Workload("relu_tall_16384x512x4096", 16384, 512, 4096, True,
+                                         "normal", 1.0, 5),
+}
+
+# The headline: 4096^3 with the ReLU epilogue on, same inputs as plain_4096.
+HEADLINE = Workload("relu_4096", 4096, 4096, 4096, True, "normal", 1.0, 2)
+
+
+def _draw(rng: np.random.Generator, shape, dist: str, std: float) -> np.ndarray:
+    if dist == "normal":
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+    elif dist == "uniform":
+        x = rng.random(shape, dtype=np.float32)
+        x *= np.float32(2.0)
+        x -= np.float32(1.0)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return x.astype(np.float16)
+
+
+def make_inputs(M: int, N: int, K: int, dist: str = "normal", std: float = 1.0, seed: int = 0):
+    """Return (A, B): float16 arrays of shape (M, K) and (K, N), C-contiguous."""
+    rng = np.random.default_rng(seed)
+    A = _draw(rng, (M, K), dist, std)
+    B = _draw(rng, (K, N), dist, std)
+    return A, B
+
+
+def digest(x: np.ndarray) -> str:
+    """SHA-256 of the raw bytes (recorded with results so runs can be matched)."""
+    return hashlib.sha256(np.ascontiguousarray(x).tobytes()).hexdigest()
