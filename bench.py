@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark: fp16 GEMM + fused ReLU through libtgemm on one MI355X.
+
+One step = one gemm_f16 call over the whole workload (C = ReLU(A @ B), M = N = K = 4096,
+fp16 inputs drawn N(0,1) from seed 2, fp32 accumulate, fp16 out, row-major), inputs
+already resident in HBM. W untimed warm-up steps, then exactly K timed steps bracketed
+by device synchronisation. Prints ONE JSON line on stdout; details go to stderr.
+
+  value            = 2*M*N*K*steps / wall time of the timed steps, in TFLOP/s
+  roofline.achieved = 2*M*N*K / mean kernel duration, from HIP events recorded on the
+                     stream the kernels are launched on, against the dense fp16 MFMA peak
+  cpu_baseline     = the CPU oracle (as it stands) timed on the host on a slab of rows of
+                     the same workload, in TFLOP/s, with the threads it used
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp16 GEMM+ReLU TFLOP/s at 4096^3 on 1 MI355X; % of dense fp16 MFMA peak"
+# Dense fp16 MFMA peak of MI355X: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz (AMD's ~2.5 PFLOP/s).
+PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("tgemm_kernels.hip", "tgemm_internal.h", "tgemm_api.cpp"):
+        with open(os.path.join(ROOT, "tiled_dense_gemm_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, cfg_name: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{cfg_name}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        eprint(f"traffic counters in {path} are from another kernel version; reporting null")
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, B, relu, c_gpu_bits, target_s: float):
+    """Time the oracle on the first R rows of the workload; R sized for ~target_s."""
+    import numpy as np
+    import oracle
+
+    orc = oracle.default()
+    threads = orc.max_threads()
+    M, K = A.shape
+    N = B.shape[1]
+    r0 = 8
+    t = time.perf_counter()
+    orc.gemm(A[:r0], B, relu)
+    dt = time.perf_counter() - t
+    rate = 2.0 * r0 * N * K / max(dt, 1e-9)
+    rows = int(min(M, max(r0, rate * target_s / (2.0 * N * K))))
+    t = time.perf_counter()
+    ref = orc.gemm(A[:rows], B, relu)
+    dt = time.perf_counter() - t
+    flops = 2.0 * rows * N * K
+    rep = oracle.compare(c_gpu_bits[:rows], ref, K)
+    eprint(f"cpu oracle: {rows} rows x {N} x {K} in {dt:.2f} s on {threads} threads "
+           f"({flops / dt / 1e9:.2f} GFLOP/s); GPU rows vs oracle: {rep}")
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {rows} of {M} rows of the same workload (all N={N} columns, K={K}), "
+                  f"{dt:.1f} s; GPU output on those rows vs oracle: {rep['fails']} tolerance failures",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="relu_4096",
+                    help="relu_4096 (headline) or a name from tgemm_workloads.WORKLOADS")
+    ap.add_argument("--cfg", type=int, default=None, help="force a config index (sweeps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "libtgemm runs on one GPU; multi-GPU runs are not part of this "
+                                   "build (an output-row split needs no communication, see DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tgemm_workloads as W
+    import tiled_dense_gemm_04_amd as tg
+
+    if not torch.cuda.is_available():
+        eprint("bench.py needs a GPU")
+        return 1
+    w = W.HEADLINE if args.workload == "relu_4096" else W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A, B = w.inputs()
+    a = torch.from_numpy(A).to(dev)
+    b = torch.from_numpy(B).to(dev)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.Stream(dev)
+    cfg = args.cfg if args.cfg is not None else tg.tgemm_select_config(
+        w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), c.data_ptr(), c.stride(0))
+    cfg_name = tg.tgemm_config_desc(cfg)["name"]
+    eprint(f"{torch.cuda.get_device_name(dev)}; {tg.tgemm_version()}; workload {w.name} "
+           f"{w.M}x{w.N}x{w.K} relu={w.relu}; config {cfg} {cfg_name}")
+
+    def step():
+        tg.gemm_f16(a, b, c, relu=w.relu, stream=stream, cfg=args.cfg)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    wall = t1 - t0
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    flop = float(w.flop)
+    value = flop * args.steps / wall / 1e12
+    achieved = flop / (kern_ms * 1e-3) / 1e12
+    eprint(f"wall {wall * 1e3:.2f} ms for {args.steps} steps -> {value:.1f} TFLOP/s; "
+           f"event mean {kern_ms * 1e3:.2f} us/launch -> {achieved:.1f} TFLOP/s "
+           f"({100 * achieved / PEAK_TFLOPS:.1f} % of {PEAK_TFLOPS:.1f})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "M": w.M, "N": w.N, "K": w.K,
+            "relu": w.relu,
+            "inputs": f"fp16 iid {'N(0,%g)' % w.std if w.dist == 'normal' else 'U(-1,1)'} seed {w.seed}",
+            "accumulate": "fp32",
+            "kernel_config": cfg_name,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * achieved / PEAK_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": load_traffic(w.name, cfg_name),
+            "kernel_us": round(kern_ms * 1e3, 3),
+            "kernel_source_hash": kernel_source_hash(),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        c_bits = c.cpu().numpy().view(np.uint16)
+        out["cpu_baseline"] = cpu_baseline(A, B, w.relu, c_bits, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

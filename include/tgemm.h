@@ -1,0 +1,129 @@
+/*
+ * tgemm.h -- C ABI of libtgemm: tiled fp16 GEMM with fp32 accumulation and an
+ * optional fused ReLU epilogue, C = ReLU(A @ B), on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one of "Writing High-Performance Kernels in TileLang, from
+ * GEMM to MLA" (atlascloud.ai), section "Let's write a GEMM": A is M x K, B is K x N,
+ * C is M x N, all IEEE binary16; the accumulator is float32 and is cleared before the
+ * K loop; ReLU is max(x, 0) applied to the float32 sum; the result is written back as
+ * binary16 (round to nearest even). Without ReLU it is the plain GEMM of
+ * "TileLang-MUSA operator development" (7yue.com), section 3.
+ *
+ * Conventions for every entry point below:
+ *   - Row-major storage: element (i, j) of X lives at X[i * ldX + j] (in elements).
+ *   - A, B, C are DEVICE pointers on the current HIP device, owned by the caller.
+ *     C must not overlap A or B. The library allocates nothing per call and keeps
+ *     no state beyond an immutable config table and a per-device architecture check.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream). Calls only
+ *     enqueue work and return; kernel completion and any device fault surface at the
+ *     caller's next synchronisation, as usual in HIP.
+ *   - ReLU maps x to x if x > 0, else +0 (so -0 and NaN become +0).
+ *   - Nothing is printed, nothing aborts, no exception crosses the ABI; errors are
+ *     returned as the negative codes below, detected before any work is enqueued
+ *     (except TGEMM_ELAUNCH).
+ */
+#ifndef TGEMM_H_
+#define TGEMM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define TGEMM_API __attribute__((visibility("default")))
+#else
+#define TGEMM_API
+#endif
+
+#define TGEMM_OK 0
+#define TGEMM_EINVAL_DIM (-1)   /* M, N or K negative, or larger than TGEMM_MAX_DIM        */
+#define TGEMM_EINVAL_LD (-2)    /* lda < max(1,K), ldb < max(1,N), ldc < max(1,N), or an   */
+                                /* ld larger than TGEMM_MAX_LD                              */
+#define TGEMM_ENULL (-3)        /* NULL pointer for an operand with a nonzero extent        */
+#define TGEMM_EDEVICE (-4)      /* current HIP device is not gfx950, or no device           */
+#define TGEMM_ELAUNCH (-5)      /* the kernel launch was rejected by the HIP runtime        */
+#define TGEMM_EINVAL_CFG (-6)   /* config index out of range, or config not usable here     */
+#define TGEMM_EALIGN (-7)       /* A, B or C not aligned to 2 bytes (one binary16 element)   */
+
+#define TGEMM_MAX_DIM ((int64_t)1 << 31)  /* M, N, K must be < 2^31                        */
+#define TGEMM_MAX_LD ((int64_t)1 << 22)   /* lda, ldb, ldc must be <= 2^22 elements         */
+
+/*
+ * C = ReLU(A @ B) if relu != 0, else C = A @ B.
+ *   M, N, K   : sizes; M == 0 or N == 0 is a no-op; K == 0 writes C = 0 (the empty sum).
+ *   A, lda    : M x K binary16 matrix and its row stride in elements (lda >= max(1, K)).
+ *   B, ldb    : K x N binary16 matrix and its row stride (ldb >= max(1, N)).
+ *   C, ldc    : M x N binary16 output and its row stride (ldc >= max(1, N)); only the
+ *               M x N elements are written, padding between rows is untouched.
+ *   relu      : 0 = plain GEMM, any other value = fused ReLU.
+ *   stream    : hipStream_t as void*, NULL for the default stream.
+ * The fast path needs A, B, C 16-byte aligned, lda, ldb, ldc multiples of 8 and K, N
+ * multiples of 8; other arguments take a slower generic kernel with the same results
+ * (within the stated tolerance; both accumulate in float32).
+ * Returns TGEMM_OK or a negative TGEMM_E* code.
+ */
+TGEMM_API int gemm_f16(int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t lda,
+             const void* B, int64_t ldb,
+             void* C, int64_t ldc,
+             int relu, void* stream);
+
+/* Human-readable text for a return code (static storage, never NULL). */
+TGEMM_API const char* tgemm_strerror(int code);
+
+/* Library version string (static storage). */
+TGEMM_API const char* tgemm_version(void);
+
+/* ---- tooling: config table (used by the offline sweep, the benchmark and tests) ---- */
+
+/* Description of one compiled kernel configuration. */
+typedef struct tgemm_config_info {
+    int32_t block_m, block_n, block_k; /* workgroup tile (elements)                     */
+    int32_t stages;                    /* LDS pipeline depth                            */
+    int32_t waves_m, waves_n;          /* wavefront grid inside the workgroup           */
+    int32_t panel;                     /* tile-rows per panel of the workgroup order    */
+    int32_t xcd_remap;                 /* 1 = consecutive tiles kept on one XCD         */
+    int32_t generic;                   /* 1 = unaligned-capable generic kernel          */
+    int32_t lds_bytes;                 /* dynamic LDS per workgroup                     */
+    char name[48];
+} tgemm_config_info;
+
+/* Number of configurations in the table. */
+TGEMM_API int tgemm_num_configs(void);
+
+/* Fills *out for config idx; returns TGEMM_OK or TGEMM_EINVAL_CFG / TGEMM_ENULL. */
+TGEMM_API int tgemm_config_desc(int idx, tgemm_config_info* out);
+
+/* Index of the config gemm_f16 would use for these arguments (pure host logic, no HIP
+ * call). Returns a negative TGEMM_E* code for invalid arguments, or -100 when the call
+ * launches nothing (M == 0 or N == 0) and -101 when it only zero-fills C (K == 0). */
+TGEMM_API int tgemm_select_config(int64_t M, int64_t N, int64_t K,
+                        const void* A, int64_t lda,
+                        const void* B, int64_t ldb,
+                        const void* C, int64_t ldc);
+
+/* gemm_f16 forced to config idx (same arguments and error codes; TGEMM_EINVAL_CFG if
+ * idx is out of range or the fast config cannot take these pointers / strides). */
+TGEMM_API int gemm_f16_cfg(int idx, int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 void* C, int64_t ldc,
+                 int relu, void* stream);
+
+/* Host replica of the device's workgroup -> output-tile map of config idx (the same
+ * inline function the kernels run): for workgroup id wg of a launch over an M x N
+ * output, writes the tile coordinates (*tile_m, *tile_n). Returns TGEMM_OK,
+ * TGEMM_EINVAL_CFG, or TGEMM_EINVAL_DIM if wg is outside the launch. */
+TGEMM_API int tgemm_tile_of(int idx, int64_t M, int64_t N, int64_t wg,
+                  int64_t* tile_m, int64_t* tile_n);
+
+/* Number of workgroups config idx launches for an M x N output. */
+TGEMM_API int64_t tgemm_num_workgroups(int idx, int64_t M, int64_t N);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H_ */

@@ -1,0 +1,294 @@
+"""GPU parity: libtgemm (through its C ABI) against the CPU oracle, element by element,
+on the same seeded inputs. Tolerance |c - ref| <= 4e-3 |ref| + 1e-3 sqrt(K) (scaled by
+sigma_A sigma_B for inputs that are not unit-variance), bit-exact where the result is
+exact (closed forms, identity, ReLU sign symmetry, determinism)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import tgemm_workloads as W
+from gpu_util import assert_close, log, relu_bits, run, sample_entries, to_dev, torch_cuda
+
+import tiled_dense_gemm_04_amd as tg
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = torch_cuda()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.lib()
+    oracle.default()
+    log(f"device: {torch.cuda.get_device_name(0)}; library {tg.tgemm_version()}")
+    return torch
+
+
+def _fast_cfgs():
+    return [i for i, c in enumerate(tg.configs()) if not c["generic"]]
+
+
+SMALL = [(256, 256, 64), (512, 384, 192), (300, 264, 136), (1, 8, 8), (257, 136, 72),
+         (640, 1152, 1000), (33, 520, 520), (1024, 256, 24)]
+
+
+@pytest.mark.parametrize("idx", list(range(6)))
+def test_small_shapes_each_config(idx):
+    if idx >= tg.tgemm_num_configs():
+        pytest.skip("config not in table")
+    shapes = list(SMALL)
+    if tg.tgemm_config_desc(idx)["generic"]:
+        shapes += [(17, 23, 29), (1, 1, 1), (65, 63, 33), (130, 7, 250)]
+    for s, (M, N, K) in enumerate(shapes):
+        A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=100 + s)
+        for relu in (True, False):
+            log(f"cfg {idx} {tg.tgemm_config_desc(idx)['name']} M={M} N={N} K={K} relu={relu}")
+            c = run(A, B, relu, cfg=idx)
+            assert_close(c, oracle.gemm(A, B, relu), K, what=f"cfg{idx} {M}x{N}x{K} relu={relu}")
+
+
+EDGE = [1, 15, 16, 17, 31, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+EDGE8 = [8, 16, 24, 56, 64, 72, 120, 128, 136, 248, 256, 264]
+
+
+def test_edge_sweep_default_selection():
+    rng = np.random.default_rng(2024)
+    triples = [tuple(int(v) for v in rng.choice(EDGE, 3)) for _ in range(60)]
+    triples += [tuple(int(v) for v in (rng.choice(EDGE), rng.choice(EDGE8), rng.choice(EDGE8)))
+                for _ in range(60)]
+    for t, (M, N, K) in enumerate(triples):
+        A, B = W.make_inputs(M, N, K, "uniform", 1.0, seed=500 + t)
+        relu = bool(t % 2)
+        log(f"edge M={M} N={N} K={K} relu={relu} cfg={tg.tgemm_select_config(M, N, K)}")
+        c = run(A, B, relu)
+        assert_close(c, oracle.gemm(A, B, relu), K, scale=1 / 3, what=f"edge {M}x{N}x{K}")
+
+
+def test_edge_sweep_fast_configs_ragged():
+    """Every fast config on shapes that leave ragged M, N and K tails inside one tile."""
+    rng = np.random.default_rng(77)
+    for idx in _fast_cfgs():
+        for t in range(12):
+            M = int(rng.choice(EDGE))
+            N = int(rng.choice(EDGE8))
+            K = int(rng.choice(EDGE8))
+            A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=900 + t)
+            log(f"fast cfg {idx} M={M} N={N} K={K}")
+            c = run(A, B, True, cfg=idx)
+            assert_close(c, oracle.gemm(A, B, True), K, what=f"cfg{idx} {M}x{N}x{K}")
+
+
+# ------------------------------------------------------------------ measured workloads
+def test_workload_relu_1024_full():
+    w = W.WORKLOADS["relu_1024"]
+    A, B = w.inputs()
+    log(f"workload {w.name}")
+    c = run(A, B, w.relu)
+    assert_close(c, oracle.gemm(A, B, w.relu), w.K, w.scale, w.name)
+
+
+def test_workload_edge_4095x3000x1000_full():
+    w = W.WORKLOADS["relu_edge_4095x3000x1000"]
+    A, B = w.inputs()
+    log(f"workload {w.name} (cfg {tg.tgemm_select_config(w.M, w.N, w.K)})")
+    c = run(A, B, w.relu)
+    ref = oracle.gemm(A, B, w.relu)
+    assert_close(c, ref, w.K, 1.0, w.name)       # the stated tolerance
+    assert_close(c, ref, w.K, w.scale, w.name)   # scale-aware (sigma^2 = 1/3)
+
+
+@pytest.mark.parametrize("name", ["plain_4096", "relu_tall_16384x512x4096", "relu_8192"])
+def test_workload_full_size_sampled(name):
+    w = W.WORKLOADS[name]
+    A, B = w.inputs()
+    log(f"workload {w.name} (cfg {tg.tgemm_select_config(w.M, w.N, w.K)})")
+    c = run(A, B, w.relu)
+    rng = np.random.default_rng(w.seed)
+    rows, cols = sample_entries(w.M, w.N, rng, n_rows=4, n_cols=4, n_rand=8192)
+    ref = oracle.gemm_entries(A, B, rows, cols, w.relu)
+    got = c[rows, cols]
+    assert_close(got, ref, w.K, 1.0, w.name)
+    assert_close(got, ref, w.K, w.scale, w.name)
+    if w.relu:
+        assert not np.any(c & 0x8000), "ReLU output has a sign bit set"
+    assert not np.any((c & 0x7C00) == 0x7C00), "inf/NaN in output"
+
+
+def test_headline_relu_4096_matches_plain():
+    """4096^3 with ReLU on (the headline) equals max(plain output, +0) bit for bit, and
+    matches the oracle on sampled entries."""
+    w = W.HEADLINE
+    A, B = w.inputs()
+    log("headline relu_4096 + plain_4096")
+    c_relu = run(A, B, True)
+    c_plain = run(A, B, False)
+    assert np.array_equal(c_relu, relu_bits(c_plain))
+    rng = np.random.default_rng(99)
+    rows, cols = sample_entries(w.M, w.N, rng, n_rows=2, n_cols=2, n_rand=4096)
+    assert_close(c_relu[rows, cols], oracle.gemm_entries(A, B, rows, cols, True), w.K, 1.0, "relu_4096")
+
+
+# ------------------------------------------------------------------ closed forms, invariants
+@pytest.mark.parametrize("K", [1000, 2048, 2051, 4095, 4096])
+def test_ones_closed_form_bitwise(K):
+    M = N = 256
+    A = np.ones((M, K), np.float16)
+    B = np.ones((K, N), np.float16)
+    expect = int(oracle.f16_encode(np.array([float(K)]))[0])
+    for cfg in [None] + _fast_cfgs() + [0]:
+        log(f"ones K={K} cfg={cfg}")
+        c = run(A, B, True, cfg=cfg)
+        assert np.all(c == expect), (K, cfg, hex(expect), np.unique(c)[:4])
+
+
+def test_identity_bitwise():
+    rng = np.random.default_rng(3)
+    M, K = 300, 256
+    A = rng.standard_normal((M, K)).astype(np.float16)
+    I = np.eye(K, dtype=np.float16)
+    for cfg in [None] + _fast_cfgs() + [0]:
+        log(f"identity cfg={cfg}")
+        c = run(A, I, False, cfg=cfg)
+        a = A.view(np.uint16)
+        # an fp32 sum of +0 terms and one exact product: equal up to the sign of zero
+        assert np.array_equal(np.where(a == 0x8000, 0, a), np.where(c == 0x8000, 0, c))
+        cr = run(A, I, True, cfg=cfg)
+        assert np.array_equal(cr, relu_bits(a))
+
+
+def test_relu_sign_symmetry_bitwise():
+    rng = np.random.default_rng(4)
+    A = rng.standard_normal((512, 1000)).astype(np.float16)
+    B = rng.standard_normal((1000, 384)).astype(np.float16)
+    Bn = (B.view(np.uint16) ^ np.uint16(0x8000)).view(np.float16)
+    for cfg in [None, 0]:
+        log(f"relu symmetry cfg={cfg}")
+        plain = run(A, B, False, cfg=cfg)
+        neg = run(A, Bn, True, cfg=cfg)
+        # same summation order, negated terms: ReLU(A @ -B) = max(-(A @ B), +0) exactly
+        assert np.array_equal(neg, relu_bits(plain ^ np.uint16(0x8000)))
+        pos = run(A, B, True, cfg=cfg)
+        assert np.array_equal(pos, relu_bits(plain))
+        assert not np.any(pos & 0x8000) and not np.any(neg & 0x8000)
+
+
+def test_deterministic_repeat():
+    A, B = W.make_inputs(2048, 2048, 2048, "normal", 1.0, seed=8)
+    log("determinism 2048^3 x3")
+    c0 = run(A, B, True)
+    for _ in range(2):
+        assert np.array_equal(run(A, B, True), c0)
+
+
+def test_side_stream():
+    torch = torch_cuda()
+    A, B = W.make_inputs(1024, 1024, 512, "normal", 1.0, seed=9)
+    log("side stream")
+    s = torch.cuda.Stream()
+    a, b = to_dev(A), to_dev(B)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = tg.gemm_f16(a, b, relu=True)  # current stream inside the context
+    s.synchronize()
+    assert_close(c.cpu().numpy().view(np.uint16), oracle.gemm(A, B, True), 512)
+    c2 = tg.gemm_f16(a, b, relu=True, stream=s)
+    s.synchronize()
+    assert np.array_equal(c2.cpu().numpy(), c.cpu().numpy())
+
+
+# ------------------------------------------------------------------ layouts and degenerate
+def test_strided_views_and_padding_untouched():
+    torch = torch_cuda()
+    M, N, K = 520, 264, 328
+    A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=10)
+    a_big = to_dev(np.zeros((M, K + 64), np.float16))
+    b_big = to_dev(np.zeros((K, N + 40), np.float16))
+    a_big[:, 8:8 + K] = to_dev(A)
+    b_big[:, 16:16 + N] = to_dev(B)
+    c_big = torch.full((M, N + 24), 7.0, dtype=torch.float16, device="cuda")
+    a, b, c = a_big[:, 8:8 + K], b_big[:, 16:16 + N], c_big[:, 8:8 + N]
+    ref = oracle.gemm(A, B, True)
+    for cfg in [None] + _fast_cfgs() + [0]:
+        log(f"strided cfg={cfg} (select {tg.tgemm_select_config(M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), c.data_ptr(), c.stride(0))})")
+        c_big.fill_(7.0)
+        tg.gemm_f16(a, b, c, relu=True, cfg=cfg)
+        torch.cuda.synchronize()
+        out = c_big.cpu().numpy()
+        assert np.all(out[:, :8] == 7.0) and np.all(out[:, 8 + N:] == 7.0), "padding written"
+        assert_close(out[:, 8:8 + N].copy().view(np.uint16), ref, K, what=f"strided cfg {cfg}")
+
+
+def test_unaligned_pointer_takes_generic_path():
+    torch = torch_cuda()
+    M, N, K = 200, 136, 96
+    A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=11)
+    flat = to_dev(np.concatenate([np.zeros(1, np.float16), A.ravel()]))
+    a = flat[1:].view(M, K)  # 2-byte aligned only
+    b = to_dev(B)
+    sel = tg.tgemm_select_config(M, N, K, a.data_ptr(), K, b.data_ptr(), N, b.data_ptr(), N)
+    assert sel == 0
+    log("unaligned A -> generic")
+    c = tg.gemm_f16(a, b, relu=True)
+    torch.cuda.synchronize()
+    assert_close(c.cpu().numpy().view(np.uint16), oracle.gemm(A, B, True), K)
+    with pytest.raises(tg.TgemmError) as e:
+        tg.gemm_f16(a, b, relu=True, cfg=_fast_cfgs()[0])
+    assert e.value.code == tg.TGEMM_EINVAL_CFG
+
+
+def test_odd_sizes_generic():
+    for t, (M, N, K) in enumerate([(33, 17, 9), (129, 250, 1001), (7, 3, 4095)]):
+        A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=20 + t)
+        log(f"odd sizes {M}x{N}x{K}")
+        c = run(A, B, True)
+        assert_close(c, oracle.gemm(A, B, True), K, what=f"odd {M}x{N}x{K}")
+
+
+def test_k_zero_and_empty():
+    torch = torch_cuda()
+    log("K = 0 and empty outputs")
+    a = torch.empty((37, 0), dtype=torch.float16, device="cuda")
+    b = torch.empty((0, 40), dtype=torch.float16, device="cuda")
+    for relu in (True, False):
+        c = torch.full((37, 40), float("nan"), dtype=torch.float16, device="cuda")
+        tg.gemm_f16(a, b, c, relu=relu)
+        torch.cuda.synchronize()
+        out = c.cpu().numpy().view(np.uint16)
+        assert np.all(out == 0), "K = 0 must write +0"
+    c = torch.full((0, 40), 1.0, dtype=torch.float16, device="cuda")
+    tg.gemm_f16(torch.empty((0, 5), dtype=torch.float16, device="cuda"),
+                torch.empty((5, 40), dtype=torch.float16, device="cuda"), c)
+    torch.cuda.synchronize()
+
+
+def test_max_leading_dimension():
+    """lda at the documented maximum (2^22 elements): buffer ranges stay below 2^31 bytes."""
+    torch = torch_cuda()
+    M, N, K = 3, 128, 64
+    lda = 1 << 22
+    A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=12)
+    a_big = torch.zeros(((M - 1) * lda + K,), dtype=torch.float16, device="cuda")
+    for i in range(M):
+        a_big[i * lda:i * lda + K] = to_dev(A[i])
+    a = a_big.as_strided((M, K), (lda, 1))
+    b = to_dev(B)
+    for cfg in [None] + _fast_cfgs():
+        log(f"max lda cfg={cfg}")
+        c = tg.gemm_f16(a, b, relu=False, cfg=cfg)
+        torch.cuda.synchronize()
+        assert_close(c.cpu().numpy().view(np.uint16), oracle.gemm(A, B, False), K)
+
+
+def test_pages_own_check():
+    """The pages' own acceptance check on their 1024^3 example: close to relu(a @ b) at
+    rtol = atol = 1e-2, with the reference product taken in float32 on the CPU."""
+    torch = torch_cuda()
+    a = torch.randn(1024, 1024, generator=torch.Generator().manual_seed(0)).half()
+    b = torch.randn(1024, 1024, generator=torch.Generator().manual_seed(1)).half()
+    log("pages' check 1024^3")
+    c = tg.gemm_f16(a.cuda(), b.cuda(), relu=True)
+    ref = torch.relu(a.float() @ b.float()).half()
+    torch.testing.assert_close(c.cpu(), ref, rtol=1e-2, atol=1e-2)

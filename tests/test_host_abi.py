@@ -1,0 +1,168 @@
+"""libtgemm on the CPU: the C-ABI library loads and exports every symbol the header
+declares; argument validation, error codes, config selection and the workgroup -> tile
+map are checked without any GPU work (every call here returns before touching HIP)."""
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_04_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(tg.LIBRARY):
+        from tiled_dense_gemm_04_amd import build
+        build.build()
+    tg.lib()
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    text = text.replace("#define TGEMM_API __attribute__((visibility(\"default\")))", "")
+    return sorted(set(re.findall(r"^TGEMM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_header_symbol():
+    syms = header_symbols()
+    assert len(syms) == 9, syms
+    assert sorted(tg.EXPORTS) == syms
+    L = tg.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_only_header_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", tg.LIBRARY], capture_output=True, text=True,
+                         check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    ours = {n for n in names if n.startswith(("gemm_", "tgemm_"))}
+    assert ours == set(header_symbols())
+
+
+def test_error_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    codes = dict((m.group(1), int(m.group(2)))
+                 for m in re.finditer(r"#define (TGEMM_E\w+|TGEMM_OK)\s+\(?(-?\d+)\)?", text))
+    for name, val in codes.items():
+        assert getattr(tg, name) == val, name
+    for val in codes.values():
+        assert tg.tgemm_strerror(val) != "unknown error code"
+    assert tg.tgemm_strerror(12345) == "unknown error code"
+    assert "gfx950" in tg.tgemm_version()
+
+
+def test_config_table():
+    n = tg.tgemm_num_configs()
+    assert n >= 2
+    cfgs = tg.configs()
+    assert cfgs[0]["generic"] == 1
+    for c in cfgs[1:]:
+        assert c["generic"] == 0
+        assert c["lds_bytes"] <= 160 * 1024
+        assert c["lds_bytes"] == c["stages"] * (c["block_m"] * c["block_k"] + c["block_k"] * c["block_n"]) * 2
+        assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
+        assert c["block_n"] >= 128 and c["block_k"] in (32, 64, 128)
+        threads = 64 * c["waves_m"] * c["waves_n"]
+        assert (c["block_m"] * c["block_k"] // 8) % threads == 0
+        assert (c["block_k"] * c["block_n"] // 8) % threads == 0
+        assert c["name"].startswith("t%dx%dx%d" % (c["block_m"], c["block_n"], c["block_k"]))
+    with pytest.raises(tg.TgemmError):
+        tg.tgemm_config_desc(n)
+    with pytest.raises(tg.TgemmError):
+        tg.tgemm_config_desc(-1)
+
+
+A16 = 0x100000  # a fake, 16-byte-aligned address; select_config never dereferences
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 8, 8), tg.TGEMM_EINVAL_DIM),
+    ((8, -1, 8), tg.TGEMM_EINVAL_DIM),
+    ((8, 8, -1), tg.TGEMM_EINVAL_DIM),
+    ((1 << 31, 8, 8), tg.TGEMM_EINVAL_DIM),
+])
+def test_select_rejects_bad_dims(args, code):
+    M, N, K = args
+    assert tg.tgemm_select_config(M, N, K, A16, max(1, K), A16, max(1, N), A16, max(1, N)) == code
+
+
+def test_select_rejects_bad_ld_null_align():
+    s = tg.tgemm_select_config
+    assert s(8, 8, 8, A16, 7, A16, 8, A16, 8) == tg.TGEMM_EINVAL_LD
+    assert s(8, 8, 8, A16, 8, A16, 7, A16, 8) == tg.TGEMM_EINVAL_LD
+    assert s(8, 8, 8, A16, 8, A16, 8, A16, 7) == tg.TGEMM_EINVAL_LD
+    assert s(8, 8, 8, A16, (1 << 22) + 8, A16, 8, A16, 8) == tg.TGEMM_EINVAL_LD
+    assert s(8, 8, 8, A16, 1 << 22, A16, 8, A16, 8) >= 0
+    assert s(8, 8, 8, 0, 8, A16, 8, A16, 8) == tg.TGEMM_ENULL
+    assert s(8, 8, 8, A16, 8, 0, 8, A16, 8) == tg.TGEMM_ENULL
+    assert s(8, 8, 8, A16, 8, A16, 8, 0, 8) == tg.TGEMM_ENULL
+    assert s(8, 8, 8, A16 + 1, 8, A16, 8, A16, 8) == tg.TGEMM_EALIGN
+    assert s(8, 8, 8, A16, 8, A16, 8, A16 + 3, 8) == tg.TGEMM_EALIGN
+    # empty output: no pointers needed; K == 0: only C is needed
+    assert s(0, 8, 8, 0, 8, 0, 8, 0, 8) == tg.SELECT_NOOP
+    assert s(8, 0, 8, 0, 8, 0, 1, 0, 1) == tg.SELECT_NOOP
+    assert s(8, 8, 0, 0, 1, 0, 8, A16, 8) == tg.SELECT_ZERO_FILL
+    assert s(8, 8, 0, 0, 1, 0, 8, 0, 8) == tg.TGEMM_ENULL
+
+
+def test_select_fast_vs_generic():
+    s = tg.tgemm_select_config
+    big = s(4096, 4096, 4096, A16, 4096, A16, 4096, A16, 4096)
+    assert big > 0 and tg.tgemm_config_desc(big)["generic"] == 0
+    # misaligned pointer (2-byte aligned only), odd ld, K or N not a multiple of 8 -> generic
+    assert s(4096, 4096, 4096, A16 + 2, 4096, A16, 4096, A16, 4096) == 0
+    assert s(4096, 4096, 4096, A16, 4100, A16, 4096, A16, 4096) == 0
+    assert s(4096, 4096, 4095, A16, 4096, A16, 4096, A16, 4096) == 0
+    assert s(4096, 4094, 4096, A16, 4096, A16, 4096, A16, 4096) == 0
+    # ragged M is fine for the fast path
+    assert s(4095, 3000, 1000, A16, 1000, A16, 3000, A16, 3000) > 0
+
+
+def test_gemm_rejects_invalid_before_hip():
+    # invalid arguments are reported before any HIP call (works with no GPU present)
+    assert tg.gemm_f16_raw(-1, 8, 8, A16, 8, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_DIM
+    assert tg.gemm_f16_raw(8, 8, 8, A16, 4, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_LD
+    assert tg.gemm_f16_raw(8, 8, 8, 0, 8, A16, 8, A16, 8, 1, None) == tg.TGEMM_ENULL
+    assert tg.gemm_f16_raw(0, 8, 8, 0, 8, 0, 8, 0, 8, 1, None) == tg.TGEMM_OK  # no-op
+    assert tg.gemm_f16_cfg_raw(99, 8, 8, 8, A16, 8, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_CFG
+    assert tg.gemm_f16_cfg_raw(1, 8, 8, 8, A16 + 2, 8, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_CFG
+
+
+SHAPES = [(1, 1), (255, 257), (256, 256), (1024, 1024), (4096, 4096), (4095, 3000), (8192, 8192),
+          (16384, 512), (3000, 4095), (1000, 64), (64, 1000), (2304, 2304), (513, 129)]
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_tile_map_is_bijection(M, N):
+    for idx in range(tg.tgemm_num_configs()):
+        c = tg.tgemm_config_desc(idx)
+        tm = -(-M // c["block_m"])
+        tn = -(-N // c["block_n"])
+        nwg = tg.tgemm_num_workgroups(idx, M, N)
+        assert nwg == tm * tn
+        if nwg > 70000:
+            continue
+        seen = set()
+        for wg in range(nwg):
+            t = tg.tgemm_tile_of(idx, M, N, wg)
+            assert 0 <= t[0] < tm and 0 <= t[1] < tn, (idx, wg, t)
+            seen.add(t)
+        assert len(seen) == nwg, (idx, M, N)
+        with pytest.raises(tg.TgemmError):
+            tg.tgemm_tile_of(idx, M, N, nwg)
+
+
+def test_tile_map_keeps_xcd_tiles_together():
+    """With the XCD remap, the tiles one XCD runs (hardware ids x, x+8, x+16, ...) form
+    a compact block: at 4096^2 with 256^2 tiles each XCD gets a 4 x 8 block."""
+    idx = next(i for i, c in enumerate(tg.configs())
+               if (c["block_m"], c["block_n"], c["xcd_remap"], c["panel"]) == (256, 256, 1, 4))
+    for x in range(8):
+        tiles = [tg.tgemm_tile_of(idx, 4096, 4096, wg) for wg in range(x, 256, 8)]
+        rows = {t[0] for t in tiles}
+        cols = {t[1] for t in tiles}
+        assert len(tiles) == 32 and len(rows) == 4 and len(cols) == 8, (x, rows, cols)

@@ -1,0 +1,213 @@
+// tgemm_api.cpp -- host side of the libtgemm C ABI (declared in include/tgemm.h):
+// argument validation, the per-device architecture check, config selection and launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/tgemm.h"
+#include "tgemm_internal.h"
+
+namespace {
+
+using tgemm::Config;
+
+int table_size() {
+  int n = 0;
+  tgemm::config_table(&n);
+  return n;
+}
+const Config& cfg_row(int idx) {
+  int n = 0;
+  return tgemm::config_table(&n)[idx];
+}
+
+constexpr int kSelectNoop = -100;      // M == 0 or N == 0
+constexpr int kSelectZeroFill = -101;  // K == 0
+constexpr int kMaxDevices = 64;
+
+int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, const void* C, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0 || M >= TGEMM_MAX_DIM || N >= TGEMM_MAX_DIM || K >= TGEMM_MAX_DIM)
+    return TGEMM_EINVAL_DIM;
+  const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
+  if (lda < kmin || ldb < nmin || ldc < nmin) return TGEMM_EINVAL_LD;
+  if (lda > TGEMM_MAX_LD || ldb > TGEMM_MAX_LD || ldc > TGEMM_MAX_LD) return TGEMM_EINVAL_LD;
+  const bool out_nonempty = M > 0 && N > 0;
+  if (out_nonempty && C == nullptr) return TGEMM_ENULL;
+  if (out_nonempty && K > 0 && (A == nullptr || B == nullptr)) return TGEMM_ENULL;
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) |
+       reinterpret_cast<uintptr_t>(C)) & 1u)
+    return TGEMM_EALIGN;
+  return TGEMM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Can a fast (non-generic) config take these arguments?
+bool fast_eligible(int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                   const void* C, int64_t ldc) {
+  return aligned16(A) && aligned16(B) && aligned16(C) && (lda % 8) == 0 && (ldb % 8) == 0 &&
+         (ldc % 8) == 0 && (K % 8) == 0 && (N % 8) == 0;
+}
+
+int64_t workgroups(const Config& c, int64_t M, int64_t N) {
+  return tgemm::ceil_div(M, c.bm) * tgemm::ceil_div(N, c.bn);
+}
+
+// Config choice for a fast-eligible call. Large outputs take the 256 x 256 tile, which
+// gives each workgroup the most MFMA work per byte staged through LDS; smaller outputs
+// fall back to tiles that still put a workgroup on (nearly) every compute unit.
+int choose_fast(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  const int64_t t256 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256);
+  const int64_t t256x128 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 128);
+  if (t256 >= 224) return 1;
+  if (t256x128 >= 224) return 2;
+  return 3;
+}
+
+int select(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+           int64_t ldb, const void* C, int64_t ldc) {
+  const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
+  if (v != TGEMM_OK) return v;
+  if (M == 0 || N == 0) return kSelectNoop;
+  if (K == 0) return kSelectZeroFill;
+  if (fast_eligible(N, K, A, lda, B, ldb, C, ldc)) return choose_fast(M, N, K);
+  return 0;
+}
+
+// Once per device: is it gfx950? 0 = unknown, 1 = yes, 2 = no.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device(int* device_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TGEMM_EDEVICE;
+  *device_out = dev;
+  if (dev >= kMaxDevices) return TGEMM_EDEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TGEMM_EDEVICE;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? TGEMM_OK : TGEMM_EDEVICE;
+}
+
+int run(int cfg, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+        int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+  int dev = -1;
+  const int d = check_device(&dev);
+  if (d != TGEMM_OK) return d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg == kSelectZeroFill) {
+    return tgemm::launch_zero_fill(static_cast<_Float16*>(C), (int)M, (int)N, ldc, s) == hipSuccess
+               ? TGEMM_OK
+               : TGEMM_ELAUNCH;
+  }
+  const Config& c = cfg_row(cfg);
+  const int64_t nwg = workgroups(c, M, N);
+  if (nwg >= ((int64_t)1 << 31)) return TGEMM_EINVAL_DIM;
+  tgemm::GemmArgs g;
+  g.A = static_cast<const _Float16*>(A);
+  g.B = static_cast<const _Float16*>(B);
+  g.C = static_cast<_Float16*>(C);
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.relu = relu != 0;
+  g.tiles_m = (int)tgemm::ceil_div(M, c.bm);
+  g.tiles_n = (int)tgemm::ceil_div(N, c.bn);
+  return tgemm::launcher(cfg)(g, s, dev) == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+  const int cfg = select(M, N, K, A, lda, B, ldb, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
+  return run(cfg, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+}
+
+int gemm_f16_cfg(int idx, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                 const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+  if (idx < 0 || idx >= table_size()) return TGEMM_EINVAL_CFG;
+  const int cfg = select(M, N, K, A, lda, B, ldb, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
+  if (cfg == kSelectZeroFill) return run(cfg, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  if (!cfg_row(idx).generic && !fast_eligible(N, K, A, lda, B, ldb, C, ldc))
+    return TGEMM_EINVAL_CFG;
+  return run(idx, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+}
+
+int tgemm_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, const void* C, int64_t ldc) {
+  return select(M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+const char* tgemm_strerror(int code) {
+  switch (code) {
+    case TGEMM_OK: return "success";
+    case TGEMM_EINVAL_DIM: return "invalid dimension (negative, >= 2^31, or too many tiles)";
+    case TGEMM_EINVAL_LD: return "invalid leading dimension (below the row length or above 2^22)";
+    case TGEMM_ENULL: return "null pointer for a non-empty operand";
+    case TGEMM_EDEVICE: return "current HIP device is not gfx950 (MI355X) or is unavailable";
+    case TGEMM_ELAUNCH: return "kernel launch failed";
+    case TGEMM_EINVAL_CFG: return "invalid config index, or config cannot take these arguments";
+    case TGEMM_EALIGN: return "operand pointer not aligned to 2 bytes";
+    default: return "unknown error code";
+  }
+}
+
+const char* tgemm_version(void) { return "libtgemm 0.1.0 (gfx950)"; }
+
+int tgemm_num_configs(void) { return table_size(); }
+
+int tgemm_config_desc(int idx, tgemm_config_info* out) {
+  if (out == nullptr) return TGEMM_ENULL;
+  if (idx < 0 || idx >= table_size()) return TGEMM_EINVAL_CFG;
+  const Config& c = cfg_row(idx);
+  std::memset(out, 0, sizeof(*out));
+  out->block_m = c.bm;
+  out->block_n = c.bn;
+  out->block_k = c.bk;
+  out->stages = c.stages;
+  out->waves_m = c.waves_m;
+  out->waves_n = c.waves_n;
+  out->panel = c.panel;
+  out->xcd_remap = c.xcd_remap;
+  out->generic = c.generic;
+  out->lds_bytes = c.generic ? 0 : c.stages * (c.bm * c.bk + c.bk * c.bn) * 2;
+  std::strncpy(out->name, c.name, sizeof(out->name) - 1);
+  return TGEMM_OK;
+}
+
+int64_t tgemm_num_workgroups(int idx, int64_t M, int64_t N) {
+  if (idx < 0 || idx >= table_size() || M < 0 || N < 0) return -1;
+  return workgroups(cfg_row(idx), M, N);
+}
+
+int tgemm_tile_of(int idx, int64_t M, int64_t N, int64_t wg, int64_t* tile_m, int64_t* tile_n) {
+  if (idx < 0 || idx >= table_size()) return TGEMM_EINVAL_CFG;
+  if (tile_m == nullptr || tile_n == nullptr) return TGEMM_ENULL;
+  const Config& c = cfg_row(idx);
+  const int64_t tm = tgemm::ceil_div(M, c.bm), tn = tgemm::ceil_div(N, c.bn);
+  if (M <= 0 || N <= 0 || wg < 0 || wg >= tm * tn) return TGEMM_EINVAL_DIM;
+  // The generic kernel runs the plain row-panel order (panel 1, no XCD remap).
+  const int panel = c.generic ? 1 : c.panel;
+  const int xcd = c.generic ? 0 : c.xcd_remap;
+  tgemm::tile_of(wg, tm, tn, panel, xcd, tile_m, tile_n);
+  return TGEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// tgemm_internal.h -- shared between the HIP kernels and the host API of libtgemm.
+//
+// Holds the kernel-configuration table and the workgroup -> output-tile map. The map is
+// one inline function compiled for both the device (the kernels call it) and the host
+// (tgemm_tile_of exports it for tests), so the tested map is the executed map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tgemm {
+
+// Number of XCDs on MI355X; the hardware dispatcher hands consecutive workgroup ids to
+// XCDs round robin, and each XCD has its own L2.
+constexpr int kNumXcd = 8;
+
+// Work-group tile configuration (one compiled kernel instantiation per entry).
+struct Config {
+  int bm, bn, bk;       // workgroup tile
+  int stages;           // LDS ring depth
+  int waves_m, waves_n; // wavefront grid
+  int panel;            // tile-rows per panel in the workgroup order
+  int xcd_remap;        // keep consecutive logical tiles on one XCD
+  int generic;          // unaligned-capable generic kernel
+  const char* name;
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroup id -> output tile (tile_m, tile_n).
+//
+// Step 1 (XCD remap): hardware workgroup id `wg` runs on XCD wg % 8. Renumber so that each
+// XCD receives a contiguous range of logical ids: XCD x takes logical ids
+// [x*q + min(x, r), ...) where total = 8q + r. A bijection for every total.
+// Step 2 (panel order): logical ids walk the tile grid in panels of `panel` tile-rows;
+// inside a panel the tile-row index moves fastest, then the tile-column. Consecutive
+// logical ids therefore share B columns and a small set of A rows, so the tiles one XCD
+// runs at the same time re-use each other's operands from that XCD's L2. This is the
+// panel-ordered block swizzle of "Writing High-Performance Kernels in TileLang, from
+// GEMM to MLA" (atlascloud.ai), section "Let's write a GEMM" (use_swizzle with a panel
+// size and column order), made XCD-aware for MI355X.
+__host__ __device__ inline void tile_of(int64_t wg, int64_t tiles_m, int64_t tiles_n, int panel,
+                                        int xcd_remap, int64_t* tm, int64_t* tn) {
+  const int64_t total = tiles_m * tiles_n;
+  int64_t t = wg;
+  if (xcd_remap && total >= kNumXcd) {
+    const int64_t q = total / kNumXcd, r = total % kNumXcd;
+    const int64_t x = wg % kNumXcd, j = wg / kNumXcd;
+    t = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+  }
+  if (panel < 1) panel = 1;
+  const int64_t per_panel = (int64_t)panel * tiles_n;
+  const int64_t p = t / per_panel;
+  const int64_t within = t - p * per_panel;
+  int64_t rows = tiles_m - p * panel;
+  if (rows > panel) rows = panel;
+  *tm = p * panel + within % rows;
+  *tn = within / rows;
+}
+
+// Kernel arguments (passed by value).
+struct GemmArgs {
+  const _Float16* A;
+  const _Float16* B;
+  _Float16* C;
+  int64_t lda, ldb, ldc;  // elements
+  int M, N, K;
+  int relu;
+  int tiles_m, tiles_n;
+};
+
+// The table (host only). Index order is part of the tooling ABI (gemm_f16_cfg, sweep
+// results); *count receives the number of rows.
+const Config* config_table(int* count);
+
+// Launcher of table row idx (defined next to the kernels). Returns the hipError_t of the
+// launch. `device` is the current HIP device ordinal (the device the launch goes to).
+typedef hipError_t (*Launcher)(const GemmArgs&, hipStream_t, int device);
+Launcher launcher(int idx);
+
+// Zero-fill of an M x N block with row stride ldc (the K == 0 case).
+hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s);
+
+}  // namespace tgemm

@@ -1,0 +1,443 @@
+// tgemm_kernels.hip -- gfx950 kernels of libtgemm: C = ReLU?(A @ B), fp16 in, fp32
+// accumulate, fp16 out, all row-major.
+//
+// The computation follows "Writing High-Performance Kernels in TileLang, from GEMM to
+// MLA" (atlascloud.ai), section "Let's write a GEMM": a workgroup owns a block_M x
+// block_N tile of C, clears a float32 accumulator, walks K in block_K steps through a
+// multi-stage shared-memory pipeline (global -> shared copies of the A and B tiles, then a
+// tile-level matrix multiply), applies max(x, 0) and writes the tile back as fp16.
+// What is MI355X-specific here (and not on the pages):
+//   * global -> LDS copies are buffer loads that write LDS directly (no VGPR staging);
+//     the buffer descriptor's range check turns every out-of-matrix chunk into zeros,
+//     which is how edge tiles are predicated;
+//   * LDS tiles are XOR-swizzled for the 64 LDS banks of gfx950;
+//   * B (row-major, N contiguous) is read from LDS with ds_read_b64_tr_b16, which
+//     transposes 4x4 blocks of 16-bit values across lanes, so no transpose pass is needed;
+//   * 32x32x16 fp16 MFMAs accumulate in fp32; operands are fed as (B^T, A^T) so that each
+//     lane ends up holding four consecutive output columns, stored as one 8-byte write;
+//   * the workgroup order is XCD-aware and panel-ordered (tile_of in tgemm_internal.h).
+#include "tgemm_internal.h"
+
+#include <atomic>
+
+namespace tgemm {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+#define TG_LDS __attribute__((address_space(3)))
+
+// Buffer offset that lies beyond every descriptor range used here (all ranges are kept
+// below 2^31 bytes), so a load at this offset returns zeros.
+constexpr uint32_t kOob = 0x80000000u;
+constexpr uint32_t kMaxRange = 0x7FFFFFF0u;
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
+constexpr int kBufWord3 = 0x00020000;
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt and lgkmcnt at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS reads/writes, then
+// s_barrier. Outstanding buffer->LDS loads of later stages stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base address, stride 0, range in bytes, gfx9 word 3. All inputs
+// are wave-uniform, so it lives in four SGPRs.
+__device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t range_bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  int4v r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)range_bytes);
+  r[3] = kBufWord3;
+  return r;
+}
+
+// One 16-byte buffer load per lane written straight to LDS: lane u's 16 bytes land at
+// LDS byte lds_base + 16*u; a lane whose offset is outside the descriptor range writes
+// zeros. Written as inline assembly so that the compiler does not treat the LDS write
+// as pending before unrelated LDS reads (it cannot tell the ring slots apart and would
+// wait for every copy in flight); completion is awaited explicitly with wait_vmcnt.
+// M0 carries the LDS base; the kernels use M0 for nothing else (no indirect register
+// indexing, no messages), so clobbering it is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_to_lds(const int4v& rsrc, uint32_t lds_base, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const TG_LDS char*)p;
+}
+
+// ------------------------------------------------------------------------------------
+// LDS layouts of the fast kernel.
+//
+// A stage: BM rows x BK halves, row r at byte r*BK*2, split in 16-byte chunks; logical
+// chunk c of row r is stored at chunk c ^ swz_a(r). A fragment read (ds_read_b128) has 16
+// lanes on 16 consecutive rows and the same logical chunk; with 64 banks x 4 bytes a
+// 256-byte bank window holds 128/BK rows, and the XOR spreads the 16 rows over the 16
+// chunk slots of the window.
+template <int BK>
+__host__ __device__ constexpr int swz_a(int r) {
+  return (r / (128 / BK)) % (BK / 8);
+}
+// B stage: BK rows (k) x BN halves (n), row k at byte k*BN*2 (a multiple of 256 bytes);
+// logical chunk c of row k is stored at chunk c ^ swz_b(k). A transposed read by 32 lanes
+// touches 4 consecutive k rows x 4 consecutive chunks (c0 % 4 == 0); XOR by 4*(k%4) puts
+// the 16 (row, chunk) pairs on 16 distinct 16-byte slots of the bank window.
+__host__ __device__ constexpr int swz_b(int k) { return 4 * (k & 3); }
+
+// ------------------------------------------------------------------------------------
+// Fast kernel: BM x BN x BK tile, WM x WN waves, STAGES-deep LDS ring fed by buffer->LDS
+// loads. Requirements (checked by the host): A, B, C 16-byte aligned; lda, ldb, ldc,
+// K and N multiples of 8; K > 0.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int A_CH_ROW = BK / 8, B_CH_ROW = BN / 8;
+  constexpr int A_UNITS = BM * A_CH_ROW, B_UNITS = BK * B_CH_ROW;
+  constexpr int A_LD = A_UNITS / NT, B_LD = B_UNITS / NT;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+  static_assert(A_UNITS % NT == 0 && B_UNITS % NT == 0, "loads must split evenly");
+  static_assert(BK % 16 == 0 && BK >= 32 && BK <= 128, "block_k");
+  static_assert(BN >= 128 && (BN * 2) % 256 == 0, "B rows must span the bank window");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(A_LD + B_LD <= 16, "vmcnt budget");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const a_lds = smem;
+  char* const b_lds = smem + STAGES * A_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int64_t tm64, tn64;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
+  const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
+  const int K = g.K;
+
+  // Per-thread buffer offsets (bytes) of each chunk this thread copies, relative to the
+  // tile's base at k0 = 0. Load i of wave w fills LDS bytes [(i*NW + w) * 1024, +1024):
+  // lane u writes chunk slot (i*NW + w)*64 + u.
+  uint32_t a_off[A_LD];
+  int a_kc[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int u = (i * NW + wave) * 64 + lane;
+    const int r = u / A_CH_ROW;
+    const int c = (u % A_CH_ROW) ^ swz_a<BK>(r);
+    a_kc[i] = 8 * c;
+    a_off[i] = (r < mvalid) ? (uint32_t)(((int64_t)r * g.lda + 8 * c) * 2) : kOob;
+  }
+  uint32_t b_off[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int u = (i * NW + wave) * 64 + lane;
+    const int k = u / B_CH_ROW;
+    const int c = (u % B_CH_ROW) ^ swz_b(k);
+    b_off[i] = (8 * c < nvalid) ? (uint32_t)(((int64_t)k * g.ldb + 8 * c) * 2) : kOob;
+  }
+  const _Float16* const a_tile = g.A + (int64_t)row0 * g.lda;
+  const _Float16* const b_tile = g.B + col0;
+  const int nk = (K + BK - 1) / BK;
+
+  // Issue the buffer->LDS copies of k-tile kt into ring slot `slot`.
+  auto issue = [&](int kt, int slot) {
+    const int k0 = kt * BK;
+    const int krem = K - k0;  // > 0
+    const int kin = krem < BK ? krem : BK;
+    // A: rows < mvalid, columns < kin are in range. The last row's range ends at kin;
+    // columns >= kin of the other rows are masked below (only in a K-tail tile).
+    const int64_t a_range = ((int64_t)(mvalid - 1) * g.lda + kin) * 2;
+    const int4v ra = make_rsrc(a_tile + k0, (uint32_t)(a_range < kMaxRange ? a_range : kMaxRange));
+    // B: rows < kin, columns < nvalid; rows >= kin fall past the range and read as zero.
+    const int64_t b_range = ((int64_t)(kin - 1) * g.ldb + nvalid) * 2;
+    const int4v rb = make_rsrc(b_tile + (int64_t)k0 * g.ldb,
+                               (uint32_t)(b_range < kMaxRange ? b_range : kMaxRange));
+    const uint32_t a_dst = lds_addr(a_lds) + slot * A_BYTES + wave * 1024;
+    const uint32_t b_dst = lds_addr(b_lds) + slot * B_BYTES + wave * 1024;
+    if (kin == BK) {
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) dma_to_lds(ra, a_dst + i * NW * 1024, a_off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) dma_to_lds(ra, a_dst + i * NW * 1024, a_kc[i] < kin ? a_off[i] : kOob);
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) dma_to_lds(rb, b_dst + i * NW * 1024, b_off[i]);
+  };
+
+  // Wave position and per-lane LDS read offsets.
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  // A fragment (32 rows x 16 k): lane reads row wm*WTM + fm*32 + l32, k chunk 2*ks + lhi.
+  const int a_row_off = (wm * WTM + l32) * BK * 2;
+  const int a_sw = swz_a<BK>(l32);  // fm*32 and wm*WTM are multiples of the swizzle period
+  // B fragment (16 k x 32 n) via two transposed reads; lane = 16g + 4j + q.
+  const int bg = lane >> 4, bj = (lane >> 2) & 3, bq = lane & 3;
+  const int b_krow = 8 * (bg >> 1) + bj;                         // + 16*ks + 4*h
+  const int b_chunk = (wn * WTN) / 8 + 2 * (bg & 1) + (bq >> 1);  // + 4*fn
+  const int b_half = (bq & 1) * 8;
+
+  float16v acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // LDS -> VGPR fragments of k-substep ks (16 k values) of ring slot `slot`.
+  auto load_frags = [&](int slot, int ks, half8 (&af)[FM], half8 (&bf)[FN]) {
+    const char* const As = a_lds + slot * A_BYTES;
+    const char* const Bs = b_lds + slot * B_BYTES;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int off = a_row_off + fm * 32 * BK * 2 + (((2 * ks + lhi) ^ a_sw) << 4);
+      af[fm] = *(const TG_LDS half8*)(As + off);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      short4v part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = 16 * ks + 4 * h + b_krow;
+        const int off = k * BN * 2 + (((b_chunk + 4 * fn) ^ swz_b(k)) << 4) + b_half;
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(Bs + off));
+      }
+      const short8v s8 = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      bf[fn] = __builtin_bit_cast(half8, s8);
+    }
+  };
+  auto mma = [&](const half8 (&af)[FM], const half8 (&bf)[FN]) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[fn], af[fm], acc[fm][fn], 0, 0, 0);
+  };
+  // One k-tile: fragments of substep ks+1 are read while the MFMAs of substep ks run.
+  auto compute = [&](int slot) {
+    half8 af[2][FM];
+    half8 bf[2][FN];
+    load_frags(slot, 0, af[0], bf[0]);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) load_frags(slot, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(af[ks & 1], bf[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Pipeline: STAGES-1 tiles in flight ahead of the one being multiplied.
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
+  constexpr int PER_TILE = A_LD + B_LD;
+  for (int kt = 0; kt < nk; ++kt) {
+    // Tile kt has landed once at most min(STAGES-2, nk-1-kt) later tiles are in flight.
+    const int ahead = nk - 1 - kt;
+    if (STAGES >= 4 && ahead >= 2)
+      wait_vmcnt<(STAGES >= 4 ? 2 : 0) * PER_TILE>();
+    else if (STAGES >= 3 && ahead >= 1)
+      wait_vmcnt<(STAGES >= 3 ? 1 : 0) * PER_TILE>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    compute(kt % STAGES);
+  }
+
+  // Epilogue: ReLU in fp32, round to fp16 (nearest even), 8-byte stores. Lane holds, for
+  // tile (fm, fn) and group g4, row m = ... + l32 and columns n = ... + 8*g4 + 4*lhi + 0..3.
+  const bool relu = g.relu != 0;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = wm * WTM + fm * 32 + l32;
+    if (m >= mvalid) continue;
+    _Float16* const crow = g.C + (int64_t)(row0 + m) * g.ldc + col0;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int n = wn * WTN + fn * 32 + 8 * g4 + 4 * lhi;
+        if (n >= nvalid) continue;
+        float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
+        float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
+        if (relu) {
+          v0 = relu_f(v0);
+          v1 = relu_f(v1);
+          v2 = relu_f(v2);
+          v3 = relu_f(v3);
+        }
+        half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+        *(half4*)(crow + n) = h;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Generic kernel: 64 x 64 x 32 tile, 4 waves (2 x 2 of 32 x 32), element-wise predicated
+// loads (any 2-byte-aligned pointers, any strides and sizes). A is staged as [m][k] and B
+// transposed to [n][k] in LDS so both fragments are plain 16-byte reads.
+constexpr int GB_M = 64, GB_N = 64, GB_K = 32, G_PAD = 8;
+
+__global__ __launch_bounds__(256) void gemm_generic(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[GB_M][GB_K + G_PAD];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[GB_N][GB_K + G_PAD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, 1, 0, &tm, &tn);
+  const int row0 = (int)tm * GB_M, col0 = (int)tn * GB_N;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lhi = lane >> 5;
+
+  float16v acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+  for (int k0 = 0; k0 < g.K; k0 += GB_K) {
+#pragma unroll
+    for (int e = 0; e < (GB_M * GB_K) / 256; ++e) {
+      const int idx = tid + 256 * e;
+      const int r = idx / GB_K, kk = idx % GB_K;
+      const int gr = row0 + r, gk = k0 + kk;
+      As[r][kk] = (gr < g.M && gk < g.K) ? g.A[(int64_t)gr * g.lda + gk] : (_Float16)0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < (GB_K * GB_N) / 256; ++e) {
+      const int idx = tid + 256 * e;
+      const int kk = idx / GB_N, n = idx % GB_N;
+      const int gk = k0 + kk, gc = col0 + n;
+      Bs[n][kk] = (gk < g.K && gc < g.N) ? g.B[(int64_t)gk * g.ldb + gc] : (_Float16)0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < GB_K / 16; ++ks) {
+      const half8 a = *(const half8*)&As[wm * 32 + l32][16 * ks + 8 * lhi];
+      const half8 b = *(const half8*)&Bs[wn * 32 + l32][16 * ks + 8 * lhi];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  const int m = row0 + wm * 32 + l32;
+  if (m >= g.M) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int n = col0 + wn * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
+    if (n < g.N) {
+      const float v = g.relu ? relu_f(acc[r]) : acc[r];
+      g.C[(int64_t)m * g.ldc + n] = (_Float16)v;
+    }
+  }
+}
+
+// C[i, j] = +0 for i < M, j < N (the empty sum when K == 0).
+__global__ __launch_bounds__(256) void zero_fill(_Float16* C, int M, int N, int64_t ldc) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = t / N, j = t - i * N;
+    C[i * ldc + j] = (_Float16)0.0f;
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
+hipError_t launch_fast(const GemmArgs& g, hipStream_t s, int device) {
+  constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
+  auto kern = gemm_fast<BM, BN, BK, WM, WN, STAGES, PANEL, XCD>;
+  // Opt in to more than 64 KiB of dynamic LDS, once per device.
+  static std::atomic<uint64_t> ready{0};
+  const uint64_t bit = 1ull << (device & 63);
+  if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * WM * WN), lds, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_generic(const GemmArgs& g, hipStream_t s, int) {
+  const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL(gemm_generic, dim3((unsigned)nwg), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s) {
+  const int64_t total = (int64_t)M * N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_fill, dim3((unsigned)blocks), dim3(256), 0, s, C, M, N, ldc);
+  return hipGetLastError();
+}
+
+// The config table: one X-macro list drives both the table rows and the kernel
+// instantiations, so a row always describes the kernel it launches.
+//   X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP)
+#define TGEMM_FAST_CONFIGS(X)      \
+  X(256, 256, 64, 2, 4, 2, 4, 1)   \
+  X(256, 128, 64, 2, 2, 2, 4, 1)   \
+  X(128, 128, 64, 2, 2, 2, 4, 1)   \
+  X(128, 128, 64, 2, 2, 3, 4, 1)   \
+  X(256, 256, 32, 2, 4, 4, 4, 1)
+
+#define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_fast<BM, BN, BK, WM, WN, S, P, X>,
+#define TGEMM_COUNT(BM, BN, BK, WM, WN, S, P, X) 0,
+
+// Function-local statics: host-only tables (the device pass parses these bodies, which
+// instantiates every kernel, but emits no host data).
+const Config* config_table(int* count) {
+  static const Config table[] = {
+      {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, "generic_64x64x32"},
+      TGEMM_FAST_CONFIGS(TGEMM_ROW)};
+  *count = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+Launcher launcher(int idx) {
+  static const Launcher table[] = {launch_generic, TGEMM_FAST_CONFIGS(TGEMM_LAUNCHER)};
+  static_assert(sizeof(table) / sizeof(table[0]) ==
+                    1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT)}) / sizeof(int),
+                "one launcher per config");
+  return table[idx];
+}
+
+}  // namespace tgemm
