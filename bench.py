@@ -65,12 +65,14 @@ def cpu_baseline(A, B, relu, c_gpu_bits, target_s: float):
     threads = orc.max_threads()
     M, K = A.shape
     N = B.shape[1]
-    r0 = 8
-    t = time.perf_counter()
-    orc.gemm(A[:r0], B, relu)
-    dt = time.perf_counter() - t
-    rate = 2.0 * r0 * N * K / max(dt, 1e-9)
-    rows = int(min(M, max(r0, rate * target_s / (2.0 * N * K))))
+    # calibrate on two slab sizes so the one-off decode of B cancels out of the rate
+    times = {}
+    for r in (16, 64):
+        t = time.perf_counter()
+        orc.gemm(A[:r], B, relu)
+        times[r] = time.perf_counter() - t
+    rate = 2.0 * (64 - 16) * N * K / max(times[64] - times[16], 1e-9)
+    rows = int(min(M, max(64, rate * target_s / (2.0 * N * K))))
     t = time.perf_counter()
     ref = orc.gemm(A[:rows], B, relu)
     dt = time.perf_counter() - t

@@ -69,7 +69,7 @@ def test_config_table():
         threads = 64 * c["waves_m"] * c["waves_n"]
         assert (c["block_m"] * c["block_k"] // 8) % threads == 0
         assert (c["block_k"] * c["block_n"] // 8) % threads == 0
-        assert c["name"].startswith("t%dx%dx%d" % (c["block_m"], c["block_n"], c["block_k"]))
+        assert c["name"][1:].startswith("%dx%dx%d" % (c["block_m"], c["block_n"], c["block_k"]))
     with pytest.raises(tg.TgemmError):
         tg.tgemm_config_desc(n)
     with pytest.raises(tg.TgemmError):

@@ -307,6 +307,225 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------------------
+// Pipelined kernel: same tiles, LDS layouts and edge handling as gemm_fast, but the
+// fragments of k-tile kt+1 are read from LDS into a second register set while the MFMAs
+// of k-tile kt run, interleaved instruction by instruction. After each workgroup barrier
+// a wave therefore starts issuing MFMAs at once (its fragments were loaded during the
+// previous k-tile), and the LDS ring (STAGES slots) keeps STAGES-1 k-tiles of global
+// loads in flight: at iteration kt, slot kt % STAGES (tile kt, already in registers) is
+// refilled with tile kt + STAGES while tile kt+1 is being read.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int KS = BK / 16;
+  constexpr int A_CH_ROW = BK / 8, B_CH_ROW = BN / 8;
+  constexpr int A_UNITS = BM * A_CH_ROW, B_UNITS = BK * B_CH_ROW;
+  constexpr int A_LD = A_UNITS / NT, B_LD = B_UNITS / NT;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+  constexpr int PER_TILE = A_LD + B_LD;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+  static_assert(A_UNITS % NT == 0 && B_UNITS % NT == 0, "loads must split evenly");
+  static_assert(BK % 16 == 0 && BK >= 32 && BK <= 128, "block_k");
+  static_assert(BN >= 128 && (BN * 2) % 256 == 0, "B rows must span the bank window");
+  static_assert(STAGES >= 2, "stages");
+  static_assert(PER_TILE * STAGES < 64, "vmcnt budget");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const a_lds = smem;
+  char* const b_lds = smem + STAGES * A_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int64_t tm64, tn64;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
+  const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
+  const int K = g.K;
+
+  uint32_t a_off[A_LD];
+  int a_kc[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int u = (i * NW + wave) * 64 + lane;
+    const int r = u / A_CH_ROW;
+    const int c = (u % A_CH_ROW) ^ swz_a<BK>(r);
+    a_kc[i] = 8 * c;
+    a_off[i] = (r < mvalid) ? (uint32_t)(((int64_t)r * g.lda + 8 * c) * 2) : kOob;
+  }
+  uint32_t b_off[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int u = (i * NW + wave) * 64 + lane;
+    const int k = u / B_CH_ROW;
+    const int c = (u % B_CH_ROW) ^ swz_b(k);
+    b_off[i] = (8 * c < nvalid) ? (uint32_t)(((int64_t)k * g.ldb + 8 * c) * 2) : kOob;
+  }
+  const _Float16* const a_tile = g.A + (int64_t)row0 * g.lda;
+  const _Float16* const b_tile = g.B + col0;
+  const int nk = (K + BK - 1) / BK;
+
+  auto issue = [&](int kt, int slot) {
+    const int k0 = kt * BK;
+    const int krem = K - k0;
+    const int kin = krem < BK ? krem : BK;
+    const int64_t a_range = ((int64_t)(mvalid - 1) * g.lda + kin) * 2;
+    const int4v ra = make_rsrc(a_tile + k0, (uint32_t)(a_range < kMaxRange ? a_range : kMaxRange));
+    const int64_t b_range = ((int64_t)(kin - 1) * g.ldb + nvalid) * 2;
+    const int4v rb = make_rsrc(b_tile + (int64_t)k0 * g.ldb,
+                               (uint32_t)(b_range < kMaxRange ? b_range : kMaxRange));
+    const uint32_t a_dst = lds_addr(a_lds) + slot * A_BYTES + wave * 1024;
+    const uint32_t b_dst = lds_addr(b_lds) + slot * B_BYTES + wave * 1024;
+    if (kin == BK) {
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) dma_to_lds(ra, a_dst + i * NW * 1024, a_off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) dma_to_lds(ra, a_dst + i * NW * 1024, a_kc[i] < kin ? a_off[i] : kOob);
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) dma_to_lds(rb, b_dst + i * NW * 1024, b_off[i]);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int a_row_off = (wm * WTM + l32) * BK * 2;
+  const int a_sw = swz_a<BK>(l32);
+  const int bg = lane >> 4, bj = (lane >> 2) & 3, bq = lane & 3;
+  const int b_krow = 8 * (bg >> 1) + bj;
+  const int b_chunk = (wn * WTN) / 8 + 2 * (bg & 1) + (bq >> 1);
+  const int b_half = (bq & 1) * 8;
+
+  struct Frags {
+    half8 a[KS][FM];
+    half8 b[KS][FN];
+  };
+  auto read_tile = [&](int slot, Frags& f) {
+    const char* const As = a_lds + slot * A_BYTES;
+    const char* const Bs = b_lds + slot * B_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int off = a_row_off + fm * 32 * BK * 2 + (((2 * ks + lhi) ^ a_sw) << 4);
+        f.a[ks][fm] = *(const TG_LDS half8*)(As + off);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        short4v part[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = 16 * ks + 4 * h + b_krow;
+          const int off = k * BN * 2 + (((b_chunk + 4 * fn) ^ swz_b(k)) << 4) + b_half;
+          part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(Bs + off));
+        }
+        const short8v s8 = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        f.b[ks][fn] = __builtin_bit_cast(half8, s8);
+      }
+    }
+  };
+
+  float16v acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // MFMAs of one k-tile from `cur` with the LDS reads of the next k-tile (slot `nslot`)
+  // into `nxt`, interleaved: one MFMA, then a share of the reads, and so on.
+  constexpr int N_MFMA = KS * FM * FN;
+  constexpr int N_READ = KS * (FM + 2 * FN);
+  auto step = [&](const Frags& cur, Frags& nxt, int nslot) {
+    read_tile(nslot, nxt);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[ks][fn], cur.a[ks][fm], acc[fm][fn], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < N_MFMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int per = (N_READ + N_MFMA - 1) / N_MFMA;
+      if (i * per < N_READ) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+    }
+  };
+
+  // Wait until at most `n` k-tiles issued after the one needed are still in flight
+  // (vmcnt counts this thread's buffer->LDS loads, PER_TILE per k-tile, oldest first).
+  auto wait_tiles_in_flight = [&](int n) {
+    if (PER_TILE * 4 < 64 && n >= 4) wait_vmcnt<(PER_TILE * 4 < 64 ? PER_TILE * 4 : 0)>();
+    else if (n >= 3) wait_vmcnt<PER_TILE * 3>();
+    else if (n >= 2) wait_vmcnt<PER_TILE * 2>();
+    else if (n >= 1) wait_vmcnt<PER_TILE>();
+    else wait_vmcnt<0>();
+  };
+  static_assert(STAGES <= 5, "wait_tiles_in_flight covers up to 4 tiles in flight");
+
+  // Tile t lives in ring slot t % STAGES. Prologue: tiles 0 .. STAGES-1 in flight, tile 0
+  // read into registers.
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nk) issue(s, s);
+  Frags f0, f1;
+  wait_tiles_in_flight(min(nk - 1, STAGES - 1));
+  lds_barrier();
+  read_tile(0, f0);
+
+  // Iteration kt (tiles issued so far: 0 .. min(nk-1, kt+STAGES-1)):
+  //  1. wait for this thread's copies of tile kt+1, then the barrier: every wave's copies
+  //     of tile kt+1 have landed, and every wave has finished reading tile kt (done in
+  //     iteration kt-1), so slot kt % STAGES is free;
+  //  2. refill that slot with tile kt+STAGES;
+  //  3. MFMAs of tile kt from registers, interleaved with the reads of tile kt+1.
+  auto iteration = [&](int kt, const Frags& cur, Frags& nxt) {
+    if (kt + 1 < nk) wait_tiles_in_flight(min(nk - 1, kt + STAGES - 1) - (kt + 1));
+    lds_barrier();
+    if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
+    // after the last tile the reads hit a settled slot and are never used
+    step(cur, nxt, (kt + 1) % STAGES);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    iteration(kt, f0, f1);
+    iteration(kt + 1, f1, f0);
+  }
+  if (kt < nk) iteration(kt, f0, f1);
+
+  const bool relu = g.relu != 0;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = wm * WTM + fm * 32 + l32;
+    if (m >= mvalid) continue;
+    _Float16* const crow = g.C + (int64_t)(row0 + m) * g.ldc + col0;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int n = wn * WTN + fn * 32 + 8 * g4 + 4 * lhi;
+        if (n >= nvalid) continue;
+        float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
+        float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
+        if (relu) {
+          v0 = relu_f(v0);
+          v1 = relu_f(v1);
+          v2 = relu_f(v2);
+          v3 = relu_f(v3);
+        }
+        half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+        *(half4*)(crow + n) = h;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Generic kernel: 64 x 64 x 32 tile, 4 waves (2 x 2 of 32 x 32), element-wise predicated
 // loads (any 2-byte-aligned pointers, any strides and sizes). A is staged as [m][k] and B
 // transposed to [n][k] in LDS so both fragments are plain 16-byte reads.
@@ -390,6 +609,23 @@ hipError_t launch_fast(const GemmArgs& g, hipStream_t s, int device) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
+hipError_t launch_pipe(const GemmArgs& g, hipStream_t s, int device) {
+  constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
+  auto kern = gemm_pipe<BM, BN, BK, WM, WN, STAGES, PANEL, XCD>;
+  static std::atomic<uint64_t> ready{0};
+  const uint64_t bit = 1ull << (device & 63);
+  if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * WM * WN), lds, s, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_generic(const GemmArgs& g, hipStream_t s, int) {
   const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
   hipLaunchKernelGGL(gemm_generic, dim3((unsigned)nwg), dim3(256), 0, s, g);
@@ -417,25 +653,37 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
   X(128, 128, 64, 2, 2, 3, 4, 1)   \
   X(256, 256, 32, 2, 4, 4, 4, 1)
 
+// Pipelined kernel instantiations: X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP)
+#define TGEMM_PIPE_CONFIGS(X)      \
+  X(256, 256, 32, 2, 2, 4, 4, 1)   \
+  X(256, 256, 32, 2, 4, 4, 4, 1)   \
+  X(256, 256, 64, 2, 2, 2, 4, 1)   \
+  X(128, 128, 64, 2, 2, 2, 4, 1)
+
 #define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
   {BM, BN, BK, S, WM, WN, P, X, 0, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
 #define TGEMM_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_fast<BM, BN, BK, WM, WN, S, P, X>,
 #define TGEMM_COUNT(BM, BN, BK, WM, WN, S, P, X) 0,
+#define TGEMM_PIPE_ROW(BM, BN, BK, WM, WN, S, P, X) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, "p" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PIPE_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pipe<BM, BN, BK, WM, WN, S, P, X>,
 
 // Function-local statics: host-only tables (the device pass parses these bodies, which
 // instantiates every kernel, but emits no host data).
 const Config* config_table(int* count) {
   static const Config table[] = {
       {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, "generic_64x64x32"},
-      TGEMM_FAST_CONFIGS(TGEMM_ROW)};
+      TGEMM_FAST_CONFIGS(TGEMM_ROW) TGEMM_PIPE_CONFIGS(TGEMM_PIPE_ROW)};
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
 }
 
 Launcher launcher(int idx) {
-  static const Launcher table[] = {launch_generic, TGEMM_FAST_CONFIGS(TGEMM_LAUNCHER)};
+  static const Launcher table[] = {launch_generic, TGEMM_FAST_CONFIGS(TGEMM_LAUNCHER)
+                                       TGEMM_PIPE_CONFIGS(TGEMM_PIPE_LAUNCHER)};
   static_assert(sizeof(table) / sizeof(table[0]) ==
-                    1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT)}) / sizeof(int),
+                    1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT) TGEMM_PIPE_CONFIGS(TGEMM_COUNT)}) /
+                            sizeof(int),
                 "one launcher per config");
   return table[idx];
 }

@@ -1,0 +1,79 @@
+"""Offline config sweep: time every applicable table config of libtgemm on the measured
+workloads and report the fastest per workload (the evidence behind the config choice in
+tgemm_api.cpp's choose_fast). Needs a GPU.
+
+  python -m tiled_dense_gemm_04_amd.sweep [--out results.json] [--iters 30]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+
+
+def time_config(tg, torch, a, b, c, relu, cfg, iters, warmup=5):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        tg.gemm_f16(a, b, c, relu=relu, cfg=cfg)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        tg.gemm_f16(a, b, c, relu=relu, cfg=cfg)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e3  # us
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--iters", type=int, default=30)
+    ap.add_argument("--workloads", default=None, help="comma-separated names (default: all)")
+    args = ap.parse_args()
+
+    import torch
+
+    import tgemm_workloads as W
+    import tiled_dense_gemm_04_amd as tg
+
+    works = [W.HEADLINE] + list(W.WORKLOADS.values())
+    if args.workloads:
+        keep = set(args.workloads.split(","))
+        works = [w for w in works if w.name in keep]
+    cfgs = tg.configs()
+    results = []
+    for w in works:
+        A, B = w.inputs()
+        a = torch.from_numpy(A).cuda()
+        b = torch.from_numpy(B).cuda()
+        c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+        default = tg.tgemm_select_config(w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(),
+                                         b.stride(0), c.data_ptr(), c.stride(0))
+        row = {"workload": w.name, "default_cfg": default, "times_us": {}}
+        for i, cd in enumerate(cfgs):
+            us = time_config(tg, torch, a, b, c, w.relu, i, args.iters)
+            tf = w.flop / (us * 1e-6) / 1e12
+            row["times_us"][cd["name"]] = round(us, 2)
+            print(f"{w.name:28s} cfg {i} {cd['name']:30s} {us:9.2f} us {tf:8.1f} TFLOP/s "
+                  f"({100 * tf / PEAK_TFLOPS:5.1f} %){' <- default' if i == default else ''}", flush=True)
+        best = min(row["times_us"], key=row["times_us"].get)
+        row["best"] = best
+        results.append(row)
+        del a, b, c
+        torch.cuda.empty_cache()
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(results, f, indent=1)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
