@@ -100,7 +100,22 @@ def main() -> int:
     ap.add_argument("--cfg", type=int, default=None, help="force a config index (sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 5 times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe // 2
+        src = torch.ones(n, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint(f"copied {2 * n} bytes 5 times")
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -65,7 +65,7 @@ def test_config_table():
         assert c["lds_bytes"] <= 160 * 1024
         assert c["lds_bytes"] == c["stages"] * (c["block_m"] * c["block_k"] + c["block_k"] * c["block_n"]) * 2
         assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
-        assert c["block_n"] >= 128 and c["block_k"] in (32, 64, 128)
+        assert c["block_n"] >= 128 and c["block_k"] in (16, 32, 64, 128)
         threads = 64 * c["waves_m"] * c["waves_n"]
         assert (c["block_m"] * c["block_k"] // 8) % threads == 0
         assert (c["block_k"] * c["block_n"] // 8) % threads == 0

@@ -307,13 +307,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------------------
-// Pipelined kernel: same tiles, LDS layouts and edge handling as gemm_fast, but the
-// fragments of k-tile kt+1 are read from LDS into a second register set while the MFMAs
-// of k-tile kt run, interleaved instruction by instruction. After each workgroup barrier
-// a wave therefore starts issuing MFMAs at once (its fragments were loaded during the
-// previous k-tile), and the LDS ring (STAGES slots) keeps STAGES-1 k-tiles of global
-// loads in flight: at iteration kt, slot kt % STAGES (tile kt, already in registers) is
-// refilled with tile kt + STAGES while tile kt+1 is being read.
+// Pipelined kernel: same tiles, LDS layouts and edge handling as gemm_fast, scheduled so
+// that the MFMA pipe never waits on memory instructions:
+//   * the fragments of k-tile kt+1 are read from LDS into a second register set while the
+//     MFMAs of k-tile kt run, interleaved instruction by instruction, so after each
+//     workgroup barrier a wave issues MFMAs at once;
+//   * the LDS ring has STAGES slots; tile t lives in slot t % STAGES and is copied
+//     STAGES-1 iterations before it is read;
+//   * every iteration issues exactly PER_TILE buffer->LDS copies, one between each group
+//     of MFMAs (copies for tiles past the end use an empty buffer range and only write
+//     zeros into a slot no later read needs), so the number of copies in flight is the
+//     same at every wait and one constant s_waitcnt suffices;
+//   * descriptors advance by a constant stride; only the last k-tile has its own range.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
   constexpr int NW = WM * WN, NT = 64 * NW;
@@ -325,12 +330,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
   constexpr int A_LD = A_UNITS / NT, B_LD = B_UNITS / NT;
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
   constexpr int PER_TILE = A_LD + B_LD;
+  constexpr int N_MFMA = KS * FM * FN;
+  constexpr int N_READ = KS * (FM + 2 * FN);
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(A_UNITS % NT == 0 && B_UNITS % NT == 0, "loads must split evenly");
-  static_assert(BK % 16 == 0 && BK >= 32 && BK <= 128, "block_k");
+  static_assert(BK % 16 == 0 && BK >= 16 && BK <= 128, "block_k");
   static_assert(BN >= 128 && (BN * 2) % 256 == 0, "B rows must span the bank window");
   static_assert(STAGES >= 2, "stages");
   static_assert(PER_TILE * STAGES < 64, "vmcnt budget");
+  static_assert(N_MFMA >= PER_TILE, "at least one MFMA between copies");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const a_lds = smem;
@@ -345,16 +353,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
   const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
   const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
   const int K = g.K;
+  const int nk = (K + BK - 1) / BK;
+  const int kin_last = K - (nk - 1) * BK;  // 1 .. BK
 
-  uint32_t a_off[A_LD];
-  int a_kc[A_LD];
+  // Per-thread copy offsets (bytes from the descriptor base of a k-tile). A rows at or
+  // past mvalid fall outside the A range and read as zero; B columns at or past nvalid
+  // are masked here; A columns past K exist only in the last k-tile (masked there).
+  uint32_t a_off[A_LD], a_off_last[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int u = (i * NW + wave) * 64 + lane;
     const int r = u / A_CH_ROW;
     const int c = (u % A_CH_ROW) ^ swz_a<BK>(r);
-    a_kc[i] = 8 * c;
-    a_off[i] = (r < mvalid) ? (uint32_t)(((int64_t)r * g.lda + 8 * c) * 2) : kOob;
+    a_off[i] = (uint32_t)(((int64_t)r * g.lda + 8 * c) * 2);
+    a_off_last[i] = 8 * c < kin_last ? a_off[i] : kOob;
   }
   uint32_t b_off[B_LD];
 #pragma unroll
@@ -364,30 +376,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
     const int c = (u % B_CH_ROW) ^ swz_b(k);
     b_off[i] = (8 * c < nvalid) ? (uint32_t)(((int64_t)k * g.ldb + 8 * c) * 2) : kOob;
   }
-  const _Float16* const a_tile = g.A + (int64_t)row0 * g.lda;
-  const _Float16* const b_tile = g.B + col0;
-  const int nk = (K + BK - 1) / BK;
+  // Descriptor ranges (bytes) for a full k-tile and for the last one.
+  const int64_t a_rng_full64 = ((int64_t)(mvalid - 1) * g.lda + BK) * 2;
+  const int64_t a_rng_last64 = ((int64_t)(mvalid - 1) * g.lda + kin_last) * 2;
+  const int64_t b_rng_full64 = ((int64_t)(BK - 1) * g.ldb + nvalid) * 2;
+  const int64_t b_rng_last64 = ((int64_t)(kin_last - 1) * g.ldb + nvalid) * 2;
+  const uint32_t a_rng_full = (uint32_t)(a_rng_full64 < kMaxRange ? a_rng_full64 : kMaxRange);
+  const uint32_t a_rng_last = (uint32_t)(a_rng_last64 < kMaxRange ? a_rng_last64 : kMaxRange);
+  const uint32_t b_rng_full = (uint32_t)(b_rng_full64 < kMaxRange ? b_rng_full64 : kMaxRange);
+  const uint32_t b_rng_last = (uint32_t)(b_rng_last64 < kMaxRange ? b_rng_last64 : kMaxRange);
+  const char* const a_base = (const char*)(g.A + (int64_t)row0 * g.lda);
+  const char* const b_base = (const char*)(g.B + col0);
+  const int64_t a_step = (int64_t)BK * 2, b_step = (int64_t)BK * g.ldb * 2;
+  const uint32_t a_lds0 = lds_addr(a_lds) + wave * 1024;
+  const uint32_t b_lds0 = lds_addr(b_lds) + wave * 1024;
 
-  auto issue = [&](int kt, int slot) {
-    const int k0 = kt * BK;
-    const int krem = K - k0;
-    const int kin = krem < BK ? krem : BK;
-    const int64_t a_range = ((int64_t)(mvalid - 1) * g.lda + kin) * 2;
-    const int4v ra = make_rsrc(a_tile + k0, (uint32_t)(a_range < kMaxRange ? a_range : kMaxRange));
-    const int64_t b_range = ((int64_t)(kin - 1) * g.ldb + nvalid) * 2;
-    const int4v rb = make_rsrc(b_tile + (int64_t)k0 * g.ldb,
-                               (uint32_t)(b_range < kMaxRange ? b_range : kMaxRange));
-    const uint32_t a_dst = lds_addr(a_lds) + slot * A_BYTES + wave * 1024;
-    const uint32_t b_dst = lds_addr(b_lds) + slot * B_BYTES + wave * 1024;
-    if (kin == BK) {
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) dma_to_lds(ra, a_dst + i * NW * 1024, a_off[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) dma_to_lds(ra, a_dst + i * NW * 1024, a_kc[i] < kin ? a_off[i] : kOob);
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) dma_to_lds(rb, b_dst + i * NW * 1024, b_off[i]);
+  // Copy j (0 .. PER_TILE-1) of k-tile t into its slot. Tiles past the end get range 0.
+  struct Dma {
+    int4v ra, rb;
+    uint32_t a_dst, b_dst;
+    bool last;
+  };
+  auto dma_setup = [&](int t) {
+    Dma d;
+    const uint32_t ar = t < nk - 1 ? a_rng_full : (t == nk - 1 ? a_rng_last : 0u);
+    const uint32_t br = t < nk - 1 ? b_rng_full : (t == nk - 1 ? b_rng_last : 0u);
+    const int tt = t < nk ? t : nk - 1;  // keep the base inside the matrix
+    d.ra = make_rsrc(a_base + tt * a_step, ar);
+    d.rb = make_rsrc(b_base + tt * b_step, br);
+    const int slot = t % STAGES;
+    d.a_dst = a_lds0 + slot * A_BYTES;
+    d.b_dst = b_lds0 + slot * B_BYTES;
+    d.last = t == nk - 1;
+    return d;
+  };
+  auto dma_one = [&](const Dma& d, int j) {
+    if (j < A_LD)
+      dma_to_lds(d.ra, d.a_dst + j * NW * 1024, d.last ? a_off_last[j] : a_off[j]);
+    else
+      dma_to_lds(d.rb, d.b_dst + (j - A_LD) * NW * 1024, b_off[j - A_LD]);
   };
 
   const int wm = wave / WN, wn = wave % WN;
@@ -401,30 +428,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 
   struct Frags {
     half8 a[KS][FM];
-    half8 b[KS][FN];
+    short4v b[KS][FN][2];
   };
-  auto read_tile = [&](int slot, Frags& f) {
-    const char* const As = a_lds + slot * A_BYTES;
-    const char* const Bs = b_lds + slot * B_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int off = a_row_off + fm * 32 * BK * 2 + (((2 * ks + lhi) ^ a_sw) << 4);
-        f.a[ks][fm] = *(const TG_LDS half8*)(As + off);
-      }
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        short4v part[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = 16 * ks + 4 * h + b_krow;
-          const int off = k * BN * 2 + (((b_chunk + 4 * fn) ^ swz_b(k)) << 4) + b_half;
-          part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(Bs + off));
-        }
-        const short8v s8 = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        f.b[ks][fn] = __builtin_bit_cast(half8, s8);
-      }
+  // Read number r (0 .. N_READ-1) of a k-tile: per substep FM A reads, then 2*FN B reads.
+  auto read_one = [&](int slot, Frags& f, int r) {
+    const int ks = r / (FM + 2 * FN), q = r % (FM + 2 * FN);
+    if (q < FM) {
+      const char* const As = a_lds + slot * A_BYTES;
+      const int off = a_row_off + q * 32 * BK * 2 + (((2 * ks + lhi) ^ a_sw) << 4);
+      f.a[ks][q] = *(const TG_LDS half8*)(As + off);
+    } else {
+      const int fn = (q - FM) / 2, h = (q - FM) % 2;
+      const char* const Bs = b_lds + slot * B_BYTES;
+      const int k = 16 * ks + 4 * h + b_krow;
+      const int off = k * BN * 2 + (((b_chunk + 4 * fn) ^ swz_b(k)) << 4) + b_half;
+      f.b[ks][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(Bs + off));
     }
   };
 
@@ -436,60 +454,59 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // MFMAs of one k-tile from `cur` with the LDS reads of the next k-tile (slot `nslot`)
-  // into `nxt`, interleaved: one MFMA, then a share of the reads, and so on.
-  constexpr int N_MFMA = KS * FM * FN;
-  constexpr int N_READ = KS * (FM + 2 * FN);
-  auto step = [&](const Frags& cur, Frags& nxt, int nslot) {
-    read_tile(nslot, nxt);
+  auto mfma_one = [&](const Frags& f, int m) {
+    const int ks = m / (FM * FN), fm = (m / FN) % FM, fn = m % FN;
+    const short8v b8 = __builtin_shufflevector(f.b[ks][fn][0], f.b[ks][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, b8), f.a[ks][fm],
+                                                         acc[fm][fn], 0, 0, 0);
+  };
+
+  // One k-tile: MFMAs from `cur`, the reads of the next tile (slot nslot) into `nxt`, and
+  // the PER_TILE copies of tile kt+STAGES, in PER_TILE groups: the group's MFMAs with its
+  // share of the reads interleaved (RPM reads after each MFMA), then one copy.
+  constexpr int RPM = (N_READ + N_MFMA - 1) / N_MFMA;
+  auto step = [&](const Frags& cur, Frags& nxt, int nslot, const Dma& d) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int grp = 0; grp < PER_TILE; ++grp) {
+      const int mb = grp * N_MFMA / PER_TILE, me = (grp + 1) * N_MFMA / PER_TILE;
+      const int rb = grp * N_READ / PER_TILE, re = (grp + 1) * N_READ / PER_TILE;
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int m = mb; m < me; ++m) mfma_one(cur, m);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[ks][fn], cur.a[ks][fm], acc[fm][fn], 0, 0, 0);
+      for (int r = rb; r < re; ++r) read_one(nslot, nxt, r);
 #pragma unroll
-    for (int i = 0; i < N_MFMA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      constexpr int per = (N_READ + N_MFMA - 1) / N_MFMA;
-      if (i * per < N_READ) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+      for (int m = mb; m < me; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dma_one(d, grp);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Wait until at most `n` k-tiles issued after the one needed are still in flight
-  // (vmcnt counts this thread's buffer->LDS loads, PER_TILE per k-tile, oldest first).
-  auto wait_tiles_in_flight = [&](int n) {
-    if (PER_TILE * 4 < 64 && n >= 4) wait_vmcnt<(PER_TILE * 4 < 64 ? PER_TILE * 4 : 0)>();
-    else if (n >= 3) wait_vmcnt<PER_TILE * 3>();
-    else if (n >= 2) wait_vmcnt<PER_TILE * 2>();
-    else if (n >= 1) wait_vmcnt<PER_TILE>();
-    else wait_vmcnt<0>();
-  };
-  static_assert(STAGES <= 5, "wait_tiles_in_flight covers up to 4 tiles in flight");
-
-  // Tile t lives in ring slot t % STAGES. Prologue: tiles 0 .. STAGES-1 in flight, tile 0
-  // read into registers.
+  // Prologue: tiles 0 .. STAGES-1 in flight (PER_TILE copies each), tile 0 into registers.
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (s < nk) issue(s, s);
+  for (int t = 0; t < STAGES; ++t) {
+    const Dma d = dma_setup(t);
+#pragma unroll
+    for (int j = 0; j < PER_TILE; ++j) dma_one(d, j);
+  }
   Frags f0, f1;
-  wait_tiles_in_flight(min(nk - 1, STAGES - 1));
+  wait_vmcnt<PER_TILE * (STAGES - 1)>();
   lds_barrier();
-  read_tile(0, f0);
+#pragma unroll
+  for (int r = 0; r < N_READ; ++r) read_one(0, f0, r);
 
-  // Iteration kt (tiles issued so far: 0 .. min(nk-1, kt+STAGES-1)):
-  //  1. wait for this thread's copies of tile kt+1, then the barrier: every wave's copies
-  //     of tile kt+1 have landed, and every wave has finished reading tile kt (done in
-  //     iteration kt-1), so slot kt % STAGES is free;
-  //  2. refill that slot with tile kt+STAGES;
-  //  3. MFMAs of tile kt from registers, interleaved with the reads of tile kt+1.
+  // Iteration kt: wait for this thread's copies of tile kt+1 (the tiles issued after it,
+  // kt+2 .. kt+STAGES-1, may still fly), then the barrier (every wave's copies of tile
+  // kt+1 have landed and every wave has finished reading tile kt, so slot kt % STAGES is
+  // free), then MFMAs of tile kt + reads of tile kt+1 + copies of tile kt+STAGES.
   auto iteration = [&](int kt, const Frags& cur, Frags& nxt) {
-    if (kt + 1 < nk) wait_tiles_in_flight(min(nk - 1, kt + STAGES - 1) - (kt + 1));
+    const Dma d = dma_setup(kt + STAGES);
+    wait_vmcnt<PER_TILE * (STAGES - 2)>();
     lds_barrier();
-    if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
-    // after the last tile the reads hit a settled slot and are never used
-    step(cur, nxt, (kt + 1) % STAGES);
+    step(cur, nxt, (kt + 1) % STAGES, d);
   };
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -497,6 +514,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
     iteration(kt + 1, f1, f0);
   }
   if (kt < nk) iteration(kt, f0, f1);
+  // Drain: no copy may still be writing LDS when the workgroup exits.
+  wait_vmcnt<0>();
 
   const bool relu = g.relu != 0;
 #pragma unroll
@@ -648,17 +667,19 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
 //   X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP)
 #define TGEMM_FAST_CONFIGS(X)      \
   X(256, 256, 64, 2, 4, 2, 4, 1)   \
-  X(256, 128, 64, 2, 2, 2, 4, 1)   \
-  X(128, 128, 64, 2, 2, 2, 4, 1)   \
-  X(128, 128, 64, 2, 2, 3, 4, 1)   \
-  X(256, 256, 32, 2, 4, 4, 4, 1)
+  X(128, 128, 64, 2, 2, 2, 4, 1)
 
 // Pipelined kernel instantiations: X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP)
 #define TGEMM_PIPE_CONFIGS(X)      \
-  X(256, 256, 32, 2, 2, 4, 4, 1)   \
   X(256, 256, 32, 2, 4, 4, 4, 1)   \
-  X(256, 256, 64, 2, 2, 2, 4, 1)   \
-  X(128, 128, 64, 2, 2, 2, 4, 1)
+  X(256, 256, 32, 2, 2, 4, 4, 1)   \
+  X(128, 128, 32, 2, 2, 4, 4, 1)   \
+  X(256, 128, 32, 2, 2, 4, 4, 1)   \
+  X(128, 128, 64, 2, 2, 2, 4, 1)   \
+  X(256, 256, 32, 2, 2, 4, 8, 1)   \
+  X(256, 256, 32, 2, 2, 4, 2, 1)   \
+  X(256, 256, 32, 2, 2, 4, 16, 1)  \
+  X(256, 256, 32, 2, 2, 4, 4, 0)
 
 #define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
   {BM, BN, BK, S, WM, WN, P, X, 0, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},

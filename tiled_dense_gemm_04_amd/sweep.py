@@ -37,6 +37,8 @@ def main():
     ap.add_argument("--out", default=None)
     ap.add_argument("--iters", type=int, default=30)
     ap.add_argument("--workloads", default=None, help="comma-separated names (default: all)")
+    ap.add_argument("--torch", action="store_true",
+                    help="also time torch.matmul (+ relu) on the same inputs, as context only")
     args = ap.parse_args()
 
     import torch
@@ -64,6 +66,24 @@ def main():
             row["times_us"][cd["name"]] = round(us, 2)
             print(f"{w.name:28s} cfg {i} {cd['name']:30s} {us:9.2f} us {tf:8.1f} TFLOP/s "
                   f"({100 * tf / PEAK_TFLOPS:5.1f} %){' <- default' if i == default else ''}", flush=True)
+        if args.torch:
+            def tmm():
+                r = torch.matmul(a, b)
+                return torch.relu_(r) if w.relu else r
+            for _ in range(5):
+                tmm()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.iters):
+                tmm()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / args.iters * 1e3
+            tf = w.flop / (us * 1e-6) / 1e12
+            row["torch_matmul_us"] = round(us, 2)
+            print(f"{w.name:28s} torch.matmul{'+relu' if w.relu else ''} (context) {us:9.2f} us {tf:8.1f} TFLOP/s "
+                  f"({100 * tf / PEAK_TFLOPS:5.1f} %)", flush=True)
         best = min(row["times_us"], key=row["times_us"].get)
         row["best"] = best
         results.append(row)
