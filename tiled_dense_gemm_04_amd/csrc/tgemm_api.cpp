@@ -56,19 +56,16 @@ int64_t workgroups(const Config& c, int64_t M, int64_t N) {
   return tgemm::ceil_div(M, c.bm) * tgemm::ceil_div(N, c.bn);
 }
 
-// Config choice for a fast-eligible call (table rows: 3 = 8-wave 256x256 pipelined,
-// 4 = 4-wave 256x256 pipelined, 7 = 4-wave 128x128 pipelined with BK 64). From the
-// offline sweep on the measured workloads: when the 256 x 256 tiles fill the 256 compute
-// units (one or more whole waves of workgroups) the 4-wave kernel is fastest; a
-// partial wave of 256 x 256 tiles (160-255 tiles, e.g. 4095 x 3000) favours the 8-wave
-// kernel; below that, 128 x 128 tiles keep more compute units busy.
-constexpr int kCfgPipe8 = 3, kCfgPipe4 = 4, kCfgPipe128 = 7;
+// Config choice for a fast-eligible call (rows of the table in tgemm_kernels.hip:
+// 9 = 16x16x32 ping-pong 256x256, 7 = 4-wave pipelined 128x128 with BK 64). From the
+// offline sweep on the measured workloads: 256 x 256 ping-pong tiles win as soon as they
+// cover most of the 256 compute units (160+ tiles, e.g. 4095 x 3000 has 192); below
+// that, 128 x 128 tiles keep more compute units busy.
+constexpr int kCfgBig = 9, kCfgSmall = 7;
 int choose_fast(int64_t M, int64_t N, int64_t K) {
   (void)K;
   const int64_t t256 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256);
-  if (t256 >= 256) return kCfgPipe4;
-  if (t256 >= 160) return kCfgPipe8;
-  return kCfgPipe128;
+  return t256 >= 160 ? kCfgBig : kCfgSmall;
 }
 
 int select(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,

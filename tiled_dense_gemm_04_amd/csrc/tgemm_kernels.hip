@@ -104,11 +104,23 @@ template <int BK>
 __host__ __device__ constexpr int swz_a(int r) {
   return (r / (128 / BK)) % (BK / 8);
 }
+// The same for 16x16x32 A fragments (16 lanes on 16 rows, four lane groups on the four
+// 16-byte chunks of a 64-byte row, BK = 32). Measured with SQ_LDS_BANK_CONFLICT on gfx950:
+// XOR by (r / 2) % 4 is conflict-free for this pattern, while (r / 4) % 4 (the 32x32x16
+// choice above) conflicts 2-way.
+template <int BK, int MF>
+__host__ __device__ constexpr int swz_a_mf(int r) {
+  static_assert(MF == 32 || BK == 32, "16x16x32 fragments are laid out for BK = 32");
+  return MF == 16 ? (r >> 1) & 3 : swz_a<BK>(r);
+}
 // B stage: BK rows (k) x BN halves (n), row k at byte k*BN*2 (a multiple of 256 bytes);
 // logical chunk c of row k is stored at chunk c ^ swz_b(k). A transposed read by 32 lanes
-// touches 4 consecutive k rows x 4 consecutive chunks (c0 % 4 == 0); XOR by 4*(k%4) puts
-// the 16 (row, chunk) pairs on 16 distinct 16-byte slots of the bank window.
-__host__ __device__ constexpr int swz_b(int k) { return 4 * (k & 3); }
+// touches either 4 consecutive k rows x 4 consecutive chunks (32x32x16 B fragments,
+// c0 % 4 == 0, k < 8 within the group of 8) or rows k and k+8 for 4 consecutive k x 2
+// chunks (16x16x32 fragments, c0 % 2 == 0). XOR by 4*(k%4) spreads the four rows of a
+// group, XOR by 2*((k/8)%2) separates rows k and k+8: in both patterns the 16 (row,
+// chunk) pairs land on 16 distinct 16-byte slots of the bank window.
+__host__ __device__ constexpr int swz_b(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 
 // ------------------------------------------------------------------------------------
 // Fast kernel: BM x BN x BK tile, WM x WN waves, STAGES-deep LDS ring fed by buffer->LDS
@@ -545,6 +557,296 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------------------
+// Ping-pong kernel: 8 waves in two groups of 4 (waves 0-3 and 4-7), one wave of each
+// group per SIMD. Every iteration (one k-tile) has two phases separated by workgroup
+// barriers; in each phase one group only issues MFMAs (from registers) while the other
+// only moves data (LDS -> its fragment registers, and its share of the buffer->LDS
+// copies), then they swap. Each SIMD's MFMA pipe is fed by a wave that never waits on a
+// memory instruction, and LDS/TA stalls land on the partner wave.
+//
+// Schedule (tile t lives in ring slot t % STAGES; PT copies per thread per tile):
+//   prologue: group 0 copies tiles 0 .. STAGES-1, group 1 tiles 0 .. STAGES-2; both wait
+//             for tile 0; barrier; group 0 reads tile 0.
+//   iteration kt, phase 1: group 0: MFMAs of tile kt.
+//                          group 1: reads tile kt; copies tile kt+STAGES-1.
+//             wait (tile kt+1 landed for this thread), barrier B2
+//             phase 2: group 0: reads tile kt+1; copies tile kt+STAGES.
+//                          group 1: MFMAs of tile kt.
+//             barrier B1
+// Slot safety: a copy of tile t+STAGES (group 0, phase 2 of kt = t) or t+STAGES-1 (group 1,
+// phase 1 of kt = t+1... i.e. into the slot of tile kt-1) only ever targets a slot whose
+// last reads finished before the preceding B2 (its readers were group 0 in phase 2 of
+// the iteration before and group 1 in phase 1 of the same iteration). Copies past the
+// last tile use an empty range, so every thread issues exactly PT copies per iteration
+// and at each B2 exactly STAGES-2 later tiles may still be in flight for every thread.
+// SYNC2 adds a second barrier per k-tile (B1) that holds the two groups exactly a phase
+// apart: 0 = none, 1 = plain s_barrier, 2 = s_barrier after this wave's LDS reads
+// completed. Every overwrite of a slot is already ordered after its last reads by B2
+// alone, so B1 only shapes the timing.
+// CIM = true issues each group's buffer->LDS copies from its MFMA phase (one copy after
+// every group of MFMAs) instead of its memory phase, so memory phases are LDS reads only.
+// Group 0 then copies tile kt+STAGES-1 in phase 1 of iteration kt (its slot's last reads
+// ended before B2 of iteration kt-1) and group 1 copies tile kt+STAGES in phase 2 of
+// iteration kt (after B2 of iteration kt); at every B2 each thread still has exactly
+// STAGES-2 later tiles in flight.
+// MF selects the MFMA: 32 = v_mfma_f32_32x32x16_f16, 16 = v_mfma_f32_16x16x32_f16 (half
+// the accumulator traffic per FLOP, twice the instructions).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int SYNC2,
+          bool CIM, int MF = 32>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int KS = BK / (512 / MF);  // k per MFMA: 16 (32x32x16) or 32 (16x16x32)
+  static_assert(MF == 32 || MF == 16, "MFMA shape");
+  constexpr int A_CH_ROW = BK / 8, B_CH_ROW = BN / 8;
+  constexpr int A_UNITS = BM * A_CH_ROW, B_UNITS = BK * B_CH_ROW;
+  constexpr int A_LD = A_UNITS / NT, B_LD = B_UNITS / NT;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+  constexpr int PT = A_LD + B_LD;
+  static_assert(NW == 8, "two groups of four waves");
+  static_assert(WTM % MF == 0 && WTN % MF == 0 && KS >= 1, "wave tile must be a multiple of the MFMA");
+  static_assert(A_UNITS % NT == 0 && B_UNITS % NT == 0, "loads must split evenly");
+  static_assert(BK % 16 == 0 && BK >= 16 && BK <= 128, "block_k");
+  static_assert(BN >= 128 && (BN * 2) % 256 == 0, "B rows must span the bank window");
+  static_assert(STAGES >= 3, "the ring needs a slot being read, one in flight and one free");
+  static_assert(PT * STAGES < 64, "vmcnt budget");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const a_lds = smem;
+  char* const b_lds = smem + STAGES * A_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w+4 share SIMD w % 4
+
+  int64_t tm64, tn64;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
+  const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
+  const int K = g.K;
+  const int nk = (K + BK - 1) / BK;
+  const int kin_last = K - (nk - 1) * BK;
+
+  uint32_t a_off[A_LD], a_off_last[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int u = (i * NW + wave) * 64 + lane;
+    const int r = u / A_CH_ROW;
+    const int c = (u % A_CH_ROW) ^ swz_a_mf<BK, MF>(r);
+    a_off[i] = (uint32_t)(((int64_t)r * g.lda + 8 * c) * 2);
+    a_off_last[i] = 8 * c < kin_last ? a_off[i] : kOob;
+  }
+  uint32_t b_off[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int u = (i * NW + wave) * 64 + lane;
+    const int k = u / B_CH_ROW;
+    const int c = (u % B_CH_ROW) ^ swz_b(k);
+    b_off[i] = (8 * c < nvalid) ? (uint32_t)(((int64_t)k * g.ldb + 8 * c) * 2) : kOob;
+  }
+  const int64_t a_rng_full64 = ((int64_t)(mvalid - 1) * g.lda + BK) * 2;
+  const int64_t a_rng_last64 = ((int64_t)(mvalid - 1) * g.lda + kin_last) * 2;
+  const int64_t b_rng_full64 = ((int64_t)(BK - 1) * g.ldb + nvalid) * 2;
+  const int64_t b_rng_last64 = ((int64_t)(kin_last - 1) * g.ldb + nvalid) * 2;
+  const uint32_t a_rng_full = (uint32_t)(a_rng_full64 < kMaxRange ? a_rng_full64 : kMaxRange);
+  const uint32_t a_rng_last = (uint32_t)(a_rng_last64 < kMaxRange ? a_rng_last64 : kMaxRange);
+  const uint32_t b_rng_full = (uint32_t)(b_rng_full64 < kMaxRange ? b_rng_full64 : kMaxRange);
+  const uint32_t b_rng_last = (uint32_t)(b_rng_last64 < kMaxRange ? b_rng_last64 : kMaxRange);
+  const char* const a_base = (const char*)(g.A + (int64_t)row0 * g.lda);
+  const char* const b_base = (const char*)(g.B + col0);
+  const int64_t a_step = (int64_t)BK * 2, b_step = (int64_t)BK * g.ldb * 2;
+  const uint32_t a_lds0 = lds_addr(a_lds) + wave * 1024;
+  const uint32_t b_lds0 = lds_addr(b_lds) + wave * 1024;
+
+  // This thread's PT copies of k-tile t (empty range past the last tile).
+  struct Dma {
+    int4v ra, rb;
+    uint32_t a_dst, b_dst;
+    bool last;
+  };
+  auto dma_setup = [&](int t) {
+    Dma d;
+    const uint32_t ar = t < nk - 1 ? a_rng_full : (t == nk - 1 ? a_rng_last : 0u);
+    const uint32_t br = t < nk - 1 ? b_rng_full : (t == nk - 1 ? b_rng_last : 0u);
+    const int tt = t < nk ? t : nk - 1;
+    d.ra = make_rsrc(a_base + tt * a_step, ar);
+    d.rb = make_rsrc(b_base + tt * b_step, br);
+    const int slot = t % STAGES;
+    d.a_dst = a_lds0 + slot * A_BYTES;
+    d.b_dst = b_lds0 + slot * B_BYTES;
+    d.last = t == nk - 1;
+    return d;
+  };
+  auto dma_one = [&](const Dma& d, int j) {
+    if (j < A_LD)
+      dma_to_lds(d.ra, d.a_dst + j * NW * 1024, d.last ? a_off_last[j] : a_off[j]);
+    else
+      dma_to_lds(d.rb, d.b_dst + (j - A_LD) * NW * 1024, b_off[j - A_LD]);
+  };
+  auto copy_tile = [&](int t) {
+    const Dma d = dma_setup(t);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) dma_one(d, j);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  // Fragment lane maps. 32x32x16: row/col = lane % 32, k group = lane / 32 (8 k each).
+  // 16x16x32: row/col = lane % 16, k group = lane / 16 (8 k each).
+  const int lrow = lane % MF, lkg = lane / MF;
+  const int a_row_off = (wm * WTM + lrow) * BK * 2;
+  const int a_sw = swz_a_mf<BK, MF>(lrow);  // fm*MF and wm*WTM are multiples of the period
+  // B fragments by two transposed reads: lane = 16 g + 4 j + q reads row k0 + j of its
+  // group's 4-row block and columns 4q .. 4q+3 of its 16-column block.
+  const int bg = lane >> 4, bj = (lane >> 2) & 3, bq = lane & 3;
+  const int b_krow = (MF == 32 ? 8 * (bg >> 1) : 8 * bg) + bj;
+  const int b_chunk = (wn * WTN) / 8 + (MF == 32 ? 2 * (bg & 1) : 0) + (bq >> 1);
+  const int b_half = (bq & 1) * 8;
+  constexpr int KPM = 512 / MF;  // k per MFMA
+
+  half8 fa[KS][FM];
+  short4v fb[KS][FN][2];
+  auto read_tile = [&](int slot) {
+    const char* const As = a_lds + slot * A_BYTES;
+    const char* const Bs = b_lds + slot * B_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int chunk = (KPM / 8) * ks + lkg;
+        const int off = a_row_off + fm * MF * BK * 2 + ((chunk ^ a_sw) << 4);
+        fa[ks][fm] = *(const TG_LDS half8*)(As + off);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = KPM * ks + 4 * h + b_krow;
+          const int off = k * BN * 2 + (((b_chunk + (MF / 8) * fn) ^ swz_b(k)) << 4) + b_half;
+          fb[ks][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(Bs + off));
+        }
+    }
+  };
+
+  constexpr int NACC = MF * MF / 64;  // accumulator floats per lane per MFMA tile
+  typedef float accv __attribute__((ext_vector_type(NACC)));
+  accv acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.0f;
+
+  auto mma_one = [&](int m) {
+    const int ks = m / (FM * FN), fm = (m / FN) % FM, fn = m % FN;
+    const short8v b8 = __builtin_shufflevector(fb[ks][fn][0], fb[ks][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (MF == 32)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, b8), fa[ks][fm],
+                                                           acc[fm][fn], 0, 0, 0);
+    else
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b8), fa[ks][fm],
+                                                           acc[fm][fn], 0, 0, 0);
+  };
+  constexpr int N_MFMA = KS * FM * FN;
+  auto mma_tile = [&]() {
+#pragma unroll
+    for (int m = 0; m < N_MFMA; ++m) mma_one(m);
+  };
+  // MFMAs of one tile with the PT copies of tile t spread among them.
+  auto mma_tile_copy = [&](int t) {
+    const Dma d = dma_setup(t);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+#pragma unroll
+      for (int m = j * N_MFMA / PT; m < (j + 1) * N_MFMA / PT; ++m) mma_one(m);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_one(d, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue. Without CIM group 0 starts one copy ahead of group 1 (its next copy is in
+  // phase 2); with CIM group 1 is the one a copy ahead.
+  constexpr int G_AHEAD = CIM ? 1 : 0;
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t) copy_tile(t);
+  if (grp == G_AHEAD) {
+    copy_tile(STAGES - 1);
+    wait_vmcnt<PT * (STAGES - 1)>();
+  } else {
+    wait_vmcnt<PT * (STAGES - 2)>();
+  }
+  lds_barrier();
+  if (grp == 0) read_tile(0);
+
+  // sched_barrier(0) pins every phase: the compiler may not move MFMAs (register-only,
+  // so not ordered by s_barrier) from one phase into the other.
+  if (grp == 0) {
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (CIM) mma_tile_copy(kt + STAGES - 1);  // phase 1: MFMAs of tile kt
+      else mma_tile();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<PT * (STAGES - 2)>();
+      lds_barrier();                 // B2: tile kt+1 landed everywhere; reads of tile kt done
+      __builtin_amdgcn_sched_barrier(0);
+      read_tile((kt + 1) % STAGES);  // phase 2 (past the last tile: a settled slot, unused)
+      if (!CIM) copy_tile(kt + STAGES);
+      __builtin_amdgcn_sched_barrier(0);
+      if (SYNC2 == 2) lds_barrier();  // B1
+      if (SYNC2 == 1) __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_tile(kt % STAGES);        // phase 1
+      if (!CIM) copy_tile(kt + STAGES - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<PT * (STAGES - 2)>();
+      lds_barrier();                 // B2
+      __builtin_amdgcn_sched_barrier(0);
+      if (CIM) mma_tile_copy(kt + STAGES);  // phase 2: MFMAs of tile kt
+      else mma_tile();
+      __builtin_amdgcn_sched_barrier(0);
+      if (SYNC2 == 2) lds_barrier();  // B1
+      if (SYNC2 == 1) __builtin_amdgcn_s_barrier();
+    }
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue: lane holds, for tile (fm, fn), row m = fm*MF + lane % MF of the wave tile and
+  // columns n = fn*MF + 8*g4 + 4*(lane / MF) .. +3 (32x32) or fn*16 + 4*(lane / 16) .. +3
+  // (16x16). ReLU in fp32, round to fp16 (nearest even), one 8-byte store per 4 columns.
+  const bool relu = g.relu != 0;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = wm * WTM + fm * MF + lrow;
+    if (m >= mvalid) continue;
+    _Float16* const crow = g.C + (int64_t)(row0 + m) * g.ldc + col0;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+      for (int g4 = 0; g4 < NACC / 4; ++g4) {
+        const int n = wn * WTN + fn * MF + 8 * g4 + 4 * lkg;
+        if (n >= nvalid) continue;
+        float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
+        float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
+        if (relu) {
+          v0 = relu_f(v0);
+          v1 = relu_f(v1);
+          v2 = relu_f(v2);
+          v3 = relu_f(v3);
+        }
+        half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+        *(half4*)(crow + n) = h;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Generic kernel: 64 x 64 x 32 tile, 4 waves (2 x 2 of 32 x 32), element-wise predicated
 // loads (any 2-byte-aligned pointers, any strides and sizes). A is staged as [m][k] and B
 // transposed to [n][k] in LDS so both fragments are plain 16-byte reads.
@@ -628,6 +930,24 @@ hipError_t launch_fast(const GemmArgs& g, hipStream_t s, int device) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int SYNC2, bool CIM,
+          int MF = 32>
+hipError_t launch_pp(const GemmArgs& g, hipStream_t s, int device) {
+  constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
+  auto kern = gemm_pingpong<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, SYNC2, CIM, MF>;
+  static std::atomic<uint64_t> ready{0};
+  const uint64_t bit = 1ull << (device & 63);
+  if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * WM * WN), lds, s, g);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
 hipError_t launch_pipe(const GemmArgs& g, hipStream_t s, int device) {
   constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
@@ -675,11 +995,23 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
   X(256, 256, 32, 2, 2, 4, 4, 1)   \
   X(128, 128, 32, 2, 2, 4, 4, 1)   \
   X(256, 128, 32, 2, 2, 4, 4, 1)   \
-  X(128, 128, 64, 2, 2, 2, 4, 1)   \
-  X(256, 256, 32, 2, 2, 4, 8, 1)   \
-  X(256, 256, 32, 2, 2, 4, 2, 1)   \
-  X(256, 256, 32, 2, 2, 4, 16, 1)  \
-  X(256, 256, 32, 2, 2, 4, 4, 0)
+  X(128, 128, 64, 2, 2, 2, 4, 1)
+
+// Ping-pong kernel instantiations (8 waves): X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD)
+#define TGEMM_PP_CONFIGS(X)        \
+  X(256, 256, 32, 2, 4, 4, 4, 1)
+// Ping-pong with 16x16x32 MFMAs (the default for large grids), with variants of the
+// wave grid, ring depth and workgroup order kept for the sweep.
+#define TGEMM_PP1_CONFIGS(X)       \
+  X(256, 256, 32, 2, 4, 4, 4, 1)   \
+  X(256, 256, 32, 4, 2, 4, 4, 1)   \
+  X(256, 256, 32, 2, 4, 5, 4, 1)   \
+  X(256, 256, 32, 2, 4, 4, 8, 1)   \
+  X(256, 256, 32, 2, 4, 4, 2, 1)   \
+  X(256, 256, 32, 2, 4, 4, 4, 0)   \
+  X(128, 128, 32, 2, 4, 4, 4, 1)   \
+  X(256, 128, 32, 2, 4, 4, 4, 1)   \
+  X(128, 256, 32, 2, 4, 4, 4, 1)
 
 #define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
   {BM, BN, BK, S, WM, WN, P, X, 0, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
@@ -688,22 +1020,32 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
 #define TGEMM_PIPE_ROW(BM, BN, BK, WM, WN, S, P, X) \
   {BM, BN, BK, S, WM, WN, P, X, 0, "p" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
 #define TGEMM_PIPE_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pipe<BM, BN, BK, WM, WN, S, P, X>,
+#define TGEMM_PP_ROW(BM, BN, BK, WM, WN, S, P, X) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, "q" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PP_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pp<BM, BN, BK, WM, WN, S, P, X, 2, false>,
+#define TGEMM_PP1_ROW(BM, BN, BK, WM, WN, S, P, X) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, "m" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PP1_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pp<BM, BN, BK, WM, WN, S, P, X, 2, false, 16>,
 
 // Function-local statics: host-only tables (the device pass parses these bodies, which
 // instantiates every kernel, but emits no host data).
 const Config* config_table(int* count) {
   static const Config table[] = {
       {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, "generic_64x64x32"},
-      TGEMM_FAST_CONFIGS(TGEMM_ROW) TGEMM_PIPE_CONFIGS(TGEMM_PIPE_ROW)};
+      TGEMM_FAST_CONFIGS(TGEMM_ROW) TGEMM_PIPE_CONFIGS(TGEMM_PIPE_ROW) TGEMM_PP_CONFIGS(TGEMM_PP_ROW)
+          TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW)};
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
 }
 
 Launcher launcher(int idx) {
   static const Launcher table[] = {launch_generic, TGEMM_FAST_CONFIGS(TGEMM_LAUNCHER)
-                                       TGEMM_PIPE_CONFIGS(TGEMM_PIPE_LAUNCHER)};
+                                       TGEMM_PIPE_CONFIGS(TGEMM_PIPE_LAUNCHER)
+                                           TGEMM_PP_CONFIGS(TGEMM_PP_LAUNCHER)
+                                               TGEMM_PP1_CONFIGS(TGEMM_PP1_LAUNCHER)};
   static_assert(sizeof(table) / sizeof(table[0]) ==
-                    1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT) TGEMM_PIPE_CONFIGS(TGEMM_COUNT)}) /
+                    1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT) TGEMM_PIPE_CONFIGS(TGEMM_COUNT)
+                                           TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT)}) /
                             sizeof(int),
                 "one launcher per config");
   return table[idx];
