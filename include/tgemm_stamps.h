@@ -1,0 +1,52 @@
+/*
+ * tgemm_stamps.h -- extra entry points of libtgemm_stamps.so, the instrumented build of
+ * libtgemm (same sources compiled with TGEMM_STAMPS; it also exports everything in
+ * tgemm.h). Not part of the product library: libtgemm.so does not export these.
+ *
+ * In the instrumented build every workgroup of the GEMM kernels (all configs except the
+ * generic one) and of the MFMA probe records, at its end, TGEMM_STAMP_WORDS 64-bit words
+ * into a device-side table indexed by workgroup id (ids below TGEMM_STAMP_WORKGROUPS; each
+ * launch overwrites the rows of its workgroups):
+ *   [0] wall clock at kernel start      (s_memrealtime, 100 MHz ticks)
+ *   [1] wall clock at main-loop start
+ *   [2] wall clock at main-loop end
+ *   [3] wall clock after every wave's stores completed
+ *   [4] shader-clock ticks from kernel start to main-loop end (s_memtime counts at the
+ *       current shader clock, so [4] / ([2] - [0]) * 100 MHz is the clock the workgroup
+ *       ran at)
+ *   [5] main-loop iterations (k-tiles, or probe rounds)
+ *   [6] threads per workgroup
+ *   [7] 1 once written
+ * The stamps cost a few instructions per workgroup and one extra barrier at its end.
+ */
+#ifndef TGEMM_STAMPS_H_
+#define TGEMM_STAMPS_H_
+
+#include <stdint.h>
+
+#include "tgemm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TGEMM_STAMP_WORKGROUPS 4096
+#define TGEMM_STAMP_WORDS 8
+
+/* Writes the table's shape; returns TGEMM_OK or TGEMM_ENULL. */
+TGEMM_API int tgemm_stamps_capacity(int* workgroups, int* words_per_workgroup);
+
+/* Copies the first `words` words of the table of the current device to host memory
+ * (synchronous; words <= TGEMM_STAMP_WORKGROUPS * TGEMM_STAMP_WORDS). Returns TGEMM_OK,
+ * TGEMM_ENULL, TGEMM_EINVAL_DIM or TGEMM_ELAUNCH (the copy failed). */
+TGEMM_API int tgemm_stamps_read(uint64_t* host, int64_t words);
+
+/* Zeroes the table of the current device (synchronous). Returns TGEMM_OK or
+ * TGEMM_ELAUNCH. */
+TGEMM_API int tgemm_stamps_clear(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_STAMPS_H_ */

@@ -117,6 +117,18 @@ def test_workload_full_size_sampled(name):
     assert not np.any((c & 0x7C00) == 0x7C00), "inf/NaN in output"
 
 
+@pytest.mark.parametrize("name", ["plain_4096", "relu_tall_16384x512x4096", "relu_8192"])
+def test_workload_full_size_every_element(name):
+    """The whole output of each full-size workload against the whole oracle matrix."""
+    w = W.WORKLOADS[name]
+    A, B = w.inputs()
+    log(f"workload {w.name} full matrix (cfg {tg.tgemm_select_config(w.M, w.N, w.K)})")
+    c = run(A, B, w.relu)
+    ref = oracle.gemm(A, B, w.relu)
+    assert_close(c, ref, w.K, 1.0, w.name)
+    assert_close(c, ref, w.K, w.scale, w.name)
+
+
 def test_headline_relu_4096_matches_plain():
     """4096^3 with ReLU on (the headline) equals max(plain output, +0) bit for bit, and
     matches the oracle on sampled entries."""

@@ -13,21 +13,30 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module", autouse=True)
 def built():
-    if not os.path.exists(tg.LIBRARY):
+    if not (os.path.exists(tg.LIBRARY) and os.path.exists(tg.STAMPS_LIBRARY)):
         from tiled_dense_gemm_04_amd import build
-        build.build()
+        build.build_all()
     tg.lib()
+    tg.stamps_lib()
 
 
-def header_symbols():
-    text = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+def header_symbols(name="tgemm.h"):
+    text = open(os.path.join(ROOT, "include", name)).read()
     text = text.replace("#define TGEMM_API __attribute__((visibility(\"default\")))", "")
     return sorted(set(re.findall(r"^TGEMM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)))
 
 
+def exported(path):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    return {n for n in names if n.startswith(("gemm_", "tgemm_"))}
+
+
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 9, syms
+    assert len(syms) == 10, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -35,12 +44,40 @@ def test_exports_every_header_symbol():
 
 
 def test_only_header_symbols_are_exported():
-    import subprocess
-    out = subprocess.run(["nm", "-D", "--defined-only", tg.LIBRARY], capture_output=True, text=True,
-                         check=True).stdout
-    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
-    ours = {n for n in names if n.startswith(("gemm_", "tgemm_"))}
-    assert ours == set(header_symbols())
+    assert exported(tg.LIBRARY) == set(header_symbols())
+
+
+def test_instrumented_build_exports():
+    """libtgemm_stamps.so exports tgemm.h plus tgemm_stamps.h, and nothing else."""
+    extra = header_symbols("tgemm_stamps.h")
+    assert sorted(tg.STAMPS_EXPORTS) == extra
+    assert exported(tg.STAMPS_LIBRARY) == set(header_symbols()) | set(extra)
+    assert not (exported(tg.LIBRARY) & set(extra))
+    S = tg.stamps_lib()
+    import ctypes
+    nwg, words = ctypes.c_int(), ctypes.c_int()
+    assert S.tgemm_stamps_capacity(ctypes.byref(nwg), ctypes.byref(words)) == tg.TGEMM_OK
+    text = open(os.path.join(ROOT, "include", "tgemm_stamps.h")).read()
+    assert f"#define TGEMM_STAMP_WORKGROUPS {nwg.value}" in text
+    assert f"#define TGEMM_STAMP_WORDS {words.value}" in text
+    assert S.tgemm_stamps_capacity(None, ctypes.byref(words)) == tg.TGEMM_ENULL
+    assert S.tgemm_stamps_read(None, 8) == tg.TGEMM_ENULL
+    buf = (ctypes.c_uint64 * 8)()
+    assert S.tgemm_stamps_read(buf, -1) == tg.TGEMM_EINVAL_DIM
+    assert S.tgemm_stamps_read(buf, nwg.value * words.value + 1) == tg.TGEMM_EINVAL_DIM
+
+
+def test_probe_argument_checks():
+    """Rejected before any HIP call; the shape constants match the header."""
+    L = tg.lib()
+    text = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    assert f"#define TGEMM_PROBE_THREADS {tg.PROBE_THREADS}" in text
+    assert f"#define TGEMM_PROBE_MFMA_PER_ITER {tg.PROBE_MFMA_PER_ITER}" in text
+    assert L.tgemm_mfma_probe(1, 1, None, None) == tg.TGEMM_ENULL
+    assert L.tgemm_mfma_probe(0, 1, 16, None) == tg.TGEMM_EINVAL_DIM
+    assert L.tgemm_mfma_probe((1 << 20) + 1, 1, 16, None) == tg.TGEMM_EINVAL_DIM
+    assert L.tgemm_mfma_probe(1, 0, 16, None) == tg.TGEMM_EINVAL_DIM
+    assert L.tgemm_mfma_probe(1, (1 << 24) + 1, 16, None) == tg.TGEMM_EINVAL_DIM
 
 
 def test_error_codes_match_header():

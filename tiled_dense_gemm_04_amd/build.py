@@ -1,6 +1,8 @@
-"""Build libtgemm.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libtgemm.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and its
+instrumented twin libtgemm_stamps.so (the same sources with per-workgroup timestamps,
+used only by the measurement tools).
 
-Usage: python -m tiled_dense_gemm_04_amd.build   (always recompiles)
+Usage: python -m tiled_dense_gemm_04_amd.build   (always recompiles both)
 """
 from __future__ import annotations
 
@@ -13,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libtgemm.so")
+STAMPS_LIBRARY = os.path.join(PKG, "libtgemm_stamps.so")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "tgemm_kernels.hip"), os.path.join(CSRC, "tgemm_api.cpp")]
@@ -36,9 +39,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtgemm)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + ["-o", tmp] + SOURCES
+def build(verbose: bool = False, extra_flags=None, stamps: bool = False) -> str:
+    target = STAMPS_LIBRARY if stamps else LIBRARY
+    tmp = target + ".tmp"
+    flags = list(extra_flags or []) + (["-DTGEMM_STAMPS"] if stamps else [])
+    cmd = [hipcc()] + HIPCC_FLAGS + flags + ["-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,10 +54,20 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, target)
+    return target
+
+
+def build_all(verbose: bool = False):
+    """Both libraries, compiled in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(2) as ex:
+        futs = [ex.submit(build, verbose, None, st) for st in (False, True)]
+        return [f.result() for f in futs]
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    for path in build_all(verbose=True):
+        print(path)
     sys.exit(0)

@@ -7,7 +7,14 @@
 #include <cstring>
 
 #include "../../include/tgemm.h"
+#ifdef TGEMM_STAMPS
+#include "../../include/tgemm_stamps.h"
+#endif
 #include "tgemm_internal.h"
+
+static_assert(TGEMM_PROBE_THREADS == tgemm::kProbeThreads &&
+                  TGEMM_PROBE_MFMA_PER_ITER == tgemm::kProbeMfmaPerIter,
+              "probe shape in the header matches the kernel");
 
 namespace {
 
@@ -209,5 +216,41 @@ int tgemm_tile_of(int idx, int64_t M, int64_t N, int64_t wg, int64_t* tile_m, in
   tgemm::tile_of(wg, tm, tn, panel, xcd, tile_m, tile_n);
   return TGEMM_OK;
 }
+
+int tgemm_mfma_probe(int blocks, int iters, void* out, void* stream) {
+  if (out == nullptr) return TGEMM_ENULL;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24)) return TGEMM_EINVAL_DIM;
+  int dev = -1;
+  const int d = check_device(&dev);
+  if (d != TGEMM_OK) return d;
+  return tgemm::launch_mfma_probe(blocks, iters, static_cast<float*>(out),
+                                  static_cast<hipStream_t>(stream)) == hipSuccess
+             ? TGEMM_OK
+             : TGEMM_ELAUNCH;
+}
+
+#ifdef TGEMM_STAMPS
+static_assert(TGEMM_STAMP_WORKGROUPS == tgemm::kStampWorkgroups &&
+                  TGEMM_STAMP_WORDS == tgemm::kStampWords,
+              "stamp table shape in the header matches the kernels");
+
+int tgemm_stamps_capacity(int* workgroups, int* words_per_workgroup) {
+  if (workgroups == nullptr || words_per_workgroup == nullptr) return TGEMM_ENULL;
+  *workgroups = tgemm::kStampWorkgroups;
+  *words_per_workgroup = tgemm::kStampWords;
+  return TGEMM_OK;
+}
+
+int tgemm_stamps_read(uint64_t* host, int64_t words) {
+  if (host == nullptr) return TGEMM_ENULL;
+  if (words < 0 || words > (int64_t)tgemm::kStampWorkgroups * tgemm::kStampWords) return TGEMM_EINVAL_DIM;
+  if (words == 0) return TGEMM_OK;
+  return tgemm::stamps_read(reinterpret_cast<unsigned long long*>(host), words) == hipSuccess
+             ? TGEMM_OK
+             : TGEMM_ELAUNCH;
+}
+
+int tgemm_stamps_clear(void) { return tgemm::stamps_clear() == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH; }
+#endif
 
 }  // extern "C"

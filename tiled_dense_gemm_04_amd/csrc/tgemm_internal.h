@@ -81,4 +81,19 @@ Launcher launcher(int idx);
 // Zero-fill of an M x N block with row stride ldc (the K == 0 case).
 hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s);
 
+// MFMA throughput probe (tooling): `blocks` workgroups of 8 waves, each wave issuing
+// iters x 16 independent 16x16x32 fp16 MFMAs; one float per thread goes to out
+// (blocks * 512 floats).
+constexpr int kProbeThreads = 512, kProbeMfmaPerIter = 16;
+hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s);
+
+// Workgroup timestamps of the instrumented build (TGEMM_STAMPS): kStampWords words per
+// workgroup for the first kStampWorkgroups workgroups of every launch (later launches
+// overwrite earlier ones).
+constexpr int kStampWorkgroups = 4096, kStampWords = 8;
+#ifdef TGEMM_STAMPS
+hipError_t stamps_read(unsigned long long* host, int64_t words);
+hipError_t stamps_clear();
+#endif
+
 }  // namespace tgemm

@@ -54,6 +54,51 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
 
+// Per-workgroup timestamps, compiled in only for the instrumented build (TGEMM_STAMPS) and
+// empty otherwise. Words per workgroup: wall clock (s_memrealtime, 100 MHz) at kernel
+// start, main-loop start, main-loop end and after every wave's stores completed; shader
+// clock ticks (s_memtime, which counts at the current shader clock) from kernel start to
+// main-loop end; main-loop iterations; threads per workgroup; 1 (written). Ticks divided
+// by wall time is the shader clock the workgroup ran at.
+#ifdef TGEMM_STAMPS
+__device__ unsigned long long g_stamps[kStampWorkgroups * kStampWords];
+struct WgClock {
+  unsigned long long rt0, ct0, rt1, rt2, ct2;
+  __device__ void start() {
+    rt0 = __builtin_amdgcn_s_memrealtime();
+    ct0 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ void loop_begin() { rt1 = __builtin_amdgcn_s_memrealtime(); }
+  __device__ void loop_end() {
+    rt2 = __builtin_amdgcn_s_memrealtime();
+    ct2 = __builtin_amdgcn_s_memtime();
+  }
+  // Called by every thread of the workgroup, at its very end.
+  __device__ void finish(int iterations) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kStampWorkgroups) {
+      unsigned long long* o = &g_stamps[(size_t)blockIdx.x * kStampWords];
+      o[0] = rt0;
+      o[1] = rt1;
+      o[2] = rt2;
+      o[3] = __builtin_amdgcn_s_memrealtime();
+      o[4] = ct2 - ct0;
+      o[5] = (unsigned long long)iterations;
+      o[6] = blockDim.x;
+      o[7] = 1;
+    }
+  }
+};
+#else
+struct WgClock {
+  __device__ void start() {}
+  __device__ void loop_begin() {}
+  __device__ void loop_end() {}
+  __device__ void finish(int) {}
+};
+#endif
+
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor: base address, stride 0, range in bytes, gfx9 word 3. All inputs
@@ -128,6 +173,8 @@ __host__ __device__ constexpr int swz_b(int k) { return (4 * (k & 3)) ^ (2 * ((k
 // K and N multiples of 8; K > 0.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
+  WgClock clk;
+  clk.start();
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -275,6 +322,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue(s, s);
   constexpr int PER_TILE = A_LD + B_LD;
+  clk.loop_begin();
   for (int kt = 0; kt < nk; ++kt) {
     // Tile kt has landed once at most min(STAGES-2, nk-1-kt) later tiles are in flight.
     const int ahead = nk - 1 - kt;
@@ -288,6 +336,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     compute(kt % STAGES);
   }
+
+  clk.loop_end();
 
   // Epilogue: ReLU in fp32, round to fp16 (nearest even), 8-byte stores. Lane holds, for
   // tile (fm, fn) and group g4, row m = ... + l32 and columns n = ... + 8*g4 + 4*lhi + 0..3.
@@ -316,6 +366,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
       }
     }
   }
+  clk.finish(nk);
 }
 
 // ------------------------------------------------------------------------------------
@@ -333,6 +384,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
 //   * descriptors advance by a constant stride; only the last k-tile has its own range.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
+  WgClock clk;
+  clk.start();
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -520,6 +573,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
     lds_barrier();
     step(cur, nxt, (kt + 1) % STAGES, d);
   };
+  clk.loop_begin();
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     iteration(kt, f0, f1);
@@ -528,6 +582,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
   if (kt < nk) iteration(kt, f0, f1);
   // Drain: no copy may still be writing LDS when the workgroup exits.
   wait_vmcnt<0>();
+  clk.loop_end();
 
   const bool relu = g.relu != 0;
 #pragma unroll
@@ -554,6 +609,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
       }
     }
   }
+  clk.finish(nk);
 }
 
 // ------------------------------------------------------------------------------------
@@ -594,6 +650,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int SYNC2,
           bool CIM, int MF = 32>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
+  WgClock clk;
+  clk.start();
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
@@ -781,6 +839,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   lds_barrier();
   if (grp == 0) read_tile(0);
 
+  clk.loop_begin();
   // sched_barrier(0) pins every phase: the compiler may not move MFMAs (register-only,
   // so not ordered by s_barrier) from one phase into the other.
   if (grp == 0) {
@@ -815,22 +874,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
     }
   }
   wait_vmcnt<0>();
+  clk.loop_end();
 
-  // Epilogue: lane holds, for tile (fm, fn), row m = fm*MF + lane % MF of the wave tile and
-  // columns n = fn*MF + 8*g4 + 4*(lane / MF) .. +3 (32x32) or fn*16 + 4*(lane / 16) .. +3
-  // (16x16). ReLU in fp32, round to fp16 (nearest even), one 8-byte store per 4 columns.
+  // Epilogue. Lane holds, for tile (fm, fn), row fm*MF + lane % MF of the wave tile and
+  // columns fn*MF + 8*g4 + 4*(lane / MF) .. +3 (32x32) or fn*16 + 4*(lane / 16) .. +3
+  // (16x16). ReLU in fp32 and rounding to fp16 (nearest even) happen in registers; then
+  // every wave stages its WTM x WTN fp16 sub-tile in its own LDS region (the ring is free:
+  // every copy, including the empty-range ones past the last tile, has landed once all
+  // waves pass the barrier below) and writes it back row by row, 16 bytes per lane and
+  // WTN / 8 lanes per row, so each store covers whole 16-byte-aligned row segments instead
+  // of 8-byte pieces of MF rows. Staged row r, 16-byte chunk c sits at chunk
+  // c ^ ((r / 2) % (WTN / 8)): conflict-free LDS writes for the 16x16 layout (2-way for
+  // 32x32) and conflict-free row reads. N and ldc are multiples of 8 on this path, so a
+  // chunk is either wholly inside the matrix or wholly outside.
+  constexpr int RB = WTN * 2, CPR = WTN / 8;
+  static_assert(BM * BN * 2 <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
+  static_assert((CPR & (CPR - 1)) == 0 && 64 % CPR == 0 && (WTM * CPR) % 64 == 0, "row-copy shape");
+  __syncthreads();
+  char* const stage = smem + wave * (WTM * RB);
   const bool relu = g.relu != 0;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const int m = wm * WTM + fm * MF + lrow;
-    if (m >= mvalid) continue;
-    _Float16* const crow = g.C + (int64_t)(row0 + m) * g.ldc + col0;
+    const int mw = fm * MF + lrow;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
       for (int g4 = 0; g4 < NACC / 4; ++g4) {
-        const int n = wn * WTN + fn * MF + 8 * g4 + 4 * lkg;
-        if (n >= nvalid) continue;
+        const int nw = fn * MF + 8 * g4 + 4 * lkg;
         float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
         float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
         if (relu) {
@@ -839,11 +909,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
           v2 = relu_f(v2);
           v3 = relu_f(v3);
         }
-        half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        *(half4*)(crow + n) = h;
+        const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+        const int off = mw * RB + ((((nw >> 3) ^ ((mw >> 1) % CPR))) << 4) + (nw & 7) * 2;
+        *(TG_LDS half4*)(stage + off) = h;
       }
     }
   }
+  // The rows read back below were written by other lanes of this wave: keep the compiler
+  // from moving the reads above the writes (LDS executes one wave's instructions in order).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+  for (int i = 0; i < WTM * CPR / 64; ++i) {
+    const int idx = i * 64 + lane;
+    const int r = idx / CPR, c = idx % CPR;
+    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % CPR)) << 4));
+    const int m = wm * WTM + r, n = wn * WTN + 8 * c;
+    if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
+  }
+  clk.finish(nk);
 }
 
 // ------------------------------------------------------------------------------------
@@ -900,6 +985,54 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g) {
       g.C[(int64_t)m * g.ldc + n] = (_Float16)v;
     }
   }
+}
+
+// MFMA throughput probe (tooling, not part of the GEMM): every wave keeps 16 independent
+// 16x16x32 accumulators and issues them back to back, `iters` rounds, on register operands
+// filled with pseudo-random binary16 values (random sign and mantissa, magnitudes 2^-2 to
+// 2^1, so the multipliers toggle like they do on N(0,1) data). Each thread stores the sum
+// of its accumulators so the work stays live. Measures the MFMA rate this board sustains
+// at its power limit, with no memory traffic at all.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe(int iters, float* out) {
+  WgClock clk;
+  clk.start();
+  const uint32_t tid = blockIdx.x * kProbeThreads + threadIdx.x;
+  half8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t ha = mix32(tid * 64u + 8u * i + e), hb = mix32(~(tid * 64u + 8u * i + e));
+      const uint16_t ba = (uint16_t)(((ha >> 31) << 15) | ((13u + ((ha >> 10) & 3u)) << 10) | (ha & 0x3FFu));
+      const uint16_t bb = (uint16_t)(((hb >> 31) << 15) | ((13u + ((hb >> 10) & 3u)) << 10) | (hb & 0x3FFu));
+      a[i][e] = __builtin_bit_cast(_Float16, ba);
+      b[i][e] = __builtin_bit_cast(_Float16, bb);
+    }
+  typedef float float4v __attribute__((ext_vector_type(4)));
+  float4v acc[kProbeMfmaPerIter];
+#pragma unroll
+  for (int j = 0; j < kProbeMfmaPerIter; ++j) acc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  clk.loop_begin();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kProbeMfmaPerIter; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 3], a[j >> 2], acc[j], 0, 0, 0);
+  }
+  clk.loop_end();
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kProbeMfmaPerIter; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  out[tid] = sum;
+  clk.finish(iters);
 }
 
 // C[i, j] = +0 for i < M, j < N (the empty sum when K == 0).
@@ -972,6 +1105,22 @@ hipError_t launch_generic(const GemmArgs& g, hipStream_t s, int) {
 }
 
 }  // namespace
+
+hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters, out);
+  return hipGetLastError();
+}
+
+#ifdef TGEMM_STAMPS
+hipError_t stamps_read(unsigned long long* host, int64_t words) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_stamps), (size_t)words * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost);
+}
+hipError_t stamps_clear() {
+  static const unsigned long long zeros[kStampWorkgroups * kStampWords] = {};
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_stamps), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
+}
+#endif
 
 hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s) {
   const int64_t total = (int64_t)M * N;

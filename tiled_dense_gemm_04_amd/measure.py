@@ -1,0 +1,263 @@
+"""Timing protocol for every measured workload (one MI355X), beyond bench.py's one line.
+
+For each workload, with the config gemm_f16 picks:
+  * warm: 10 untimed calls, then 7 trials of R back-to-back calls (R chosen so a trial
+    lasts >= 20 ms), each trial bracketed by HIP events on the launch stream; the median
+    trial gives us per call, TFLOP/s = 2MNK / t, and % of the dense fp16 MFMA peak
+    (256 CU x 4096 FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s) and of the measured MFMA ceiling;
+  * cold: the same with >= 4 distinct (A, B, C) buffer sets totalling more than 288 MiB
+    (more than the 256 MiB Infinity Cache), rotated call by call, so every call starts
+    with its operands out of every cache;
+  * phases: one more trial through the instrumented build (libtgemm_stamps.so); the
+    stamps of its last call give, per workgroup, prologue / main loop / epilogue wall
+    time, the shader clock the workgroup ran at, and the main loop's average per XCD;
+  * context: torch.matmul (hipBLASLt) (+ relu_ when the workload has ReLU) timed the
+    same way. Context only; never a target.
+The MFMA ceiling is the library's MFMA probe (no memory traffic, pseudo-random
+operands) timed the same way, with its own clock from the stamps.
+
+  python -m tiled_dense_gemm_04_amd.measure [--workloads a,b] [--no-cold] [--no-torch]
+      [--json out.json] [--md out.md]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+REALTIME_HZ = 100e6          # s_memrealtime
+CACHE_BYTES = 288 << 20      # cold sets must exceed this in total (Infinity Cache: 256 MiB)
+NUM_XCD = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed_trials(torch, stream, call, trials=7, min_ms=20.0, warm=10):
+    """Median microseconds per call over `trials` trials of R calls each."""
+    for _ in range(warm):
+        call(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(5):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est_ms = e0.elapsed_time(e1) / 5
+    reps = max(5, math.ceil(min_ms / max(est_ms, 1e-3)))
+    per = []
+    for _ in range(trials):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps * 1e3)
+    return {"median_us": statistics.median(per), "min_us": min(per), "max_us": max(per),
+            "calls_per_trial": reps, "trials": trials}
+
+
+def phases(stamps):
+    """Summary of a stamp table (rows = workgroups of one launch)."""
+    import numpy as np
+    st = stamps[stamps[:, 7] == 1].astype(np.float64)
+    if len(st) == 0:
+        return None
+    t0 = st[:, 0].min()
+    pro = (st[:, 1] - st[:, 0]) / REALTIME_HZ * 1e6
+    loop = (st[:, 2] - st[:, 1]) / REALTIME_HZ * 1e6
+    epi = (st[:, 3] - st[:, 2]) / REALTIME_HZ * 1e6
+    clk = st[:, 4] / np.maximum(st[:, 2] - st[:, 0], 1) * REALTIME_HZ / 1e9
+    ids = np.nonzero(stamps[:, 7] == 1)[0]
+    per_xcd = [float(loop[ids % NUM_XCD == x].mean()) if np.any(ids % NUM_XCD == x) else None
+               for x in range(NUM_XCD)]
+    iters = float(st[:, 5].mean())
+    return {
+        "workgroups": int(len(st)),
+        "prologue_us": float(pro.mean()),
+        "loop_us": float(loop.mean()),
+        "loop_us_max": float(loop.max()),
+        "epilogue_us": float(epi.mean()),
+        "span_us": float((st[:, 3].max() - t0) / REALTIME_HZ * 1e6),
+        "start_spread_us": float((st[:, 0].max() - t0) / REALTIME_HZ * 1e6),
+        "loop_iterations": iters,
+        "ns_per_iteration": float(loop.mean() / max(iters, 1) * 1e3),
+        "shader_clock_ghz": float(clk.mean()),
+        "loop_us_per_xcd": per_xcd,
+    }
+
+
+def measure_probe(torch, tg, stream, blocks=512, iters=2000):
+    out = torch.empty(blocks * tg.PROBE_THREADS, dtype=torch.float32, device="cuda")
+    flop = blocks * (tg.PROBE_THREADS // 64) * iters * tg.PROBE_MFMA_PER_ITER * tg.PROBE_FLOP_PER_MFMA
+
+    def call(_i, library=None):
+        tg.tgemm_mfma_probe(blocks, iters, out, stream=stream, library=library)
+
+    t = timed_trials(torch, stream, call)
+    S = tg.stamps_lib()
+    timed_trials(torch, stream, lambda i: call(i, S), trials=1, warm=2)
+    ph = phases(tg.tgemm_stamps_read(blocks))
+    torch.cuda.synchronize()
+    if not torch.isfinite(out).all():
+        raise RuntimeError("MFMA probe produced non-finite values")
+    tf = flop / (t["median_us"] * 1e-6) / 1e12
+    res = {"blocks": blocks, "iters": iters, "flop": flop, **t, "tflops": tf,
+           "pct_of_peak": 100 * tf / PEAK_TFLOPS, "phases": ph}
+    log(f"MFMA probe: {t['median_us']:.1f} us/launch, {tf:.1f} TFLOP/s ({100 * tf / PEAK_TFLOPS:.1f} % of "
+        f"{PEAK_TFLOPS:.1f}); shader clock {ph['shader_clock_ghz'] if ph else float('nan'):.3f} GHz")
+    return res
+
+
+def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceiling=None):
+    A, B = w.inputs()
+    a = torch.from_numpy(A).cuda()
+    b = torch.from_numpy(B).cuda()
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    cfg = tg.tgemm_select_config(w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
+                                 c.data_ptr(), c.stride(0))
+    desc = tg.tgemm_config_desc(cfg)
+    res = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "relu": w.relu, "flop": w.flop,
+           "config": desc["name"], "config_index": cfg,
+           "compulsory_bytes": 2 * (w.M * w.K + w.K * w.N + w.M * w.N)}
+
+    def tf(us):
+        return w.flop / (us * 1e-6) / 1e12
+
+    hot = timed_trials(torch, stream, lambda i: tg.gemm_f16(a, b, c, relu=w.relu, stream=stream))
+    res["hot"] = {**hot, "tflops": tf(hot["median_us"]), "pct_of_peak": 100 * tf(hot["median_us"]) / PEAK_TFLOPS}
+    if ceiling:
+        res["hot"]["pct_of_mfma_ceiling"] = 100 * tf(hot["median_us"]) / ceiling
+    log(f"{w.name}: {desc['name']} hot {hot['median_us']:.2f} us ({tf(hot['median_us']):.1f} TFLOP/s)")
+
+    if cold:
+        per_set = res["compulsory_bytes"]
+        nsets = max(4, math.ceil(CACHE_BYTES / per_set) + 1)
+        sets = [(a.clone(), b.clone(), torch.empty_like(c)) for _ in range(nsets)]
+        cold_t = timed_trials(torch, stream, lambda i: tg.gemm_f16(sets[i % nsets][0], sets[i % nsets][1],
+                                                                 sets[i % nsets][2], relu=w.relu, stream=stream))
+        res["cold"] = {**cold_t, "sets": nsets, "bytes_total": nsets * per_set,
+                       "tflops": tf(cold_t["median_us"]), "pct_of_peak": 100 * tf(cold_t["median_us"]) / PEAK_TFLOPS}
+        log(f"{w.name}: cold ({nsets} sets, {nsets * per_set / 2**20:.0f} MiB) {cold_t['median_us']:.2f} us")
+        del sets
+        torch.cuda.empty_cache()
+
+    S = tg.stamps_lib()
+    timed_trials(torch, stream, lambda i: tg.gemm_f16(a, b, c, relu=w.relu, stream=stream, library=S),
+                 trials=1, warm=3)
+    nwg = tg.tgemm_num_workgroups(cfg, w.M, w.N)
+    res["phases"] = phases(tg.tgemm_stamps_read(nwg))
+    if res["phases"]:
+        ph = res["phases"]
+        log(f"{w.name}: phases prologue {ph['prologue_us']:.2f} loop {ph['loop_us']:.2f} "
+            f"epilogue {ph['epilogue_us']:.2f} us, clock {ph['shader_clock_ghz']:.3f} GHz")
+
+    if with_torch:
+        def tmm(_i):
+            r = torch.matmul(a, b)
+            if w.relu:
+                torch.relu_(r)
+        with torch.cuda.stream(stream):
+            th = timed_trials(torch, stream, tmm)
+        res["torch_matmul"] = {**th, "tflops": tf(th["median_us"]), "note": "context only (hipBLASLt"
+                               + (" + separate relu_ kernel)" if w.relu else ")")}
+        log(f"{w.name}: torch.matmul{'+relu_' if w.relu else ''} {th['median_us']:.2f} us")
+    del a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
+def markdown(results, probe, host) -> str:
+    L = []
+    L.append(f"Device: {host['device']}; {host['library']}; torch {host['torch']}.")
+    L.append("")
+    if probe:
+        ph = probe.get("phases") or {}
+        L.append(f"MFMA ceiling (probe: {probe['blocks']} workgroups x 8 waves, {probe['iters']} rounds of 16 "
+                 f"independent 16x16x32 fp16 MFMAs, pseudo-random operands, no memory traffic): "
+                 f"**{probe['tflops']:.1f} TFLOP/s** = {probe['pct_of_peak']:.1f} % of {PEAK_TFLOPS:.1f}, "
+                 f"shader clock {ph.get('shader_clock_ghz', float('nan')):.3f} GHz (s_memtime / s_memrealtime).")
+        L.append("")
+    L.append("| workload | config | hot us (min-max) | TFLOP/s | % peak | % MFMA ceiling | cold us | "
+             "hipBLASLt us (context) |")
+    L.append("|---|---|---|---|---|---|---|---|")
+    for r in results:
+        h = r["hot"]
+        cold = f"{r['cold']['median_us']:.2f} ({r['cold']['sets']} sets)" if "cold" in r else "-"
+        th = f"{r['torch_matmul']['median_us']:.2f}" if "torch_matmul" in r else "-"
+        ceil = f"{h['pct_of_mfma_ceiling']:.1f}" if "pct_of_mfma_ceiling" in h else "-"
+        L.append(f"| {r['workload']} ({r['M']}x{r['N']}x{r['K']}) | {r['config']} | {h['median_us']:.2f} "
+                 f"({h['min_us']:.2f}-{h['max_us']:.2f}) | {h['tflops']:.1f} | {h['pct_of_peak']:.1f} | {ceil} | "
+                 f"{cold} | {th} |")
+    L.append("")
+    L.append("Phases of the last call of one more trial, instrumented build (means over workgroups):")
+    L.append("")
+    L.append("| workload | workgroups | prologue us | main loop us (max) | epilogue us | launch span us | "
+             "ns per k-tile | shader clock GHz | main loop us per XCD 0..7 |")
+    L.append("|---|---|---|---|---|---|---|---|---|")
+    for r in results:
+        ph = r.get("phases")
+        if not ph:
+            continue
+        xcd = " ".join(f"{v:.1f}" if v is not None else "-" for v in ph["loop_us_per_xcd"])
+        L.append(f"| {r['workload']} | {ph['workgroups']} | {ph['prologue_us']:.2f} | {ph['loop_us']:.2f} "
+                 f"({ph['loop_us_max']:.2f}) | {ph['epilogue_us']:.2f} | {ph['span_us']:.2f} | "
+                 f"{ph['ns_per_iteration']:.0f} | {ph['shader_clock_ghz']:.3f} | {xcd} |")
+    return "\n".join(L) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--workloads", default=None, help="comma-separated names (default: all)")
+    ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--no-torch", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--json", default=None)
+    ap.add_argument("--md", default=None)
+    args = ap.parse_args()
+
+    import torch
+
+    import tgemm_workloads as W
+    import tiled_dense_gemm_04_amd as tg
+
+    if not torch.cuda.is_available():
+        log("measure needs a GPU")
+        return 1
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    works = [W.HEADLINE] + list(W.WORKLOADS.values())
+    if args.workloads:
+        keep = set(args.workloads.split(","))
+        works = [w for w in works if w.name in keep]
+    host = {"device": torch.cuda.get_device_name(0), "library": tg.tgemm_version(), "torch": torch.__version__,
+            "time": time.strftime("%Y-%m-%d %H:%M:%S")}
+    probe = None if args.no_probe else measure_probe(torch, tg, stream)
+    ceiling = probe["tflops"] if probe else None
+    results = [measure_workload(torch, tg, W, w, stream, cold=not args.no_cold, with_torch=not args.no_torch,
+                                ceiling=ceiling) for w in works]
+    md = markdown(results, probe, host)
+    print(md)
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump({"host": host, "probe": probe, "results": results}, f, indent=1)
+    if args.md:
+        with open(args.md, "w") as f:
+            f.write(md)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
