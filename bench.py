@@ -96,7 +96,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="relu_4096",
-                    help="relu_4096 (headline) or a name from tgemm_workloads.WORKLOADS")
+                    help="relu_4096 (headline) or another name from tgemm_workloads.all_workloads()")
     ap.add_argument("--cfg", type=int, default=None, help="force a config index (sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -133,22 +133,24 @@ def main() -> int:
     if not torch.cuda.is_available():
         eprint("bench.py needs a GPU")
         return 1
-    w = W.HEADLINE if args.workload == "relu_4096" else W.WORKLOADS[args.workload]
+    w = W.by_name(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     A, B = w.inputs()
-    a = torch.from_numpy(A).to(dev)
-    b = torch.from_numpy(B).to(dev)
+    SA, SB = w.stored(A, B)
+    a = torch.from_numpy(SA).to(dev)
+    b = torch.from_numpy(SB).to(dev)
     c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     stream = torch.cuda.Stream(dev)
-    cfg = args.cfg if args.cfg is not None else tg.tgemm_select_config(
-        w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), c.data_ptr(), c.stride(0))
+    cfg = args.cfg if args.cfg is not None else tg.tgemm_select_config_ex(
+        w.trans_a, w.trans_b, w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
+        c.data_ptr(), c.stride(0))
     cfg_name = tg.tgemm_config_desc(cfg)["name"]
     eprint(f"{torch.cuda.get_device_name(dev)}; {tg.tgemm_version()}; workload {w.name} "
            f"{w.M}x{w.N}x{w.K} relu={w.relu}; config {cfg} {cfg_name}")
 
     def step():
-        tg.gemm_f16(a, b, c, relu=w.relu, stream=stream, cfg=args.cfg)
+        tg.gemm_f16_ex(a, b, c, w.trans_a, w.trans_b, relu=w.relu, stream=stream, cfg=args.cfg)
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -192,6 +194,8 @@ def main() -> int:
             "workload": w.name,
             "M": w.M, "N": w.N, "K": w.K,
             "relu": w.relu,
+            "trans_a": w.trans_a,
+            "trans_b": w.trans_b,
             "inputs": f"fp16 iid {'N(0,%g)' % w.std if w.dist == 'normal' else 'U(-1,1)'} seed {w.seed}",
             "accumulate": "fp32",
             "kernel_config": cfg_name,

@@ -39,8 +39,9 @@ extern "C" {
 
 #define TGEMM_OK 0
 #define TGEMM_EINVAL_DIM (-1)   /* M, N or K negative, or larger than TGEMM_MAX_DIM        */
-#define TGEMM_EINVAL_LD (-2)    /* lda < max(1,K), ldb < max(1,N), ldc < max(1,N), or an   */
-                                /* ld larger than TGEMM_MAX_LD                              */
+#define TGEMM_EINVAL_LD (-2)    /* lda < max(1,K), ldb < max(1,N), ldc < max(1,N) (with    */
+                                /* transposed operands lda < max(1,M), ldb < max(1,K)), or */
+                                /* an ld larger than TGEMM_MAX_LD                          */
 #define TGEMM_ENULL (-3)        /* NULL pointer for an operand with a nonzero extent        */
 #define TGEMM_EDEVICE (-4)      /* current HIP device is not gfx950, or no device           */
 #define TGEMM_ELAUNCH (-5)      /* the kernel launch was rejected by the HIP runtime        */
@@ -70,6 +71,27 @@ TGEMM_API int gemm_f16(int64_t M, int64_t N, int64_t K,
              void* C, int64_t ldc,
              int relu, void* stream);
 
+/*
+ * C = ReLU(op(A) @ op(B)) if relu != 0, else C = op(A) @ op(B), with the operands given
+ * either way round -- the transposed-operand GEMMs of the autograd wrapper in
+ * "TileLang-MUSA operator development" (7yue.com), section 6, whose backward computes
+ * dA = dC @ B^T and dB = A^T @ dC:
+ *   trans_a == 0 : op(A) = A, stored M x K row-major, lda >= max(1, K);
+ *   trans_a != 0 : op(A) = A^T, A stored K x M row-major, lda >= max(1, M);
+ *   trans_b == 0 : op(B) = B, stored K x N row-major, ldb >= max(1, N);
+ *   trans_b != 0 : op(B) = B^T, B stored N x K row-major, ldb >= max(1, K).
+ * Everything else as gemm_f16 (which is gemm_f16_ex(0, 0, ...)). The fast path needs A, B,
+ * C 16-byte aligned, lda, ldb, ldc multiples of 8, N a multiple of 8 and each operand's
+ * contiguous dimension (K for A and for B^T, M for A^T, N for B) a multiple of 8; other
+ * arguments take the generic kernel. On the fast path the result is bit-for-bit the same
+ * for all four layouts of the same logical operands.
+ */
+TGEMM_API int gemm_f16_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda,
+                          const void* B, int64_t ldb,
+                          void* C, int64_t ldc,
+                          int relu, void* stream);
+
 /* Human-readable text for a return code (static storage, never NULL). */
 TGEMM_API const char* tgemm_strerror(int code);
 
@@ -87,6 +109,7 @@ typedef struct tgemm_config_info {
     int32_t xcd_remap;                 /* 1 = consecutive tiles kept on one XCD         */
     int32_t generic;                   /* 1 = unaligned-capable generic kernel          */
     int32_t lds_bytes;                 /* dynamic LDS per workgroup                     */
+    int32_t layouts;                   /* bit (2*trans_a + trans_b) set: layout accepted */
     char name[48];
 } tgemm_config_info;
 
@@ -103,6 +126,20 @@ TGEMM_API int tgemm_select_config(int64_t M, int64_t N, int64_t K,
                         const void* A, int64_t lda,
                         const void* B, int64_t ldb,
                         const void* C, int64_t ldc);
+
+/* tgemm_select_config for gemm_f16_ex's operand layouts. */
+TGEMM_API int tgemm_select_config_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                        const void* A, int64_t lda,
+                        const void* B, int64_t ldb,
+                        const void* C, int64_t ldc);
+
+/* gemm_f16_ex forced to config idx (TGEMM_EINVAL_CFG also when the config does not take
+ * this operand layout, see tgemm_config_info.layouts). */
+TGEMM_API int gemm_f16_ex_cfg(int idx, int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda,
+                  const void* B, int64_t ldb,
+                  void* C, int64_t ldc,
+                  int relu, void* stream);
 
 /* gemm_f16 forced to config idx (same arguments and error codes; TGEMM_EINVAL_CFG if
  * idx is out of range or the fast config cannot take these pointers / strides). */

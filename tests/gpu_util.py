@@ -20,12 +20,16 @@ def to_dev(x: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
 
 
-def run(A: np.ndarray, B: np.ndarray, relu: bool, cfg=None, stream=None) -> np.ndarray:
-    """fp16 numpy in -> fp16 output bits (uint16 numpy) out."""
+def run(A: np.ndarray, B: np.ndarray, relu: bool, cfg=None, stream=None, trans_a=False,
+        trans_b=False) -> np.ndarray:
+    """fp16 numpy in (the logical op(A) M x K and op(B) K x N) -> fp16 output bits (uint16
+    numpy) out. With trans_a / trans_b the operand goes to the library stored transposed
+    (a row-major copy of its transpose) through gemm_f16_ex."""
     torch = torch_cuda()
-    a, b = to_dev(A), to_dev(B)
+    a = to_dev(A.T if trans_a else A)
+    b = to_dev(B.T if trans_b else B)
     c = torch.full((A.shape[0], B.shape[1]), float("nan"), dtype=torch.float16, device="cuda")
-    tg.gemm_f16(a, b, c, relu=relu, cfg=cfg, stream=stream)
+    tg.gemm_f16_ex(a, b, c, trans_a=trans_a, trans_b=trans_b, relu=relu, cfg=cfg, stream=stream)
     torch.cuda.synchronize()
     return c.cpu().numpy().view(np.uint16)
 

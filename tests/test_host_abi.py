@@ -36,7 +36,7 @@ def exported(path):
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 13, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -167,6 +167,45 @@ def test_gemm_rejects_invalid_before_hip():
     assert tg.gemm_f16_raw(0, 8, 8, 0, 8, 0, 8, 0, 8, 1, None) == tg.TGEMM_OK  # no-op
     assert tg.gemm_f16_cfg_raw(99, 8, 8, 8, A16, 8, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_CFG
     assert tg.gemm_f16_cfg_raw(1, 8, 8, 8, A16 + 2, 8, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_CFG
+
+
+def test_config_layouts():
+    """Every config takes A and B as given; the generic kernel and the ping-pong configs
+    the selector uses for transposed operands take all four layouts."""
+    cfgs = tg.configs()
+    for c in cfgs:
+        assert c["layouts"] & 1 and c["layouts"] in (1, 0xF)
+    assert cfgs[0]["layouts"] == 0xF
+    P = dict(A=A16, B=A16, C=A16)
+    for ta in (0, 1):
+        for tb in (0, 1):
+            for M, N, K in [(4096, 4096, 4096), (1024, 1024, 1024), (16384, 512, 4096), (4096, 3000, 1000)]:
+                idx = tg.tgemm_select_config_ex(ta, tb, M, N, K, **P)
+                assert idx >= 0 and cfgs[idx]["layouts"] & (1 << (2 * ta + tb)), (ta, tb, M, N, K, idx)
+
+
+def test_select_ex_leading_dimensions_and_eligibility():
+    s = tg.tgemm_select_config_ex
+    # A^T is K x M: lda >= M; B^T is N x K: ldb >= K
+    assert s(1, 0, 64, 64, 128, A16, 63, A16, 64, A16, 64) == tg.TGEMM_EINVAL_LD
+    assert s(1, 0, 64, 64, 128, A16, 64, A16, 64, A16, 64) > 0
+    assert s(0, 1, 64, 64, 128, A16, 128, A16, 127, A16, 64) == tg.TGEMM_EINVAL_LD
+    assert s(0, 1, 64, 64, 128, A16, 128, A16, 128, A16, 64) > 0
+    # the contiguous dimension decides the fast path: M for A^T, K for B^T, N for C
+    assert s(1, 0, 4092, 4096, 4096, A16, 4096, A16, 4096, A16, 4096) == 0
+    assert s(0, 0, 4092, 4096, 4096, A16, 4096, A16, 4096, A16, 4096) > 0
+    assert s(1, 0, 4096, 4096, 4092, A16, 4096, A16, 4096, A16, 4096) > 0
+    assert s(0, 1, 4096, 4096, 4092, A16, 4096, A16, 4096, A16, 4096) == 0
+    assert s(0, 1, 4096, 4092, 4096, A16, 4096, A16, 4096, A16, 4096) == 0
+    # the NN form is the (0, 0) case of the ex form
+    for M, N, K in [(4096, 4096, 4096), (100, 104, 96), (1024, 1024, 1024)]:
+        args = (M, N, K, A16, K, A16, N, A16, N)
+        assert tg.tgemm_select_config(*args) == s(0, 0, *args)
+    # a config that only takes A and B as given refuses transposed operands
+    nn_only = [i for i, c in enumerate(tg.configs()) if c["layouts"] == 1][0]
+    assert tg.gemm_f16_ex_cfg_raw(nn_only, 1, 0, 256, 256, 256, A16, 256, A16, 256, A16, 256, 1,
+                                  None) == tg.TGEMM_EINVAL_CFG
+    assert tg.gemm_f16_ex_raw(1, 0, 8, 8, 8, A16, 7, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_LD
 
 
 SHAPES = [(1, 1), (255, 257), (256, 256), (1024, 1024), (4096, 4096), (4095, 3000), (8192, 8192),

@@ -33,6 +33,8 @@ class Workload:
     dist: str       # "normal" or "uniform"
     std: float      # standard deviation for "normal" (ignored for "uniform")
     seed: int
+    trans_a: bool = False  # A handed to the library stored transposed (K x M)
+    trans_b: bool = False  # B handed to the library stored transposed (N x K)
 
     @property
     def flop(self) -> int:
@@ -45,7 +47,13 @@ class Workload:
         return s * s
 
     def inputs(self):
+        """The logical operands op(A) (M x K) and op(B) (K x N)."""
         return make_inputs(self.M, self.N, self.K, self.dist, self.std, self.seed)
+
+    def stored(self, A, B):
+        """The matrices as handed to the library: transposed copies where trans_a/trans_b."""
+        return (np.ascontiguousarray(A.T) if self.trans_a else A,
+                np.ascontiguousarray(B.T) if self.trans_b else B)
 
 
 # The five measured configurations (seed = position, A drawn before B).
@@ -61,6 +69,28 @@ WORKLOADS = {
 
 # The headline: 4096^3 with the ReLU epilogue on, same inputs as plain_4096.
 HEADLINE = Workload("relu_4096", 4096, 4096, 4096, True, "normal", 1.0, 2)
+
+# Transposed-operand GEMMs at 4096^3 on the same logical inputs: the two backward GEMMs
+# of the autograd wrapper (dA = dC @ B^T takes its second operand stored transposed,
+# dB = A^T @ dC its first) and both transposed with ReLU.
+LAYOUT_WORKLOADS = {
+    "plain_4096_nt": Workload("plain_4096_nt", 4096, 4096, 4096, False, "normal", 1.0, 2, trans_b=True),
+    "plain_4096_tn": Workload("plain_4096_tn", 4096, 4096, 4096, False, "normal", 1.0, 2, trans_a=True),
+    "relu_4096_tt": Workload("relu_4096_tt", 4096, 4096, 4096, True, "normal", 1.0, 2, trans_a=True,
+                             trans_b=True),
+}
+
+
+def all_workloads():
+    """Headline, the five measured configurations, then the transposed-operand ones."""
+    return [HEADLINE] + list(WORKLOADS.values()) + list(LAYOUT_WORKLOADS.values())
+
+
+def by_name(name: str) -> Workload:
+    for w in all_workloads():
+        if w.name == name:
+            return w
+    raise KeyError(name)
 
 
 def _draw(rng: np.random.Generator, shape, dist: str, std: float) -> np.ndarray:

@@ -5,9 +5,13 @@ kernels (``csrc/``), reached through the C ABI declared in ``include/tgemm.h``. 
 is used for device memory and streams. There is no CPU fallback: if ``libtgemm.so`` is
 missing or cannot be loaded, every call raises.
 
-The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_cfg``, ``tgemm_strerror``,
-``tgemm_version``, ``tgemm_num_configs``, ``tgemm_config_desc``, ``tgemm_select_config``,
-``tgemm_tile_of``, ``tgemm_num_workgroups`` and ``tgemm_mfma_probe``; the instrumented
+The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
+``gemm_f16_cfg``, ``gemm_f16_ex_cfg`` (as ``cfg=``), ``tgemm_strerror``, ``tgemm_version``,
+``tgemm_num_configs``, ``tgemm_config_desc``, ``tgemm_select_config``,
+``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups`` and
+``tgemm_mfma_probe``. ``matmul`` takes row- or column-major operand views and picks the
+layout; ``GemmFunction`` is the autograd wrapper (backward: dA = dC B^T, dB = A^T dC
+through gemm_f16_ex). The instrumented
 twin ``libtgemm_stamps.so`` (``stamps_lib()``, measurement tools only) adds
 ``tgemm_stamps_capacity``, ``tgemm_stamps_read`` and ``tgemm_stamps_clear``
 (``include/tgemm_stamps.h``).
@@ -33,9 +37,9 @@ SELECT_NOOP = -100
 SELECT_ZERO_FILL = -101
 
 # Every symbol include/tgemm.h declares.
-EXPORTS = ("gemm_f16", "gemm_f16_cfg", "tgemm_strerror", "tgemm_version", "tgemm_num_configs",
-           "tgemm_config_desc", "tgemm_select_config", "tgemm_tile_of", "tgemm_num_workgroups",
-           "tgemm_mfma_probe")
+EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_strerror",
+           "tgemm_version", "tgemm_num_configs", "tgemm_config_desc", "tgemm_select_config",
+           "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups", "tgemm_mfma_probe")
 # The extra symbols include/tgemm_stamps.h declares (instrumented build only).
 STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear")
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
@@ -55,7 +59,7 @@ class ConfigInfo(ctypes.Structure):
                 ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("panel", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("generic", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("name", ctypes.c_char * 48)]
+                ("layouts", ctypes.c_int32), ("name", ctypes.c_char * 48)]
 
     def as_dict(self) -> dict:
         d = {f: getattr(self, f) for f, _ in self._fields_ if f != "name"}
@@ -77,6 +81,12 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.gemm_f16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i32, p]
     L.gemm_f16_cfg.restype = i32
     L.gemm_f16_cfg.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p]
+    L.gemm_f16_ex.restype = i32
+    L.gemm_f16_ex.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p]
+    L.gemm_f16_ex_cfg.restype = i32
+    L.gemm_f16_ex_cfg.argtypes = [i32, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p]
+    L.tgemm_select_config_ex.restype = i32
+    L.tgemm_select_config_ex.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64]
     L.tgemm_strerror.restype = ctypes.c_char_p
     L.tgemm_strerror.argtypes = [i32]
     L.tgemm_version.restype = ctypes.c_char_p
@@ -129,6 +139,16 @@ def gemm_f16_cfg_raw(idx, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, library
     return (library or lib()).gemm_f16_cfg(idx, M, N, K, A, lda, B, ldb, C, ldc, int(relu), stream)
 
 
+def gemm_f16_ex_raw(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, library=None) -> int:
+    return (library or lib()).gemm_f16_ex(int(ta), int(tb), M, N, K, A, lda, B, ldb, C, ldc, int(relu),
+                                          stream)
+
+
+def gemm_f16_ex_cfg_raw(idx, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, library=None) -> int:
+    return (library or lib()).gemm_f16_ex_cfg(idx, int(ta), int(tb), M, N, K, A, lda, B, ldb, C, ldc,
+                                              int(relu), stream)
+
+
 def tgemm_strerror(code: int) -> str:
     return lib().tgemm_strerror(int(code)).decode()
 
@@ -154,6 +174,13 @@ def tgemm_select_config(M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None) ->
     ldb = max(1, N) if ldb is None else ldb
     ldc = max(1, N) if ldc is None else ldc
     return int(lib().tgemm_select_config(M, N, K, A, lda, B, ldb, C, ldc))
+
+
+def tgemm_select_config_ex(trans_a, trans_b, M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None) -> int:
+    lda = max(1, M if trans_a else K) if lda is None else lda
+    ldb = max(1, K if trans_b else N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    return int(lib().tgemm_select_config_ex(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc))
 
 
 def tgemm_tile_of(idx: int, M: int, N: int, wg: int):
@@ -224,17 +251,28 @@ def _operand(t, name):
     return rows, cols, ld
 
 
-def gemm_f16(a, b, c=None, relu: bool = True, stream=None, cfg: int | None = None, library=None):
-    """C = ReLU(a @ b) (relu=True) or a @ b, through the library. a: (M, K) fp16,
-    b: (K, N) fp16, c: (M, N) fp16 output (allocated if None). Row-major views with
-    any row stride are accepted. ``stream`` is a torch.cuda.Stream or raw handle; by
-    default the current stream of a's device. ``cfg`` forces a table config.
-    ``library`` selects another loaded build (``stamps_lib()``); default libtgemm.so."""
+def _stream_handle(stream, device):
     import torch
-    M, K, lda = _operand(a, "a")
-    K2, N, ldb = _operand(b, "b")
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def gemm_f16_ex(a, b, c=None, trans_a: bool = False, trans_b: bool = False, relu: bool = True,
+                stream=None, cfg: int | None = None, library=None):
+    """C = ReLU(op(a) @ op(b)) (relu=True) or op(a) @ op(b), through the library. ``a`` is
+    the stored matrix: (M, K) fp16, or (K, M) when trans_a; ``b`` is (K, N), or (N, K) when
+    trans_b; both row-major views with any row stride. ``c``: (M, N) fp16 output (allocated
+    if None). ``stream``: a torch.cuda.Stream or raw handle, by default the current stream
+    of a's device. ``cfg`` forces a table config. ``library`` selects another loaded build
+    (``stamps_lib()``); default libtgemm.so."""
+    import torch
+    ra, ca, lda = _operand(a, "a")
+    rb, cb, ldb = _operand(b, "b")
+    M, K = (ca, ra) if trans_a else (ra, ca)
+    K2, N = (cb, rb) if trans_b else (rb, cb)
     if K2 != K:
-        raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+        raise ValueError(f"inner dimensions differ: op(a) is {M}x{K}, op(b) is {K2}x{N}")
     if c is None:
         c = torch.empty((M, N), dtype=torch.float16, device=a.device)
     Mc, Nc, ldc = _operand(c, "c")
@@ -242,22 +280,81 @@ def gemm_f16(a, b, c=None, relu: bool = True, stream=None, cfg: int | None = Non
         raise ValueError(f"c has shape {tuple(c.shape)}, expected {(M, N)}")
     if not (a.device == b.device == c.device):
         raise ValueError("a, b and c must be on the same device")
-    if stream is None:
-        handle = torch.cuda.current_stream(a.device).cuda_stream
-    elif isinstance(stream, int):
-        handle = stream
-    else:
-        handle = stream.cuda_stream
+    handle = _stream_handle(stream, a.device)
+    args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(), ldc, relu, handle, library)
     with torch.cuda.device(a.device):
-        if cfg is None:
-            rc = gemm_f16_raw(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(), ldc,
-                              relu, handle, library)
+        if not trans_a and not trans_b:
+            rc = gemm_f16_raw(*args) if cfg is None else gemm_f16_cfg_raw(cfg, *args)
         else:
-            rc = gemm_f16_cfg_raw(cfg, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(),
-                                  ldc, relu, handle, library)
+            rc = (gemm_f16_ex_raw(trans_a, trans_b, *args) if cfg is None
+                  else gemm_f16_ex_cfg_raw(cfg, trans_a, trans_b, *args))
     if rc != TGEMM_OK:
-        raise TgemmError(rc, "gemm_f16" if cfg is None else f"gemm_f16_cfg[{cfg}]")
+        where = "gemm_f16" if not (trans_a or trans_b) else "gemm_f16_ex"
+        raise TgemmError(rc, where if cfg is None else f"{where}_cfg[{cfg}]")
     return c
+
+
+def gemm_f16(a, b, c=None, relu: bool = True, stream=None, cfg: int | None = None, library=None):
+    """C = ReLU(a @ b) (relu=True) or a @ b, through the library. a: (M, K) fp16,
+    b: (K, N) fp16, c: (M, N) fp16 output (allocated if None). Row-major views with
+    any row stride are accepted. ``stream`` is a torch.cuda.Stream or raw handle; by
+    default the current stream of a's device. ``cfg`` forces a table config.
+    ``library`` selects another loaded build (``stamps_lib()``); default libtgemm.so."""
+    return gemm_f16_ex(a, b, c, False, False, relu, stream, cfg, library)
+
+
+def _as_stored(x, name):
+    """(stored tensor, transposed?) for a logical 2-D operand view: row-major views are
+    used as they are; a column-major view (e.g. ``t.t()`` of a row-major t) is passed as
+    its row-major transpose with the trans flag set. Anything else is rejected (no hidden
+    copies)."""
+    rows, cols = x.shape
+    if cols <= 1 or x.stride(1) == 1:
+        return x, False
+    if rows <= 1 or x.stride(0) == 1:
+        return x.t(), True
+    raise ValueError(f"{name} must be row-major or column-major (strides {tuple(x.stride())})")
+
+
+def matmul(a, b, relu: bool = False, out=None, stream=None):
+    """op(a) @ op(b) (+ ReLU) for logical (M, K) and (K, N) fp16 views, each row- or
+    column-major: transposed views such as ``w.t()`` go to the library as transposed
+    operands, with no copy."""
+    sa, ta = _as_stored(a, "a")
+    sb, tb = _as_stored(b, "b")
+    return gemm_f16_ex(sa, sb, out, ta, tb, relu, stream)
+
+
+def _autograd_function():
+    import torch
+
+    class GemmFunction(torch.autograd.Function):
+        """C = A @ B with the backward of the pages' autograd wrapper: dA = dC @ B^T and
+        dB = A^T @ dC, both as transposed-operand GEMMs in the library (no ReLU: the
+        wrapper's forward is the plain GEMM)."""
+
+        @staticmethod
+        def forward(ctx, A, B):
+            ctx.save_for_backward(A, B)
+            return matmul(A, B, relu=False)
+
+        @staticmethod
+        def backward(ctx, dC):
+            A, B = ctx.saved_tensors
+            dC = dC if dC.stride(-1) == 1 else dC.contiguous()
+            dA = matmul(dC, B.t()) if ctx.needs_input_grad[0] else None
+            dB = matmul(A.t(), dC) if ctx.needs_input_grad[1] else None
+            return dA, dB
+
+    return GemmFunction
+
+
+def __getattr__(name):
+    if name == "GemmFunction":
+        fn = _autograd_function()
+        globals()["GemmFunction"] = fn
+        return fn
+    raise AttributeError(name)
 
 
 def configs() -> list:

@@ -101,7 +101,7 @@ def main():
     import tgemm_workloads as W
     from bench import kernel_source_hash
 
-    works = [W.HEADLINE] + list(W.WORKLOADS.values())
+    works = W.all_workloads()
     if args.workloads:
         keep = set(args.workloads.split(","))
         works = [w for w in works if w.name in keep]

@@ -34,12 +34,15 @@ constexpr int kSelectNoop = -100;      // M == 0 or N == 0
 constexpr int kSelectZeroFill = -101;  // K == 0
 constexpr int kMaxDevices = 64;
 
-int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+// layout = 2 * trans_a + trans_b. A is M x K (lda >= K) or, transposed, K x M (lda >= M);
+// B is K x N (ldb >= N) or, transposed, N x K (ldb >= K).
+int validate(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
              int64_t ldb, const void* C, int64_t ldc) {
   if (M < 0 || N < 0 || K < 0 || M >= TGEMM_MAX_DIM || N >= TGEMM_MAX_DIM || K >= TGEMM_MAX_DIM)
     return TGEMM_EINVAL_DIM;
-  const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
-  if (lda < kmin || ldb < nmin || ldc < nmin) return TGEMM_EINVAL_LD;
+  const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1, mmin = M > 1 ? M : 1;
+  const int64_t amin = (layout & 2) ? mmin : kmin, bmin = (layout & 1) ? kmin : nmin;
+  if (lda < amin || ldb < bmin || ldc < nmin) return TGEMM_EINVAL_LD;
   if (lda > TGEMM_MAX_LD || ldb > TGEMM_MAX_LD || ldc > TGEMM_MAX_LD) return TGEMM_EINVAL_LD;
   const bool out_nonempty = M > 0 && N > 0;
   if (out_nonempty && C == nullptr) return TGEMM_ENULL;
@@ -52,11 +55,14 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Can a fast (non-generic) config take these arguments?
-bool fast_eligible(int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                   const void* C, int64_t ldc) {
+// Can a fast (non-generic) config take these arguments? 16-byte chunks along each
+// operand's contiguous dimension (K for A as given and for B transposed, M for A
+// transposed, N for B as given) and along the rows of C.
+bool fast_eligible(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                   const void* B, int64_t ldb, const void* C, int64_t ldc) {
+  const int64_t a_contig = (layout & 2) ? M : K, b_contig = (layout & 1) ? K : N;
   return aligned16(A) && aligned16(B) && aligned16(C) && (lda % 8) == 0 && (ldb % 8) == 0 &&
-         (ldc % 8) == 0 && (K % 8) == 0 && (N % 8) == 0;
+         (ldc % 8) == 0 && (a_contig % 8) == 0 && (b_contig % 8) == 0 && (N % 8) == 0;
 }
 
 int64_t workgroups(const Config& c, int64_t M, int64_t N) {
@@ -68,22 +74,27 @@ int64_t workgroups(const Config& c, int64_t M, int64_t N) {
 // offline sweep on the measured workloads: 256 x 256 ping-pong tiles win as soon as they
 // cover most of the 256 compute units (160+ tiles, e.g. 4095 x 3000 has 192); below
 // that, 128 x 128 tiles keep more compute units busy.
-constexpr int kCfgBig = 9, kCfgSmall = 7;
-int choose_fast(int64_t M, int64_t N, int64_t K) {
+// Transposed operands take the ping-pong kernels only (15 = 128x128 ping-pong for small
+// grids).
+constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15;
+int choose_fast(int layout, int64_t M, int64_t N, int64_t K) {
   (void)K;
   const int64_t t256 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256);
-  return t256 >= 160 ? kCfgBig : kCfgSmall;
+  if (t256 >= 160) return kCfgBig;
+  return layout == 0 ? kCfgSmall : kCfgSmallT;
 }
 
-int select(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+int select(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
            int64_t ldb, const void* C, int64_t ldc) {
-  const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
+  const int v = validate(layout, M, N, K, A, lda, B, ldb, C, ldc);
   if (v != TGEMM_OK) return v;
   if (M == 0 || N == 0) return kSelectNoop;
   if (K == 0) return kSelectZeroFill;
-  if (fast_eligible(N, K, A, lda, B, ldb, C, ldc)) return choose_fast(M, N, K);
+  if (fast_eligible(layout, M, N, K, A, lda, B, ldb, C, ldc)) return choose_fast(layout, M, N, K);
   return 0;
 }
+
+int layout_of(int trans_a, int trans_b) { return (trans_a ? 2 : 0) | (trans_b ? 1 : 0); }
 
 // Once per device: is it gfx950? 0 = unknown, 1 = yes, 2 = no.
 std::atomic<int> g_arch_ok[kMaxDevices];
@@ -103,8 +114,8 @@ int check_device(int* device_out) {
   return st == 1 ? TGEMM_OK : TGEMM_EDEVICE;
 }
 
-int run(int cfg, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-        int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+int run(int cfg, int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+        const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
   int dev = -1;
   const int d = check_device(&dev);
   if (d != TGEMM_OK) return d;
@@ -130,6 +141,7 @@ int run(int cfg, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   g.relu = relu != 0;
   g.tiles_m = (int)tgemm::ceil_div(M, c.bm);
   g.tiles_n = (int)tgemm::ceil_div(N, c.bn);
+  g.layout = layout;
   return tgemm::launcher(cfg)(g, s, dev) == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH;
 }
 
@@ -137,36 +149,54 @@ int run(int cfg, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 
 extern "C" {
 
-int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-             int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
-  const int cfg = select(M, N, K, A, lda, B, ldb, C, ldc);
+int gemm_f16_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A,
+                int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+  const int layout = layout_of(trans_a, trans_b);
+  const int cfg = select(layout, M, N, K, A, lda, B, ldb, C, ldc);
   if (cfg == kSelectNoop) return TGEMM_OK;
   if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
-  return run(cfg, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  return run(cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+}
+
+int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+  return gemm_f16_ex(0, 0, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+}
+
+int gemm_f16_ex_cfg(int idx, int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A,
+                    int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+  if (idx < 0 || idx >= table_size()) return TGEMM_EINVAL_CFG;
+  const int layout = layout_of(trans_a, trans_b);
+  const int cfg = select(layout, M, N, K, A, lda, B, ldb, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
+  if (cfg == kSelectZeroFill) return run(cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  const Config& c = cfg_row(idx);
+  if (!(c.layouts & (1 << layout))) return TGEMM_EINVAL_CFG;
+  if (!c.generic && !fast_eligible(layout, M, N, K, A, lda, B, ldb, C, ldc)) return TGEMM_EINVAL_CFG;
+  return run(idx, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
 }
 
 int gemm_f16_cfg(int idx, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                  const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
-  if (idx < 0 || idx >= table_size()) return TGEMM_EINVAL_CFG;
-  const int cfg = select(M, N, K, A, lda, B, ldb, C, ldc);
-  if (cfg == kSelectNoop) return TGEMM_OK;
-  if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
-  if (cfg == kSelectZeroFill) return run(cfg, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
-  if (!cfg_row(idx).generic && !fast_eligible(N, K, A, lda, B, ldb, C, ldc))
-    return TGEMM_EINVAL_CFG;
-  return run(idx, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  return gemm_f16_ex_cfg(idx, 0, 0, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+}
+
+int tgemm_select_config_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A,
+                           int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc) {
+  return select(layout_of(trans_a, trans_b), M, N, K, A, lda, B, ldb, C, ldc);
 }
 
 int tgemm_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         const void* B, int64_t ldb, const void* C, int64_t ldc) {
-  return select(M, N, K, A, lda, B, ldb, C, ldc);
+  return select(0, M, N, K, A, lda, B, ldb, C, ldc);
 }
 
 const char* tgemm_strerror(int code) {
   switch (code) {
     case TGEMM_OK: return "success";
     case TGEMM_EINVAL_DIM: return "invalid dimension (negative, >= 2^31, or too many tiles)";
-    case TGEMM_EINVAL_LD: return "invalid leading dimension (below the row length or above 2^22)";
+    case TGEMM_EINVAL_LD: return "invalid leading dimension (below the stored row length or above 2^22)";
     case TGEMM_ENULL: return "null pointer for a non-empty operand";
     case TGEMM_EDEVICE: return "current HIP device is not gfx950 (MI355X) or is unavailable";
     case TGEMM_ELAUNCH: return "kernel launch failed";
@@ -194,6 +224,7 @@ int tgemm_config_desc(int idx, tgemm_config_info* out) {
   out->panel = c.panel;
   out->xcd_remap = c.xcd_remap;
   out->generic = c.generic;
+  out->layouts = c.layouts;
   out->lds_bytes = c.generic ? 0 : c.stages * (c.bm * c.bk + c.bk * c.bn) * 2;
   std::strncpy(out->name, c.name, sizeof(out->name) - 1);
   return TGEMM_OK;

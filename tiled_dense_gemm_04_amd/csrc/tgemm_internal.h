@@ -22,6 +22,7 @@ struct Config {
   int panel;            // tile-rows per panel in the workgroup order
   int xcd_remap;        // keep consecutive logical tiles on one XCD
   int generic;          // unaligned-capable generic kernel
+  int layouts;          // bit (2 * trans_a + trans_b) set: the config takes that layout
   const char* name;
 };
 
@@ -67,6 +68,7 @@ struct GemmArgs {
   int M, N, K;
   int relu;
   int tiles_m, tiles_n;
+  int layout;  // 2 * trans_a + trans_b: A given as K x M, B given as N x K
 };
 
 // The table (host only). Index order is part of the tooling ABI (gemm_f16_cfg, sweep

@@ -613,6 +613,117 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------------------
+// Operand staging of the ping-pong kernel. An operand tile spans R output rows (A, R = BM)
+// or columns (B, R = BN) and BK values of k. In memory the operand is either k-contiguous
+// ("K-major": A as given, or B given transposed, N x K) or m/n-contiguous ("MN-major": B
+// as given, or A given transposed, K x M). The LDS slot keeps the memory orientation:
+//   K-major : R rows of BK halves; 16-byte chunk c of row r sits at chunk c ^ swz_a_mf(r);
+//             a fragment (8 consecutive k of one m or n) is one ds_read_b128;
+//   MN-major: BK rows of R halves (R*2 bytes, a multiple of the 256-byte bank window);
+//             chunk c of row k sits at chunk c ^ swz_b(k); a fragment is two
+//             ds_read_b64_tr_b16 (each gives a lane 4 k values of its m or n, gathered
+//             from the rows of 4 lanes).
+// Either way a lane ends up with the same fragment: 8 consecutive k (group lane / MF) of
+// m or n index lane % MF, so the MFMA core does not depend on the layouts.
+// Copies: 16-byte unit u of a k-tile lands at LDS byte 16u of the slot (the lane order of
+// the LDS-DMA); the swizzle chooses which global chunk feeds it. Edges: rows past the
+// matrix lie outside the descriptor range (K-major: m/n rows; MN-major: the k rows past K
+// in the last tile) and read as zeros; chunks past the matrix along the contiguous
+// dimension get an out-of-range offset (K-major: the k chunks past K in the last tile;
+// MN-major: the m/n chunks past the edge). The contiguous dimension is a multiple of 8 on
+// this path, so a chunk is wholly inside or wholly outside.
+template <int R, int BK, int MF, bool KMAJ, int NW>
+struct PpOperand {
+  static constexpr int NT = 64 * NW;
+  static constexpr int BYTES = R * BK * 2;
+  static constexpr int CPR = KMAJ ? BK / 8 : R / 8;  // 16-byte chunks per LDS row
+  static constexpr int UNITS = R * BK / 8;
+  static constexpr int LD = UNITS / NT;              // copies per thread per k-tile
+  static constexpr int KPM = 512 / MF;               // k per MFMA
+  static_assert(UNITS % NT == 0, "copies must split evenly over the threads");
+  static_assert(KMAJ || (R * 2) % 256 == 0, "MN-major rows must span the 256-byte bank window");
+
+  const char* base;  // the tile's first element at k-tile 0
+  int64_t step;      // bytes from one k-tile to the next
+  uint32_t rng_full, rng_last;
+  uint32_t off[LD], off_last[LD];
+  int fr_base, fr_x, fr_k, fr_half;  // this lane's fragment-read constants
+
+  __device__ static int swz(int row) { return KMAJ ? swz_a_mf<BK, MF>(row) : swz_b(row); }
+
+  // X, ld: operand base and row stride (elements); r0: the tile's first m or n; rvalid:
+  // its m or n extent inside the matrix; kin_last: k values in the last k-tile.
+  __device__ void init_copies(const _Float16* X, int64_t ld, int r0, int rvalid, int kin_last, int wave,
+                              int lane) {
+    base = (const char*)(KMAJ ? X + (int64_t)r0 * ld : X + r0);
+    step = KMAJ ? (int64_t)BK * 2 : (int64_t)BK * ld * 2;
+    const int64_t full = KMAJ ? ((int64_t)(rvalid - 1) * ld + BK) * 2 : ((int64_t)(BK - 1) * ld + rvalid) * 2;
+    const int64_t last =
+        KMAJ ? ((int64_t)(rvalid - 1) * ld + kin_last) * 2 : ((int64_t)(kin_last - 1) * ld + rvalid) * 2;
+    rng_full = (uint32_t)(full < kMaxRange ? full : kMaxRange);
+    rng_last = (uint32_t)(last < kMaxRange ? last : kMaxRange);
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int u = (i * NW + wave) * 64 + lane;
+      const int row = u / CPR;
+      const int c = (u % CPR) ^ swz(row);
+      const uint32_t o = (uint32_t)(((int64_t)row * ld + 8 * c) * 2);
+      if (KMAJ) {
+        off[i] = o;
+        off_last[i] = 8 * c < kin_last ? o : kOob;
+      } else {
+        off[i] = 8 * c < rvalid ? o : kOob;
+        off_last[i] = off[i];
+      }
+    }
+  }
+
+  // Descriptor of k-tile t; an empty range past the last tile, so that copy only writes
+  // zeros into a slot no later read uses.
+  __device__ int4v rsrc(int t, int nk) const {
+    const uint32_t r = t < nk - 1 ? rng_full : (t == nk - 1 ? rng_last : 0u);
+    const int tt = t < nk ? t : nk - 1;
+    return make_rsrc(base + tt * step, r);
+  }
+
+  // wbase: the wave's first m or n inside the tile (a multiple of the swizzle periods).
+  __device__ void init_frags(int wbase, int lane) {
+    const int lrow = lane % MF, lkg = lane / MF;
+    if (KMAJ) {
+      fr_base = (wbase + lrow) * BK * 2;
+      fr_x = swz(lrow);
+      fr_k = lkg;
+      fr_half = 0;
+    } else {
+      // transposed reads: lane 16 g + 4 j + q reads row k0 + j of its group's 4-row block,
+      // m/n 4q .. 4q+3 of its 16-wide block
+      const int bg = lane >> 4, bj = (lane >> 2) & 3, bq = lane & 3;
+      fr_k = (MF == 32 ? 8 * (bg >> 1) : 8 * bg) + bj;
+      fr_x = wbase / 8 + (MF == 32 ? 2 * (bg & 1) : 0) + (bq >> 1);
+      fr_half = (bq & 1) * 8;
+      fr_base = 0;
+    }
+  }
+
+  // Fragment f (the f-th MF block of the wave's range), k substep ks, from slot S.
+  __device__ half8 frag(const char* S, int f, int ks) const {
+    if (KMAJ) {
+      const int chunk = (KPM / 8) * ks + fr_k;
+      return *(const TG_LDS half8*)(S + fr_base + f * MF * BK * 2 + ((chunk ^ fr_x) << 4));
+    } else {
+      short4v h[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int k = KPM * ks + 4 * i + fr_k;
+        const int off = k * R * 2 + (((fr_x + (MF / 8) * f) ^ swz_b(k)) << 4) + fr_half;
+        h[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(S + off));
+      }
+      return __builtin_bit_cast(half8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------
 // Ping-pong kernel: 8 waves in two groups of 4 (waves 0-3 and 4-7), one wave of each
 // group per SIMD. Every iteration (one k-tile) has two phases separated by workgroup
 // barriers; in each phase one group only issues MFMAs (from registers) while the other
@@ -630,43 +741,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 //                          group 1: MFMAs of tile kt.
 //             barrier B1
 // Slot safety: a copy of tile t+STAGES (group 0, phase 2 of kt = t) or t+STAGES-1 (group 1,
-// phase 1 of kt = t+1... i.e. into the slot of tile kt-1) only ever targets a slot whose
+// phase 1 of kt = t+1, i.e. into the slot of tile kt-1) only ever targets a slot whose
 // last reads finished before the preceding B2 (its readers were group 0 in phase 2 of
 // the iteration before and group 1 in phase 1 of the same iteration). Copies past the
 // last tile use an empty range, so every thread issues exactly PT copies per iteration
 // and at each B2 exactly STAGES-2 later tiles may still be in flight for every thread.
-// SYNC2 adds a second barrier per k-tile (B1) that holds the two groups exactly a phase
-// apart: 0 = none, 1 = plain s_barrier, 2 = s_barrier after this wave's LDS reads
-// completed. Every overwrite of a slot is already ordered after its last reads by B2
-// alone, so B1 only shapes the timing.
-// CIM = true issues each group's buffer->LDS copies from its MFMA phase (one copy after
-// every group of MFMAs) instead of its memory phase, so memory phases are LDS reads only.
-// Group 0 then copies tile kt+STAGES-1 in phase 1 of iteration kt (its slot's last reads
-// ended before B2 of iteration kt-1) and group 1 copies tile kt+STAGES in phase 2 of
-// iteration kt (after B2 of iteration kt); at every B2 each thread still has exactly
-// STAGES-2 later tiles in flight.
+// B1 (after this wave's LDS reads completed) holds the two groups exactly a phase apart;
+// every overwrite of a slot is already ordered after its last reads by B2 alone, so B1
+// only shapes the timing.
 // MF selects the MFMA: 32 = v_mfma_f32_32x32x16_f16, 16 = v_mfma_f32_16x16x32_f16 (half
-// the accumulator traffic per FLOP, twice the instructions).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int SYNC2,
-          bool CIM, int MF = 32>
+// the accumulator traffic per FLOP, twice the instructions). TA / TB: A given transposed
+// (K x M, lda >= M) / B given transposed (N x K, ldb >= K).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA,
+          bool TB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   WgClock clk;
   clk.start();
-  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
-  constexpr int KS = BK / (512 / MF);  // k per MFMA: 16 (32x32x16) or 32 (16x16x32)
+  constexpr int KS = BK / (512 / MF);  // MFMA k-substeps per k-tile
   static_assert(MF == 32 || MF == 16, "MFMA shape");
-  constexpr int A_CH_ROW = BK / 8, B_CH_ROW = BN / 8;
-  constexpr int A_UNITS = BM * A_CH_ROW, B_UNITS = BK * B_CH_ROW;
-  constexpr int A_LD = A_UNITS / NT, B_LD = B_UNITS / NT;
-  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
-  constexpr int PT = A_LD + B_LD;
+  using OpA = PpOperand<BM, BK, MF, !TA, NW>;
+  using OpB = PpOperand<BN, BK, MF, TB, NW>;
+  constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
+  constexpr int PT = OpA::LD + OpB::LD;
   static_assert(NW == 8, "two groups of four waves");
   static_assert(WTM % MF == 0 && WTN % MF == 0 && KS >= 1, "wave tile must be a multiple of the MFMA");
-  static_assert(A_UNITS % NT == 0 && B_UNITS % NT == 0, "loads must split evenly");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tiles start on swizzle periods");
   static_assert(BK % 16 == 0 && BK >= 16 && BK <= 128, "block_k");
-  static_assert(BN >= 128 && (BN * 2) % 256 == 0, "B rows must span the bank window");
   static_assert(STAGES >= 3, "the ring needs a slot being read, one in flight and one free");
   static_assert(PT * STAGES < 64, "vmcnt budget");
 
@@ -687,38 +790,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   const int nk = (K + BK - 1) / BK;
   const int kin_last = K - (nk - 1) * BK;
 
-  uint32_t a_off[A_LD], a_off_last[A_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int u = (i * NW + wave) * 64 + lane;
-    const int r = u / A_CH_ROW;
-    const int c = (u % A_CH_ROW) ^ swz_a_mf<BK, MF>(r);
-    a_off[i] = (uint32_t)(((int64_t)r * g.lda + 8 * c) * 2);
-    a_off_last[i] = 8 * c < kin_last ? a_off[i] : kOob;
-  }
-  uint32_t b_off[B_LD];
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int u = (i * NW + wave) * 64 + lane;
-    const int k = u / B_CH_ROW;
-    const int c = (u % B_CH_ROW) ^ swz_b(k);
-    b_off[i] = (8 * c < nvalid) ? (uint32_t)(((int64_t)k * g.ldb + 8 * c) * 2) : kOob;
-  }
-  const int64_t a_rng_full64 = ((int64_t)(mvalid - 1) * g.lda + BK) * 2;
-  const int64_t a_rng_last64 = ((int64_t)(mvalid - 1) * g.lda + kin_last) * 2;
-  const int64_t b_rng_full64 = ((int64_t)(BK - 1) * g.ldb + nvalid) * 2;
-  const int64_t b_rng_last64 = ((int64_t)(kin_last - 1) * g.ldb + nvalid) * 2;
-  const uint32_t a_rng_full = (uint32_t)(a_rng_full64 < kMaxRange ? a_rng_full64 : kMaxRange);
-  const uint32_t a_rng_last = (uint32_t)(a_rng_last64 < kMaxRange ? a_rng_last64 : kMaxRange);
-  const uint32_t b_rng_full = (uint32_t)(b_rng_full64 < kMaxRange ? b_rng_full64 : kMaxRange);
-  const uint32_t b_rng_last = (uint32_t)(b_rng_last64 < kMaxRange ? b_rng_last64 : kMaxRange);
-  const char* const a_base = (const char*)(g.A + (int64_t)row0 * g.lda);
-  const char* const b_base = (const char*)(g.B + col0);
-  const int64_t a_step = (int64_t)BK * 2, b_step = (int64_t)BK * g.ldb * 2;
+  OpA opa;
+  OpB opb;
+  opa.init_copies(g.A, g.lda, row0, mvalid, kin_last, wave, lane);
+  opb.init_copies(g.B, g.ldb, col0, nvalid, kin_last, wave, lane);
   const uint32_t a_lds0 = lds_addr(a_lds) + wave * 1024;
   const uint32_t b_lds0 = lds_addr(b_lds) + wave * 1024;
 
-  // This thread's PT copies of k-tile t (empty range past the last tile).
+  // This thread's PT copies of k-tile t.
   struct Dma {
     int4v ra, rb;
     uint32_t a_dst, b_dst;
@@ -726,64 +805,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   };
   auto dma_setup = [&](int t) {
     Dma d;
-    const uint32_t ar = t < nk - 1 ? a_rng_full : (t == nk - 1 ? a_rng_last : 0u);
-    const uint32_t br = t < nk - 1 ? b_rng_full : (t == nk - 1 ? b_rng_last : 0u);
-    const int tt = t < nk ? t : nk - 1;
-    d.ra = make_rsrc(a_base + tt * a_step, ar);
-    d.rb = make_rsrc(b_base + tt * b_step, br);
+    d.ra = opa.rsrc(t, nk);
+    d.rb = opb.rsrc(t, nk);
     const int slot = t % STAGES;
     d.a_dst = a_lds0 + slot * A_BYTES;
     d.b_dst = b_lds0 + slot * B_BYTES;
     d.last = t == nk - 1;
     return d;
   };
-  auto dma_one = [&](const Dma& d, int j) {
-    if (j < A_LD)
-      dma_to_lds(d.ra, d.a_dst + j * NW * 1024, d.last ? a_off_last[j] : a_off[j]);
-    else
-      dma_to_lds(d.rb, d.b_dst + (j - A_LD) * NW * 1024, b_off[j - A_LD]);
-  };
   auto copy_tile = [&](int t) {
     const Dma d = dma_setup(t);
 #pragma unroll
-    for (int j = 0; j < PT; ++j) dma_one(d, j);
+    for (int j = 0; j < OpA::LD; ++j)
+      dma_to_lds(d.ra, d.a_dst + j * NW * 1024, d.last ? opa.off_last[j] : opa.off[j]);
+#pragma unroll
+    for (int j = 0; j < OpB::LD; ++j)
+      dma_to_lds(d.rb, d.b_dst + j * NW * 1024, d.last ? opb.off_last[j] : opb.off[j]);
   };
 
   const int wm = wave / WN, wn = wave % WN;
-  // Fragment lane maps. 32x32x16: row/col = lane % 32, k group = lane / 32 (8 k each).
-  // 16x16x32: row/col = lane % 16, k group = lane / 16 (8 k each).
   const int lrow = lane % MF, lkg = lane / MF;
-  const int a_row_off = (wm * WTM + lrow) * BK * 2;
-  const int a_sw = swz_a_mf<BK, MF>(lrow);  // fm*MF and wm*WTM are multiples of the period
-  // B fragments by two transposed reads: lane = 16 g + 4 j + q reads row k0 + j of its
-  // group's 4-row block and columns 4q .. 4q+3 of its 16-column block.
-  const int bg = lane >> 4, bj = (lane >> 2) & 3, bq = lane & 3;
-  const int b_krow = (MF == 32 ? 8 * (bg >> 1) : 8 * bg) + bj;
-  const int b_chunk = (wn * WTN) / 8 + (MF == 32 ? 2 * (bg & 1) : 0) + (bq >> 1);
-  const int b_half = (bq & 1) * 8;
-  constexpr int KPM = 512 / MF;  // k per MFMA
+  opa.init_frags(wm * WTM, lane);
+  opb.init_frags(wn * WTN, lane);
 
-  half8 fa[KS][FM];
-  short4v fb[KS][FN][2];
+  half8 fa[KS][FM], fb[KS][FN];
   auto read_tile = [&](int slot) {
     const char* const As = a_lds + slot * A_BYTES;
     const char* const Bs = b_lds + slot * B_BYTES;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int chunk = (KPM / 8) * ks + lkg;
-        const int off = a_row_off + fm * MF * BK * 2 + ((chunk ^ a_sw) << 4);
-        fa[ks][fm] = *(const TG_LDS half8*)(As + off);
-      }
+      for (int fm = 0; fm < FM; ++fm) fa[ks][fm] = opa.frag(As, fm, ks);
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = KPM * ks + 4 * h + b_krow;
-          const int off = k * BN * 2 + (((b_chunk + (MF / 8) * fn) ^ swz_b(k)) << 4) + b_half;
-          fb[ks][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(Bs + off));
-        }
+      for (int fn = 0; fn < FN; ++fn) fb[ks][fn] = opb.frag(Bs, fn, ks);
     }
   };
 
@@ -797,40 +851,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.0f;
 
+  // Operands go in as (B fragment, A fragment): D^T = B^T A^T, so a lane's accumulator
+  // holds consecutive output columns of one row.
   auto mma_one = [&](int m) {
     const int ks = m / (FM * FN), fm = (m / FN) % FM, fn = m % FN;
-    const short8v b8 = __builtin_shufflevector(fb[ks][fn][0], fb[ks][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
     if constexpr (MF == 32)
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, b8), fa[ks][fm],
-                                                           acc[fm][fn], 0, 0, 0);
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[ks][fn], fa[ks][fm], acc[fm][fn], 0, 0, 0);
     else
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b8), fa[ks][fm],
-                                                           acc[fm][fn], 0, 0, 0);
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[ks][fn], fa[ks][fm], acc[fm][fn], 0, 0, 0);
   };
   constexpr int N_MFMA = KS * FM * FN;
   auto mma_tile = [&]() {
 #pragma unroll
     for (int m = 0; m < N_MFMA; ++m) mma_one(m);
   };
-  // MFMAs of one tile with the PT copies of tile t spread among them.
-  auto mma_tile_copy = [&](int t) {
-    const Dma d = dma_setup(t);
-#pragma unroll
-    for (int j = 0; j < PT; ++j) {
-#pragma unroll
-      for (int m = j * N_MFMA / PT; m < (j + 1) * N_MFMA / PT; ++m) mma_one(m);
-      __builtin_amdgcn_sched_barrier(0);
-      dma_one(d, j);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
 
-  // Prologue. Without CIM group 0 starts one copy ahead of group 1 (its next copy is in
-  // phase 2); with CIM group 1 is the one a copy ahead.
-  constexpr int G_AHEAD = CIM ? 1 : 0;
+  // Prologue: group 0 starts one copy ahead of group 1 (its next copy is in phase 2).
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) copy_tile(t);
-  if (grp == G_AHEAD) {
+  if (grp == 0) {
     copy_tile(STAGES - 1);
     wait_vmcnt<PT * (STAGES - 1)>();
   } else {
@@ -845,32 +884,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   if (grp == 0) {
     for (int kt = 0; kt < nk; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
-      if (CIM) mma_tile_copy(kt + STAGES - 1);  // phase 1: MFMAs of tile kt
-      else mma_tile();
+      mma_tile();                    // phase 1: MFMAs of tile kt
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<PT * (STAGES - 2)>();
       lds_barrier();                 // B2: tile kt+1 landed everywhere; reads of tile kt done
       __builtin_amdgcn_sched_barrier(0);
       read_tile((kt + 1) % STAGES);  // phase 2 (past the last tile: a settled slot, unused)
-      if (!CIM) copy_tile(kt + STAGES);
+      copy_tile(kt + STAGES);
       __builtin_amdgcn_sched_barrier(0);
-      if (SYNC2 == 2) lds_barrier();  // B1
-      if (SYNC2 == 1) __builtin_amdgcn_s_barrier();
+      lds_barrier();                 // B1
     }
   } else {
     for (int kt = 0; kt < nk; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
       read_tile(kt % STAGES);        // phase 1
-      if (!CIM) copy_tile(kt + STAGES - 1);
+      copy_tile(kt + STAGES - 1);
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<PT * (STAGES - 2)>();
       lds_barrier();                 // B2
       __builtin_amdgcn_sched_barrier(0);
-      if (CIM) mma_tile_copy(kt + STAGES);  // phase 2: MFMAs of tile kt
-      else mma_tile();
+      mma_tile();                    // phase 2: MFMAs of tile kt
       __builtin_amdgcn_sched_barrier(0);
-      if (SYNC2 == 2) lds_barrier();  // B1
-      if (SYNC2 == 1) __builtin_amdgcn_s_barrier();
+      lds_barrier();                 // B1
     }
   }
   wait_vmcnt<0>();
@@ -933,8 +968,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
 
 // ------------------------------------------------------------------------------------
 // Generic kernel: 64 x 64 x 32 tile, 4 waves (2 x 2 of 32 x 32), element-wise predicated
-// loads (any 2-byte-aligned pointers, any strides and sizes). A is staged as [m][k] and B
-// transposed to [n][k] in LDS so both fragments are plain 16-byte reads.
+// loads (any 2-byte-aligned pointers, any strides and sizes, any operand layout). A is
+// staged as [m][k] and B transposed to [n][k] in LDS so both fragments are plain 16-byte
+// reads.
 constexpr int GB_M = 64, GB_N = 64, GB_K = 32, G_PAD = 8;
 
 __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g) {
@@ -957,14 +993,16 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g) {
       const int idx = tid + 256 * e;
       const int r = idx / GB_K, kk = idx % GB_K;
       const int gr = row0 + r, gk = k0 + kk;
-      As[r][kk] = (gr < g.M && gk < g.K) ? g.A[(int64_t)gr * g.lda + gk] : (_Float16)0.0f;
+      const int64_t ia = (g.layout & 2) ? (int64_t)gk * g.lda + gr : (int64_t)gr * g.lda + gk;
+      As[r][kk] = (gr < g.M && gk < g.K) ? g.A[ia] : (_Float16)0.0f;
     }
 #pragma unroll
     for (int e = 0; e < (GB_K * GB_N) / 256; ++e) {
       const int idx = tid + 256 * e;
       const int kk = idx / GB_N, n = idx % GB_N;
       const int gk = k0 + kk, gc = col0 + n;
-      Bs[n][kk] = (gk < g.K && gc < g.N) ? g.B[(int64_t)gk * g.ldb + gc] : (_Float16)0.0f;
+      const int64_t ib = (g.layout & 1) ? (int64_t)gc * g.ldb + gk : (int64_t)gk * g.ldb + gc;
+      Bs[n][kk] = (gk < g.K && gc < g.N) ? g.B[ib] : (_Float16)0.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -1063,11 +1101,10 @@ hipError_t launch_fast(const GemmArgs& g, hipStream_t s, int device) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int SYNC2, bool CIM,
-          int MF = 32>
-hipError_t launch_pp(const GemmArgs& g, hipStream_t s, int device) {
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA, bool TB>
+hipError_t launch_pp_layout(const GemmArgs& g, hipStream_t s, int device) {
   constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
-  auto kern = gemm_pingpong<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, SYNC2, CIM, MF>;
+  auto kern = gemm_pingpong<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>;
   static std::atomic<uint64_t> ready{0};
   const uint64_t bit = 1ull << (device & 63);
   if (!(ready.load(std::memory_order_acquire) & bit)) {
@@ -1079,6 +1116,23 @@ hipError_t launch_pp(const GemmArgs& g, hipStream_t s, int device) {
   const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * WM * WN), lds, s, g);
   return hipGetLastError();
+}
+
+// ALL: the config is instantiated for every operand layout (g.layout = 2 * trans_a +
+// trans_b); otherwise only for A and B as given (the host never sends it another layout).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool ALL>
+hipError_t launch_pp(const GemmArgs& g, hipStream_t s, int device) {
+  if constexpr (ALL) {
+    switch (g.layout) {
+      case 1: return launch_pp_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, false, true>(g, s, device);
+      case 2: return launch_pp_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, true, false>(g, s, device);
+      case 3: return launch_pp_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, true, true>(g, s, device);
+      default: break;
+    }
+  } else {
+    if (g.layout != 0) return hipErrorInvalidValue;
+  }
+  return launch_pp_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, false, false>(g, s, device);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
@@ -1150,37 +1204,39 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
 #define TGEMM_PP_CONFIGS(X)        \
   X(256, 256, 32, 2, 4, 4, 4, 1)
 // Ping-pong with 16x16x32 MFMAs (the default for large grids), with variants of the
-// wave grid, ring depth and workgroup order kept for the sweep.
-#define TGEMM_PP1_CONFIGS(X)       \
-  X(256, 256, 32, 2, 4, 4, 4, 1)   \
-  X(256, 256, 32, 4, 2, 4, 4, 1)   \
-  X(256, 256, 32, 2, 4, 5, 4, 1)   \
-  X(256, 256, 32, 2, 4, 4, 8, 1)   \
-  X(256, 256, 32, 2, 4, 4, 2, 1)   \
-  X(256, 256, 32, 2, 4, 4, 4, 0)   \
-  X(128, 128, 32, 2, 4, 4, 4, 1)   \
-  X(256, 128, 32, 2, 4, 4, 4, 1)   \
-  X(128, 256, 32, 2, 4, 4, 4, 1)
+// wave grid, ring depth and workgroup order kept for the sweep. Last column: 1 = also
+// instantiated for transposed operands (all four layouts).
+#define TGEMM_PP1_CONFIGS(X)          \
+  X(256, 256, 32, 2, 4, 4, 4, 1, 1)   \
+  X(256, 256, 32, 4, 2, 4, 4, 1, 0)   \
+  X(256, 256, 32, 2, 4, 5, 4, 1, 0)   \
+  X(256, 256, 32, 2, 4, 4, 8, 1, 0)   \
+  X(256, 256, 32, 2, 4, 4, 2, 1, 0)   \
+  X(256, 256, 32, 2, 4, 4, 4, 0, 0)   \
+  X(128, 128, 32, 2, 4, 4, 4, 1, 1)   \
+  X(256, 128, 32, 2, 4, 4, 4, 1, 1)   \
+  X(128, 256, 32, 2, 4, 4, 4, 1, 1)
 
 #define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+  {BM, BN, BK, S, WM, WN, P, X, 0, 1, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
 #define TGEMM_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_fast<BM, BN, BK, WM, WN, S, P, X>,
 #define TGEMM_COUNT(BM, BN, BK, WM, WN, S, P, X) 0,
 #define TGEMM_PIPE_ROW(BM, BN, BK, WM, WN, S, P, X) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, "p" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+  {BM, BN, BK, S, WM, WN, P, X, 0, 1, "p" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
 #define TGEMM_PIPE_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pipe<BM, BN, BK, WM, WN, S, P, X>,
 #define TGEMM_PP_ROW(BM, BN, BK, WM, WN, S, P, X) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, "q" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
-#define TGEMM_PP_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pp<BM, BN, BK, WM, WN, S, P, X, 2, false>,
-#define TGEMM_PP1_ROW(BM, BN, BK, WM, WN, S, P, X) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, "m" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
-#define TGEMM_PP1_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pp<BM, BN, BK, WM, WN, S, P, X, 2, false, 16>,
+  {BM, BN, BK, S, WM, WN, P, X, 0, 1, "q" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PP_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pp<BM, BN, BK, WM, WN, S, P, X, 32, false>,
+#define TGEMM_PP1_ROW(BM, BN, BK, WM, WN, S, P, X, ALL) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, ALL ? 0xF : 1, "m" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PP1_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, ALL) launch_pp<BM, BN, BK, WM, WN, S, P, X, 16, ALL>,
+#define TGEMM_COUNT9(BM, BN, BK, WM, WN, S, P, X, ALL) 0,
 
 // Function-local statics: host-only tables (the device pass parses these bodies, which
 // instantiates every kernel, but emits no host data).
 const Config* config_table(int* count) {
   static const Config table[] = {
-      {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, "generic_64x64x32"},
+      {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, 0xF, "generic_64x64x32"},
       TGEMM_FAST_CONFIGS(TGEMM_ROW) TGEMM_PIPE_CONFIGS(TGEMM_PIPE_ROW) TGEMM_PP_CONFIGS(TGEMM_PP_ROW)
           TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW)};
   *count = (int)(sizeof(table) / sizeof(table[0]));
@@ -1194,7 +1250,7 @@ Launcher launcher(int idx) {
                                                TGEMM_PP1_CONFIGS(TGEMM_PP1_LAUNCHER)};
   static_assert(sizeof(table) / sizeof(table[0]) ==
                     1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT) TGEMM_PIPE_CONFIGS(TGEMM_COUNT)
-                                           TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT)}) /
+                                           TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT9)}) /
                             sizeof(int),
                 "one launcher per config");
   return table[idx];

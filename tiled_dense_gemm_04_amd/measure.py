@@ -122,21 +122,25 @@ def measure_probe(torch, tg, stream, blocks=512, iters=2000):
 
 
 def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceiling=None):
-    A, B = w.inputs()
-    a = torch.from_numpy(A).cuda()
-    b = torch.from_numpy(B).cuda()
+    SA, SB = w.stored(*w.inputs())
+    a = torch.from_numpy(SA).cuda()
+    b = torch.from_numpy(SB).cuda()
     c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
-    cfg = tg.tgemm_select_config(w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
-                                 c.data_ptr(), c.stride(0))
+    cfg = tg.tgemm_select_config_ex(w.trans_a, w.trans_b, w.M, w.N, w.K, a.data_ptr(), a.stride(0),
+                                    b.data_ptr(), b.stride(0), c.data_ptr(), c.stride(0))
     desc = tg.tgemm_config_desc(cfg)
     res = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "relu": w.relu, "flop": w.flop,
+           "trans_a": w.trans_a, "trans_b": w.trans_b,
            "config": desc["name"], "config_index": cfg,
            "compulsory_bytes": 2 * (w.M * w.K + w.K * w.N + w.M * w.N)}
 
     def tf(us):
         return w.flop / (us * 1e-6) / 1e12
 
-    hot = timed_trials(torch, stream, lambda i: tg.gemm_f16(a, b, c, relu=w.relu, stream=stream))
+    def gemm(x, y, z, library=None):
+        tg.gemm_f16_ex(x, y, z, w.trans_a, w.trans_b, relu=w.relu, stream=stream, library=library)
+
+    hot = timed_trials(torch, stream, lambda i: gemm(a, b, c))
     res["hot"] = {**hot, "tflops": tf(hot["median_us"]), "pct_of_peak": 100 * tf(hot["median_us"]) / PEAK_TFLOPS}
     if ceiling:
         res["hot"]["pct_of_mfma_ceiling"] = 100 * tf(hot["median_us"]) / ceiling
@@ -146,8 +150,7 @@ def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceilin
         per_set = res["compulsory_bytes"]
         nsets = max(4, math.ceil(CACHE_BYTES / per_set) + 1)
         sets = [(a.clone(), b.clone(), torch.empty_like(c)) for _ in range(nsets)]
-        cold_t = timed_trials(torch, stream, lambda i: tg.gemm_f16(sets[i % nsets][0], sets[i % nsets][1],
-                                                                 sets[i % nsets][2], relu=w.relu, stream=stream))
+        cold_t = timed_trials(torch, stream, lambda i: gemm(*sets[i % nsets]))
         res["cold"] = {**cold_t, "sets": nsets, "bytes_total": nsets * per_set,
                        "tflops": tf(cold_t["median_us"]), "pct_of_peak": 100 * tf(cold_t["median_us"]) / PEAK_TFLOPS}
         log(f"{w.name}: cold ({nsets} sets, {nsets * per_set / 2**20:.0f} MiB) {cold_t['median_us']:.2f} us")
@@ -155,8 +158,7 @@ def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceilin
         torch.cuda.empty_cache()
 
     S = tg.stamps_lib()
-    timed_trials(torch, stream, lambda i: tg.gemm_f16(a, b, c, relu=w.relu, stream=stream, library=S),
-                 trials=1, warm=3)
+    timed_trials(torch, stream, lambda i: gemm(a, b, c, library=S), trials=1, warm=3)
     nwg = tg.tgemm_num_workgroups(cfg, w.M, w.N)
     res["phases"] = phases(tg.tgemm_stamps_read(nwg))
     if res["phases"]:
@@ -165,8 +167,11 @@ def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceilin
             f"epilogue {ph['epilogue_us']:.2f} us, clock {ph['shader_clock_ghz']:.3f} GHz")
 
     if with_torch:
+        opa = a.t() if w.trans_a else a
+        opb = b.t() if w.trans_b else b
+
         def tmm(_i):
-            r = torch.matmul(a, b)
+            r = torch.matmul(opa, opb)
             if w.relu:
                 torch.relu_(r)
         with torch.cuda.stream(stream):
@@ -238,7 +243,7 @@ def main():
         return 1
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
-    works = [W.HEADLINE] + list(W.WORKLOADS.values())
+    works = W.all_workloads()
     if args.workloads:
         keep = set(args.workloads.split(","))
         works = [w for w in works if w.name in keep]
