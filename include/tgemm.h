@@ -46,7 +46,9 @@ extern "C" {
 #define TGEMM_EDEVICE (-4)      /* current HIP device is not gfx950, or no device           */
 #define TGEMM_ELAUNCH (-5)      /* the kernel launch was rejected by the HIP runtime        */
 #define TGEMM_EINVAL_CFG (-6)   /* config index out of range, or config not usable here     */
-#define TGEMM_EALIGN (-7)       /* A, B or C not aligned to 2 bytes (one binary16 element)   */
+#define TGEMM_EALIGN (-7)       /* A, B or C not aligned to 2 bytes (one binary16 element), */
+                                /* or a workspace not aligned to 256 bytes                 */
+#define TGEMM_EWORKSPACE (-8)   /* workspace smaller than tgemm_workspace_bytes requires    */
 
 #define TGEMM_MAX_DIM ((int64_t)1 << 31)  /* M, N, K must be < 2^31                        */
 #define TGEMM_MAX_LD ((int64_t)1 << 22)   /* lda, ldb, ldc must be <= 2^22 elements         */
@@ -91,6 +93,34 @@ TGEMM_API int gemm_f16_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_
                           const void* B, int64_t ldb,
                           void* C, int64_t ldc,
                           int relu, void* stream);
+
+/*
+ * Split-K for output grids too small to fill the GPU: gemm_f16_ex's operation, computed
+ * by `splits` workgroups per output tile, each over a contiguous range of k-tiles, the
+ * partial sums combined in a fixed order. This carries the pages' idea of splitting a
+ * long reduction across compute units and combining the parts afterwards (the Split-KV
+ * decoding of "Writing High-Performance Kernels in TileLang, from GEMM to MLA"
+ * (atlascloud.ai), MLA section) over to the GEMM's K.
+ *   workspace, workspace_bytes : caller-owned device memory, 256-byte aligned, at least
+ *       tgemm_workspace_bytes(trans_a, trans_b, M, N, K) bytes (0 means the call does not
+ *       split and the workspace may be NULL). The whole workspace must be zero-filled
+ *       before its first use; every call leaves its counter region at zero again, so one
+ *       workspace serves any number of calls of any shapes in stream order. Calls that
+ *       may overlap in time (different streams) need different workspaces.
+ * The library picks the tile config and the split count (tgemm_split_plan shows them);
+ * when the output grid fills the GPU it does not split and equals gemm_f16_ex. Results
+ * are deterministic: the last split to finish a tile adds the fp32 partial tiles in split
+ * order, whichever it is, then applies ReLU and rounds to fp16 once. They differ from the
+ * unsplit kernel's only by fp32 summation order (same tolerance).
+ * Returns TGEMM_OK, the argument errors of gemm_f16_ex, TGEMM_ENULL (workspace NULL when
+ * needed), TGEMM_EALIGN (workspace alignment) or TGEMM_EWORKSPACE.
+ */
+TGEMM_API int64_t tgemm_workspace_bytes(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K);
+TGEMM_API int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda,
+                          const void* B, int64_t ldb,
+                          void* C, int64_t ldc,
+                          int relu, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Human-readable text for a return code (static storage, never NULL). */
 TGEMM_API const char* tgemm_strerror(int code);
@@ -140,6 +170,25 @@ TGEMM_API int gemm_f16_ex_cfg(int idx, int trans_a, int trans_b, int64_t M, int6
                   const void* B, int64_t ldb,
                   void* C, int64_t ldc,
                   int relu, void* stream);
+
+/* The plan gemm_f16_ws would use for these arguments: config index, split count (1 = no
+ * split) and the workspace bytes it needs. Pure host logic. Returns TGEMM_OK, TGEMM_ENULL
+ * for a NULL output pointer or an argument error of gemm_f16_ex. */
+TGEMM_API int tgemm_split_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda,
+                  const void* B, int64_t ldb,
+                  const void* C, int64_t ldc,
+                  int* cfg, int* splits, int64_t* workspace_bytes);
+
+/* gemm_f16_ws forced to config idx and split count splits (1 .. 8; > 1 only for configs
+ * taking all four layouts, at most ceil(K / block_k) splits and 1024 output tiles;
+ * otherwise TGEMM_EINVAL_CFG). */
+TGEMM_API int gemm_f16_ws_cfg(int idx, int splits, int trans_a, int trans_b,
+                  int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda,
+                  const void* B, int64_t ldb,
+                  void* C, int64_t ldc,
+                  int relu, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* gemm_f16 forced to config idx (same arguments and error codes; TGEMM_EINVAL_CFG if
  * idx is out of range or the fast config cannot take these pointers / strides). */

@@ -36,7 +36,7 @@ def exported(path):
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 17, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -206,6 +206,48 @@ def test_select_ex_leading_dimensions_and_eligibility():
     assert tg.gemm_f16_ex_cfg_raw(nn_only, 1, 0, 256, 256, 256, A16, 256, A16, 256, A16, 256, 1,
                                   None) == tg.TGEMM_EINVAL_CFG
     assert tg.gemm_f16_ex_raw(1, 0, 8, 8, 8, A16, 7, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_LD
+
+
+def test_split_plans_and_workspace_sizes():
+    """Small grids split to about one workgroup per compute unit; grids that fill the GPU
+    do not split and need no workspace."""
+    plan = tg.tgemm_split_plan
+    cfgs = tg.configs()
+    for ta in (0, 1):
+        for tb in (0, 1):
+            for (M, N, K), want in [((1024, 1024, 32768), 4), ((512, 512, 16384), 8), ((2048, 2048, 16384), 2),
+                                    ((512, 4096, 4096), 2), ((1024, 1024, 1024), 1), ((16384, 512, 4096), 1),
+                                    ((4096, 1024, 8192), 1), ((4096, 4096, 4096), 1), ((4095, 3000, 1000), 1),
+                                    ((8192, 8192, 8192), 1)]:
+                cfg, sp, wb = plan(ta, tb, M, N, K)
+                assert sp == want, (M, N, K, cfg, sp)
+                c = cfgs[cfg]
+                tiles = -(-M // c["block_m"]) * -(-N // c["block_n"])
+                assert wb == (4096 + tiles * sp * c["block_m"] * c["block_n"] * 4 if sp > 1 else 0)
+                assert tg.tgemm_workspace_bytes(ta, tb, M, N, K) == wb
+                if sp > 1:
+                    assert c["layouts"] == 0xF and 128 <= tiles * sp <= 256
+                    assert -(-K // c["block_k"]) // sp >= 64
+    # generic arguments never split
+    assert plan(0, 0, 1024, 1024, 1020)[1] == 1 and plan(0, 0, 1024, 1024, 1020)[2] == 0
+
+
+def test_workspace_errors_before_hip():
+    L = tg.lib()
+    M, N, K = 1024, 1024, 32768  # a shape that splits
+    args = (0, 0, M, N, K, A16, K, A16, N, A16, N, 1)
+    need = tg.tgemm_workspace_bytes(0, 0, M, N, K)
+    assert L.gemm_f16_ws(*args, None, 0, None) == tg.TGEMM_ENULL
+    assert L.gemm_f16_ws(*args, A16 + 16, need, None) == tg.TGEMM_EALIGN
+    assert L.gemm_f16_ws(*args, A16, need - 1, None) == tg.TGEMM_EWORKSPACE
+    assert L.gemm_f16_ws_cfg(15, 9, *args, A16, need, None) == tg.TGEMM_EINVAL_CFG     # > 8 splits
+    assert L.gemm_f16_ws_cfg(7, 2, *args, A16, need, None) == tg.TGEMM_EINVAL_CFG      # not split-capable
+    assert L.gemm_f16_ws_cfg(15, 4, *args, A16, need - 1, None) == tg.TGEMM_EWORKSPACE
+    assert L.gemm_f16_ws_cfg(15, 4, 0, 0, 64, 64, 64, A16, 64, A16, 64, A16, 64, 1, A16, 1 << 30,
+                             None) == tg.TGEMM_EINVAL_CFG                                  # 4 splits of 2 k-tiles
+    # (a shape that does not split needs no workspace: covered on the GPU, since such a call
+    # goes on to launch)
+    assert tg.tgemm_strerror(tg.TGEMM_EWORKSPACE) != "unknown error code"
 
 
 SHAPES = [(1, 1), (255, 257), (256, 256), (1024, 1024), (4096, 4096), (4095, 3000), (8192, 8192),

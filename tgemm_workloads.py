@@ -81,9 +81,22 @@ LAYOUT_WORKLOADS = {
 }
 
 
+# Small output grids: a weight-gradient GEMM of the autograd wrapper's backward
+# (dB = A^T @ dC for a 1024 x 1024 weight over 32768 rows of activations, A stored
+# transposed) and one GPU's row shard of the 4096^3 headline split over 8 GPUs
+# (M = 4096 / 8); the shapes split-K is for.
+SPLIT_WORKLOADS = {
+    "plain_tn_1024x1024x32768": Workload("plain_tn_1024x1024x32768", 1024, 1024, 32768, False, "normal", 1.0, 6,
+                                         trans_a=True),
+    "relu_shard_512x4096x4096": Workload("relu_shard_512x4096x4096", 512, 4096, 4096, True, "normal", 1.0, 7),
+}
+
+
 def all_workloads():
-    """Headline, the five measured configurations, then the transposed-operand ones."""
-    return [HEADLINE] + list(WORKLOADS.values()) + list(LAYOUT_WORKLOADS.values())
+    """Headline, the five measured configurations, the transposed-operand ones, then the
+    small-grid (split-K) ones."""
+    return ([HEADLINE] + list(WORKLOADS.values()) + list(LAYOUT_WORKLOADS.values())
+            + list(SPLIT_WORKLOADS.values()))
 
 
 def by_name(name: str) -> Workload:

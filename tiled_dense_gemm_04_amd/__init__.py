@@ -8,8 +8,10 @@ missing or cannot be loaded, every call raises.
 The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
 ``gemm_f16_cfg``, ``gemm_f16_ex_cfg`` (as ``cfg=``), ``tgemm_strerror``, ``tgemm_version``,
 ``tgemm_num_configs``, ``tgemm_config_desc``, ``tgemm_select_config``,
-``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups`` and
-``tgemm_mfma_probe``. ``matmul`` takes row- or column-major operand views and picks the
+``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``,
+``tgemm_mfma_probe``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
+stream unless given), ``gemm_f16_ws_cfg`` (as ``cfg=``/``splits=``),
+``tgemm_workspace_bytes`` and ``tgemm_split_plan``. ``matmul`` takes row- or column-major operand views and picks the
 layout; ``GemmFunction`` is the autograd wrapper (backward: dA = dC B^T, dB = A^T dC
 through gemm_f16_ex). The instrumented
 twin ``libtgemm_stamps.so`` (``stamps_lib()``, measurement tools only) adds
@@ -33,13 +35,15 @@ TGEMM_EDEVICE = -4
 TGEMM_ELAUNCH = -5
 TGEMM_EINVAL_CFG = -6
 TGEMM_EALIGN = -7
+TGEMM_EWORKSPACE = -8
 SELECT_NOOP = -100
 SELECT_ZERO_FILL = -101
 
 # Every symbol include/tgemm.h declares.
 EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_strerror",
            "tgemm_version", "tgemm_num_configs", "tgemm_config_desc", "tgemm_select_config",
-           "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups", "tgemm_mfma_probe")
+           "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups", "tgemm_mfma_probe",
+           "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan")
 # The extra symbols include/tgemm_stamps.h declares (instrumented build only).
 STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear")
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
@@ -103,6 +107,15 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.tgemm_num_workgroups.argtypes = [i32, i64, i64]
     L.tgemm_mfma_probe.restype = i32
     L.tgemm_mfma_probe.argtypes = [i32, i32, p, p]
+    L.gemm_f16_ws.restype = i32
+    L.gemm_f16_ws.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p, i64, p]
+    L.gemm_f16_ws_cfg.restype = i32
+    L.gemm_f16_ws_cfg.argtypes = [i32, i32, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p, i64, p]
+    L.tgemm_workspace_bytes.restype = i64
+    L.tgemm_workspace_bytes.argtypes = [i32, i32, i64, i64, i64]
+    L.tgemm_split_plan.restype = i32
+    L.tgemm_split_plan.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32), ctypes.POINTER(i64)]
     if stamps:
         L.tgemm_stamps_capacity.restype = i32
         L.tgemm_stamps_capacity.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -181,6 +194,23 @@ def tgemm_select_config_ex(trans_a, trans_b, M, N, K, A=0, lda=None, B=0, ldb=No
     ldb = max(1, K if trans_b else N) if ldb is None else ldb
     ldc = max(1, N) if ldc is None else ldc
     return int(lib().tgemm_select_config_ex(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc))
+
+
+def tgemm_workspace_bytes(trans_a, trans_b, M, N, K) -> int:
+    return int(lib().tgemm_workspace_bytes(int(trans_a), int(trans_b), M, N, K))
+
+
+def tgemm_split_plan(trans_a, trans_b, M, N, K, A=256, lda=None, B=256, ldb=None, C=256, ldc=None):
+    """(config index, splits, workspace bytes) gemm_f16_ws would use (pure host logic)."""
+    lda = max(1, M if trans_a else K) if lda is None else lda
+    ldb = max(1, K if trans_b else N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    cfg, sp, wb = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    rc = lib().tgemm_split_plan(int(trans_a), int(trans_b), M, N, K, A, lda, B, ldb, C, ldc,
+                                ctypes.byref(cfg), ctypes.byref(sp), ctypes.byref(wb))
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "tgemm_split_plan")
+    return cfg.value, sp.value, wb.value
 
 
 def tgemm_tile_of(idx: int, M: int, N: int, wg: int):
@@ -294,6 +324,70 @@ def gemm_f16_ex(a, b, c=None, trans_a: bool = False, trans_b: bool = False, relu
     return c
 
 
+_workspaces = {}
+
+
+def workspace_for(nbytes: int, device, stream_handle: int):
+    """A zero-filled device workspace of at least nbytes for calls on this stream (grown on
+    demand; the library keeps its counter region zero between calls in stream order)."""
+    import torch
+    key = (torch.device(device).index, int(stream_handle or 0))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        torch.cuda.synchronize(device)  # the fill is complete before any stream uses it
+        _workspaces[key] = ws
+    return ws
+
+
+def gemm_f16_ws(a, b, c=None, trans_a: bool = False, trans_b: bool = False, relu: bool = True,
+                stream=None, workspace=None, cfg: int | None = None, splits: int | None = None,
+                library=None):
+    """gemm_f16_ex with split-K for small output grids (gemm_f16_ws / gemm_f16_ws_cfg).
+    ``workspace``: a uint8 device tensor (zero-filled before its first use, 256-byte
+    aligned); by default one is kept per device and stream. ``cfg`` and ``splits`` force
+    the plan (both or neither)."""
+    import torch
+    ra, ca, lda = _operand(a, "a")
+    rb, cb, ldb = _operand(b, "b")
+    M, K = (ca, ra) if trans_a else (ra, ca)
+    K2, N = (cb, rb) if trans_b else (rb, cb)
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: op(a) is {M}x{K}, op(b) is {K2}x{N}")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    Mc, Nc, ldc = _operand(c, "c")
+    if (Mc, Nc) != (M, N):
+        raise ValueError(f"c has shape {tuple(c.shape)}, expected {(M, N)}")
+    if not (a.device == b.device == c.device):
+        raise ValueError("a, b and c must be on the same device")
+    if (cfg is None) != (splits is None):
+        raise ValueError("give both cfg and splits, or neither")
+    handle = _stream_handle(stream, a.device)
+    L = library or lib()
+    if workspace is None:
+        if cfg is None:
+            need = tgemm_split_plan(trans_a, trans_b, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb,
+                                    c.data_ptr(), ldc)[2]
+        else:
+            d = tgemm_config_desc(cfg)
+            tiles = -(-M // d["block_m"]) * -(-N // d["block_n"])
+            need = 4096 + tiles * splits * d["block_m"] * d["block_n"] * 4 if splits > 1 else 0
+        workspace = workspace_for(need, a.device, handle) if need else None
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(a.device):
+        if cfg is None:
+            rc = L.gemm_f16_ws(int(trans_a), int(trans_b), M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb,
+                               c.data_ptr(), ldc, int(relu), wptr, wbytes, handle)
+        else:
+            rc = L.gemm_f16_ws_cfg(cfg, splits, int(trans_a), int(trans_b), M, N, K, a.data_ptr(), lda,
+                                   b.data_ptr(), ldb, c.data_ptr(), ldc, int(relu), wptr, wbytes, handle)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "gemm_f16_ws" if cfg is None else f"gemm_f16_ws_cfg[{cfg}, {splits}]")
+    return c
+
+
 def gemm_f16(a, b, c=None, relu: bool = True, stream=None, cfg: int | None = None, library=None):
     """C = ReLU(a @ b) (relu=True) or a @ b, through the library. a: (M, K) fp16,
     b: (K, N) fp16, c: (M, N) fp16 output (allocated if None). Row-major views with
@@ -319,10 +413,11 @@ def _as_stored(x, name):
 def matmul(a, b, relu: bool = False, out=None, stream=None):
     """op(a) @ op(b) (+ ReLU) for logical (M, K) and (K, N) fp16 views, each row- or
     column-major: transposed views such as ``w.t()`` go to the library as transposed
-    operands, with no copy."""
+    operands, with no copy. Runs through gemm_f16_ws, so small output grids with a long K
+    (weight gradients) are split over the GPU with a workspace kept per device and stream."""
     sa, ta = _as_stored(a, "a")
     sb, tb = _as_stored(b, "b")
-    return gemm_f16_ex(sa, sb, out, ta, tb, relu, stream)
+    return gemm_f16_ws(sa, sb, out, ta, tb, relu, stream)
 
 
 def _autograd_function():

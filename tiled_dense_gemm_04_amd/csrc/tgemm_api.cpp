@@ -114,8 +114,62 @@ int check_device(int* device_out) {
   return st == 1 ? TGEMM_OK : TGEMM_EDEVICE;
 }
 
+// Split-K plan, for output grids too small to fill the GPU's 256 compute units when K is
+// long. From a sweep on MI355X (split-K costs one round trip of fp32 partial tiles through
+// the device-coherence point, so each split must keep a long run of k-tiles):
+//   128 x 128 tiles if there are at most 128 of them: splits = min(8, 256 / tiles,
+//     k-tiles / 64);
+//   else 256 x 256 tiles if there are at most 128 of them: splits = min(8, 256 / tiles,
+//     k-tiles / 256);
+//   no split if that gives fewer than 2 (e.g. 1024^3, 16384 x 512 x 4096, 4096^3).
+// Measured: 1024 x 1024 x 32768 299 -> 101 us, 512 x 512 x 16384 159 -> 44 us, 2048 x 2048
+// x 16384 173 -> 162 us. Only the 16x16x32 ping-pong configs take splits.
+constexpr int kMaxSplits = 8, kNumCu = 256;
+struct SplitPlan {
+  int cfg, splits;
+};
+
+SplitPlan split_plan(int layout, int64_t M, int64_t N, int64_t K, int base_cfg) {
+  (void)layout;
+  SplitPlan p{base_cfg, 1};
+  if (cfg_row(base_cfg).generic) return p;
+  const int64_t t256 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256);
+  const int64_t t128 = tgemm::ceil_div(M, 128) * tgemm::ceil_div(N, 128);
+  if (t256 >= 160) return p;
+  int cfg;
+  int64_t s;
+  if (t128 <= 128) {
+    cfg = kCfgSmallT;
+    s = kNumCu / t128;
+    const int64_t by_k = tgemm::ceil_div(K, cfg_row(cfg).bk) / 64;
+    if (s > by_k) s = by_k;
+  } else if (t256 <= 128) {
+    cfg = kCfgBig;
+    s = kNumCu / t256;
+    const int64_t by_k = tgemm::ceil_div(K, cfg_row(cfg).bk) / 256;
+    if (s > by_k) s = by_k;
+  } else {
+    return p;
+  }
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 2) return p;
+  return SplitPlan{cfg, (int)s};
+}
+
+// Workspace layout of a split launch: a fixed region of kMaxSplitTiles tile counters (so
+// calls of any shape on one workspace use the same counter bytes, which every call leaves
+// at zero), then splits fp32 partial tiles per output tile.
+constexpr int64_t kMaxSplitTiles = 1024, kWsParts = kMaxSplitTiles * 4;
+int64_t ws_bytes(const Config& c, int splits, int64_t M, int64_t N) {
+  if (splits <= 1) return 0;
+  return kWsParts + workgroups(c, M, N) * splits * (int64_t)c.bm * c.bn * 4;
+}
+
+bool split_capable(const Config& c) { return !c.generic && c.layouts == 0xF; }
+
 int run(int cfg, int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-        const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+        const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream, int splits = 1,
+        void* ws = nullptr) {
   int dev = -1;
   const int d = check_device(&dev);
   if (d != TGEMM_OK) return d;
@@ -126,7 +180,7 @@ int run(int cfg, int layout, int64_t M, int64_t N, int64_t K, const void* A, int
                : TGEMM_ELAUNCH;
   }
   const Config& c = cfg_row(cfg);
-  const int64_t nwg = workgroups(c, M, N);
+  const int64_t nwg = workgroups(c, M, N) * splits;
   if (nwg >= ((int64_t)1 << 31)) return TGEMM_EINVAL_DIM;
   tgemm::GemmArgs g;
   g.A = static_cast<const _Float16*>(A);
@@ -142,6 +196,9 @@ int run(int cfg, int layout, int64_t M, int64_t N, int64_t K, const void* A, int
   g.tiles_m = (int)tgemm::ceil_div(M, c.bm);
   g.tiles_n = (int)tgemm::ceil_div(N, c.bn);
   g.layout = layout;
+  g.splits = splits;
+  g.ws = ws;
+  g.ws_parts = splits > 1 ? kWsParts : 0;
   return tgemm::launcher(cfg)(g, s, dev) == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH;
 }
 
@@ -182,6 +239,74 @@ int gemm_f16_cfg(int idx, int64_t M, int64_t N, int64_t K, const void* A, int64_
   return gemm_f16_ex_cfg(idx, 0, 0, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
 }
 
+int64_t tgemm_workspace_bytes(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K) {
+  const int layout = layout_of(trans_a, trans_b);
+  if (M <= 0 || N <= 0 || K <= 0 || M >= TGEMM_MAX_DIM || N >= TGEMM_MAX_DIM || K >= TGEMM_MAX_DIM)
+    return 0;
+  // the plan for 16-byte-aligned operands with tight leading dimensions (other arguments
+  // either plan the same or take the generic kernel, which needs no workspace)
+  const int64_t lda = (layout & 2) ? M : K, ldb = (layout & 1) ? K : N;
+  const uintptr_t a16 = 256;
+  const int cfg = select(layout, M, N, K, (const void*)a16, lda, (const void*)a16, ldb, (const void*)a16, N);
+  if (cfg < 0) return 0;
+  const SplitPlan p = split_plan(layout, M, N, K, cfg);
+  return ws_bytes(cfg_row(p.cfg), p.splits, M, N);
+}
+
+int tgemm_split_plan(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, const void* C, int64_t ldc, int* cfg_out, int* splits_out,
+                     int64_t* workspace_bytes_out) {
+  if (cfg_out == nullptr || splits_out == nullptr || workspace_bytes_out == nullptr) return TGEMM_ENULL;
+  const int layout = layout_of(trans_a, trans_b);
+  const int cfg = select(layout, M, N, K, A, lda, B, ldb, C, ldc);
+  if (cfg < 0 && cfg != kSelectNoop && cfg != kSelectZeroFill) return cfg;
+  SplitPlan p{cfg, 1};
+  if (cfg >= 0) p = split_plan(layout, M, N, K, cfg);
+  *cfg_out = p.cfg;
+  *splits_out = p.splits;
+  *workspace_bytes_out = cfg >= 0 ? ws_bytes(cfg_row(p.cfg), p.splits, M, N) : 0;
+  return TGEMM_OK;
+}
+
+int gemm_f16_ws_cfg(int idx, int splits, int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                    const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int relu,
+                    void* workspace, int64_t workspace_bytes, void* stream) {
+  if (idx < 0 || idx >= table_size()) return TGEMM_EINVAL_CFG;
+  if (splits < 1 || splits > kMaxSplits) return TGEMM_EINVAL_CFG;
+  const int layout = layout_of(trans_a, trans_b);
+  const int cfg = select(layout, M, N, K, A, lda, B, ldb, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
+  if (cfg == kSelectZeroFill) return run(cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  const Config& c = cfg_row(idx);
+  if (!(c.layouts & (1 << layout))) return TGEMM_EINVAL_CFG;
+  if (!c.generic && !fast_eligible(layout, M, N, K, A, lda, B, ldb, C, ldc)) return TGEMM_EINVAL_CFG;
+  if (splits > 1) {
+    if (!split_capable(c) || splits > tgemm::ceil_div(K, c.bk) || workgroups(c, M, N) > kMaxSplitTiles)
+      return TGEMM_EINVAL_CFG;
+    if (workspace == nullptr) return TGEMM_ENULL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TGEMM_EALIGN;
+    if (workspace_bytes < ws_bytes(c, splits, M, N)) return TGEMM_EWORKSPACE;
+  }
+  return run(idx, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, splits, workspace);
+}
+
+int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* workspace,
+                int64_t workspace_bytes, void* stream) {
+  const int layout = layout_of(trans_a, trans_b);
+  const int cfg = select(layout, M, N, K, A, lda, B, ldb, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
+  if (cfg == kSelectZeroFill) return run(cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  const SplitPlan p = split_plan(layout, M, N, K, cfg);
+  if (p.splits == 1) return run(cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  if (workspace == nullptr) return TGEMM_ENULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TGEMM_EALIGN;
+  if (workspace_bytes < ws_bytes(cfg_row(p.cfg), p.splits, M, N)) return TGEMM_EWORKSPACE;
+  return run(p.cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, p.splits, workspace);
+}
+
 int tgemm_select_config_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A,
                            int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc) {
   return select(layout_of(trans_a, trans_b), M, N, K, A, lda, B, ldb, C, ldc);
@@ -201,7 +326,8 @@ const char* tgemm_strerror(int code) {
     case TGEMM_EDEVICE: return "current HIP device is not gfx950 (MI355X) or is unavailable";
     case TGEMM_ELAUNCH: return "kernel launch failed";
     case TGEMM_EINVAL_CFG: return "invalid config index, or config cannot take these arguments";
-    case TGEMM_EALIGN: return "operand pointer not aligned to 2 bytes";
+    case TGEMM_EALIGN: return "operand pointer not aligned to 2 bytes, or workspace not aligned to 256 bytes";
+    case TGEMM_EWORKSPACE: return "workspace smaller than tgemm_workspace_bytes for these sizes";
     default: return "unknown error code";
   }
 }

@@ -69,6 +69,9 @@ struct GemmArgs {
   int relu;
   int tiles_m, tiles_n;
   int layout;  // 2 * trans_a + trans_b: A given as K x M, B given as N x K
+  int splits;  // split-K factor (1 = none); > 1 only for split-capable configs
+  void* ws;    // split-K workspace: tile counters at 0, partial tiles at byte ws_parts
+  int64_t ws_parts;
 };
 
 // The table (host only). Index order is part of the tooling ABI (gemm_f16_cfg, sweep

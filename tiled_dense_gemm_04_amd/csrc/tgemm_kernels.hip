@@ -678,10 +678,10 @@ struct PpOperand {
     }
   }
 
-  // Descriptor of k-tile t; an empty range past the last tile, so that copy only writes
-  // zeros into a slot no later read uses.
-  __device__ int4v rsrc(int t, int nk) const {
-    const uint32_t r = t < nk - 1 ? rng_full : (t == nk - 1 ? rng_last : 0u);
+  // Descriptor of k-tile t (of nk); an empty range from t_end on, so such a copy only
+  // writes zeros into a slot no later read uses.
+  __device__ int4v rsrc(int t, int t_end, int nk) const {
+    const uint32_t r = t < t_end ? (t == nk - 1 ? rng_last : rng_full) : 0u;
     const int tt = t < nk ? t : nk - 1;
     return make_rsrc(base + tt * step, r);
   }
@@ -782,13 +782,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // waves w and w+4 share SIMD w % 4
 
+  // Split-K (g.splits > 1): consecutive workgroup ids are the splits of one output tile;
+  // split s covers k-tiles [s * nk / splits, (s + 1) * nk / splits).
+  const int splits = g.splits;
+  const int tile_id = (int)(blockIdx.x / (unsigned)splits), split = (int)blockIdx.x - tile_id * splits;
   int64_t tm64, tn64;
-  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  tile_of(tile_id, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
   const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
   const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
   const int K = g.K;
   const int nk = (K + BK - 1) / BK;
   const int kin_last = K - (nk - 1) * BK;
+  const int kt0 = (int)((int64_t)split * nk / splits);
+  const int nloc = (int)((int64_t)(split + 1) * nk / splits) - kt0;  // k-tiles of this workgroup
 
   OpA opa;
   OpB opb;
@@ -797,7 +803,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   const uint32_t a_lds0 = lds_addr(a_lds) + wave * 1024;
   const uint32_t b_lds0 = lds_addr(b_lds) + wave * 1024;
 
-  // This thread's PT copies of k-tile t.
+  // This thread's PT copies of this workgroup's k-tile t (global k-tile kt0 + t; an empty
+  // range from t = nloc on).
   struct Dma {
     int4v ra, rb;
     uint32_t a_dst, b_dst;
@@ -805,12 +812,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   };
   auto dma_setup = [&](int t) {
     Dma d;
-    d.ra = opa.rsrc(t, nk);
-    d.rb = opb.rsrc(t, nk);
+    const int kt = kt0 + t, kt_end = kt0 + nloc;
+    d.ra = opa.rsrc(kt, kt_end, nk);
+    d.rb = opb.rsrc(kt, kt_end, nk);
     const int slot = t % STAGES;
     d.a_dst = a_lds0 + slot * A_BYTES;
     d.b_dst = b_lds0 + slot * B_BYTES;
-    d.last = t == nk - 1;
+    d.last = kt == nk - 1;
     return d;
   };
   auto copy_tile = [&](int t) {
@@ -882,7 +890,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   // sched_barrier(0) pins every phase: the compiler may not move MFMAs (register-only,
   // so not ordered by s_barrier) from one phase into the other.
   if (grp == 0) {
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < nloc; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
       mma_tile();                    // phase 1: MFMAs of tile kt
       __builtin_amdgcn_sched_barrier(0);
@@ -895,7 +903,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
       lds_barrier();                 // B1
     }
   } else {
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < nloc; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
       read_tile(kt % STAGES);        // phase 1
       copy_tile(kt + STAGES - 1);
@@ -910,6 +918,64 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   }
   wait_vmcnt<0>();
   clk.loop_end();
+
+  // Split-K fixup. Every split stores its fp32 partial tile to the workspace in register
+  // order (thread tid's j-th group of 4 accumulators at float4 index j * NT + tid:
+  // coalesced, and the reader needs no reshuffle) and counts itself in with one atomic on
+  // the tile's counter. The split that brings the count to `splits` is the last: it
+  // resets the counter for the next call, adds the partial tiles in split order 0, 1, ...
+  // (the same order whichever split finishes last, so results are deterministic) and runs
+  // the epilogue; the others are done. The partial tiles cross XCDs, whose L2s are not
+  // coherent with each other: they are stored and loaded with the device-coherence cache
+  // policy (sc1, what device-scope atomic accesses use), which goes to the coherence
+  // point, so no L2 write-back or invalidation is needed; every wave waits for its stores
+  // to complete before the barrier that precedes the counter update.
+  if (splits > 1) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int NT = 64 * NW, Q = NACC / 4, TILE_BYTES = BM * BN * 4;
+    constexpr int kDeviceCoherent = 16;  // cache policy bit sc1
+    unsigned int* const counter = (unsigned int*)g.ws + tile_id;
+    char* const parts = (char*)g.ws + g.ws_parts + (size_t)tile_id * splits * TILE_BYTES;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(parts, 0, splits * TILE_BYTES, kBufWord3);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const f4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+          const int off = split * TILE_BYTES + (((fm * FN + fn) * Q + q) * NT + tid) * 16;
+          __builtin_amdgcn_raw_buffer_store_b128(v, prs, off, 0, kDeviceCoherent);
+        }
+    wait_vmcnt<0>();
+    __syncthreads();  // (also: every copy into the ring has landed, so smem is free)
+    if (tid == 0) {
+      const unsigned int before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = before == (unsigned int)(splits - 1);
+      if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *(TG_LDS int*)smem = last;
+    }
+    __syncthreads();
+    const int last = *(const TG_LDS int*)smem;
+    if (!last) {
+      clk.finish(nloc);
+      return;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const int off = (((fm * FN + fn) * Q + q) * NT + tid) * 16;
+          f4 sum = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kDeviceCoherent);
+          for (int sp = 1; sp < splits; ++sp)
+            sum += __builtin_amdgcn_raw_buffer_load_b128(prs, sp * TILE_BYTES + off, 0, kDeviceCoherent);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[fm][fn][4 * q + e] = sum[e];
+        }
+    __syncthreads();  // the flag in smem is overwritten by the staging below
+  }
 
   // Epilogue. Lane holds, for tile (fm, fn), row fm*MF + lane % MF of the wave tile and
   // columns fn*MF + 8*g4 + 4*(lane / MF) .. +3 (32x32) or fn*16 + 4*(lane / 16) .. +3
@@ -963,7 +1029,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
     const int m = wm * WTM + r, n = wn * WTN + 8 * c;
     if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
   }
-  clk.finish(nk);
+  clk.finish(nloc);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1113,7 +1179,7 @@ hipError_t launch_pp_layout(const GemmArgs& g, hipStream_t s, int device) {
     if (attr != hipSuccess) return attr;
     ready.fetch_or(bit, std::memory_order_acq_rel);
   }
-  const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
+  const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n * g.splits;  // splits per tile
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * WM * WN), lds, s, g);
   return hipGetLastError();
 }

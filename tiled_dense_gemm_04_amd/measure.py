@@ -11,6 +11,8 @@ For each workload, with the config gemm_f16 picks:
   * phases: one more trial through the instrumented build (libtgemm_stamps.so); the
     stamps of its last call give, per workgroup, prologue / main loop / epilogue wall
     time, the shader clock the workgroup ran at, and the main loop's average per XCD;
+  * split-K: where gemm_f16_ws would split (small output grids), the same timing through
+    gemm_f16_ws with its planned config and split count;
   * context: torch.matmul (hipBLASLt) (+ relu_ when the workload has ReLU) timed the
     same way. Context only; never a target.
 The MFMA ceiling is the library's MFMA probe (no memory traffic, pseudo-random
@@ -146,6 +148,17 @@ def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceilin
         res["hot"]["pct_of_mfma_ceiling"] = 100 * tf(hot["median_us"]) / ceiling
     log(f"{w.name}: {desc['name']} hot {hot['median_us']:.2f} us ({tf(hot['median_us']):.1f} TFLOP/s)")
 
+    plan = tg.tgemm_split_plan(w.trans_a, w.trans_b, w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(),
+                               b.stride(0), c.data_ptr(), c.stride(0))
+    if plan[1] > 1:
+        ws = tg.workspace_for(plan[2], a.device, stream.cuda_stream)
+        sk = timed_trials(torch, stream, lambda i: tg.gemm_f16_ws(a, b, c, w.trans_a, w.trans_b, relu=w.relu,
+                                                                stream=stream, workspace=ws))
+        res["split_k"] = {**sk, "config": tg.tgemm_config_desc(plan[0])["name"], "splits": plan[1],
+                          "workspace_bytes": plan[2], "tflops": tf(sk["median_us"]),
+                          "pct_of_peak": 100 * tf(sk["median_us"]) / PEAK_TFLOPS}
+        log(f"{w.name}: split-K {plan[1]} x {res['split_k']['config']} {sk['median_us']:.2f} us")
+
     if cold:
         per_set = res["compulsory_bytes"]
         nsets = max(4, math.ceil(CACHE_BYTES / per_set) + 1)
@@ -196,16 +209,19 @@ def markdown(results, probe, host) -> str:
                  f"shader clock {ph.get('shader_clock_ghz', float('nan')):.3f} GHz (s_memtime / s_memrealtime).")
         L.append("")
     L.append("| workload | config | hot us (min-max) | TFLOP/s | % peak | % MFMA ceiling | cold us | "
-             "hipBLASLt us (context) |")
-    L.append("|---|---|---|---|---|---|---|---|")
+             "split-K (gemm_f16_ws) us | hipBLASLt us (context) |")
+    L.append("|---|---|---|---|---|---|---|---|---|")
     for r in results:
         h = r["hot"]
         cold = f"{r['cold']['median_us']:.2f} ({r['cold']['sets']} sets)" if "cold" in r else "-"
         th = f"{r['torch_matmul']['median_us']:.2f}" if "torch_matmul" in r else "-"
         ceil = f"{h['pct_of_mfma_ceiling']:.1f}" if "pct_of_mfma_ceiling" in h else "-"
+        sk = r.get("split_k")
+        sks = (f"{sk['median_us']:.2f} ({sk['splits']} x {sk['config']}, {sk['tflops']:.1f} TFLOP/s)"
+               if sk else "- (no split)")
         L.append(f"| {r['workload']} ({r['M']}x{r['N']}x{r['K']}) | {r['config']} | {h['median_us']:.2f} "
                  f"({h['min_us']:.2f}-{h['max_us']:.2f}) | {h['tflops']:.1f} | {h['pct_of_peak']:.1f} | {ceil} | "
-                 f"{cold} | {th} |")
+                 f"{cold} | {sks} | {th} |")
     L.append("")
     L.append("Phases of the last call of one more trial, instrumented build (means over workgroups):")
     L.append("")
