@@ -70,17 +70,20 @@ int64_t workgroups(const Config& c, int64_t M, int64_t N) {
 }
 
 // Config choice for a fast-eligible call (rows of the table in tgemm_kernels.hip:
-// 9 = 16x16x32 ping-pong 256x256, 7 = 4-wave pipelined 128x128 with BK 64). From the
-// offline sweep on the measured workloads: 256 x 256 ping-pong tiles win as soon as they
-// cover most of the 256 compute units (160+ tiles, e.g. 4095 x 3000 has 192); below
-// that, 128 x 128 tiles keep more compute units busy.
-// Transposed operands take the ping-pong kernels only (15 = 128x128 ping-pong for small
-// grids).
-constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15;
+// 9 = 16x16x32 ping-pong 256x256, 16 = the same with 256x128 tiles, 15 = 128x128,
+// 7 = 4-wave pipelined 128x128 with BK 64). From the offline sweep on the measured
+// workloads: 256 x 256 ping-pong tiles win as soon as they cover most of the 256 compute
+// units (160+ tiles, e.g. 4095 x 3000 has 192); below that, 256 x 128 tiles when they
+// give about one workgroup per compute unit (16384 x 512: 67.9 us against 69.6 us), and
+// the 128 x 128 pipelined kernel for the smallest grids (1024^3: 11.3 us against 15.2 us
+// for the 128 x 128 ping-pong). Transposed operands take the ping-pong kernels only.
+constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15, kCfgMid = 16;
 int choose_fast(int layout, int64_t M, int64_t N, int64_t K) {
   (void)K;
   const int64_t t256 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256);
   if (t256 >= 160) return kCfgBig;
+  const int64_t t256x128 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 128);
+  if (t256x128 >= 200 && t256x128 <= 256) return kCfgMid;
   return layout == 0 ? kCfgSmall : kCfgSmallT;
 }
 

@@ -1,8 +1,11 @@
 """Offline config sweep: time every applicable table config of libtgemm on the measured
 workloads and report the fastest per workload (the evidence behind the config choice in
-tgemm_api.cpp's choose_fast). Needs a GPU.
+tgemm_api.cpp's choose_fast). With --split, time split-K instead: the 256 x 256 and
+128 x 128 ping-pong configs at 1, 2, 4 and 8 splits per output tile on small-grid shapes
+(the evidence behind split_plan). Needs a GPU.
 
   python -m tiled_dense_gemm_04_amd.sweep [--out results.json] [--iters 30]
+  python -m tiled_dense_gemm_04_amd.sweep --split [--md out.md]
 """
 from __future__ import annotations
 
@@ -32,6 +35,56 @@ def time_config(tg, torch, a, b, c, relu, cfg, iters, warmup=5):
     return e0.elapsed_time(e1) / iters * 1e3  # us
 
 
+SPLIT_SHAPES = [(1024, 1024, 1024), (16384, 512, 4096), (512, 4096, 4096), (1024, 1024, 32768),
+                (512, 512, 16384), (2048, 2048, 16384), (4096, 1024, 8192)]
+
+
+def split_sweep(md_path=None):
+    import torch
+
+    import tgemm_workloads as W
+    import tiled_dense_gemm_04_amd as tg
+    from tiled_dense_gemm_04_amd.measure import timed_trials
+
+    stream = torch.cuda.Stream()
+    names = {i: c["name"] for i, c in enumerate(tg.configs())}
+    split_cfgs = [i for i, c in enumerate(tg.configs()) if c["layouts"] == 0xF and not c["generic"]
+                  and c["block_m"] == c["block_n"]]
+    lines = ["| M x N x K | gemm_f16 (no split) us | planned (cfg, splits) | "
+             + " | ".join(f"{names[c][:9]} x{s}" for c in split_cfgs for s in (1, 2, 4, 8)) + " |",
+             "|---|---|---|" + "---|" * (4 * len(split_cfgs))]
+    for (M, N, K) in SPLIT_SHAPES:
+        A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=5)
+        a = torch.from_numpy(A).cuda()
+        b = torch.from_numpy(B).cuda()
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        base = timed_trials(torch, stream, lambda i: tg.gemm_f16(a, b, c, relu=True, stream=stream),
+                            trials=5)["median_us"]
+        plan = tg.tgemm_split_plan(False, False, M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N)
+        cells = []
+        for cfg in split_cfgs:
+            d = tg.tgemm_config_desc(cfg)
+            tiles = -(-M // d["block_m"]) * -(-N // d["block_n"])
+            nk = -(-K // d["block_k"])
+            for sp in (1, 2, 4, 8):
+                if sp > nk or tiles > 1024:
+                    cells.append("-")
+                    continue
+                t = timed_trials(torch, stream, lambda i: tg.gemm_f16_ws(a, b, c, relu=True, stream=stream,
+                                                                       cfg=cfg, splits=sp), trials=5)["median_us"]
+                cells.append(f"{t:.1f}")
+        row = f"| {M}x{N}x{K} | {base:.1f} | {names[plan[0]][:9]}, {plan[1]} | " + " | ".join(cells) + " |"
+        print(row, flush=True)
+        lines.append(row)
+        del a, b, c
+        torch.cuda.empty_cache()
+    md = "\n".join(lines) + "\n"
+    if md_path:
+        with open(md_path, "w") as f:
+            f.write(md)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=None)
@@ -39,7 +92,11 @@ def main():
     ap.add_argument("--workloads", default=None, help="comma-separated names (default: all)")
     ap.add_argument("--torch", action="store_true",
                     help="also time torch.matmul (+ relu) on the same inputs, as context only")
+    ap.add_argument("--split", action="store_true", help="split-K sweep on small-grid shapes")
+    ap.add_argument("--md", default=None, help="with --split: write the table here")
     args = ap.parse_args()
+    if args.split:
+        return split_sweep(args.md)
 
     import torch
 
