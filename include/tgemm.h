@@ -122,6 +122,30 @@ TGEMM_API int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_
                           void* C, int64_t ldc,
                           int relu, void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * Grouped GEMM: count independent GEMMs C_i = ReLU?(op(A_i) @ op(B_i)) with one operand
+ * layout and one ReLU flag for all, any sizes per GEMM (e.g. the experts of a
+ * mixture-of-experts layer, each with its own number of rows: the "MoE GroupGEMM" planned
+ * in "TileLang-MUSA operator development" (7yue.com), section 7). GEMMs on the fast path
+ * are launched together, up to 32 per launch, with one tile config chosen from their
+ * total size; the others (K == 0, or arguments only the generic kernel takes) get a
+ * launch of their own; M_i == 0 or N_i == 0 is skipped. gemms: host array of count
+ * descriptors (read during the call only). Every descriptor is validated before any work
+ * is enqueued; the first invalid one's error code is returned. C_i must not overlap any
+ * A_j, B_j or another C_j. Otherwise as gemm_f16_ex.
+ */
+typedef struct tgemm_gemm_desc {
+    int64_t M, N, K;
+    const void* A;
+    int64_t lda;
+    const void* B;
+    int64_t ldb;
+    void* C;
+    int64_t ldc;
+} tgemm_gemm_desc;
+TGEMM_API int gemm_f16_grouped(int trans_a, int trans_b, int count, const tgemm_gemm_desc* gemms,
+                               int relu, void* stream);
+
 /* Human-readable text for a return code (static storage, never NULL). */
 TGEMM_API const char* tgemm_strerror(int code);
 

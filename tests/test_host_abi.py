@@ -36,7 +36,7 @@ def exported(path):
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 17, syms
+    assert len(syms) == 18, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -248,6 +248,26 @@ def test_workspace_errors_before_hip():
     # (a shape that does not split needs no workspace: covered on the GPU, since such a call
     # goes on to launch)
     assert tg.tgemm_strerror(tg.TGEMM_EWORKSPACE) != "unknown error code"
+
+
+def test_grouped_validation_before_hip():
+    """Every descriptor is checked before anything is enqueued (no GPU needed)."""
+    import ctypes
+    L = tg.lib()
+    good = tg.GemmDesc(256, 256, 256, A16, 256, A16, 256, A16, 256)
+    bad_ld = tg.GemmDesc(256, 256, 256, A16, 255, A16, 256, A16, 256)
+    bad_null = tg.GemmDesc(256, 256, 256, 0, 256, A16, 256, A16, 256)
+    arr = (tg.GemmDesc * 3)(good, bad_ld, good)
+    assert L.gemm_f16_grouped(0, 0, 3, arr, 1, None) == tg.TGEMM_EINVAL_LD
+    arr = (tg.GemmDesc * 2)(good, bad_null)
+    assert L.gemm_f16_grouped(0, 0, 2, arr, 1, None) == tg.TGEMM_ENULL
+    assert L.gemm_f16_grouped(0, 0, 1, None, 1, None) == tg.TGEMM_ENULL
+    assert L.gemm_f16_grouped(0, 0, -1, None, 1, None) == tg.TGEMM_EINVAL_DIM
+    assert L.gemm_f16_grouped(0, 0, 0, None, 1, None) == tg.TGEMM_OK
+    # transposed A: lda >= M
+    tA = tg.GemmDesc(256, 128, 64, A16, 200, A16, 128, A16, 128)
+    assert L.gemm_f16_grouped(1, 0, 1, (tg.GemmDesc * 1)(tA), 1, None) == tg.TGEMM_EINVAL_LD
+    assert ctypes.sizeof(tg.GemmDesc) == 72
 
 
 SHAPES = [(1, 1), (255, 257), (256, 256), (1024, 1024), (4096, 4096), (4095, 3000), (8192, 8192),

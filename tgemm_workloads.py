@@ -92,6 +92,34 @@ SPLIT_WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class GroupedWorkload:
+    """Independent GEMMs of one layout: expert e multiplies its M[e] rows by its own K x N
+    weight (a mixture-of-experts layer with uneven routing)."""
+    name: str
+    Ms: tuple
+    N: int
+    K: int
+    relu: bool
+    seed: int
+
+    @property
+    def flop(self) -> int:
+        return 2 * sum(self.Ms) * self.N * self.K
+
+    def inputs(self):
+        """[(A_e, B_e)] from seeds seed, seed + 1, ... (same recipe as make_inputs)."""
+        return [make_inputs(m, self.N, self.K, "normal", 1.0, self.seed + e) for e, m in enumerate(self.Ms)]
+
+
+# 8 experts, 16384 routed rows in all, hidden 4096 -> expert width 2048 (the up projection).
+GROUPED_WORKLOADS = {
+    "moe_8x_16384x2048x4096": GroupedWorkload("moe_8x_16384x2048x4096",
+                                              (3072, 2560, 2048, 2048, 1792, 1536, 1280, 2048), 2048, 4096,
+                                              True, 20),
+}
+
+
 def all_workloads():
     """Headline, the five measured configurations, the transposed-operand ones, then the
     small-grid (split-K) ones."""

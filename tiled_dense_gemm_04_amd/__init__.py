@@ -11,7 +11,7 @@ The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
 ``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``,
 ``tgemm_mfma_probe``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
 stream unless given), ``gemm_f16_ws_cfg`` (as ``cfg=``/``splits=``),
-``tgemm_workspace_bytes`` and ``tgemm_split_plan``. ``matmul`` takes row- or column-major operand views and picks the
+``tgemm_workspace_bytes`` and ``tgemm_split_plan``; grouped GEMMs: ``gemm_f16_grouped``. ``matmul`` takes row- or column-major operand views and picks the
 layout; ``GemmFunction`` is the autograd wrapper (backward: dA = dC B^T, dB = A^T dC
 through gemm_f16_ex). The instrumented
 twin ``libtgemm_stamps.so`` (``stamps_lib()``, measurement tools only) adds
@@ -43,7 +43,8 @@ SELECT_ZERO_FILL = -101
 EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_strerror",
            "tgemm_version", "tgemm_num_configs", "tgemm_config_desc", "tgemm_select_config",
            "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups", "tgemm_mfma_probe",
-           "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan")
+           "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan",
+           "gemm_f16_grouped")
 # The extra symbols include/tgemm_stamps.h declares (instrumented build only).
 STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear")
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
@@ -69,6 +70,13 @@ class ConfigInfo(ctypes.Structure):
         d = {f: getattr(self, f) for f, _ in self._fields_ if f != "name"}
         d["name"] = self.name.decode()
         return d
+
+
+class GemmDesc(ctypes.Structure):
+    """tgemm_gemm_desc"""
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("B", ctypes.c_void_p),
+                ("ldb", ctypes.c_int64), ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
 
 
 _lib = None
@@ -113,6 +121,8 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.gemm_f16_ws_cfg.argtypes = [i32, i32, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p, i64, p]
     L.tgemm_workspace_bytes.restype = i64
     L.tgemm_workspace_bytes.argtypes = [i32, i32, i64, i64, i64]
+    L.gemm_f16_grouped.restype = i32
+    L.gemm_f16_grouped.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, p]
     L.tgemm_split_plan.restype = i32
     L.tgemm_split_plan.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(i64)]
@@ -275,6 +285,8 @@ def _operand(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     rows, cols = t.shape
+    if t.numel() == 0:  # an empty operand has no meaningful strides
+        return rows, cols, max(1, cols)
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must be row-major (stride(1) == 1)")
     ld = t.stride(0) if rows > 1 else max(1, cols)
@@ -386,6 +398,43 @@ def gemm_f16_ws(a, b, c=None, trans_a: bool = False, trans_b: bool = False, relu
     if rc != TGEMM_OK:
         raise TgemmError(rc, "gemm_f16_ws" if cfg is None else f"gemm_f16_ws_cfg[{cfg}, {splits}]")
     return c
+
+
+def gemm_f16_grouped(problems, trans_a: bool = False, trans_b: bool = False, relu: bool = True,
+                     stream=None, library=None):
+    """Independent GEMMs in as few launches as possible: ``problems`` is a list of (a, b) or
+    (a, b, c) with a, b stored as in gemm_f16_ex (same trans_a / trans_b for all) and c
+    allocated when missing. Returns the list of outputs."""
+    import torch
+    if not problems:
+        return []
+    descs = (GemmDesc * len(problems))()
+    outs = []
+    dev = problems[0][0].device
+    for i, pr in enumerate(problems):
+        a, b = pr[0], pr[1]
+        c = pr[2] if len(pr) > 2 else None
+        ra, ca, lda = _operand(a, f"problems[{i}].a")
+        rb, cb, ldb = _operand(b, f"problems[{i}].b")
+        M, K = (ca, ra) if trans_a else (ra, ca)
+        K2, N = (cb, rb) if trans_b else (rb, cb)
+        if K2 != K:
+            raise ValueError(f"problems[{i}]: op(a) is {M}x{K}, op(b) is {K2}x{N}")
+        if c is None:
+            c = torch.empty((M, N), dtype=torch.float16, device=a.device)
+        Mc, Nc, ldc = _operand(c, f"problems[{i}].c")
+        if (Mc, Nc) != (M, N):
+            raise ValueError(f"problems[{i}]: c has shape {tuple(c.shape)}, expected {(M, N)}")
+        if not (a.device == b.device == c.device == dev):
+            raise ValueError("all operands must be on one device")
+        descs[i] = GemmDesc(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(), ldc)
+        outs.append(c)
+    with torch.cuda.device(dev):
+        rc = (library or lib()).gemm_f16_grouped(int(trans_a), int(trans_b), len(problems), descs, int(relu),
+                                                 _stream_handle(stream, dev))
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "gemm_f16_grouped")
+    return outs
 
 
 def gemm_f16(a, b, c=None, relu: bool = True, stream=None, cfg: int | None = None, library=None):

@@ -310,6 +310,78 @@ int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const
   return run(p.cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, p.splits, workspace);
 }
 
+int gemm_f16_grouped(int trans_a, int trans_b, int count, const tgemm_gemm_desc* gemms, int relu,
+                     void* stream) {
+  if (count < 0) return TGEMM_EINVAL_DIM;
+  if (count == 0) return TGEMM_OK;
+  if (gemms == nullptr) return TGEMM_ENULL;
+  const int layout = layout_of(trans_a, trans_b);
+  // validate everything before enqueueing anything
+  int64_t t256 = 0;
+  for (int i = 0; i < count; ++i) {
+    const tgemm_gemm_desc& d = gemms[i];
+    const int v = select(layout, d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc);
+    if (v < 0 && v != kSelectNoop && v != kSelectZeroFill) return v;
+    if (v >= 0 && fast_eligible(layout, d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc))
+      t256 += tgemm::ceil_div(d.M, 256) * tgemm::ceil_div(d.N, 256);
+  }
+  int dev = -1;
+  const int dc = check_device(&dev);
+  if (dc != TGEMM_OK) return dc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // one tile config for the whole group: 256 x 256 when the group's tiles cover most of
+  // the GPU, else 128 x 128
+  const int cfg = t256 >= 160 ? kCfgBig : kCfgSmallT;
+  const tgemm::GroupedLauncher gl = tgemm::grouped_launcher(cfg);
+  const Config& c = cfg_row(cfg);
+  if (gl == nullptr) return TGEMM_ELAUNCH;
+  tgemm::GroupedArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.relu = relu != 0;
+  ga.layout = layout;
+  int64_t nwg = 0;
+  auto flush = [&]() -> int {
+    if (ga.count == 0) return TGEMM_OK;
+    ga.wg_start[ga.count] = (int)nwg;
+    const hipError_t e = gl(ga, nwg, s, dev);
+    ga.count = 0;
+    nwg = 0;
+    return e == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH;
+  };
+  for (int i = 0; i < count; ++i) {
+    const tgemm_gemm_desc& d = gemms[i];
+    const int v = select(layout, d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc);
+    if (v == kSelectNoop) continue;
+    if (v == kSelectZeroFill || !fast_eligible(layout, d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc)) {
+      // K == 0, or arguments only the generic kernel takes: a launch of its own
+      const int r = run(v, layout, d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc, relu, stream);
+      if (r != TGEMM_OK) return r;
+      continue;
+    }
+    const int64_t tm = tgemm::ceil_div(d.M, c.bm), tn = tgemm::ceil_div(d.N, c.bn);
+    if (ga.count == tgemm::kMaxGroups || nwg + tm * tn >= ((int64_t)1 << 31)) {
+      const int r = flush();
+      if (r != TGEMM_OK) return r;
+    }
+    tgemm::GroupEntry& e = ga.e[ga.count];
+    e.A = static_cast<const _Float16*>(d.A);
+    e.B = static_cast<const _Float16*>(d.B);
+    e.C = static_cast<_Float16*>(d.C);
+    e.lda = d.lda;
+    e.ldb = d.ldb;
+    e.ldc = d.ldc;
+    e.M = (int)d.M;
+    e.N = (int)d.N;
+    e.K = (int)d.K;
+    e.tiles_m = (int)tm;
+    e.tiles_n = (int)tn;
+    ga.wg_start[ga.count] = (int)nwg;
+    nwg += tm * tn;
+    ++ga.count;
+  }
+  return flush();
+}
+
 int tgemm_select_config_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A,
                            int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc) {
   return select(layout_of(trans_a, trans_b), M, N, K, A, lda, B, ldb, C, ldc);

@@ -83,6 +83,26 @@ const Config* config_table(int* count);
 typedef hipError_t (*Launcher)(const GemmArgs&, hipStream_t, int device);
 Launcher launcher(int idx);
 
+// Grouped launch: independent GEMMs sharing operand layout and ReLU flag. GEMM i owns
+// workgroups [wg_start[i], wg_start[i+1]) of the launch (tiles_m * tiles_n each).
+constexpr int kMaxGroups = 32;
+struct GroupEntry {
+  const _Float16* A;
+  const _Float16* B;
+  _Float16* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  int tiles_m, tiles_n;
+};
+struct GroupedArgs {
+  int count, relu, layout;
+  int wg_start[kMaxGroups + 1];
+  GroupEntry e[kMaxGroups];
+};
+typedef hipError_t (*GroupedLauncher)(const GroupedArgs&, int64_t nwg, hipStream_t, int device);
+// The grouped launcher of table row idx, or nullptr if that config has none.
+GroupedLauncher grouped_launcher(int idx);
+
 // Zero-fill of an M x N block with row stride ldc (the K == 0 case).
 hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s);
 

@@ -752,9 +752,11 @@ struct PpOperand {
 // MF selects the MFMA: 32 = v_mfma_f32_32x32x16_f16, 16 = v_mfma_f32_16x16x32_f16 (half
 // the accumulator traffic per FLOP, twice the instructions). TA / TB: A given transposed
 // (K x M, lda >= M) / B given transposed (N x K, ldb >= K).
+// The body works on workgroup `wg` of one GEMM's launch (blockIdx.x for a single GEMM,
+// the index inside its GEMM for a grouped launch).
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA,
           bool TB>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
+__device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   WgClock clk;
   clk.start();
   constexpr int NW = WM * WN;
@@ -785,7 +787,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   // Split-K (g.splits > 1): consecutive workgroup ids are the splits of one output tile;
   // split s covers k-tiles [s * nk / splits, (s + 1) * nk / splits).
   const int splits = g.splits;
-  const int tile_id = (int)(blockIdx.x / (unsigned)splits), split = (int)blockIdx.x - tile_id * splits;
+  const int tile_id = wg / splits, split = wg - tile_id * splits;
   int64_t tm64, tn64;
   tile_of(tile_id, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
   const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
@@ -1032,6 +1034,43 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
   clk.finish(nloc);
 }
 
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA,
+          bool TB>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong(GemmArgs g) {
+  pingpong_body<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>(g, (int)blockIdx.x);
+}
+
+// Grouped GEMM: up to kMaxGroups independent GEMMs (same operand layout and ReLU flag, any
+// sizes) in one launch. GEMM i owns workgroups [wg_start[i], wg_start[i+1]); a workgroup
+// finds its GEMM by a scalar search over the (uniform) table in the kernel arguments.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA,
+          bool TB>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong_grouped(GroupedArgs ga) {
+  const int b = (int)blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < ga.count && b >= ga.wg_start[gi + 1]) ++gi;
+  const GroupEntry& e = ga.e[gi];
+  GemmArgs g;
+  g.A = e.A;
+  g.B = e.B;
+  g.C = e.C;
+  g.lda = e.lda;
+  g.ldb = e.ldb;
+  g.ldc = e.ldc;
+  g.M = e.M;
+  g.N = e.N;
+  g.K = e.K;
+  g.relu = ga.relu;
+  g.tiles_m = e.tiles_m;
+  g.tiles_n = e.tiles_n;
+  g.layout = ga.layout;
+  g.splits = 1;
+  g.ws = nullptr;
+  g.ws_parts = 0;
+  pingpong_body<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>(g, b - ga.wg_start[gi]);
+}
+
 // ------------------------------------------------------------------------------------
 // Generic kernel: 64 x 64 x 32 tile, 4 waves (2 x 2 of 32 x 32), element-wise predicated
 // loads (any 2-byte-aligned pointers, any strides and sizes, any operand layout). A is
@@ -1184,6 +1223,32 @@ hipError_t launch_pp_layout(const GemmArgs& g, hipStream_t s, int device) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA, bool TB>
+hipError_t launch_pp_grouped_layout(const GroupedArgs& ga, int64_t nwg, hipStream_t s, int device) {
+  constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
+  auto kern = gemm_pingpong_grouped<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>;
+  static std::atomic<uint64_t> ready{0};
+  const uint64_t bit = 1ull << (device & 63);
+  if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * WM * WN), lds, s, ga);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF>
+hipError_t launch_pp_grouped(const GroupedArgs& ga, int64_t nwg, hipStream_t s, int device) {
+  switch (ga.layout) {
+    case 1: return launch_pp_grouped_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, false, true>(ga, nwg, s, device);
+    case 2: return launch_pp_grouped_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, true, false>(ga, nwg, s, device);
+    case 3: return launch_pp_grouped_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, true, true>(ga, nwg, s, device);
+    default: return launch_pp_grouped_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, false, false>(ga, nwg, s, device);
+  }
+}
+
 // ALL: the config is instantiated for every operand layout (g.layout = 2 * trans_a +
 // trans_b); otherwise only for A and B as given (the host never sends it another layout).
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool ALL>
@@ -1307,6 +1372,21 @@ const Config* config_table(int* count) {
           TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW)};
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
+}
+
+// Grouped launchers exist for the two ping-pong configs the grouped entry point uses
+// (9: 256 x 256, 15: 128 x 128); the table rows are checked against these shapes.
+GroupedLauncher grouped_launcher(int idx) {
+  int n = 0;
+  const Config* t = config_table(&n);
+  if (idx < 0 || idx >= n) return nullptr;
+  const Config& c = t[idx];
+  if (c.generic || c.layouts != 0xF || c.bk != 32 || c.stages != 4 || c.waves_m != 2 || c.waves_n != 4 ||
+      c.panel != 4 || c.xcd_remap != 1)
+    return nullptr;
+  if (c.bm == 256 && c.bn == 256) return launch_pp_grouped<256, 256, 32, 2, 4, 4, 4, 1, 16>;
+  if (c.bm == 128 && c.bn == 128) return launch_pp_grouped<128, 128, 32, 2, 4, 4, 4, 1, 16>;
+  return nullptr;
 }
 
 Launcher launcher(int idx) {

@@ -197,7 +197,38 @@ def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceilin
     return res
 
 
-def markdown(results, probe, host) -> str:
+def measure_grouped(torch, tg, w, stream, with_torch=True):
+    """One grouped workload: gemm_f16_grouped (one launch) against the same GEMMs issued
+    one gemm_f16 call each, and (context) a loop of torch.matmul (+ relu_)."""
+    ins = w.inputs()
+    probs = [(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()) for A, B in ins]
+    outs = [torch.empty((a.shape[0], b.shape[1]), dtype=torch.float16, device="cuda") for a, b in probs]
+    trip = [(a, b, c) for (a, b), c in zip(probs, outs)]
+
+    def tf(us):
+        return w.flop / (us * 1e-6) / 1e12
+
+    g = timed_trials(torch, stream, lambda i: tg.gemm_f16_grouped(trip, relu=w.relu, stream=stream))
+    seq = timed_trials(torch, stream, lambda i: [tg.gemm_f16(a, b, c, relu=w.relu, stream=stream) for a, b, c in trip])
+    res = {"workload": w.name, "Ms": list(w.Ms), "N": w.N, "K": w.K, "relu": w.relu, "flop": w.flop,
+           "grouped": {**g, "tflops": tf(g["median_us"]), "pct_of_peak": 100 * tf(g["median_us"]) / PEAK_TFLOPS},
+           "sequential": {**seq, "tflops": tf(seq["median_us"])}}
+    log(f"{w.name}: grouped {g['median_us']:.2f} us, one call per GEMM {seq['median_us']:.2f} us")
+    if with_torch:
+        def tmm(_i):
+            for a, b in probs:
+                r = torch.matmul(a, b)
+                if w.relu:
+                    torch.relu_(r)
+        with torch.cuda.stream(stream):
+            th = timed_trials(torch, stream, tmm)
+        res["torch_matmul"] = {**th, "tflops": tf(th["median_us"]), "note": "context only"}
+    del probs, outs, trip
+    torch.cuda.empty_cache()
+    return res
+
+
+def markdown(results, probe, host, grouped=None) -> str:
     L = []
     L.append(f"Device: {host['device']}; {host['library']}; torch {host['torch']}.")
     L.append("")
@@ -222,6 +253,18 @@ def markdown(results, probe, host) -> str:
         L.append(f"| {r['workload']} ({r['M']}x{r['N']}x{r['K']}) | {r['config']} | {h['median_us']:.2f} "
                  f"({h['min_us']:.2f}-{h['max_us']:.2f}) | {h['tflops']:.1f} | {h['pct_of_peak']:.1f} | {ceil} | "
                  f"{cold} | {sks} | {th} |")
+    if grouped:
+        L.append("")
+        L.append("Grouped GEMMs (gemm_f16_grouped, one launch) against one gemm_f16 call per GEMM:")
+        L.append("")
+        L.append("| workload | rows per GEMM | grouped us | TFLOP/s | % peak | one call each us | "
+                 "hipBLASLt loop us (context) |")
+        L.append("|---|---|---|---|---|---|---|")
+        for r in grouped:
+            th = f"{r['torch_matmul']['median_us']:.2f}" if "torch_matmul" in r else "-"
+            L.append(f"| {r['workload']} (N {r['N']}, K {r['K']}) | {' '.join(str(m) for m in r['Ms'])} | "
+                     f"{r['grouped']['median_us']:.2f} | {r['grouped']['tflops']:.1f} | "
+                     f"{r['grouped']['pct_of_peak']:.1f} | {r['sequential']['median_us']:.2f} | {th} |")
     L.append("")
     L.append("Phases of the last call of one more trial, instrumented build (means over workgroups):")
     L.append("")
@@ -269,11 +312,14 @@ def main():
     ceiling = probe["tflops"] if probe else None
     results = [measure_workload(torch, tg, W, w, stream, cold=not args.no_cold, with_torch=not args.no_torch,
                                 ceiling=ceiling) for w in works]
-    md = markdown(results, probe, host)
+    grouped = [measure_grouped(torch, tg, gw, stream, with_torch=not args.no_torch)
+               for gw in W.GROUPED_WORKLOADS.values()
+               if not args.workloads or gw.name in set(args.workloads.split(","))]
+    md = markdown(results, probe, host, grouped)
     print(md)
     if args.json:
         with open(args.json, "w") as f:
-            json.dump({"host": host, "probe": probe, "results": results}, f, indent=1)
+            json.dump({"host": host, "probe": probe, "results": results, "grouped": grouped}, f, indent=1)
     if args.md:
         with open(args.md, "w") as f:
             f.write(md)
