@@ -37,7 +37,7 @@ FAST_SHAPES = [(256, 256, 64), (520, 392, 264), (136, 264, 1000), (8, 8, 8), (10
 ODD_SHAPES = [(17, 23, 29), (65, 63, 33), (1, 1, 1), (130, 7, 250)]
 
 
-@pytest.mark.parametrize("cfg_pos", range(5))
+@pytest.mark.parametrize("cfg_pos", range(6))
 def test_layouts_each_config(cfg_pos):
     cfgs = _all_layout_cfgs()
     if cfg_pos >= len(cfgs):

@@ -42,7 +42,7 @@ def _run_ws(A, B, relu, cfg, splits, ta=False, tb=False, workspace=None):
 SHAPES = [(520, 392, 1000), (256, 256, 512), (136, 264, 2048), (1000, 1032, 520), (8, 8, 264)]
 
 
-@pytest.mark.parametrize("cfg_pos", range(4))
+@pytest.mark.parametrize("cfg_pos", range(5))
 def test_split_each_config_and_layout(cfg_pos):
     cfgs = _split_cfgs()
     if cfg_pos >= len(cfgs):

@@ -77,10 +77,15 @@ int64_t workgroups(const Config& c, int64_t M, int64_t N) {
 // give about one workgroup per compute unit (16384 x 512: 67.9 us against 69.6 us), and
 // the 128 x 128 pipelined kernel for the smallest grids (1024^3: 11.3 us against 15.2 us
 // for the 128 x 128 ping-pong). Transposed operands take the ping-pong kernels only.
-constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15, kCfgMid = 16;
+// 18 = 256 x 192 tiles: when 256 x 256 tiles leave part of the GPU idle in their last
+// (only) wave and 256 x 192 tiles still fit in one wave (4095 x 3000: 192 tiles of
+// 256 x 256 against 256 of 256 x 192).
+constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15, kCfgMid = 16, kCfg192 = 18;
 int choose_fast(int layout, int64_t M, int64_t N, int64_t K) {
   (void)K;
   const int64_t t256 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256);
+  const int64_t t192 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 192);
+  if (t256 >= 160 && t256 < 256 && t192 > t256 && t192 <= 256) return kCfg192;
   if (t256 >= 160) return kCfgBig;
   const int64_t t256x128 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 128);
   if (t256x128 >= 200 && t256x128 <= 256) return kCfgMid;
@@ -426,7 +431,8 @@ int tgemm_config_desc(int idx, tgemm_config_info* out) {
   out->xcd_remap = c.xcd_remap;
   out->generic = c.generic;
   out->layouts = c.layouts;
-  out->lds_bytes = c.generic ? 0 : c.stages * (c.bm * c.bk + c.bk * c.bn) * 2;
+  // operand tiles are held in LDS at a multiple of 128 rows / columns
+  out->lds_bytes = c.generic ? 0 : c.stages * ((c.bm + 127) / 128 * 128 + (c.bn + 127) / 128 * 128) * c.bk * 2;
   std::strncpy(out->name, c.name, sizeof(out->name) - 1);
   return TGEMM_OK;
 }

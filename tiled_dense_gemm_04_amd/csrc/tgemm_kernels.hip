@@ -632,6 +632,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 // dimension get an out-of-range offset (K-major: the k chunks past K in the last tile;
 // MN-major: the m/n chunks past the edge). The contiguous dimension is a multiple of 8 on
 // this path, so a chunk is wholly inside or wholly outside.
+// LDS extent (rows or columns) used for an operand tile of R rows or columns: R itself
+// when R is a multiple of 128 (MN-major rows then span whole 256-byte bank windows and the
+// copies split evenly), else R rounded up to 128 (e.g. 192 -> 256: the extra rows or
+// columns are out-of-range copies that only write zeros, and no fragment reads them).
+__host__ __device__ constexpr int pp_lds_extent(int R) { return (R + 127) / 128 * 128; }
+
+template <int BM, int BN, int BK, int STAGES>
+__host__ __device__ constexpr int pp_lds_bytes() {
+  return STAGES * (pp_lds_extent(BM) + pp_lds_extent(BN)) * BK * 2;
+}
+
 template <int R, int BK, int MF, bool KMAJ, int NW>
 struct PpOperand {
   static constexpr int NT = 64 * NW;
@@ -764,8 +775,8 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   constexpr int FM = WTM / MF, FN = WTN / MF;
   constexpr int KS = BK / (512 / MF);  // MFMA k-substeps per k-tile
   static_assert(MF == 32 || MF == 16, "MFMA shape");
-  using OpA = PpOperand<BM, BK, MF, !TA, NW>;
-  using OpB = PpOperand<BN, BK, MF, TB, NW>;
+  using OpA = PpOperand<pp_lds_extent(BM), BK, MF, !TA, NW>;
+  using OpB = PpOperand<pp_lds_extent(BN), BK, MF, TB, NW>;
   constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
   constexpr int PT = OpA::LD + OpB::LD;
   static_assert(NW == 8, "two groups of four waves");
@@ -990,9 +1001,13 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   // c ^ ((r / 2) % (WTN / 8)): conflict-free LDS writes for the 16x16 layout (2-way for
   // 32x32) and conflict-free row reads. N and ldc are multiples of 8 on this path, so a
   // chunk is either wholly inside the matrix or wholly outside.
-  constexpr int RB = WTN * 2, CPR = WTN / 8;
-  static_assert(BM * BN * 2 <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
-  static_assert((CPR & (CPR - 1)) == 0 && 64 % CPR == 0 && (WTM * CPR) % 64 == 0, "row-copy shape");
+  // Staged rows are padded to a power-of-two number of 16-byte chunks (SCPR); chunks past
+  // the wave's WTN / 8 are never written or stored.
+  constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
+  constexpr int RB = SCPR * 16;
+  static_assert(SCPR >= CPR && WTN % 8 == 0, "staged row shape");
+  static_assert(NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
+  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
   __syncthreads();
   char* const stage = smem + wave * (WTM * RB);
   const bool relu = g.relu != 0;
@@ -1013,7 +1028,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
           v3 = relu_f(v3);
         }
         const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        const int off = mw * RB + ((((nw >> 3) ^ ((mw >> 1) % CPR))) << 4) + (nw & 7) * 2;
+        const int off = mw * RB + ((((nw >> 3) ^ ((mw >> 1) % SCPR))) << 4) + (nw & 7) * 2;
         *(TG_LDS half4*)(stage + off) = h;
       }
     }
@@ -1024,10 +1039,11 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
-  for (int i = 0; i < WTM * CPR / 64; ++i) {
+  for (int i = 0; i < WTM * SCPR / 64; ++i) {
     const int idx = i * 64 + lane;
-    const int r = idx / CPR, c = idx % CPR;
-    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % CPR)) << 4));
+    const int r = idx / SCPR, c = idx % SCPR;
+    if (c >= CPR) continue;
+    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
     const int m = wm * WTM + r, n = wn * WTN + 8 * c;
     if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
   }
@@ -1208,7 +1224,7 @@ hipError_t launch_fast(const GemmArgs& g, hipStream_t s, int device) {
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA, bool TB>
 hipError_t launch_pp_layout(const GemmArgs& g, hipStream_t s, int device) {
-  constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
+  constexpr int lds = pp_lds_bytes<BM, BN, BK, STAGES>();
   auto kern = gemm_pingpong<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>;
   static std::atomic<uint64_t> ready{0};
   const uint64_t bit = 1ull << (device & 63);
@@ -1225,7 +1241,7 @@ hipError_t launch_pp_layout(const GemmArgs& g, hipStream_t s, int device) {
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA, bool TB>
 hipError_t launch_pp_grouped_layout(const GroupedArgs& ga, int64_t nwg, hipStream_t s, int device) {
-  constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
+  constexpr int lds = pp_lds_bytes<BM, BN, BK, STAGES>();
   auto kern = gemm_pingpong_grouped<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>;
   static std::atomic<uint64_t> ready{0};
   const uint64_t bit = 1ull << (device & 63);
@@ -1346,7 +1362,8 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
   X(256, 256, 32, 2, 4, 4, 4, 0, 0)   \
   X(128, 128, 32, 2, 4, 4, 4, 1, 1)   \
   X(256, 128, 32, 2, 4, 4, 4, 1, 1)   \
-  X(128, 256, 32, 2, 4, 4, 4, 1, 1)
+  X(128, 256, 32, 2, 4, 4, 4, 1, 1)   \
+  X(256, 192, 32, 2, 4, 4, 4, 1, 1)
 
 #define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
   {BM, BN, BK, S, WM, WN, P, X, 0, 1, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
