@@ -6,6 +6,10 @@ fp16 inputs drawn N(0,1) from seed 2, fp32 accumulate, fp16 out, row-major), inp
 already resident in HBM. W untimed warm-up steps, then exactly K timed steps bracketed
 by device synchronisation. Prints ONE JSON line on stdout; details go to stderr.
 
+From idle, the GPU raises its clocks over the first ~25 ms of load (about 200 calls at
+4096^3, each 10-30 % slower than the steady state); the default warm-up (400 calls,
+~45 ms) lies past that ramp, so the timed steps measure sustained throughput.
+
   value            = 2*M*N*K*steps / wall time of the timed steps, in TFLOP/s
   roofline.achieved = 2*M*N*K / mean kernel duration, from HIP events recorded on the
                      stream the kernels are launched on, against the dense fp16 MFMA peak
@@ -93,8 +97,8 @@ def cpu_baseline(A, B, relu, c_gpu_bits, target_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="relu_4096",
                     help="relu_4096 (headline) or another name from tgemm_workloads.all_workloads()")
     ap.add_argument("--cfg", type=int, default=None, help="force a config index (sweeps)")

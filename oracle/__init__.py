@@ -17,6 +17,12 @@ is ``x > 0 ? x : +0``.
 Pins (tests/test_oracle_*.py, all CPU): exact rational brute force, the closed forms
 ones @ ones = K and A @ I = A, the ReLU sign invariants, transpose and thread-count
 invariance, and numpy's binary16 codec over all 65536 bit patterns.
+
+The fp8 block-scaled GEMM and its block quantizer live in ``tgemm_fp8_ref.c`` (same
+library); their reading of the pages is stated at the top of that file, and their pins
+are in tests/test_oracle_fp8_pins.py (torch's CPU float8_e4m3fn codec over all 256 codes,
+ties-to-even at every midpoint, exact rational brute force, reduction to the binary16
+oracle when every scale is 1, closed forms and scale linearity).
 """
 from __future__ import annotations
 
@@ -29,14 +35,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "tgemm_ref.c")
+FP8_SOURCE = os.path.join(_HERE, "tgemm_fp8_ref.c")
 LIBRARY = os.path.join(_HERE, "liboracle_tgemm.so")
 
 
-def build(src: str = SOURCE, out: str = LIBRARY, verbose: bool = False) -> str:
-    """Compile the oracle's C source with gcc (portable -O2, OpenMP). Always recompiles."""
+def build(src: str = SOURCE, out: str = LIBRARY, verbose: bool = False, fp8_src: str = FP8_SOURCE) -> str:
+    """Compile the oracle's C sources with gcc (portable -O2, OpenMP). Always recompiles."""
     tmp = out + ".tmp"
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
-           "-o", tmp, src, "-lm"]
+           "-o", tmp, src, fp8_src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -87,6 +94,22 @@ class Oracle:
         lib.oracle_gemm_f16_entries.argtypes = [i64, p, i64, p, i64, i64, p, p, p,
                                                 ctypes.c_int, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_encode_sat.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode_sat.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3_decode_array.argtypes = [p, p, i64]
+        lib.oracle_e4m3_encode_array.argtypes = [p, p, i64]
+        lib.oracle_quant_fp8.restype = None
+        lib.oracle_quant_fp8.argtypes = [i64, i64, p, i64, i64, p, i64, p]
+        lib.oracle_gemm_fp8_block.restype = ctypes.c_int
+        lib.oracle_gemm_fp8_block.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64,
+                                              ctypes.c_int, ctypes.c_int]
+        lib.oracle_gemm_fp8_block_entries.restype = None
+        lib.oracle_gemm_fp8_block_entries.argtypes = [i64, p, i64, p, p, i64, p, i64, p, p, p,
+                                                      ctypes.c_int, ctypes.c_int]
+        lib.oracle_fp8_block_bound.restype = None
+        lib.oracle_fp8_block_bound.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p]
         self.lib = lib
         self.path = path
 
@@ -145,6 +168,84 @@ class Oracle:
     def max_threads(self) -> int:
         return int(self.lib.oracle_max_threads())
 
+    # ---------------------------------------------------------------- fp8 (E4M3) path
+    def e4m3_decode(self, codes: np.ndarray) -> np.ndarray:
+        """Exact E4M3 code -> float64 of every element (the oracle's own codec)."""
+        c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_e4m3_decode_array(c.ctypes.data, out.ctypes.data, c.size)
+        return out
+
+    def e4m3_encode(self, x: np.ndarray) -> np.ndarray:
+        """float64 -> E4M3 code, nearest even, saturating to +-448 (the oracle's own codec)."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        out = np.empty(x.shape, dtype=np.uint8)
+        self.lib.oracle_e4m3_encode_array(x.ctypes.data, out.ctypes.data, x.size)
+        return out
+
+    def quant_fp8(self, X: np.ndarray, block_rows: int):
+        """Block quantizer: binary16 X (R x K) -> (codes R x K uint8, scales RB x KB float32)."""
+        X, ldx = _rowmajor_2d(_as_u16(X))
+        R, K = X.shape
+        if block_rows < 1:
+            raise ValueError("block_rows must be positive")
+        KB = -(-K // FP8_BLOCK)
+        RB = -(-R // block_rows)
+        Q = np.zeros((R, K), dtype=np.uint8)
+        S = np.zeros((RB, KB), dtype=np.float32)
+        if R and K:
+            self.lib.oracle_quant_fp8(R, K, X.ctypes.data, ldx, block_rows, Q.ctypes.data, max(1, K),
+                                      S.ctypes.data)
+        return Q, S
+
+    @staticmethod
+    def _fp8_operands(A, SA, B, SB):
+        A, lda = _rowmajor_2d(np.asarray(A, dtype=np.uint8))
+        B, ldb = _rowmajor_2d(np.asarray(B, dtype=np.uint8))
+        M, K = A.shape
+        N, K2 = B.shape
+        if K != K2:
+            raise ValueError(f"inner dimensions differ: A {A.shape}, B (N x K) {B.shape}")
+        KB = -(-K // FP8_BLOCK)
+        SA = np.ascontiguousarray(np.asarray(SA, dtype=np.float32))
+        SB = np.ascontiguousarray(np.asarray(SB, dtype=np.float32))
+        if SA.shape != (M, KB) or SB.shape != (-(-N // FP8_BLOCK), KB):
+            raise ValueError(f"scale shapes {SA.shape}, {SB.shape} do not match M={M} N={N} K={K}")
+        return A, lda, SA, B, ldb, SB, M, N, K
+
+    def gemm_fp8(self, A, SA, B, SB, relu: bool, nthreads: int = 0) -> np.ndarray:
+        """Block-scaled product (float64, unrounded): A (M x K) and B (N x K) E4M3 codes,
+        SA (M x KB) and SB (ceil(N/128) x KB) float32 scales."""
+        A, lda, SA, B, ldb, SB, M, N, K = self._fp8_operands(A, SA, B, SB)
+        C = np.empty((M, N), dtype=np.float64)
+        if M and N:
+            self.lib.oracle_gemm_fp8_block(M, N, K, A.ctypes.data, lda, SA.ctypes.data, B.ctypes.data, ldb,
+                                           SB.ctypes.data, C.ctypes.data, N, int(bool(relu)), int(nthreads))
+        return C
+
+    def gemm_fp8_entries(self, A, SA, B, SB, rows, cols, relu: bool, nthreads: int = 0) -> np.ndarray:
+        A, lda, SA, B, ldb, SB, M, N, K = self._fp8_operands(A, SA, B, SB)
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+        if rows.shape != cols.shape:
+            raise ValueError("rows and cols differ in shape")
+        if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+            raise IndexError("entry index out of range")
+        out = np.empty(rows.shape, dtype=np.float64)
+        self.lib.oracle_gemm_fp8_block_entries(K, A.ctypes.data, lda, SA.ctypes.data, B.ctypes.data, ldb,
+                                               SB.ctypes.data, rows.size, rows.ctypes.data, cols.ctypes.data,
+                                               out.ctypes.data, int(bool(relu)), int(nthreads))
+        return out
+
+    def fp8_bound(self, A, SA, B, SB) -> np.ndarray:
+        """sum_kb |SA SB| * max|a| * max|w| per output element (float64, M x N)."""
+        A, lda, SA, B, ldb, SB, M, N, K = self._fp8_operands(A, SA, B, SB)
+        E = np.zeros((M, N), dtype=np.float64)
+        if M and N:
+            self.lib.oracle_fp8_block_bound(M, N, K, A.ctypes.data, lda, SA.ctypes.data, B.ctypes.data, ldb,
+                                            SB.ctypes.data, E.ctypes.data)
+        return E
+
 
 _default = None
 
@@ -153,7 +254,8 @@ def default() -> Oracle:
     """The oracle built from tgemm_ref.c (compiled on first use if missing or stale)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < max(
+                os.path.getmtime(SOURCE), os.path.getmtime(FP8_SOURCE)):
             build()
         _default = Oracle(LIBRARY)
     return _default
@@ -177,6 +279,33 @@ def gemm_entries(A, B, rows, cols, relu, nthreads=0):
 
 def max_threads() -> int:
     return default().max_threads()
+
+
+FP8_BLOCK = 128
+
+
+def e4m3_decode(codes):
+    return default().e4m3_decode(codes)
+
+
+def e4m3_encode(x):
+    return default().e4m3_encode(x)
+
+
+def quant_fp8(X, block_rows):
+    return default().quant_fp8(X, block_rows)
+
+
+def gemm_fp8(A, SA, B, SB, relu, nthreads=0):
+    return default().gemm_fp8(A, SA, B, SB, relu, nthreads)
+
+
+def gemm_fp8_entries(A, SA, B, SB, rows, cols, relu, nthreads=0):
+    return default().gemm_fp8_entries(A, SA, B, SB, rows, cols, relu, nthreads)
+
+
+def fp8_bound(A, SA, B, SB):
+    return default().fp8_bound(A, SA, B, SB)
 
 
 # --------------------------------------------------------------------------------------
@@ -208,5 +337,40 @@ def compare(c_bits: np.ndarray, ref: np.ndarray, K: int, scale: float = 1.0) -> 
         "fails": int(bad.sum()),
         "max_abs_err": float(err.max()) if c.size else 0.0,
         "max_ratio": float(np.nanmax(ratio)) if c.size else 0.0,
+        "first_fail": (tuple(int(v) for v in np.argwhere(bad)[0]) if bad.any() else None),
+    }
+
+
+# --------------------------------------------------------------------------------------
+# Tolerance of the fp8 path: |c - ref| <= 4e-3 * |ref| + 2^-8 * E, elementwise, with E =
+# sum_kb |SA SB| * max|a| * max|w| (fp8_bound). The fp8 matrix instructions of gfx950 sum
+# the 128 products of a block with less than float32 precision (measured: deviations up
+# to 2^-10.1 of the block's largest product, none when all products share a binade); the
+# method applies the scales and accumulates across blocks in float32 after each block,
+# which is what the block-sized scaling is for. 2^-8 keeps a 4x margin over the measured
+# deviation; float32 rounding of the scaled block sums (<= 2^-17 E) and the final rounding
+# to binary16 (covered by the relative term) sit far below it.
+# --------------------------------------------------------------------------------------
+FP8_BLOCK_ERR = 2.0 ** -8
+
+
+def tolerance_fp8(ref: np.ndarray, bound: np.ndarray) -> np.ndarray:
+    return REL_TOL * np.abs(ref) + FP8_BLOCK_ERR * bound
+
+
+def compare_fp8(c_bits: np.ndarray, ref: np.ndarray, bound: np.ndarray) -> dict:
+    """Compare binary16 output bits of the fp8 path against the float64 reference."""
+    c = f16_decode(c_bits)
+    if c.shape != ref.shape or bound.shape != ref.shape:
+        raise ValueError(f"shape mismatch {c.shape} / {ref.shape} / {bound.shape}")
+    err = np.abs(c - ref)
+    tol = tolerance_fp8(ref, bound)
+    bad = ~(err <= tol)
+    ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
+    return {
+        "n": int(c.size),
+        "fails": int(bad.sum()),
+        "max_abs_err": float(err.max()) if c.size else 0.0,
+        "max_ratio": float(ratio.max()) if c.size else 0.0,
         "first_fail": (tuple(int(v) for v in np.argwhere(bad)[0]) if bad.any() else None),
     }

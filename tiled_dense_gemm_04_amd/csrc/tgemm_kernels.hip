@@ -16,43 +16,12 @@
 //   * 32x32x16 fp16 MFMAs accumulate in fp32; operands are fed as (B^T, A^T) so that each
 //     lane ends up holding four consecutive output columns, stored as one 8-byte write;
 //   * the workgroup order is XCD-aware and panel-ordered (tile_of in tgemm_internal.h).
-#include "tgemm_internal.h"
+#include "tgemm_device.h"
 
 #include <atomic>
 
 namespace tgemm {
 namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef short short8v __attribute__((ext_vector_type(8)));
-typedef float float16v __attribute__((ext_vector_type(16)));
-#define TG_LDS __attribute__((address_space(3)))
-
-// Buffer offset that lies beyond every descriptor range used here (all ranges are kept
-// below 2^31 bytes), so a load at this offset returns zeros.
-constexpr uint32_t kOob = 0x80000000u;
-constexpr uint32_t kMaxRange = 0x7FFFFFF0u;
-// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
-constexpr int kBufWord3 = 0x00020000;
-
-// s_waitcnt with only the vector-memory counter constrained (expcnt and lgkmcnt at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier that orders LDS only: waits for this wave's LDS reads/writes, then
-// s_barrier. Outstanding buffer->LDS loads of later stages stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
 
 // Per-workgroup timestamps, compiled in only for the instrumented build (TGEMM_STAMPS) and
 // empty otherwise. Words per workgroup: wall clock (s_memrealtime, 100 MHz) at kernel
@@ -99,73 +68,6 @@ struct WgClock {
 };
 #endif
 
-typedef int int4v __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor: base address, stride 0, range in bytes, gfx9 word 3. All inputs
-// are wave-uniform, so it lives in four SGPRs.
-__device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t range_bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  int4v r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)range_bytes);
-  r[3] = kBufWord3;
-  return r;
-}
-
-// One 16-byte buffer load per lane written straight to LDS: lane u's 16 bytes land at
-// LDS byte lds_base + 16*u; a lane whose offset is outside the descriptor range writes
-// zeros. Written as inline assembly so that the compiler does not treat the LDS write
-// as pending before unrelated LDS reads (it cannot tell the ring slots apart and would
-// wait for every copy in flight); completion is awaited explicitly with wait_vmcnt.
-// M0 carries the LDS base; the kernels use M0 for nothing else (no indirect register
-// indexing, no messages), so clobbering it is safe here.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_to_lds(const int4v& rsrc, uint32_t lds_base, uint32_t voffset) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds_base), "v"(voffset), "s"(rsrc)
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const TG_LDS char*)p;
-}
-
-// ------------------------------------------------------------------------------------
-// LDS layouts of the fast kernel.
-//
-// A stage: BM rows x BK halves, row r at byte r*BK*2, split in 16-byte chunks; logical
-// chunk c of row r is stored at chunk c ^ swz_a(r). A fragment read (ds_read_b128) has 16
-// lanes on 16 consecutive rows and the same logical chunk; with 64 banks x 4 bytes a
-// 256-byte bank window holds 128/BK rows, and the XOR spreads the 16 rows over the 16
-// chunk slots of the window.
-template <int BK>
-__host__ __device__ constexpr int swz_a(int r) {
-  return (r / (128 / BK)) % (BK / 8);
-}
-// The same for 16x16x32 A fragments (16 lanes on 16 rows, four lane groups on the four
-// 16-byte chunks of a 64-byte row, BK = 32). Measured with SQ_LDS_BANK_CONFLICT on gfx950:
-// XOR by (r / 2) % 4 is conflict-free for this pattern, while (r / 4) % 4 (the 32x32x16
-// choice above) conflicts 2-way.
-template <int BK, int MF>
-__host__ __device__ constexpr int swz_a_mf(int r) {
-  static_assert(MF == 32 || BK == 32, "16x16x32 fragments are laid out for BK = 32");
-  return MF == 16 ? (r >> 1) & 3 : swz_a<BK>(r);
-}
-// B stage: BK rows (k) x BN halves (n), row k at byte k*BN*2 (a multiple of 256 bytes);
-// logical chunk c of row k is stored at chunk c ^ swz_b(k). A transposed read by 32 lanes
-// touches either 4 consecutive k rows x 4 consecutive chunks (32x32x16 B fragments,
-// c0 % 4 == 0, k < 8 within the group of 8) or rows k and k+8 for 4 consecutive k x 2
-// chunks (16x16x32 fragments, c0 % 2 == 0). XOR by 4*(k%4) spreads the four rows of a
-// group, XOR by 2*((k/8)%2) separates rows k and k+8: in both patterns the 16 (row,
-// chunk) pairs land on 16 distinct 16-byte slots of the bank window.
-__host__ __device__ constexpr int swz_b(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 
 // ------------------------------------------------------------------------------------
 // Fast kernel: BM x BN x BK tile, WM x WN waves, STAGES-deep LDS ring fed by buffer->LDS
@@ -611,128 +513,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
   }
   clk.finish(nk);
 }
-
-// ------------------------------------------------------------------------------------
-// Operand staging of the ping-pong kernel. An operand tile spans R output rows (A, R = BM)
-// or columns (B, R = BN) and BK values of k. In memory the operand is either k-contiguous
-// ("K-major": A as given, or B given transposed, N x K) or m/n-contiguous ("MN-major": B
-// as given, or A given transposed, K x M). The LDS slot keeps the memory orientation:
-//   K-major : R rows of BK halves; 16-byte chunk c of row r sits at chunk c ^ swz_a_mf(r);
-//             a fragment (8 consecutive k of one m or n) is one ds_read_b128;
-//   MN-major: BK rows of R halves (R*2 bytes, a multiple of the 256-byte bank window);
-//             chunk c of row k sits at chunk c ^ swz_b(k); a fragment is two
-//             ds_read_b64_tr_b16 (each gives a lane 4 k values of its m or n, gathered
-//             from the rows of 4 lanes).
-// Either way a lane ends up with the same fragment: 8 consecutive k (group lane / MF) of
-// m or n index lane % MF, so the MFMA core does not depend on the layouts.
-// Copies: 16-byte unit u of a k-tile lands at LDS byte 16u of the slot (the lane order of
-// the LDS-DMA); the swizzle chooses which global chunk feeds it. Edges: rows past the
-// matrix lie outside the descriptor range (K-major: m/n rows; MN-major: the k rows past K
-// in the last tile) and read as zeros; chunks past the matrix along the contiguous
-// dimension get an out-of-range offset (K-major: the k chunks past K in the last tile;
-// MN-major: the m/n chunks past the edge). The contiguous dimension is a multiple of 8 on
-// this path, so a chunk is wholly inside or wholly outside.
-// LDS extent (rows or columns) used for an operand tile of R rows or columns: R itself
-// when R is a multiple of 128 (MN-major rows then span whole 256-byte bank windows and the
-// copies split evenly), else R rounded up to 128 (e.g. 192 -> 256: the extra rows or
-// columns are out-of-range copies that only write zeros, and no fragment reads them).
-__host__ __device__ constexpr int pp_lds_extent(int R) { return (R + 127) / 128 * 128; }
-
-template <int BM, int BN, int BK, int STAGES>
-__host__ __device__ constexpr int pp_lds_bytes() {
-  return STAGES * (pp_lds_extent(BM) + pp_lds_extent(BN)) * BK * 2;
-}
-
-template <int R, int BK, int MF, bool KMAJ, int NW>
-struct PpOperand {
-  static constexpr int NT = 64 * NW;
-  static constexpr int BYTES = R * BK * 2;
-  static constexpr int CPR = KMAJ ? BK / 8 : R / 8;  // 16-byte chunks per LDS row
-  static constexpr int UNITS = R * BK / 8;
-  static constexpr int LD = UNITS / NT;              // copies per thread per k-tile
-  static constexpr int KPM = 512 / MF;               // k per MFMA
-  static_assert(UNITS % NT == 0, "copies must split evenly over the threads");
-  static_assert(KMAJ || (R * 2) % 256 == 0, "MN-major rows must span the 256-byte bank window");
-
-  const char* base;  // the tile's first element at k-tile 0
-  int64_t step;      // bytes from one k-tile to the next
-  uint32_t rng_full, rng_last;
-  uint32_t off[LD], off_last[LD];
-  int fr_base, fr_x, fr_k, fr_half;  // this lane's fragment-read constants
-
-  __device__ static int swz(int row) { return KMAJ ? swz_a_mf<BK, MF>(row) : swz_b(row); }
-
-  // X, ld: operand base and row stride (elements); r0: the tile's first m or n; rvalid:
-  // its m or n extent inside the matrix; kin_last: k values in the last k-tile.
-  __device__ void init_copies(const _Float16* X, int64_t ld, int r0, int rvalid, int kin_last, int wave,
-                              int lane) {
-    base = (const char*)(KMAJ ? X + (int64_t)r0 * ld : X + r0);
-    step = KMAJ ? (int64_t)BK * 2 : (int64_t)BK * ld * 2;
-    const int64_t full = KMAJ ? ((int64_t)(rvalid - 1) * ld + BK) * 2 : ((int64_t)(BK - 1) * ld + rvalid) * 2;
-    const int64_t last =
-        KMAJ ? ((int64_t)(rvalid - 1) * ld + kin_last) * 2 : ((int64_t)(kin_last - 1) * ld + rvalid) * 2;
-    rng_full = (uint32_t)(full < kMaxRange ? full : kMaxRange);
-    rng_last = (uint32_t)(last < kMaxRange ? last : kMaxRange);
-#pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const int u = (i * NW + wave) * 64 + lane;
-      const int row = u / CPR;
-      const int c = (u % CPR) ^ swz(row);
-      const uint32_t o = (uint32_t)(((int64_t)row * ld + 8 * c) * 2);
-      if (KMAJ) {
-        off[i] = o;
-        off_last[i] = 8 * c < kin_last ? o : kOob;
-      } else {
-        off[i] = 8 * c < rvalid ? o : kOob;
-        off_last[i] = off[i];
-      }
-    }
-  }
-
-  // Descriptor of k-tile t (of nk); an empty range from t_end on, so such a copy only
-  // writes zeros into a slot no later read uses.
-  __device__ int4v rsrc(int t, int t_end, int nk) const {
-    const uint32_t r = t < t_end ? (t == nk - 1 ? rng_last : rng_full) : 0u;
-    const int tt = t < nk ? t : nk - 1;
-    return make_rsrc(base + tt * step, r);
-  }
-
-  // wbase: the wave's first m or n inside the tile (a multiple of the swizzle periods).
-  __device__ void init_frags(int wbase, int lane) {
-    const int lrow = lane % MF, lkg = lane / MF;
-    if (KMAJ) {
-      fr_base = (wbase + lrow) * BK * 2;
-      fr_x = swz(lrow);
-      fr_k = lkg;
-      fr_half = 0;
-    } else {
-      // transposed reads: lane 16 g + 4 j + q reads row k0 + j of its group's 4-row block,
-      // m/n 4q .. 4q+3 of its 16-wide block
-      const int bg = lane >> 4, bj = (lane >> 2) & 3, bq = lane & 3;
-      fr_k = (MF == 32 ? 8 * (bg >> 1) : 8 * bg) + bj;
-      fr_x = wbase / 8 + (MF == 32 ? 2 * (bg & 1) : 0) + (bq >> 1);
-      fr_half = (bq & 1) * 8;
-      fr_base = 0;
-    }
-  }
-
-  // Fragment f (the f-th MF block of the wave's range), k substep ks, from slot S.
-  __device__ half8 frag(const char* S, int f, int ks) const {
-    if (KMAJ) {
-      const int chunk = (KPM / 8) * ks + fr_k;
-      return *(const TG_LDS half8*)(S + fr_base + f * MF * BK * 2 + ((chunk ^ fr_x) << 4));
-    } else {
-      short4v h[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int k = KPM * ks + 4 * i + fr_k;
-        const int off = k * R * 2 + (((fr_x + (MF / 8) * f) ^ swz_b(k)) << 4) + fr_half;
-        h[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(S + off));
-      }
-      return __builtin_bit_cast(half8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  }
-};
 
 // ------------------------------------------------------------------------------------
 // Ping-pong kernel: 8 waves in two groups of 4 (waves 0-3 and 4-7), one wave of each

@@ -1,7 +1,7 @@
 """Timing protocol for every measured workload (one MI355X), beyond bench.py's one line.
 
 For each workload, with the config gemm_f16 picks:
-  * warm: 10 untimed calls, then 7 trials of R back-to-back calls (R chosen so a trial
+  * warm: 10 untimed calls and >= 50 ms of calls, then 7 trials of R back-to-back calls (R chosen so a trial
     lasts >= 20 ms), each trial bracketed by HIP events on the launch stream; the median
     trial gives us per call, TFLOP/s = 2MNK / t, and % of the dense fp16 MFMA peak
     (256 CU x 4096 FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s) and of the measured MFMA ceiling;
@@ -18,8 +18,15 @@ For each workload, with the config gemm_f16 picks:
 The MFMA ceiling is the library's MFMA probe (no memory traffic, pseudo-random
 operands) timed the same way, with its own clock from the stamps.
 
+--ramp NAME instead records one event pair per call over a long back-to-back run of one
+workload (twice, 2 s idle in between) and prints the mean per-call time in windows of
+the run: from idle the GPU raises its clocks over the first tens of milliseconds of
+load, so a timing that starts that early reads low. This sets how much warm-up the
+other timings and bench.py need.
+
   python -m tiled_dense_gemm_04_amd.measure [--workloads a,b] [--no-cold] [--no-torch]
       [--json out.json] [--md out.md]
+  python -m tiled_dense_gemm_04_amd.measure --ramp relu_4096 [--ramp-launches 3000]
 """
 from __future__ import annotations
 
@@ -45,12 +52,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def timed_trials(torch, stream, call, trials=7, min_ms=20.0, warm=10):
-    """Median microseconds per call over `trials` trials of R calls each."""
+def timed_trials(torch, stream, call, trials=7, min_ms=20.0, warm=10, warm_ms=50.0):
+    """Median microseconds per call over `trials` trials of R calls each, after at least
+    `warm` calls and `warm_ms` of back-to-back calls (past the clock ramp from idle)."""
     for _ in range(warm):
         call(0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            call(0)
+        torch.cuda.synchronize()
     e0.record(stream)
     for i in range(5):
         call(i)
@@ -69,6 +82,48 @@ def timed_trials(torch, stream, call, trials=7, min_ms=20.0, warm=10):
         per.append(e0.elapsed_time(e1) / reps * 1e3)
     return {"median_us": statistics.median(per), "min_us": min(per), "max_us": max(per),
             "calls_per_trial": reps, "trials": trials}
+
+
+def ramp(torch, tg, w, stream, launches=3000, runs=2, idle_s=2.0):
+    """Per-call durations (us) of `runs` back-to-back runs of `launches` calls each."""
+    A, B = w.inputs()
+    SA, SB = w.stored(A, B)
+    a = torch.from_numpy(SA).cuda()
+    b = torch.from_numpy(SB).cuda()
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+    out = []
+    for r in range(runs):
+        if r:
+            time.sleep(idle_s)
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(launches):
+            tg.gemm_f16_ex(a, b, c, w.trans_a, w.trans_b, relu=w.relu, stream=stream)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        out.append([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(launches)])
+        log(f"ramp run {r}: {launches} calls of {w.name}")
+    return out
+
+
+def ramp_markdown(w, runs, host) -> str:
+    n = len(runs[0])
+    edges = [0, 1, 20, 40, 60, 80, 100, 150, 200, 400, 700, 1000, 1500, 2000, 3000, 5000, 10000]
+    edges = [e for e in edges if e < n] + [n]
+    L = [f"Device: {host['device']}; {host['library']}; torch {host['torch']}.", "",
+         f"{w.name} ({w.M}x{w.N}x{w.K}), {n} back-to-back calls per run, one event pair per call "
+         "(the events add a small gap between calls); mean / min us per call in each window, "
+         "elapsed ms at the window's end.", "",
+         "| calls | " + " | ".join(f"run {r} mean | run {r} min | run {r} ms" for r in range(len(runs))) + " |",
+         "|---|" + "---|---|---|" * len(runs)]
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        cells = []
+        for d in runs:
+            seg = d[lo:hi]
+            cells += [f"{statistics.mean(seg):.2f}", f"{min(seg):.2f}", f"{sum(d[:hi]) / 1e3:.1f}"]
+        L.append(f"| {lo}-{hi} | " + " | ".join(cells) + " |")
+    return "\n".join(L) + "\n"
 
 
 def phases(stamps):
@@ -290,6 +345,8 @@ def main():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--json", default=None)
     ap.add_argument("--md", default=None)
+    ap.add_argument("--ramp", default=None, metavar="WORKLOAD", help="only the clock-ramp trace of WORKLOAD")
+    ap.add_argument("--ramp-launches", type=int, default=3000)
     args = ap.parse_args()
 
     import torch
@@ -308,6 +365,14 @@ def main():
         works = [w for w in works if w.name in keep]
     host = {"device": torch.cuda.get_device_name(0), "library": tg.tgemm_version(), "torch": torch.__version__,
             "time": time.strftime("%Y-%m-%d %H:%M:%S")}
+    if args.ramp:
+        w = W.by_name(args.ramp)
+        md = ramp_markdown(w, ramp(torch, tg, w, stream, args.ramp_launches), host)
+        print(md)
+        if args.md:
+            with open(args.md, "w") as f:
+                f.write(md)
+        return 0
     probe = None if args.no_probe else measure_probe(torch, tg, stream)
     ceiling = probe["tflops"] if probe else None
     results = [measure_workload(torch, tg, W, w, stream, cold=not args.no_cold, with_torch=not args.no_torch,
