@@ -41,7 +41,7 @@ LIBRARY = os.path.join(_HERE, "liboracle_tgemm.so")
 
 def build(src: str = SOURCE, out: str = LIBRARY, verbose: bool = False, fp8_src: str = FP8_SOURCE) -> str:
     """Compile the oracle's C sources with gcc (portable -O2, OpenMP). Always recompiles."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.{os.getpid()}.tmp"  # per process: parallel test workers may build at once
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
            "-o", tmp, src, fp8_src, "-lm"]
     if verbose:
