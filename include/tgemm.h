@@ -155,6 +155,55 @@ TGEMM_API const char* tgemm_version(void);
 /* ---- tooling: config table (used by the offline sweep, the benchmark and tests) ---- */
 
 /* Description of one compiled kernel configuration. */
+/*
+ * fp8 (E4M3) block-scaled GEMM -- the fp8_block_scaled_linear(x, w_fp8, scale_w,
+ * block=128) of "TileLang-MUSA operator development" (7yue.com), section 8.2, with the
+ * per-block scaling the TileLang write-up measured on A100 (nxmr.cn 138173), section 7,
+ * names ("block scaling as in CUTLASS"). The pages fix neither the fp8 encoding nor the
+ * block shapes nor the scale type; the reading taken here is the block-scaled recipe those
+ * names refer to:
+ *   codes      : OCP E4M3 ("E4M3FN"): 1 sign, 4 exponent bits (bias 7), 3 fraction bits,
+ *                no infinities, S.1111.111 = NaN, largest finite 448;
+ *   A, lda     : M x K codes (one byte each), row-major with k contiguous (activations),
+ *                lda in bytes >= max(1, K);
+ *   scale_a    : M x KB float32, contiguous (row i at scale_a + i * KB), KB = ceil(K/128):
+ *                one scale per 1 x 128 block of A;
+ *   B, ldb     : N x K codes, row-major with k contiguous (a linear layer's weight, out x
+ *                in features), ldb >= max(1, K);
+ *   scale_b    : ceil(N/128) x KB float32, contiguous: one scale per 128 x 128 block of B;
+ *   C, ldc     : M x N binary16 output (round to nearest even), ldc >= max(1, N);
+ *   C[i,j] = ReLU?( sum_kb scale_a[i,kb] * scale_b[j/128,kb] * sum_{k in kb} a[i,k] * b[j,k] )
+ * where block kb holds k in [128 kb, min(K, 128 kb + 128)). On the fast path each block's
+ * 128 products are summed by the fp8 matrix instructions (exact products; their block sum
+ * may deviate from the exact one by up to about 2^-10 of the block's largest product) and
+ * the scaled block sums are accumulated in float32 -- the per-block promotion the scaling
+ * is for. The fast path needs A and B 16-byte aligned, lda, ldb and K multiples of 16, C
+ * 16-byte aligned and ldc, N multiples of 8; other arguments take a generic kernel that
+ * sums each block in float32. M == 0 or N == 0 is a no-op, K == 0 writes C = 0. Device
+ * pointers, ownership, streams and errors as for gemm_f16; scale_a and scale_b must be
+ * 4-byte aligned (else TGEMM_EALIGN) and, when K > 0, non-NULL (else TGEMM_ENULL).
+ */
+TGEMM_API int gemm_fp8_block(int64_t M, int64_t N, int64_t K,
+                             const void* A, int64_t lda, const float* scale_a,
+                             const void* B, int64_t ldb, const float* scale_b,
+                             void* C, int64_t ldc, int relu, void* stream);
+
+/*
+ * Block quantizer to E4M3 for gemm_fp8_block (the step that brings x to fp8 inside
+ * fp8_block_scaled_linear; the same reading as above). X: R x K binary16 (ldx elements);
+ * Q: R x K codes (ldq bytes, both >= max(1, K)); scale: ceil(R/block_rows) x KB float32,
+ * contiguous. block_rows = 1 quantizes per 1 x 128 block (activations, scale_a), 128 per
+ * 128 x 128 block (weights, scale_b); any other value is TGEMM_EINVAL_DIM. For a block
+ * whose largest magnitude is amax (float32): s = amax / 448 in float32 (s = 1 for an
+ * all-zero block), q = E4M3(x / s) with float32 division rounded to nearest, then rounded
+ * to nearest even and saturated to +-448. Finite inputs only (NaN or infinity in a block
+ * gives unspecified codes and scale). R == 0 or K == 0 is a no-op. X must be 2-byte and
+ * scale 4-byte aligned; 16-byte aligned X, 8-byte aligned Q and ldx, ldq, K multiples of 8
+ * take vector loads and stores. Otherwise as gemm_f16.
+ */
+TGEMM_API int quant_fp8_block(int64_t R, int64_t K, const void* X, int64_t ldx, int block_rows,
+                              void* Q, int64_t ldq, float* scale, void* stream);
+
 typedef struct tgemm_config_info {
     int32_t block_m, block_n, block_k; /* workgroup tile (elements)                     */
     int32_t stages;                    /* LDS pipeline depth                            */
@@ -245,6 +294,21 @@ TGEMM_API int64_t tgemm_num_workgroups(int idx, int64_t M, int64_t N);
 #define TGEMM_PROBE_THREADS 512
 #define TGEMM_PROBE_MFMA_PER_ITER 16
 TGEMM_API int tgemm_mfma_probe(int blocks, int iters, void* out, void* stream);
+
+/* fp8 tooling: the fp8 tile configs (tgemm_config_info with block_k = 128 and layouts =
+ * 2: A as given, B transposed), the config gemm_fp8_block would pick (scales not looked
+ * at; TGEMM_FP8_GENERIC for the generic kernel, -100 / -101 as for tgemm_select_config),
+ * and gemm_fp8_block forced onto config idx (or TGEMM_FP8_GENERIC; TGEMM_EINVAL_CFG if a
+ * fast config cannot take the arguments). */
+#define TGEMM_FP8_GENERIC (-102)
+TGEMM_API int tgemm_fp8_num_configs(void);
+TGEMM_API int tgemm_fp8_config_desc(int idx, tgemm_config_info* out);
+TGEMM_API int tgemm_fp8_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                      const void* B, int64_t ldb, const void* C, int64_t ldc);
+TGEMM_API int gemm_fp8_block_cfg(int idx, int64_t M, int64_t N, int64_t K,
+                                 const void* A, int64_t lda, const float* scale_a,
+                                 const void* B, int64_t ldb, const float* scale_b,
+                                 void* C, int64_t ldc, int relu, void* stream);
 
 #ifdef __cplusplus
 }

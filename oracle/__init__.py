@@ -308,6 +308,30 @@ def fp8_bound(A, SA, B, SB):
     return default().fp8_bound(A, SA, B, SB)
 
 
+def fp8_bound_entries(A, SA, B, SB, rows, cols) -> np.ndarray:
+    """fp8_bound at entries (rows[t], cols[t]) only, for sizes where the full matrix is too
+    slow. Per (row, block) maxima are taken on the codes' magnitude bits (their order is the
+    order of the values for finite codes) and decoded with the oracle's codec."""
+    A = np.asarray(A, dtype=np.uint8)
+    B = np.asarray(B, dtype=np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    KB = -(-K // FP8_BLOCK)
+    mag = np.abs(e4m3_decode(np.arange(128, dtype=np.uint8)))
+
+    def block_max(X):
+        R = X.shape[0]
+        pad = np.zeros((R, KB * FP8_BLOCK), dtype=np.uint8)
+        pad[:, :K] = X & 0x7F
+        return mag[pad.reshape(R, KB, FP8_BLOCK).max(axis=2)]
+
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    am = block_max(A) * np.abs(np.asarray(SA, dtype=np.float64))
+    bm = block_max(B) * np.abs(np.asarray(SB, dtype=np.float64))[np.arange(N) // FP8_BLOCK]
+    return np.einsum("tk,tk->t", am[rows], bm[cols])
+
+
 # --------------------------------------------------------------------------------------
 # Tolerance: |c - ref| <= 4e-3 * |ref| + 1e-3 * sqrt(K), elementwise, with c the decoded
 # binary16 GPU output and ref the oracle's unrounded float64 value. The relative term

@@ -305,6 +305,19 @@ def pin_fp8_bound(orc):
             assert abs(E[i, j] - want) <= 1e-12 * want and E[i, j] >= terms * (1 - 1e-12)
 
 
+def pin_fp8_bound_entries(orc):
+    import oracle
+    rng = np.random.default_rng(90)
+    M, N, K = 7, 300, 520
+    KB = 5
+    A, B = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
+    SA, SB = _scales(rng, (M, KB)), _scales(rng, (3, KB))
+    E = orc.fp8_bound(A, SA, B, SB)
+    rows, cols = rng.integers(0, M, 400), rng.integers(0, N, 400)
+    got = oracle.fp8_bound_entries(A, SA, B, SB, rows, cols)
+    assert np.all(np.abs(got - E[rows, cols]) <= 1e-12 * E[rows, cols])
+
+
 FP8_PINS = [
     pin_e4m3_decode_all_codes,
     pin_e4m3_encode_roundtrip,
@@ -320,4 +333,5 @@ FP8_PINS = [
     pin_fp8_gemm_scale_structure,
     pin_fp8_gemm_relu_threads_entries,
     pin_fp8_bound,
+    pin_fp8_bound_entries,
 ]

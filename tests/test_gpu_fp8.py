@@ -1,0 +1,218 @@
+"""GPU parity of the fp8 (E4M3) block-scaled path through the C ABI.
+
+gemm_fp8_block on every fp8 config and on the generic kernel against the CPU oracle,
+element by element, within |c - ref| <= 4e-3 |ref| + 2^-8 E (E = sum_kb |sa sb| max|a|
+max|b|, the size of each block's largest product: the fp8 matrix instructions sum a
+block with less than float32 precision); ragged M, N and k-tails, degenerate sizes,
+strided operands, ReLU and run-to-run determinism. quant_fp8_block bit for bit against
+the oracle (codes and scales, 1 x 128 and 128 x 128 blocks, vector and element paths).
+fp8_block_scaled_linear end to end. The measured workloads in full on sampled entries.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tgemm_workloads as W
+from gpu_util import log, relu_bits, sample_entries, to_dev, torch_cuda
+
+import tiled_dense_gemm_04_amd as tg
+
+pytestmark = pytest.mark.gpu
+
+BLOCK = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = torch_cuda()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.lib()
+    oracle.default()
+    return torch
+
+
+def _gemm(A, SA, B, SB, relu, cfg=None, a_pad=0, b_pad=0, c_pad=0):
+    """Run gemm_fp8_block on device copies (optionally inside wider row buffers) and
+    return the fp16 output bits."""
+    torch = torch_cuda()
+    M, K = A.shape
+    N = B.shape[0]
+
+    def padded(X, pad):
+        if pad == 0:
+            return to_dev(X)
+        buf = np.zeros((X.shape[0], X.shape[1] + pad), dtype=X.dtype)
+        buf[:, :X.shape[1]] = X
+        return to_dev(buf)[:, :X.shape[1]]
+
+    a, b = padded(A, a_pad), padded(B, b_pad)
+    sa, sb = to_dev(SA), to_dev(SB)
+    cbuf = torch.full((M, N + c_pad), float("nan"), dtype=torch.float16, device="cuda")
+    c = cbuf[:, :N]
+    tg.gemm_fp8_block(a, sa, b, sb, c, relu=relu, cfg=cfg)
+    torch.cuda.synchronize()
+    if c_pad:  # padding between rows untouched
+        assert torch.isnan(cbuf[:, N:]).all()
+    return c.cpu().numpy().view(np.uint16)
+
+
+def _check(A, SA, B, SB, relu, cfg=None, what="", **pads):
+    c = _gemm(A, SA, B, SB, relu, cfg, **pads)
+    ref = oracle.gemm_fp8(A, SA, B, SB, relu)
+    rep = oracle.compare_fp8(c, ref, oracle.fp8_bound(A, SA, B, SB))
+    assert rep["fails"] == 0, f"{what}: {rep}"
+    return c, rep
+
+
+SHAPES = [(256, 256, 128), (300, 264, 1008), (520, 392, 272), (1, 8, 16), (257, 136, 64),
+          (640, 1152, 1040), (33, 520, 2048), (1024, 256, 16), (129, 1000, 400)]
+ODD = [(17, 23, 29), (65, 63, 129), (1, 1, 1), (130, 7, 250), (40, 200, 100)]
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, tg.FP8_GENERIC])
+def test_each_config(cfg):
+    if cfg != tg.FP8_GENERIC and cfg >= tg.tgemm_fp8_num_configs():
+        pytest.skip("config not in table")
+    shapes = SHAPES + (ODD if cfg == tg.FP8_GENERIC else [])
+    worst = 0.0
+    for s, (M, N, K) in enumerate(shapes):
+        A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=400 + s)
+        for relu in (False, True):
+            log(f"fp8 cfg {cfg} {M}x{N}x{K} relu={relu}")
+            _, rep = _check(A, SA, B, SB, relu, cfg, what=f"cfg{cfg} {M}x{N}x{K} relu={relu}")
+            worst = max(worst, rep["max_ratio"])
+    log(f"fp8 cfg {cfg}: worst error / tolerance {worst:.3f}")
+
+
+def test_default_selection_and_edges():
+    rng = np.random.default_rng(4242)
+    for t in range(24):
+        M = int(rng.choice([1, 15, 16, 17, 127, 128, 129, 255, 256, 257]))
+        N = int(rng.choice([8, 16, 120, 128, 136, 248, 256, 264]))
+        K = int(rng.choice([16, 32, 112, 128, 144, 240, 256, 272, 1008]))
+        A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=600 + t)
+        log(f"fp8 edge {M}x{N}x{K} cfg {tg.tgemm_fp8_select_config(M, N, K)}")
+        _check(A, SA, B, SB, bool(t % 2), what=f"edge {M}x{N}x{K}")
+
+
+def test_relu_and_determinism():
+    A, SA, B, SB = W.make_fp8_inputs(520, 392, 1040, seed=701)
+    plain = _gemm(A, SA, B, SB, False)
+    again = _gemm(A, SA, B, SB, False)
+    assert np.array_equal(plain, again), "two identical calls differ"
+    r = _gemm(A, SA, B, SB, True)
+    assert np.array_equal(r, relu_bits(plain)), "ReLU output is not max(plain, +0) bit for bit"
+
+
+def test_strided_operands():
+    M, N, K = 300, 264, 1008
+    A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=702)
+    ref_fast = _gemm(A, SA, B, SB, True)
+    # row strides that keep the fast path (multiples of 16), and ones that need the generic kernel
+    assert np.array_equal(_gemm(A, SA, B, SB, True, a_pad=32, b_pad=48, c_pad=8), ref_fast)
+    log("fp8 strided generic (lda = K + 8)")
+    assert tg.tgemm_fp8_select_config(M, N, K, lda=K + 8) == tg.FP8_GENERIC
+    c, _ = _check(A, SA, B, SB, True, a_pad=8, what="lda = K + 8")
+
+
+def test_zero_k_and_empty():
+    torch = torch_cuda()
+    a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((7, 0), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((5, 0), dtype=torch.float32, device="cuda")
+    sb = torch.zeros((1, 0), dtype=torch.float32, device="cuda")
+    c = torch.full((5, 7), float("nan"), dtype=torch.float16, device="cuda")
+    tg.gemm_fp8_block(a, sa, b, sb, c, relu=True)
+    torch.cuda.synchronize()
+    assert (c == 0).all()
+    e = torch.zeros((0, 7), dtype=torch.float16, device="cuda")
+    tg.gemm_fp8_block(torch.zeros((0, 16), dtype=torch.uint8, device="cuda"),
+                      torch.zeros((0, 1), dtype=torch.float32, device="cuda"),
+                      torch.zeros((7, 16), dtype=torch.uint8, device="cuda"),
+                      torch.zeros((1, 1), dtype=torch.float32, device="cuda"), e)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- quantizer
+def _quant_inputs(R, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, 1.0, size=(R, K)) * np.exp2(rng.integers(-8, 8, size=(R, 1)))
+    x = x.astype(np.float16)
+    x[rng.random((R, K)) < 0.01] = 0
+    if R > 2 and K > 0:
+        x[1, :min(K, BLOCK)] = 0                      # an all-zero block
+        x[2, 0] = np.float16(65504.0)                 # the largest binary16
+    return x
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+def test_quant_bitexact(block_rows):
+    torch = torch_cuda()
+    for s, (R, K) in enumerate([(5, 300), (64, 4096), (129, 1000), (3, 8), (300, 256), (1, 128)]):
+        x = _quant_inputs(R, K, 800 + s)
+        Qr, Sr = oracle.quant_fp8(x, block_rows)
+        for pad in (0, 3):  # pad 3: odd row stride, element loads and stores
+            buf = np.zeros((R, K + pad), dtype=np.float16)
+            buf[:, :K] = x
+            xd = to_dev(buf)[:, :K]
+            log(f"quant block_rows={block_rows} {R}x{K} ldx={K + pad}")
+            q, sc = tg.quant_fp8_block(xd, block_rows)
+            torch.cuda.synchronize()
+            assert np.array_equal(sc.cpu().numpy().view(np.uint32), Sr.view(np.uint32)), f"scales {R}x{K}"
+            assert np.array_equal(q.cpu().numpy(), Qr), f"codes {R}x{K} block_rows={block_rows}"
+
+
+def test_fp8_linear_end_to_end():
+    torch = torch_cuda()
+    M, N, K = 257, 384, 1040
+    x, Wc, SW = W.make_fp8_linear_inputs(M, N, K, seed=900)
+    xq_ref, sx_ref = oracle.quant_fp8(x, 1)
+    ref = oracle.gemm_fp8(xq_ref, sx_ref, Wc, SW, relu=False)
+    xd, wd, swd = to_dev(x), to_dev(Wc), to_dev(SW)
+    xq, sx = tg.quant_fp8_block(xd, 1)
+    y = tg.fp8_block_scaled_linear(xd, wd, swd)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(sx.cpu().numpy(), sx_ref)
+    rep = oracle.compare_fp8(y.cpu().numpy().view(np.uint16), ref, oracle.fp8_bound(xq_ref, sx_ref, Wc, SW))
+    assert rep["fails"] == 0, rep
+    with pytest.raises(ValueError):
+        tg.fp8_block_scaled_linear(xd, wd, swd, block=64)
+
+
+# ---------------------------------------------------------------- measured workloads
+@pytest.mark.parametrize("name", ["fp8_block_4096", "fp8_block_relu_8192"])
+def test_workload_sampled(name):
+    w = W.FP8_WORKLOADS[name]
+    A, SA, B, SB = w.inputs()
+    cfg = tg.tgemm_fp8_select_config(w.M, w.N, w.K)
+    log(f"fp8 workload {name} cfg {cfg}")
+    c = _gemm(A, SA, B, SB, w.relu)
+    rng = np.random.default_rng(77)
+    rows, cols = sample_entries(w.M, w.N, rng)
+    ref = oracle.gemm_fp8_entries(A, SA, B, SB, rows, cols, w.relu)
+    E = oracle.fp8_bound_entries(A, SA, B, SB, rows, cols)
+    rep = oracle.compare_fp8(c[rows, cols], ref, E)
+    log(f"fp8 workload {name}: {rep}")
+    assert rep["fails"] == 0, rep
+    # rows beyond the sample: finite everywhere (no NaN from stale LDS or missed tiles)
+    assert np.isfinite(c.view(np.float16)).all()
+
+
+def test_workload_linear_sampled():
+    torch = torch_cuda()
+    w = W.FP8_WORKLOADS["fp8_linear_4096"]
+    x, Wc, SW = w.inputs()
+    xq_ref, sx_ref = oracle.quant_fp8(x, 1)
+    xd = to_dev(x)
+    y = tg.fp8_block_scaled_linear(xd, to_dev(Wc), to_dev(SW))
+    xq, sx = tg.quant_fp8_block(xd, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(sx.cpu().numpy(), sx_ref)
+    rng = np.random.default_rng(78)
+    rows, cols = sample_entries(w.M, w.N, rng)
+    ref = oracle.gemm_fp8_entries(xq_ref, sx_ref, Wc, SW, rows, cols, False)
+    E = oracle.fp8_bound_entries(xq_ref, sx_ref, Wc, SW, rows, cols)
+    rep = oracle.compare_fp8(y.cpu().numpy().view(np.uint16)[rows, cols], ref, E)
+    log(f"fp8 linear: {rep}")
+    assert rep["fails"] == 0, rep

@@ -31,12 +31,12 @@ def exported(path):
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
-    return {n for n in names if n.startswith(("gemm_", "tgemm_"))}
+    return {n for n in names if n.startswith(("gemm_", "tgemm_", "quant_"))}
 
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 18, syms
+    assert len(syms) == 24, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -310,3 +310,70 @@ def test_tile_map_keeps_xcd_tiles_together():
         rows = {t[0] for t in tiles}
         cols = {t[1] for t in tiles}
         assert len(tiles) == 32 and len(rows) == 4 and len(cols) == 8, (x, rows, cols)
+
+
+# ---------------------------------------------------------------- fp8 block-scaled path
+def test_fp8_config_table():
+    cfgs = tg.fp8_configs()
+    assert len(cfgs) == tg.tgemm_fp8_num_configs() >= 1
+    for c in cfgs:
+        assert c["block_k"] == 128 and c["generic"] == 0 and c["layouts"] == 2
+        assert c["block_m"] % 128 == 0 and c["block_n"] % 128 == 0
+        waves = c["waves_m"] * c["waves_n"]
+        assert c["lds_bytes"] == c["stages"] * ((c["block_m"] + c["block_n"]) * 128 + 256 * waves)
+        assert c["lds_bytes"] <= 160 * 1024
+        assert 128 % (c["block_n"] // c["waves_n"]) == 0   # a wave's columns in one scale block
+        assert c["block_m"] // 64 < waves                    # a spare wave fetches the B scales
+    with pytest.raises(tg.TgemmError):
+        tg.tgemm_fp8_config_desc(len(cfgs))
+
+
+def test_fp8_select():
+    s = tg.tgemm_fp8_select_config
+    assert s(4096, 4096, 4096) == 0                       # 256 x 256 tiles
+    assert s(16384, 512, 4096) == 2                       # 256 x 128 tiles fill the GPU
+    assert s(1024, 1024, 1024) == 1                       # 128 x 128
+    assert s(0, 8, 16) == tg.SELECT_NOOP and s(8, 8, 0) == tg.SELECT_ZERO_FILL
+    # generic kernel: K or ld not a multiple of 16, N or ldc not a multiple of 8, unaligned
+    assert s(256, 256, 100) == tg.FP8_GENERIC
+    assert s(256, 256, 256, lda=264) == tg.FP8_GENERIC
+    assert s(256, 252, 256) == tg.FP8_GENERIC
+    assert s(256, 256, 256, A=256 + 8) == tg.FP8_GENERIC
+    assert s(256, 256, 256, C=256 + 2) == tg.FP8_GENERIC
+    assert s(255, 256, 4000) == 1                         # ragged M and K (16 | K) stay fast
+    # errors
+    assert s(-1, 8, 8) == tg.TGEMM_EINVAL_DIM
+    assert s(8, 8, 32, lda=16) == tg.TGEMM_EINVAL_LD
+    assert s(8, 8, 32, ldb=16) == tg.TGEMM_EINVAL_LD
+    assert s(8, 8, 32, ldc=4) == tg.TGEMM_EINVAL_LD
+    assert s(8, 8, 32, A=0) == tg.TGEMM_ENULL
+    assert s(8, 8, 32, C=257) == tg.TGEMM_EALIGN
+
+
+def test_fp8_gemm_rejects_invalid_before_hip():
+    g = tg.gemm_fp8_block_raw
+    P, S = 256, 512   # aligned fake pointers (never dereferenced: every call returns early)
+    assert g(-1, 8, 16, P, 16, S, P, 16, S, P, 8, 0, None) == tg.TGEMM_EINVAL_DIM
+    assert g(8, 8, 16, P, 8, S, P, 16, S, P, 8, 0, None) == tg.TGEMM_EINVAL_LD
+    assert g(8, 8, 16, P, 16, 0, P, 16, S, P, 8, 0, None) == tg.TGEMM_ENULL     # scale_a
+    assert g(8, 8, 16, P, 16, S, P, 16, 0, P, 8, 0, None) == tg.TGEMM_ENULL     # scale_b
+    assert g(8, 8, 16, P, 16, S + 2, P, 16, S, P, 8, 0, None) == tg.TGEMM_EALIGN
+    assert g(0, 8, 16, 0, 16, 0, 0, 16, 0, 0, 8, 0, None) == tg.TGEMM_OK          # no-op
+    c = tg.gemm_fp8_block_cfg_raw
+    assert c(7, 8, 8, 16, P, 16, S, P, 16, S, P, 8, 0, None) == tg.TGEMM_EINVAL_CFG
+    assert c(-1, 8, 8, 16, P, 16, S, P, 16, S, P, 8, 0, None) == tg.TGEMM_EINVAL_CFG
+    # a fast config cannot take K = 100: rejected, not silently run
+    assert c(0, 8, 8, 100, P, 100, S, P, 100, S, P, 8, 0, None) == tg.TGEMM_EINVAL_CFG
+
+
+def test_fp8_quant_rejects_invalid_before_hip():
+    q = tg.quant_fp8_block_raw
+    P, S = 256, 512
+    assert q(8, 128, P, 128, 2, P, 128, S, None) == tg.TGEMM_EINVAL_DIM       # block_rows
+    assert q(-1, 128, P, 128, 1, P, 128, S, None) == tg.TGEMM_EINVAL_DIM
+    assert q(8, 128, P, 64, 1, P, 128, S, None) == tg.TGEMM_EINVAL_LD
+    assert q(8, 128, P, 128, 1, P, 100, S, None) == tg.TGEMM_EINVAL_LD
+    assert q(8, 128, P, 128, 1, P, 128, 0, None) == tg.TGEMM_ENULL
+    assert q(8, 128, P + 1, 128, 1, P, 128, S, None) == tg.TGEMM_EALIGN
+    assert q(8, 128, P, 128, 128, P, 128, S + 2, None) == tg.TGEMM_EALIGN
+    assert q(0, 128, 0, 128, 1, 0, 128, 0, None) == tg.TGEMM_OK               # no-op

@@ -13,6 +13,14 @@ The workloads mirror the pages' synthetic ``randn`` float16 inputs: the 1024^3
 example of "Writing High-Performance Kernels in TileLang, from GEMM to MLA"
 (atlascloud.ai), section "Let's write a GEMM", and the 4096^3 fp16 benchmark of the
 nxmr.cn TileLang-on-A100 write-up, section 2.2.
+
+fp8 (E4M3) block-scaled inputs (``make_fp8_inputs``) are drawn as codes, not quantized:
+sign uniform, exponent field from a normal of mean 11 and deviation 2 rounded and clipped
+to 0..15, fraction uniform, the NaN pattern S.1111.111 replaced by S.1111.110 (448).
+Scales are float32 2^u with u uniform on [-10, -5). Order: A codes, SA, B codes, SB. The
+linear workload draws x (binary16 N(0,1)) first, then the weight codes and their scales.
+No page gives fp8 inputs; these have the spread block-quantized data has (most codes
+within a few binades below the block maximum 448).
 """
 from __future__ import annotations
 
@@ -154,6 +162,72 @@ def make_inputs(M: int, N: int, K: int, dist: str = "normal", std: float = 1.0, 
     A = _draw(rng, (M, K), dist, std)
     B = _draw(rng, (K, N), dist, std)
     return A, B
+
+
+FP8_BLOCK = 128
+
+
+def _fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    sign = rng.integers(0, 2, size=shape).astype(np.uint8) << 7
+    e = np.clip(np.rint(rng.normal(11.0, 2.0, size=shape)), 0, 15).astype(np.uint8)
+    f = rng.integers(0, 8, size=shape).astype(np.uint8)
+    c = sign | (e << 3) | f
+    nan = (c & 0x7F) == 0x7F
+    c[nan] = (c[nan] & 0x80) | 0x7E
+    return c
+
+
+def _fp8_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    return np.exp2(rng.uniform(-10.0, -5.0, size=shape)).astype(np.float32)
+
+
+def make_fp8_inputs(M: int, N: int, K: int, seed: int = 0):
+    """(A codes M x K, SA M x KB, B codes N x K, SB ceil(N/128) x KB)."""
+    rng = np.random.default_rng(seed)
+    KB = -(-K // FP8_BLOCK)
+    A = _fp8_codes(rng, (M, K))
+    SA = _fp8_scales(rng, (M, KB))
+    B = _fp8_codes(rng, (N, K))
+    SB = _fp8_scales(rng, (-(-N // FP8_BLOCK), KB))
+    return A, SA, B, SB
+
+
+def make_fp8_linear_inputs(M: int, N: int, K: int, seed: int = 0):
+    """(x binary16 M x K N(0,1), weight codes N x K, weight scales ceil(N/128) x KB)."""
+    rng = np.random.default_rng(seed)
+    x = _draw(rng, (M, K), "normal", 1.0)
+    W = _fp8_codes(rng, (N, K))
+    SW = _fp8_scales(rng, (-(-N // FP8_BLOCK), -(-K // FP8_BLOCK)))
+    return x, W, SW
+
+
+@dataclass(frozen=True)
+class Fp8Workload:
+    """An fp8 block-scaled GEMM (``linear`` False: pre-quantized A, SA, B, SB) or the
+    fp8_block_scaled_linear step (``linear`` True: quantize x per 1 x 128, then the GEMM)."""
+    name: str
+    M: int
+    N: int
+    K: int
+    relu: bool
+    seed: int
+    linear: bool = False
+
+    @property
+    def flop(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def inputs(self):
+        if self.linear:
+            return make_fp8_linear_inputs(self.M, self.N, self.K, self.seed)
+        return make_fp8_inputs(self.M, self.N, self.K, self.seed)
+
+
+FP8_WORKLOADS = {
+    "fp8_block_4096": Fp8Workload("fp8_block_4096", 4096, 4096, 4096, False, 30),
+    "fp8_block_relu_8192": Fp8Workload("fp8_block_relu_8192", 8192, 8192, 8192, True, 31),
+    "fp8_linear_4096": Fp8Workload("fp8_linear_4096", 4096, 4096, 4096, False, 32, linear=True),
+}
 
 
 def digest(x: np.ndarray) -> str:

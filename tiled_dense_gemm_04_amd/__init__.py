@@ -11,8 +11,12 @@ The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
 ``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``,
 ``tgemm_mfma_probe``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
 stream unless given), ``gemm_f16_ws_cfg`` (as ``cfg=``/``splits=``),
-``tgemm_workspace_bytes`` and ``tgemm_split_plan``; grouped GEMMs: ``gemm_f16_grouped``. ``matmul`` takes row- or column-major operand views and picks the
-layout; ``GemmFunction`` is the autograd wrapper (backward: dA = dC B^T, dB = A^T dC
+``tgemm_workspace_bytes`` and ``tgemm_split_plan``; grouped GEMMs: ``gemm_f16_grouped``;
+the fp8 (E4M3) block-scaled path: ``gemm_fp8_block`` (``gemm_fp8_block_cfg`` as
+``cfg=``), ``quant_fp8_block``, ``tgemm_fp8_num_configs``, ``tgemm_fp8_config_desc``,
+``tgemm_fp8_select_config``, and ``fp8_block_scaled_linear`` (quantize x per 1 x 128
+block, then the block-scaled GEMM against an fp8 weight). ``matmul`` takes row- or
+column-major operand views and picks the layout; ``GemmFunction`` is the autograd wrapper (backward: dA = dC B^T, dB = A^T dC
 through gemm_f16_ex). The instrumented
 twin ``libtgemm_stamps.so`` (``stamps_lib()``, measurement tools only) adds
 ``tgemm_stamps_capacity``, ``tgemm_stamps_read`` and ``tgemm_stamps_clear``
@@ -38,13 +42,16 @@ TGEMM_EALIGN = -7
 TGEMM_EWORKSPACE = -8
 SELECT_NOOP = -100
 SELECT_ZERO_FILL = -101
+FP8_GENERIC = -102           # TGEMM_FP8_GENERIC
+FP8_BLOCK = 128
 
 # Every symbol include/tgemm.h declares.
 EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_strerror",
            "tgemm_version", "tgemm_num_configs", "tgemm_config_desc", "tgemm_select_config",
            "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups", "tgemm_mfma_probe",
            "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan",
-           "gemm_f16_grouped")
+           "gemm_f16_grouped", "gemm_fp8_block", "gemm_fp8_block_cfg", "quant_fp8_block",
+           "tgemm_fp8_num_configs", "tgemm_fp8_config_desc", "tgemm_fp8_select_config")
 # The extra symbols include/tgemm_stamps.h declares (instrumented build only).
 STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear")
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
@@ -126,6 +133,18 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.tgemm_split_plan.restype = i32
     L.tgemm_split_plan.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.gemm_fp8_block.restype = i32
+    L.gemm_fp8_block.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, i32, p]
+    L.gemm_fp8_block_cfg.restype = i32
+    L.gemm_fp8_block_cfg.argtypes = [i32, i64, i64, i64, p, i64, p, p, i64, p, p, i64, i32, p]
+    L.quant_fp8_block.restype = i32
+    L.quant_fp8_block.argtypes = [i64, i64, p, i64, i32, p, i64, p, p]
+    L.tgemm_fp8_num_configs.restype = i32
+    L.tgemm_fp8_num_configs.argtypes = []
+    L.tgemm_fp8_config_desc.restype = i32
+    L.tgemm_fp8_config_desc.argtypes = [i32, ctypes.POINTER(ConfigInfo)]
+    L.tgemm_fp8_select_config.restype = i32
+    L.tgemm_fp8_select_config.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
     if stamps:
         L.tgemm_stamps_capacity.restype = i32
         L.tgemm_stamps_capacity.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -503,3 +522,134 @@ def __getattr__(name):
 
 def configs() -> list:
     return [tgemm_config_desc(i) for i in range(tgemm_num_configs())]
+
+
+# ---------------------------------------------------------------- fp8 block-scaled path
+def gemm_fp8_block_raw(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, relu, stream, library=None) -> int:
+    return (library or lib()).gemm_fp8_block(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, int(relu), stream)
+
+
+def gemm_fp8_block_cfg_raw(idx, M, N, K, A, lda, SA, B, ldb, SB, C, ldc, relu, stream, library=None) -> int:
+    return (library or lib()).gemm_fp8_block_cfg(idx, M, N, K, A, lda, SA, B, ldb, SB, C, ldc, int(relu), stream)
+
+
+def quant_fp8_block_raw(R, K, X, ldx, block_rows, Q, ldq, S, stream, library=None) -> int:
+    return (library or lib()).quant_fp8_block(R, K, X, ldx, int(block_rows), Q, ldq, S, stream)
+
+
+def tgemm_fp8_num_configs() -> int:
+    return int(lib().tgemm_fp8_num_configs())
+
+
+def tgemm_fp8_config_desc(idx: int) -> dict:
+    info = ConfigInfo()
+    rc = lib().tgemm_fp8_config_desc(idx, ctypes.byref(info))
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, f"tgemm_fp8_config_desc({idx})")
+    return info.as_dict()
+
+
+def fp8_configs() -> list:
+    return [tgemm_fp8_config_desc(i) for i in range(tgemm_fp8_num_configs())]
+
+
+def tgemm_fp8_select_config(M, N, K, A=256, lda=None, B=256, ldb=None, C=256, ldc=None) -> int:
+    """Config index gemm_fp8_block would use (FP8_GENERIC for the generic kernel)."""
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, K) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    return int(lib().tgemm_fp8_select_config(M, N, K, A, lda, B, ldb, C, ldc))
+
+
+def _operand8(t, name):
+    """A 2-D row-major device tensor of E4M3 codes (uint8 or torch.float8_e4m3fn)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    rows, cols = t.shape
+    if t.numel() == 0:
+        return rows, cols, max(1, cols)
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (stride(1) == 1)")
+    return rows, cols, (t.stride(0) if rows > 1 else max(1, cols))
+
+
+def _scale_operand(t, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.numel() and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemm_fp8_block(a, scale_a, b, scale_b, c=None, relu: bool = False, stream=None, cfg: int | None = None,
+                   library=None):
+    """C = ReLU?(sum_kb scale_a[i,kb] scale_b[j/128,kb] sum_k a[i,k] b[j,k]) through the
+    library. a: (M, K) E4M3 codes, b: (N, K) codes (a linear layer's weight), scale_a:
+    (M, ceil(K/128)) float32, scale_b: (ceil(N/128), ceil(K/128)) float32; c: (M, N) fp16
+    (allocated if None). ``cfg`` forces an fp8 config (or FP8_GENERIC)."""
+    import torch
+    M, K, lda = _operand8(a, "a")
+    N, K2, ldb = _operand8(b, "b")
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: a is {M}x{K}, b (N x K) is {N}x{K2}")
+    KB = -(-K // FP8_BLOCK)
+    _scale_operand(scale_a, (M, KB), "scale_a")
+    _scale_operand(scale_b, (-(-N // FP8_BLOCK), KB), "scale_b")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    Mc, Nc, ldc = _operand(c, "c")
+    if (Mc, Nc) != (M, N):
+        raise ValueError(f"c has shape {tuple(c.shape)}, expected {(M, N)}")
+    if not (a.device == b.device == c.device == scale_a.device == scale_b.device):
+        raise ValueError("all operands must be on the same device")
+    handle = _stream_handle(stream, a.device)
+    args = (M, N, K, a.data_ptr(), lda, scale_a.data_ptr(), b.data_ptr(), ldb, scale_b.data_ptr(), c.data_ptr(),
+            ldc, relu, handle, library)
+    with torch.cuda.device(a.device):
+        rc = gemm_fp8_block_raw(*args) if cfg is None else gemm_fp8_block_cfg_raw(cfg, *args)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "gemm_fp8_block" if cfg is None else f"gemm_fp8_block_cfg[{cfg}]")
+    return c
+
+
+def quant_fp8_block(x, block_rows: int = 1, q=None, scale=None, stream=None, library=None):
+    """E4M3 codes and float32 block scales of fp16 x (R, K): blocks of block_rows x 128
+    (1: activations, 128: weights). Returns (q (R, K) uint8, scale (ceil(R/block_rows),
+    ceil(K/128)) float32)."""
+    import torch
+    R, K, ldx = _operand(x, "x")
+    KB = -(-K // FP8_BLOCK)
+    if q is None:
+        q = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((-(-R // max(1, block_rows)), KB), dtype=torch.float32, device=x.device)
+    Rq, Kq, ldq = _operand8(q, "q")
+    if (Rq, Kq) != (R, K):
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected {(R, K)}")
+    _scale_operand(scale, (-(-R // max(1, block_rows)), KB), "scale")
+    handle = _stream_handle(stream, x.device)
+    with torch.cuda.device(x.device):
+        rc = quant_fp8_block_raw(R, K, x.data_ptr(), ldx, block_rows, q.data_ptr(), ldq, scale.data_ptr(), handle,
+                                 library)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "quant_fp8_block")
+    return q, scale
+
+
+def fp8_block_scaled_linear(x, w_fp8, scale_w, block: int = 128, relu: bool = False, out=None, stream=None):
+    """y = x W^T with W = w_fp8 (N x K E4M3 codes) scaled per 128 x 128 block by scale_w:
+    x (M x K fp16) is quantized per 1 x 128 block (quant_fp8_block), then multiplied with
+    gemm_fp8_block. Both steps run in the library on the same stream."""
+    if block != FP8_BLOCK:
+        raise ValueError(f"only block = {FP8_BLOCK} is supported")
+    xq, sx = quant_fp8_block(x, 1, stream=stream)
+    return gemm_fp8_block(xq, sx, w_fp8, scale_w, c=out, relu=relu, stream=stream)

@@ -18,7 +18,8 @@ LIBRARY = os.path.join(PKG, "libtgemm.so")
 STAMPS_LIBRARY = os.path.join(PKG, "libtgemm_stamps.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "tgemm_kernels.hip"), os.path.join(CSRC, "tgemm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "tgemm_kernels.hip"), os.path.join(CSRC, "tgemm_fp8.hip"),
+           os.path.join(CSRC, "tgemm_api.cpp")]
 
 # Device code: gfx950 only. Packed-fp32 instruction selection is switched off for all
 # device code; -fvisibility=hidden keeps everything but the TGEMM_API entry points local.

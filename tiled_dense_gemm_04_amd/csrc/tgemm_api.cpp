@@ -210,9 +210,182 @@ int run(int cfg, int layout, int64_t M, int64_t N, int64_t K, const void* A, int
   return tgemm::launcher(cfg)(g, s, dev) == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH;
 }
 
+// ---------------------------------------------------------------- fp8 block-scaled path
+int fp8_table_size() {
+  int n = 0;
+  tgemm::fp8_config_table(&n);
+  return n;
+}
+const tgemm::Fp8Config& fp8_row(int idx) {
+  int n = 0;
+  return tgemm::fp8_config_table(&n)[idx];
+}
+constexpr int kFp8Generic = TGEMM_FP8_GENERIC;  // the generic kernel (-102)
+constexpr int kFp8Cfg256 = 0, kFp8Cfg128 = 1, kFp8Cfg256x128 = 2;
+
+int fp8_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const float* SA,
+                 const void* B, int64_t ldb, const float* SB, const void* C, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0 || M >= TGEMM_MAX_DIM || N >= TGEMM_MAX_DIM || K >= TGEMM_MAX_DIM)
+    return TGEMM_EINVAL_DIM;
+  const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
+  if (lda < kmin || ldb < kmin || ldc < nmin) return TGEMM_EINVAL_LD;
+  if (lda > TGEMM_MAX_LD || ldb > TGEMM_MAX_LD || ldc > TGEMM_MAX_LD) return TGEMM_EINVAL_LD;
+  const bool out_nonempty = M > 0 && N > 0;
+  if (out_nonempty && C == nullptr) return TGEMM_ENULL;
+  if (out_nonempty && K > 0 && (A == nullptr || B == nullptr || SA == nullptr || SB == nullptr))
+    return TGEMM_ENULL;
+  if ((reinterpret_cast<uintptr_t>(C) & 1u) ||
+      ((reinterpret_cast<uintptr_t>(SA) | reinterpret_cast<uintptr_t>(SB)) & 3u))
+    return TGEMM_EALIGN;
+  return TGEMM_OK;
+}
+
+// Fast configs need 16-byte operand rows in k (A, B), 16-byte output row segments (C), and
+// 32-bit scale offsets inside a 256-row tile.
+bool fp8_fast_eligible(int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, int64_t ldc) {
+  const int64_t KB = tgemm::ceil_div(K, tgemm::kFp8Block);
+  return aligned16(A) && aligned16(B) && aligned16(C) && lda % 16 == 0 && ldb % 16 == 0 && K % 16 == 0 &&
+         ldc % 8 == 0 && N % 8 == 0 && 256 * KB * 4 < ((int64_t)1 << 31);
+}
+
+// 256 x 256 tiles when they cover most compute units, else 256 x 128 when those do, else
+// 128 x 128.
+int fp8_choose(int64_t M, int64_t N) {
+  if (tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256) >= 160) return kFp8Cfg256;
+  if (tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 128) >= 160) return kFp8Cfg256x128;
+  return kFp8Cfg128;
+}
+
+int fp8_select(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const float* SA, const void* B,
+               int64_t ldb, const float* SB, const void* C, int64_t ldc) {
+  const int v = fp8_validate(M, N, K, A, lda, SA, B, ldb, SB, C, ldc);
+  if (v != TGEMM_OK) return v;
+  if (M == 0 || N == 0) return kSelectNoop;
+  if (K == 0) return kSelectZeroFill;
+  return fp8_fast_eligible(N, K, A, lda, B, ldb, C, ldc) ? fp8_choose(M, N) : kFp8Generic;
+}
+
+int fp8_run(int cfg, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const float* SA,
+            const void* B, int64_t ldb, const float* SB, void* C, int64_t ldc, int relu, void* stream) {
+  int dev = -1;
+  const int d = check_device(&dev);
+  if (d != TGEMM_OK) return d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg == kSelectZeroFill)
+    return tgemm::launch_zero_fill(static_cast<_Float16*>(C), (int)M, (int)N, ldc, s) == hipSuccess
+               ? TGEMM_OK
+               : TGEMM_ELAUNCH;
+  tgemm::Fp8Args g;
+  g.A = static_cast<const uint8_t*>(A);
+  g.B = static_cast<const uint8_t*>(B);
+  g.SA = SA;
+  g.SB = SB;
+  g.C = static_cast<_Float16*>(C);
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.KB = (int)tgemm::ceil_div(K, tgemm::kFp8Block);
+  g.relu = relu != 0;
+  if (cfg == kFp8Generic) {
+    if (tgemm::ceil_div(M, 16) * tgemm::ceil_div(N, 16) >= ((int64_t)1 << 32)) return TGEMM_EINVAL_DIM;
+    g.tiles_m = g.tiles_n = 0;
+    return tgemm::launch_fp8_generic(g, s) == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH;
+  }
+  const tgemm::Fp8Config& c = fp8_row(cfg);
+  const int64_t tm = tgemm::ceil_div(M, c.bm), tn = tgemm::ceil_div(N, c.bn);
+  if (tm * tn >= ((int64_t)1 << 31)) return TGEMM_EINVAL_DIM;
+  g.tiles_m = (int)tm;
+  g.tiles_n = (int)tn;
+  return tgemm::launch_fp8(cfg, g, s, dev) == hipSuccess ? TGEMM_OK : TGEMM_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_fp8_block(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const float* scale_a,
+                   const void* B, int64_t ldb, const float* scale_b, void* C, int64_t ldc, int relu,
+                   void* stream) {
+  const int cfg = fp8_select(M, N, K, A, lda, scale_a, B, ldb, scale_b, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill && cfg != kFp8Generic) return cfg;
+  return fp8_run(cfg, M, N, K, A, lda, scale_a, B, ldb, scale_b, C, ldc, relu, stream);
+}
+
+int gemm_fp8_block_cfg(int idx, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const float* scale_a, const void* B, int64_t ldb, const float* scale_b, void* C,
+                       int64_t ldc, int relu, void* stream) {
+  if (idx != kFp8Generic && (idx < 0 || idx >= fp8_table_size())) return TGEMM_EINVAL_CFG;
+  const int cfg = fp8_select(M, N, K, A, lda, scale_a, B, ldb, scale_b, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill && cfg != kFp8Generic) return cfg;
+  if (cfg == kSelectZeroFill) return fp8_run(cfg, M, N, K, A, lda, scale_a, B, ldb, scale_b, C, ldc, relu, stream);
+  if (idx != kFp8Generic && cfg == kFp8Generic) return TGEMM_EINVAL_CFG;  // needs the generic kernel
+  return fp8_run(idx, M, N, K, A, lda, scale_a, B, ldb, scale_b, C, ldc, relu, stream);
+}
+
+int tgemm_fp8_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, const void* C, int64_t ldc) {
+  static const float kScaleProbe[1] = {0.0f};  // only its alignment is looked at
+  return fp8_select(M, N, K, A, lda, kScaleProbe, B, ldb, kScaleProbe, C, ldc);
+}
+
+int tgemm_fp8_num_configs(void) { return fp8_table_size(); }
+
+int tgemm_fp8_config_desc(int idx, tgemm_config_info* out) {
+  if (out == nullptr) return TGEMM_ENULL;
+  if (idx < 0 || idx >= fp8_table_size()) return TGEMM_EINVAL_CFG;
+  const tgemm::Fp8Config& c = fp8_row(idx);
+  std::memset(out, 0, sizeof(*out));
+  out->block_m = c.bm;
+  out->block_n = c.bn;
+  out->block_k = tgemm::kFp8Block;
+  out->stages = c.stages;
+  out->waves_m = c.waves_m;
+  out->waves_n = c.waves_n;
+  out->panel = c.panel;
+  out->xcd_remap = c.xcd_remap;
+  out->generic = 0;
+  out->layouts = 1 << 1;  // A as given (M x K), B transposed (N x K)
+  out->lds_bytes = c.stages * ((c.bm + c.bn) * tgemm::kFp8Block + 256 * c.waves_m * c.waves_n);
+  std::strncpy(out->name, c.name, sizeof(out->name) - 1);
+  return TGEMM_OK;
+}
+
+int quant_fp8_block(int64_t R, int64_t K, const void* X, int64_t ldx, int block_rows, void* Q, int64_t ldq,
+                    float* scale, void* stream) {
+  if (R < 0 || K < 0 || R >= TGEMM_MAX_DIM || K >= TGEMM_MAX_DIM) return TGEMM_EINVAL_DIM;
+  if (block_rows != 1 && block_rows != 128) return TGEMM_EINVAL_DIM;
+  const int64_t kmin = K > 1 ? K : 1;
+  if (ldx < kmin || ldq < kmin || ldx > TGEMM_MAX_LD || ldq > TGEMM_MAX_LD) return TGEMM_EINVAL_LD;
+  if (R == 0 || K == 0) return TGEMM_OK;
+  if (X == nullptr || Q == nullptr || scale == nullptr) return TGEMM_ENULL;
+  if ((reinterpret_cast<uintptr_t>(X) & 1u) || (reinterpret_cast<uintptr_t>(scale) & 3u)) return TGEMM_EALIGN;
+  const int64_t KB = tgemm::ceil_div(K, tgemm::kFp8Block);
+  const int64_t groups = block_rows == 1 ? tgemm::ceil_div(R * KB, 16) : tgemm::ceil_div(R, 128) * KB;
+  if (groups >= ((int64_t)1 << 31)) return TGEMM_EINVAL_DIM;
+  int dev = -1;
+  const int d = check_device(&dev);
+  if (d != TGEMM_OK) return d;
+  tgemm::QuantArgs q;
+  q.X = static_cast<const _Float16*>(X);
+  q.Q = static_cast<uint8_t*>(Q);
+  q.S = scale;
+  q.ldx = ldx;
+  q.ldq = ldq;
+  q.R = (int)R;
+  q.K = (int)K;
+  q.KB = (int)KB;
+  q.block_rows = block_rows;
+  const bool vec = aligned16(X) && (reinterpret_cast<uintptr_t>(Q) & 7u) == 0 && ldx % 8 == 0 && ldq % 8 == 0 &&
+                   K % 8 == 0;
+  return tgemm::launch_quant_fp8(q, vec, static_cast<hipStream_t>(stream)) == hipSuccess ? TGEMM_OK
+                                                                                           : TGEMM_ELAUNCH;
+}
 
 int gemm_f16_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {

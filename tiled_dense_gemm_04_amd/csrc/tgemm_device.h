@@ -94,11 +94,13 @@ __host__ __device__ constexpr int swz_a(int r) {
 // The same for 16x16x32 A fragments (16 lanes on 16 rows, four lane groups on the four
 // 16-byte chunks of a 64-byte row, BK = 32). Measured with SQ_LDS_BANK_CONFLICT on gfx950:
 // XOR by (r / 2) % 4 is conflict-free for this pattern, while (r / 4) % 4 (the 32x32x16
-// choice above) conflicts 2-way.
+// choice above) conflicts 2-way. Rows of BK = 64 halves (the 128-byte rows of the fp8
+// kernels) take (r / 2) % 8: two rows share a 256-byte bank window, and the XOR puts the
+// 16 rows read by one instruction on 16 distinct 16-byte slots of it.
 template <int BK, int MF>
 __host__ __device__ constexpr int swz_a_mf(int r) {
-  static_assert(MF == 32 || BK == 32, "16x16x32 fragments are laid out for BK = 32");
-  return MF == 16 ? (r >> 1) & 3 : swz_a<BK>(r);
+  static_assert(MF == 32 || BK == 32 || BK == 64, "16x16 fragments are laid out for BK = 32 or 64");
+  return MF == 16 ? (r >> 1) % (BK / 8) : swz_a<BK>(r);
 }
 // B stage: BK rows (k) x BN halves (n), row k at byte k*BN*2 (a multiple of 256 bytes);
 // logical chunk c of row k is stored at chunk c ^ swz_b(k). A transposed read by 32 lanes

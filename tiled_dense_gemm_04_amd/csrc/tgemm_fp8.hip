@@ -1,0 +1,465 @@
+// tgemm_fp8.hip -- gfx950 kernels of the fp8 (E4M3) block-scaled GEMM and of the block
+// quantizer that feeds it.
+//
+// Operation: fp8_block_scaled_linear(x, w_fp8, scale_w, block=128) in "TileLang-MUSA
+// operator development" (7yue.com), section 8.2, with the per-block scaling named in the
+// TileLang write-up measured on A100 (nxmr.cn 138173), section 7. The pages fix neither
+// the encoding nor the block shapes; the reading taken (stated with the entry points in
+// tgemm.h) is OCP E4M3 codes with float32 scales per 1 x 128 block of A and per 128 x 128
+// block of B (N x K, a linear layer's weight):
+//   C[i,j] = ReLU?( sum_kb SA[i,kb] * SB[j/128,kb] * sum_{k in block kb} a[i,k] * b[j,k] ).
+// What is MI355X-specific:
+//   * one v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3) covers exactly one 128-wide k-block of
+//     a 16 x 16 output tile, so a k-tile is one scale block: each MFMA starts from zero and
+//     its block sum is folded into the float32 accumulator by the VALU (acc += sa*sb * P)
+//     while later MFMAs run. The fp8 MFMAs sum a block's 128 products with less than
+//     float32 precision; promoting every block to float32 is what the block size bounds;
+//   * operand tiles are K-major rows of 128 bytes. In LDS they are held exactly like the
+//     binary16 ping-pong kernel's K-major tiles of 64 halves (the same bytes): the same
+//     buffer->LDS copies, range-checked edges and swizzle. A lane's 32-byte fp8 fragment is
+//     two 16-byte reads (k bytes 16g..16g+15 and 64+16g..64+16g+15 for lane group g); A
+//     and B use the same k order, which is all the dot product needs;
+//   * the per-row scales of A (and the per-column-block scales of B) ride the same
+//     buffer->LDS copies, one dword per lane, so every wait counts copies exactly;
+//   * XCD-aware, panel-ordered tile order as in the binary16 kernels.
+#include "tgemm_device.h"
+
+#include <atomic>
+
+namespace tgemm {
+namespace {
+
+typedef int int8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned char uchar8 __attribute__((ext_vector_type(8)));
+
+constexpr int kF8Kh = kFp8Block / 2;  // k-tile width in binary16 units (the LDS view)
+
+// One 4-byte buffer load per lane written straight to LDS at lds_base + 4*lane (zeros for
+// a lane outside the descriptor range). Inline assembly for the reason given at
+// dma_to_lds; M0 is clobbered the same way.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_dword_to_lds(const int4v& rsrc, uint32_t lds_base, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ int8v cat_frag(const half8& lo, const half8& hi) {
+  const int4v l = __builtin_bit_cast(int4v, lo), h = __builtin_bit_cast(int4v, hi);
+  return __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// E4M3 code -> float (exact): exponent field 0 is f * 2^-9, S.1111.111 is NaN, otherwise
+// (1 + f/8) * 2^(e-7), i.e. float exponent field e + 120 and fraction f << 20.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15, f = c & 7;
+  float v;
+  if (e == 0)
+    v = (float)f * 0x1p-9f;
+  else if (e == 15 && f == 7)
+    v = __builtin_nanf("");
+  else
+    v = __uint_as_float(((e + 120) << 23) | (f << 20));
+  return (c & 0x80) ? -v : v;
+}
+
+// float -> E4M3 code: nearest, ties to the even fraction; |y| >= 448 (and +-inf) saturates
+// to +-448, the largest finite value (rounding could only reach 480, the NaN pattern);
+// NaN -> 0x7F with the sign. Below 2^-6 the spacing is 2^-9 (subnormals).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // 448.0f
+  if (a < 0x3C800000u) {                       // 2^-6: |y| * 2^9 < 8, rounded to 0 .. 8
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  const uint32_t e = (a >> 23) - 120;  // E4M3 exponent field, 1 .. 15
+  uint32_t m = (a >> 20) & 7;
+  const uint32_t rest = a & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m & 1))) ++m;
+  return sign | ((e << 3) + m);  // m == 8 carries into the exponent; a < 448 stays finite
+}
+
+// ------------------------------------------------------------------------------------
+// Block-scaled GEMM, fast path. BM x BN tile, WM x WN waves (wave tile WTM x WTN of 16 x 16
+// MFMA tiles), k-tile = one 128-wide scale block, STAGES-deep LDS ring.
+// Per k-tile every thread issues PT copies: its share of the A and B tiles (16 bytes each)
+// and one dword of scales: waves whose 64 lanes cover rows of A fetch SA[row, kt]; the
+// first wave past the rows fetches SB[jb, kt] for the tile's column blocks; any other
+// wave fetches nothing (an out-of-range offset writes zeros to its own scratch dwords).
+// Schedule (tile t in slot t % STAGES): copies of tiles 0 .. STAGES-1; then for each kt:
+// wait for this thread's copies of tile kt, barrier (everyone's have landed), MFMAs +
+// folds of tile kt, barrier (every wave is done with the slot), copies of tile
+// kt+STAGES into it (past the last tile: empty ranges, zeros, never read).
+// Requirements (checked by the host): A, B 16-byte aligned, lda, ldb, K multiples of 16;
+// C 16-byte aligned, ldc and N multiples of 8; (BM - 1) * KB * 4 < 2^31.
+template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  using OpA = PpOperand<BM, kF8Kh, 16, true, NW>;
+  using OpB = PpOperand<BN, kF8Kh, 16, true, NW>;
+  constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
+  constexpr int S_BYTES = 256 * NW;  // one dword per lane of every wave
+  constexpr int PT = OpA::LD + OpB::LD + 1;
+  constexpr int SB_WAVE = BM / 64;  // the wave that fetches the scales of B
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "operand tiles of whole 128-row LDS extents");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile of 16 x 16 MFMA tiles");
+  static_assert(kFp8Block % WTN == 0, "a wave's columns lie in one scale block of B");
+  static_assert(SB_WAVE < NW && BN / kFp8Block <= 64, "a spare wave fetches the scales of B");
+  static_assert(STAGES >= 2 && PT * STAGES < 64, "ring depth / vmcnt budget");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const a_lds = smem;
+  char* const b_lds = smem + STAGES * A_BYTES;
+  char* const s_lds = b_lds + STAGES * B_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int64_t tm64, tn64;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
+  const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
+  const int nk = g.KB;
+  const int kin_last = g.K - (nk - 1) * kFp8Block;  // bytes of k in the last tile (16 | it)
+
+  OpA opa;
+  OpB opb;
+  opa.init_copies((const _Float16*)g.A, g.lda / 2, row0, mvalid, kin_last / 2, wave, lane);
+  opb.init_copies((const _Float16*)g.B, g.ldb / 2, col0, nvalid, kin_last / 2, wave, lane);
+
+  // Scale copies of this wave: base (k-tile 0), per-lane offset, range.
+  const float* s_base;
+  uint32_t s_off, s_rng;
+  if (wave * 64 < BM) {
+    const int r = wave * 64 + lane;
+    s_base = g.SA + (int64_t)row0 * g.KB;
+    s_off = r < BM ? (uint32_t)(r * g.KB * 4) : kOob;
+    s_rng = (uint32_t)(((int64_t)(mvalid - 1) * g.KB + 1) * 4);
+  } else if (wave == SB_WAVE) {
+    const int nb_valid = (nvalid + kFp8Block - 1) / kFp8Block;
+    s_base = g.SB + (int64_t)(col0 / kFp8Block) * g.KB;
+    s_off = lane < BN / kFp8Block ? (uint32_t)(lane * g.KB * 4) : kOob;
+    s_rng = (uint32_t)(((int64_t)(nb_valid - 1) * g.KB + 1) * 4);
+  } else {
+    s_base = g.SA;
+    s_off = kOob;
+    s_rng = 0;
+  }
+
+  const uint32_t a_lds0 = lds_addr(a_lds) + wave * 1024;
+  const uint32_t b_lds0 = lds_addr(b_lds) + wave * 1024;
+  const uint32_t s_lds0 = lds_addr(s_lds) + wave * 256;
+  auto copy_tile = [&](int t) {
+    const int4v ra = opa.rsrc(t, nk, nk);
+    const int4v rb = opb.rsrc(t, nk, nk);
+    const int tt = t < nk ? t : nk - 1;
+    const int4v rs = make_rsrc(s_base + tt, t < nk ? s_rng : 0u);
+    const int slot = t % STAGES;
+    const bool last = t == nk - 1;
+#pragma unroll
+    for (int j = 0; j < OpA::LD; ++j)
+      dma_to_lds(ra, a_lds0 + slot * A_BYTES + j * NW * 1024, last ? opa.off_last[j] : opa.off[j]);
+#pragma unroll
+    for (int j = 0; j < OpB::LD; ++j)
+      dma_to_lds(rb, b_lds0 + slot * B_BYTES + j * NW * 1024, last ? opb.off_last[j] : opb.off[j]);
+    dma_dword_to_lds(rs, s_lds0 + slot * S_BYTES, s_off);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int lrow = lane % 16, lkg = lane / 16;
+  opa.init_frags(wm * WTM, lane);
+  opb.init_frags(wn * WTN, lane);
+  const int sb_index = SB_WAVE * 64 + (wn * WTN) / kFp8Block;
+
+  float4v acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Operands go in as (B fragment, A fragment): a lane's result holds four consecutive
+  // output columns (16 * fn + 4 * lkg ..) of one row (16 * fm + lrow) of the wave tile.
+  auto compute = [&](int slot) {
+    const char* const As = a_lds + slot * A_BYTES;
+    const char* const Bs = b_lds + slot * B_BYTES;
+    const TG_LDS float* const S = (const TG_LDS float*)(s_lds + slot * S_BYTES);
+    const float sb = S[sb_index];
+    float sc[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sc[fm] = S[wm * WTM + fm * 16 + lrow] * sb;
+    int8v fb[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
+    const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int8v fa = cat_frag(opa.frag(As, fm, 0), opa.frag(As, fm, 1));
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const float4v p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa, zero, 0, 0, 0, 0, 0, 0);
+        acc[fm][fn] += sc[fm] * p;
+      }
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < STAGES; ++t) copy_tile(t);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<PT * (STAGES - 1)>();
+    lds_barrier();
+    compute(kt % STAGES);
+    lds_barrier();
+    copy_tile(kt + STAGES);
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue: ReLU in float32, round to fp16, stage the wave's WTM x WTN sub-tile in its
+  // own LDS region (the ring is free once every wave passes the barrier) and write it back
+  // as 16-byte row segments. Staged row r, chunk c sits at chunk c ^ ((r / 2) % SCPR).
+  constexpr int CPR = WTN / 8, SCPR = CPR <= 4 ? 4 : (CPR <= 8 ? 8 : 16);
+  constexpr int RB = SCPR * 16;
+  static_assert(SCPR >= CPR && NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "staged tile fits in the ring");
+  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+  __syncthreads();
+  char* const stage = smem + wave * (WTM * RB);
+  const bool relu = g.relu != 0;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int mw = fm * 16 + lrow;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int nw = fn * 16 + 4 * lkg;
+      float v0 = acc[fm][fn][0], v1 = acc[fm][fn][1], v2 = acc[fm][fn][2], v3 = acc[fm][fn][3];
+      if (relu) {
+        v0 = relu_f(v0);
+        v1 = relu_f(v1);
+        v2 = relu_f(v2);
+        v3 = relu_f(v3);
+      }
+      const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+      *(TG_LDS half4*)(stage + mw * RB + (((nw >> 3) ^ ((mw >> 1) % SCPR)) << 4) + (nw & 7) * 2) = h;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+  for (int i = 0; i < WTM * SCPR / 64; ++i) {
+    const int idx = i * 64 + lane;
+    const int r = idx / SCPR, c = idx % SCPR;
+    if (c >= CPR) continue;
+    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
+    const int m = wm * WTM + r, n = wn * WTN + 8 * c;
+    if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+constexpr int fp8_lds_bytes() {
+  return STAGES * ((BM + BN) * kFp8Block + 256 * WM * WN);
+}
+
+// ------------------------------------------------------------------------------------
+// Block-scaled GEMM, generic path (any alignment, stride or K): one output element per
+// thread, products of decoded codes summed per block in float32, then scaled and
+// accumulated in float32 like the fast path.
+__global__ __launch_bounds__(256) void gemm_fp8_block_generic(Fp8Args g) {
+  const int64_t tiles_n = (g.N + 15) / 16;
+  const int64_t t = blockIdx.x;
+  const int i = (int)(t / tiles_n) * 16 + (int)(threadIdx.x / 16);
+  const int j = (int)(t % tiles_n) * 16 + (int)(threadIdx.x % 16);
+  if (i >= g.M || j >= g.N) return;
+  const uint8_t* const a = g.A + (int64_t)i * g.lda;
+  const uint8_t* const b = g.B + (int64_t)j * g.ldb;
+  const float* const sa = g.SA + (int64_t)i * g.KB;
+  const float* const sb = g.SB + (int64_t)(j / kFp8Block) * g.KB;
+  float acc = 0.0f;
+  for (int kb = 0; kb < g.KB; ++kb) {
+    const int k0 = kb * kFp8Block, k1 = min(g.K, k0 + kFp8Block);
+    float p = 0.0f;
+    for (int k = k0; k < k1; ++k) p += e4m3_to_f32(a[k]) * e4m3_to_f32(b[k]);
+    acc += (sa[kb] * sb[kb]) * p;
+  }
+  g.C[(int64_t)i * g.ldc + j] = (_Float16)(g.relu ? relu_f(acc) : acc);
+}
+
+// ------------------------------------------------------------------------------------
+// Block quantizer, 1 x 128 blocks (activations): a group of 16 lanes per block, 8
+// elements per lane. Scale s = amax / 448 in float32 (1 for an all-zero block), codes
+// f32_to_e4m3(x / s) with IEEE float32 division. All 64 lanes of a wave take part in the
+// shuffles; lanes of groups past the last block only skip their loads and stores.
+template <bool VEC>
+__global__ __launch_bounds__(256) void quant_fp8_rows(QuantArgs q) {
+  const int64_t blk = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+  const int sub = threadIdx.x % 16;
+  const bool active = blk < (int64_t)q.R * q.KB;
+  const int64_t row = active ? blk / q.KB : 0;
+  const int kb = active ? (int)(blk % q.KB) : 0;
+  const int k = kb * kFp8Block + 8 * sub;
+  float x[8];
+  if (VEC) {
+    half8 h = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active && k < q.K) h = *(const half8*)(q.X + row * q.ldx + k);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (active && k + e < q.K) ? (float)q.X[row * q.ldx + k + e] : 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+  for (int w = 1; w < 16; w <<= 1) m = fmaxf(m, __shfl_xor(m, w, 16));
+  const float s = m > 0.0f ? m / 448.0f : 1.0f;
+  if (!active) return;
+  if (VEC) {
+    if (k < q.K) {
+      uchar8 c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = (unsigned char)f32_to_e4m3(x[e] / s);
+      *(uchar8*)(q.Q + row * q.ldq + k) = c;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k + e < q.K) q.Q[row * q.ldq + k + e] = (uint8_t)f32_to_e4m3(x[e] / s);
+  }
+  if (sub == 0) q.S[row * q.KB + kb] = s;
+}
+
+// Block quantizer, 128 x 128 blocks (weights): one workgroup of 256 threads per block,
+// thread t on rows t / 16 + 16 i (i < 8) and columns 8 (t % 16) .. +7; the block's
+// maximum is reduced across the workgroup through LDS.
+template <bool VEC>
+__global__ __launch_bounds__(256) void quant_fp8_tiles(QuantArgs q) {
+  __shared__ float wmax[4];
+  const int kb = (int)(blockIdx.x % q.KB);
+  const int64_t rb = blockIdx.x / q.KB;
+  const int t = threadIdx.x;
+  const int c8 = 8 * (t % 16), k = kb * kFp8Block + c8;
+  const int64_t r0 = rb * 128 + t / 16;
+  float x[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + 16 * i;
+    if (VEC) {
+      half8 h = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < q.R && k < q.K) h = *(const half8*)(q.X + r * q.ldx + k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = (float)h[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = (r < q.R && k + e < q.K) ? (float)q.X[r * q.ldx + k + e] : 0.0f;
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[i][e]));
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) m = fmaxf(m, __shfl_xor(m, w, 64));
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = m > 0.0f ? m / 448.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + 16 * i;
+    if (r >= q.R) continue;
+    if (VEC) {
+      if (k < q.K) {
+        uchar8 c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = (unsigned char)f32_to_e4m3(x[i][e] / s);
+        *(uchar8*)(q.Q + r * q.ldq + k) = c;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k + e < q.K) q.Q[r * q.ldq + k + e] = (uint8_t)f32_to_e4m3(x[i][e] / s);
+    }
+  }
+  if (t == 0) q.S[rb * q.KB + kb] = s;
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD>
+hipError_t launch_fp8_cfg(const Fp8Args& g, hipStream_t s, int device) {
+  constexpr int lds = fp8_lds_bytes<BM, BN, WM, WN, STAGES>();
+  static_assert(lds <= 160 * 1024, "LDS");
+  auto kern = gemm_fp8_block_kernel<BM, BN, WM, WN, STAGES, PANEL, XCD>;
+  static std::atomic<uint64_t> ready{0};
+  const uint64_t bit = 1ull << (device & 63);
+  if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)g.tiles_m * g.tiles_n)), dim3(64 * WM * WN), lds, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// fp8 configs: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD)
+#define TGEMM_FP8_CONFIGS(X)  \
+  X(256, 256, 2, 4, 2, 4, 1)  \
+  X(128, 128, 2, 2, 3, 4, 1)  \
+  X(256, 128, 4, 2, 3, 4, 1)
+
+#define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X) {BM, BN, WM, WN, S, P, X, "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN},
+#define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X) launch_fp8_cfg<BM, BN, WM, WN, S, P, X>,
+
+const Fp8Config* fp8_config_table(int* count) {
+  static const Fp8Config table[] = {TGEMM_FP8_CONFIGS(TGEMM_FP8_ROW)};
+  *count = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+hipError_t launch_fp8(int idx, const Fp8Args& g, hipStream_t s, int device) {
+  typedef hipError_t (*L)(const Fp8Args&, hipStream_t, int);
+  static const L table[] = {TGEMM_FP8_CONFIGS(TGEMM_FP8_LAUNCHER)};
+  if (idx < 0 || idx >= (int)(sizeof(table) / sizeof(table[0]))) return hipErrorInvalidValue;
+  return table[idx](g, s, device);
+}
+
+hipError_t launch_fp8_generic(const Fp8Args& g, hipStream_t s) {
+  const int64_t tiles = (int64_t)((g.M + 15) / 16) * ((g.N + 15) / 16);
+  hipLaunchKernelGGL(gemm_fp8_block_generic, dim3((unsigned)tiles), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const QuantArgs& q, bool vec, hipStream_t s) {
+  if (q.block_rows == 1) {
+    const int64_t blocks = (int64_t)q.R * q.KB;
+    const dim3 grid((unsigned)((blocks + 15) / 16));
+    if (vec)
+      hipLaunchKernelGGL(quant_fp8_rows<true>, grid, dim3(256), 0, s, q);
+    else
+      hipLaunchKernelGGL(quant_fp8_rows<false>, grid, dim3(256), 0, s, q);
+  } else {
+    const dim3 grid((unsigned)((int64_t)((q.R + 127) / 128) * q.KB));
+    if (vec)
+      hipLaunchKernelGGL(quant_fp8_tiles<true>, grid, dim3(256), 0, s, q);
+    else
+      hipLaunchKernelGGL(quant_fp8_tiles<false>, grid, dim3(256), 0, s, q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tgemm

@@ -103,6 +103,42 @@ typedef hipError_t (*GroupedLauncher)(const GroupedArgs&, int64_t nwg, hipStream
 // The grouped launcher of table row idx, or nullptr if that config has none.
 GroupedLauncher grouped_launcher(int idx);
 
+// fp8 (E4M3) block-scaled GEMM: C = ReLU?(sum_kb SA[i,kb] SB[j/128,kb] sum_k a[i,k] b[j,k]),
+// A M x K and B N x K codes (k contiguous), SA M x KB and SB ceil(N/128) x KB float32.
+constexpr int kFp8Block = 128;
+struct Fp8Args {
+  const uint8_t* A;
+  const uint8_t* B;
+  const float* SA;
+  const float* SB;
+  _Float16* C;
+  int64_t lda, ldb, ldc;  // bytes (A, B) and elements (C)
+  int M, N, K, KB;        // KB = ceil(K / 128)
+  int relu;
+  int tiles_m, tiles_n;
+};
+// fp8 tile configs (index order is tooling ABI: gemm_fp8_block_cfg, sweeps).
+struct Fp8Config {
+  int bm, bn, waves_m, waves_n, stages, panel, xcd_remap;
+  const char* name;
+};
+const Fp8Config* fp8_config_table(int* count);
+// Launch fast config idx (A, B 16-byte aligned, lda, ldb, K multiples of 16, C 16-byte
+// aligned, ldc and N multiples of 8), or the generic kernel (any arguments).
+hipError_t launch_fp8(int idx, const Fp8Args& g, hipStream_t s, int device);
+hipError_t launch_fp8_generic(const Fp8Args& g, hipStream_t s);
+
+// Block quantizer binary16 -> E4M3 with float32 block scales (blocks of block_rows x 128).
+struct QuantArgs {
+  const _Float16* X;
+  uint8_t* Q;
+  float* S;
+  int64_t ldx, ldq;  // elements (X), bytes (Q)
+  int R, K, KB, block_rows;
+};
+// vec: X 16-byte aligned, Q 8-byte aligned, ldx, ldq and K multiples of 8.
+hipError_t launch_quant_fp8(const QuantArgs& q, bool vec, hipStream_t s);
+
 // Zero-fill of an M x N block with row stride ldc (the K == 0 case).
 hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s);
 
