@@ -15,6 +15,12 @@ From idle, the GPU raises its clocks over the first ~25 ms of load (about 200 ca
                      stream the kernels are launched on, against the dense fp16 MFMA peak
   cpu_baseline     = the CPU oracle (as it stands) timed on the host on a slab of rows of
                      the same workload, in TFLOP/s, with the threads it used
+
+--workload also takes the fp8 block-scaled workloads (fp8_block_4096, fp8_block_relu_8192:
+one gemm_fp8_block call per step on pre-quantized E4M3 inputs; fp8_linear_4096: the 1 x 128
+quantizer plus the GEMM per step); their line is priced against the dense fp8 MFMA peak
+(256 CUs x 8192 FLOP/clk/CU x 2.4 GHz = 5033.2 TFLOP/s). The default stays the fp16 4096^3
+GEMM + ReLU.
 """
 from __future__ import annotations
 
@@ -31,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fp16 GEMM+ReLU TFLOP/s at 4096^3 on 1 MI355X; % of dense fp16 MFMA peak"
 # Dense fp16 MFMA peak of MI355X: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz (AMD's ~2.5 PFLOP/s).
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+FP8_PEAK_TFLOPS = 256 * 8192 * 2.4e9 / 1e12
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -40,7 +47,7 @@ def eprint(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("tgemm_kernels.hip", "tgemm_internal.h", "tgemm_api.cpp"):
+    for f in ("tgemm_kernels.hip", "tgemm_device.h", "tgemm_fp8.hip", "tgemm_internal.h", "tgemm_api.cpp"):
         with open(os.path.join(ROOT, "tiled_dense_gemm_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -94,6 +101,105 @@ def cpu_baseline(A, B, relu, c_gpu_bits, target_s: float):
     }
 
 
+def cpu_baseline_fp8(A, SA, B, SB, relu, c_gpu_bits, target_s: float):
+    """The fp8 oracle on the first R rows (codes as given), R sized for ~target_s."""
+    import oracle
+
+    orc = oracle.default()
+    threads = orc.max_threads()
+    M, K = A.shape
+    N = B.shape[0]
+    t = time.perf_counter()
+    orc.gemm_fp8(A[:8], SA[:8], B, SB, relu)
+    rate = 2.0 * 8 * N * K / max(time.perf_counter() - t, 1e-9)
+    rows = int(min(M, max(8, rate * target_s / (2.0 * N * K))))
+    t = time.perf_counter()
+    ref = orc.gemm_fp8(A[:rows], SA[:rows], B, SB, relu)
+    dt = time.perf_counter() - t
+    flops = 2.0 * rows * N * K
+    rep = oracle.compare_fp8(c_gpu_bits[:rows], ref, orc.fp8_bound(A[:rows], SA[:rows], B, SB))
+    eprint(f"cpu fp8 oracle: {rows} rows x {N} x {K} in {dt:.2f} s on {threads} threads "
+           f"({flops / dt / 1e9:.2f} GFLOP/s); GPU rows vs oracle: {rep}")
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {rows} of {M} rows of the same workload (all N={N} columns, K={K}), "
+                  f"{dt:.1f} s; GPU output on those rows vs oracle: {rep['fails']} tolerance failures",
+    }
+
+
+def bench_fp8(args, W, tg, torch, np) -> int:
+    w = W.FP8_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    if w.linear:
+        x, Bc, SB = w.inputs()
+        xd = torch.from_numpy(x).to(dev)
+        a = torch.empty((w.M, w.K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((w.M, -(-w.K // 128)), dtype=torch.float32, device=dev)
+        A = SA = None
+    else:
+        A, SA, Bc, SB = w.inputs()
+        a, sa = torch.from_numpy(A).to(dev), torch.from_numpy(SA).to(dev)
+    b, sb = torch.from_numpy(Bc).to(dev), torch.from_numpy(SB).to(dev)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    cfg = tg.tgemm_fp8_select_config(w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
+                                     c.data_ptr(), c.stride(0))
+    cfg_name = tg.tgemm_fp8_config_desc(cfg)["name"] if cfg >= 0 else "generic"
+    eprint(f"{torch.cuda.get_device_name(dev)}; {tg.tgemm_version()}; fp8 workload {w.name} "
+           f"{w.M}x{w.N}x{w.K} relu={w.relu} linear={w.linear}; config {cfg_name}")
+
+    def step():
+        if w.linear:
+            tg.quant_fp8_block(xd, 1, a, sa, stream=stream)
+        tg.gemm_fp8_block(a, sa, b, sb, c, relu=w.relu, stream=stream)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    value = w.flop * args.steps / wall / 1e12
+    achieved = w.flop / (step_ms * 1e-3) / 1e12
+    eprint(f"wall {wall * 1e3:.2f} ms for {args.steps} steps -> {value:.1f} TFLOP/s; event mean "
+           f"{step_ms * 1e3:.2f} us/step -> {achieved:.1f} TFLOP/s ({100 * achieved / FP8_PEAK_TFLOPS:.1f} % of "
+           f"{FP8_PEAK_TFLOPS:.1f})")
+    out = {
+        "metric": f"fp8 E4M3 block-scaled GEMM TFLOP/s at {w.M}x{w.N}x{w.K} on 1 MI355X; % of dense fp8 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "relu": w.relu, "linear": w.linear,
+                   "inputs": (f"x fp16 N(0,1), weight E4M3 codes + 128x128 scales, seed {w.seed}" if w.linear else
+                              f"E4M3 codes + 1x128 / 128x128 float32 scales, seed {w.seed}"),
+                   "accumulate": "fp32 per 128-wide scale block", "kernel_config": cfg_name,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * achieved / FP8_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(FP8_PEAK_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(w.name, cfg_name), "kernel_us": round(step_ms * 1e3, 3),
+                     "kernel_source_hash": kernel_source_hash()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and not w.linear:
+        out["cpu_baseline"] = cpu_baseline_fp8(A, SA, Bc, SB, w.relu, c.cpu().numpy().view(np.uint16),
+                                               args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +243,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         eprint("bench.py needs a GPU")
         return 1
+    if args.workload in W.FP8_WORKLOADS:
+        return bench_fp8(args, W, tg, torch, np)
     w = W.by_name(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

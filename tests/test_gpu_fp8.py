@@ -216,3 +216,35 @@ def test_workload_linear_sampled():
     rep = oracle.compare_fp8(y.cpu().numpy().view(np.uint16)[rows, cols], ref, E)
     log(f"fp8 linear: {rep}")
     assert rep["fails"] == 0, rep
+
+
+def test_block_sum_precision_under_cancellation():
+    """Products that cancel: every row of A and of B holds pairs (x, -x) against (y, y), so
+    each block sums large products to a small exact value and the fp8 matrix instructions'
+    deviation (relative to the block's largest product) shows through the fp16 output.
+    Checks it against the tolerance's per-block allowance 2^-8 and reports the largest
+    deviation seen."""
+    rng = np.random.default_rng(950)
+    M, N, K = 256, 256, 1024
+    KB = K // BLOCK
+    big = rng.integers(0x60, 0x78, size=(M, K // 2)).astype(np.uint8)     # |a| in 2^5 .. 2^8
+    A = np.empty((M, K), np.uint8)
+    A[:, 0::2] = big
+    A[:, 1::2] = big | 0x80                                               # a_{2i+1} = -a_{2i}
+    small = rng.integers(0x08, 0x30, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, (M, K)) << 7).astype(np.uint8)
+    A[:, 0::16] = small[:, 0::16]                                         # every 8th pair: two small
+    A[:, 1::16] = small[:, 1::16]                                         # values, a small exact sum
+    B = rng.integers(0x30, 0x58, size=(N, K)).astype(np.uint8)
+    B[:, 1::2] = B[:, 0::2]                                               # b_{2i+1} = b_{2i}
+    SA = np.ones((M, KB), np.float32)
+    SB = np.ones((N // BLOCK, KB), np.float32)
+    c = _gemm(A, SA, B, SB, False)
+    ref = oracle.gemm_fp8(A, SA, B, SB, relu=False)
+    E = oracle.fp8_bound(A, SA, B, SB)
+    got = oracle.f16_decode(c)
+    dev = np.abs(got - ref) - 2.0 ** -11 * np.abs(ref)                    # beyond fp16 rounding
+    worst = float(np.max(dev / E))
+    log(f"fp8 block sums under cancellation: largest deviation {worst:.3g} of E (2^{np.log2(max(worst, 1e-30)):.1f}), "
+        f"allowance 2^-8")
+    rep = oracle.compare_fp8(c, ref, E)
+    assert rep["fails"] == 0, rep

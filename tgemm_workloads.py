@@ -217,6 +217,13 @@ class Fp8Workload:
     def flop(self) -> int:
         return 2 * self.M * self.N * self.K
 
+    @property
+    def compulsory_bytes(self) -> int:
+        """E4M3 operands (1 byte), float32 scales and the binary16 output, once each."""
+        KB = -(-self.K // FP8_BLOCK)
+        return (self.M * self.K + self.N * self.K + 2 * self.M * self.N
+                + 4 * (self.M * KB + -(-self.N // FP8_BLOCK) * KB))
+
     def inputs(self):
         if self.linear:
             return make_fp8_linear_inputs(self.M, self.N, self.K, self.seed)

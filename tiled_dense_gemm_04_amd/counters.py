@@ -101,14 +101,15 @@ def main():
     import tgemm_workloads as W
     from bench import kernel_source_hash
 
-    works = W.all_workloads()
+    works = W.all_workloads() + [fw for fw in W.FP8_WORKLOADS.values() if not fw.linear]
     if args.workloads:
         keep = set(args.workloads.split(","))
         works = [w for w in works if w.name in keep]
     hot = {}
     if args.measure_json:
         with open(args.measure_json) as f:
-            for r in json.load(f)["results"]:
+            mj = json.load(f)
+            for r in mj["results"] + (mj.get("fp8") or []):
                 hot[r["workload"]] = r["hot"]["median_us"]
 
     out = os.path.abspath(args.out_dir)  # the passes run from /tmp
@@ -136,7 +137,7 @@ def main():
         fetch = median_counter(d_f, "gemm", "FETCH_SIZE") * f_scale * 1024
         write = median_counter(d_w, "gemm", "WRITE_SIZE") * w_scale * 1024
         cycles = c["GRBM_GUI_ACTIVE"] / NUM_XCD
-        comp = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
+        comp = getattr(w, "compulsory_bytes", 2 * (w.M * w.K + w.K * w.N + w.M * w.N))
         row = {
             "workload": w.name, "config": name, "kernel_source_hash": src_hash,
             "mfma_busy_pct": 100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(cycles * NUM_SIMD, 1),

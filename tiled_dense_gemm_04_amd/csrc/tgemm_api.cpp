@@ -290,6 +290,11 @@ int fp8_run(int cfg, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
   g.K = (int)K;
   g.KB = (int)tgemm::ceil_div(K, tgemm::kFp8Block);
   g.relu = relu != 0;
+#ifdef TGEMM_STAMPS
+  g.stamps = tgemm::stamps_table();
+#else
+  g.stamps = nullptr;
+#endif
   if (cfg == kFp8Generic) {
     if (tgemm::ceil_div(M, 16) * tgemm::ceil_div(N, 16) >= ((int64_t)1 << 32)) return TGEMM_EINVAL_DIM;
     g.tiles_m = g.tiles_n = 0;

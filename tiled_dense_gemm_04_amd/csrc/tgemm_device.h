@@ -41,6 +41,51 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
 
+// Per-workgroup timestamps, compiled in only for the instrumented build (TGEMM_STAMPS) and
+// empty otherwise; finish() writes them to the table it is given (the library's one table,
+// defined next to the binary16 kernels and handed to the other kernels as an argument). Words per workgroup: wall clock (s_memrealtime, 100 MHz) at kernel
+// start, main-loop start, main-loop end and after every wave's stores completed; shader
+// clock ticks (s_memtime, which counts at the current shader clock) from kernel start to
+// main-loop end; main-loop iterations; threads per workgroup; 1 (written). Ticks divided
+// by wall time is the shader clock the workgroup ran at.
+#ifdef TGEMM_STAMPS
+struct WgClock {
+  unsigned long long rt0, ct0, rt1, rt2, ct2;
+  __device__ void start() {
+    rt0 = __builtin_amdgcn_s_memrealtime();
+    ct0 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ void loop_begin() { rt1 = __builtin_amdgcn_s_memrealtime(); }
+  __device__ void loop_end() {
+    rt2 = __builtin_amdgcn_s_memrealtime();
+    ct2 = __builtin_amdgcn_s_memtime();
+  }
+  // Called by every thread of the workgroup, at its very end.
+  __device__ void finish(int iterations, unsigned long long* table) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (table != nullptr && threadIdx.x == 0 && blockIdx.x < (unsigned)kStampWorkgroups) {
+      unsigned long long* o = &table[(size_t)blockIdx.x * kStampWords];
+      o[0] = rt0;
+      o[1] = rt1;
+      o[2] = rt2;
+      o[3] = __builtin_amdgcn_s_memrealtime();
+      o[4] = ct2 - ct0;
+      o[5] = (unsigned long long)iterations;
+      o[6] = blockDim.x;
+      o[7] = 1;
+    }
+  }
+};
+#else
+struct WgClock {
+  __device__ void start() {}
+  __device__ void loop_begin() {}
+  __device__ void loop_end() {}
+  __device__ void finish(int, unsigned long long*) {}
+};
+#endif
+
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor: base address, stride 0, range in bytes, gfx9 word 3. All inputs
@@ -100,7 +145,7 @@ __host__ __device__ constexpr int swz_a(int r) {
 template <int BK, int MF>
 __host__ __device__ constexpr int swz_a_mf(int r) {
   static_assert(MF == 32 || BK == 32 || BK == 64, "16x16 fragments are laid out for BK = 32 or 64");
-  return MF == 16 ? (r >> 1) % (BK / 8) : swz_a<BK>(r);
+  return MF == 16 ? (r >> 1) & (BK / 8 - 1) : swz_a<BK>(r);
 }
 // B stage: BK rows (k) x BN halves (n), row k at byte k*BN*2 (a multiple of 256 bytes);
 // logical chunk c of row k is stored at chunk c ^ swz_b(k). A transposed read by 32 lanes

@@ -104,6 +104,8 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
 // C 16-byte aligned, ldc and N multiples of 8; (BM - 1) * KB * 4 < 2^31.
 template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g) {
+  WgClock clk;
+  clk.start();
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -204,19 +206,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
     const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Software pipeline over the wave tile's FM x FN MFMA tiles, in order t = fm * FN + fn:
+    // MFMA t writes result register t % 3, and the block sum of MFMA t-2 (issued two MFMAs
+    // earlier, so complete) is folded into its accumulator right after, so no MFMA waits for
+    // a result and the folds run on the VALU under later MFMAs. The A fragment of row fm+1
+    // is read at the start of row fm (double-buffered).
+    constexpr int T = FM * FN;
+    int8v fa[2];
+    float4v p[3];
+    fa[0] = cat_frag(opa.frag(As, 0, 0), opa.frag(As, 0, 1));
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int8v fa = cat_frag(opa.frag(As, fm, 0), opa.frag(As, fm, 1));
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const float4v p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa, zero, 0, 0, 0, 0, 0, 0);
-        acc[fm][fn] += sc[fm] * p;
+    for (int t = 0; t < T + 2; ++t) {
+      if (t < T) {
+        const int fm = t / FN, fn = t % FN;
+        if (fn == 0 && fm + 1 < FM) fa[(fm + 1) & 1] = cat_frag(opa.frag(As, fm + 1, 0), opa.frag(As, fm + 1, 1));
+        p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa[fm & 1], zero, 0, 0, 0, 0, 0, 0);
       }
+      if (t >= 2) {
+        const int u = t - 2;
+        acc[u / FN][u % FN] += sc[u / FN] * p[u % 3];
+      }
+    }
+    // Keep that order: one MFMA, then the four FMAs of the fold two MFMAs back.
+#pragma unroll
+    for (int t = 0; t < T + 2; ++t) {
+      if (t < T) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
   };
 
 #pragma unroll
   for (int t = 0; t < STAGES; ++t) copy_tile(t);
+  clk.loop_begin();
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmcnt<PT * (STAGES - 1)>();
     lds_barrier();
@@ -225,6 +246,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     copy_tile(kt + STAGES);
   }
   wait_vmcnt<0>();
+  clk.loop_end();
 
   // Epilogue: ReLU in float32, round to fp16, stage the wave's WTM x WTN sub-tile in its
   // own LDS region (the ring is free once every wave passes the barrier) and write it back
@@ -265,6 +287,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     const int m = wm * WTM + r, n = wn * WTN + 8 * c;
     if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
   }
+  clk.finish(nk, g.stamps);
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
@@ -298,47 +321,62 @@ __global__ __launch_bounds__(256) void gemm_fp8_block_generic(Fp8Args g) {
 
 // ------------------------------------------------------------------------------------
 // Block quantizer, 1 x 128 blocks (activations): a group of 16 lanes per block, 8
-// elements per lane. Scale s = amax / 448 in float32 (1 for an all-zero block), codes
-// f32_to_e4m3(x / s) with IEEE float32 division. All 64 lanes of a wave take part in the
-// shuffles; lanes of groups past the last block only skip their loads and stores.
+// elements per lane; a workgroup covers 16 * QNB consecutive blocks, group g taking blocks
+// g, g + 16, ... so that each of its QNB loads (issued before any arithmetic) covers 16
+// consecutive blocks across the workgroup. Scale s = amax / 448 in float32 (1 for an
+// all-zero block), codes f32_to_e4m3(x / s) with IEEE float32 division. All 64 lanes of a
+// wave take part in the shuffles; lanes of groups past the last block skip their loads
+// and stores.
+constexpr int QNB = 1;
 template <bool VEC>
 __global__ __launch_bounds__(256) void quant_fp8_rows(QuantArgs q) {
-  const int64_t blk = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
   const int sub = threadIdx.x % 16;
-  const bool active = blk < (int64_t)q.R * q.KB;
-  const int64_t row = active ? blk / q.KB : 0;
-  const int kb = active ? (int)(blk % q.KB) : 0;
-  const int k = kb * kFp8Block + 8 * sub;
-  float x[8];
-  if (VEC) {
-    half8 h = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (active && k < q.K) h = *(const half8*)(q.X + row * q.ldx + k);
+  const int64_t nblk = (int64_t)q.R * q.KB;
+  const int64_t base = (int64_t)blockIdx.x * 16 * QNB + threadIdx.x / 16;
+  float x[QNB][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
-  } else {
+  for (int i = 0; i < QNB; ++i) {
+    const int64_t blk = base + 16 * i;
+    const bool active = blk < nblk;
+    const int64_t row = active ? blk / q.KB : 0;
+    const int k = (active ? (int)(blk % q.KB) : 0) * kFp8Block + 8 * sub;
+    if (VEC) {
+      half8 h = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (active && k < q.K) h = *(const half8*)(q.X + row * q.ldx + k);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (active && k + e < q.K) ? (float)q.X[row * q.ldx + k + e] : 0.0f;
-  }
-  float m = 0.0f;
+      for (int e = 0; e < 8; ++e) x[i][e] = (float)h[e];
+    } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-#pragma unroll
-  for (int w = 1; w < 16; w <<= 1) m = fmaxf(m, __shfl_xor(m, w, 16));
-  const float s = m > 0.0f ? m / 448.0f : 1.0f;
-  if (!active) return;
-  if (VEC) {
-    if (k < q.K) {
-      uchar8 c;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = (unsigned char)f32_to_e4m3(x[e] / s);
-      *(uchar8*)(q.Q + row * q.ldq + k) = c;
+      for (int e = 0; e < 8; ++e) x[i][e] = (active && k + e < q.K) ? (float)q.X[row * q.ldx + k + e] : 0.0f;
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (k + e < q.K) q.Q[row * q.ldq + k + e] = (uint8_t)f32_to_e4m3(x[e] / s);
   }
-  if (sub == 0) q.S[row * q.KB + kb] = s;
+#pragma unroll
+  for (int i = 0; i < QNB; ++i) {
+    const int64_t blk = base + 16 * i;
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[i][e]));
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1) m = fmaxf(m, __shfl_xor(m, w, 16));
+    const float s = m > 0.0f ? m / 448.0f : 1.0f;
+    if (blk >= nblk) continue;
+    const int64_t row = blk / q.KB;
+    const int kb = (int)(blk % q.KB);
+    const int k = kb * kFp8Block + 8 * sub;
+    if (VEC) {
+      if (k < q.K) {
+        uchar8 c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = (unsigned char)f32_to_e4m3(x[i][e] / s);
+        *(uchar8*)(q.Q + row * q.ldq + k) = c;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k + e < q.K) q.Q[row * q.ldq + k + e] = (uint8_t)f32_to_e4m3(x[i][e] / s);
+    }
+    if (sub == 0) q.S[row * q.KB + kb] = s;
+  }
 }
 
 // Block quantizer, 128 x 128 blocks (weights): one workgroup of 256 threads per block,
@@ -447,7 +485,7 @@ hipError_t launch_fp8_generic(const Fp8Args& g, hipStream_t s) {
 hipError_t launch_quant_fp8(const QuantArgs& q, bool vec, hipStream_t s) {
   if (q.block_rows == 1) {
     const int64_t blocks = (int64_t)q.R * q.KB;
-    const dim3 grid((unsigned)((blocks + 15) / 16));
+    const dim3 grid((unsigned)((blocks + 16 * QNB - 1) / (16 * QNB)));
     if (vec)
       hipLaunchKernelGGL(quant_fp8_rows<true>, grid, dim3(256), 0, s, q);
     else

@@ -116,6 +116,7 @@ struct Fp8Args {
   int M, N, K, KB;        // KB = ceil(K / 128)
   int relu;
   int tiles_m, tiles_n;
+  unsigned long long* stamps;  // instrumented build: the stamp table (else nullptr)
 };
 // fp8 tile configs (index order is tooling ABI: gemm_fp8_block_cfg, sweeps).
 struct Fp8Config {
@@ -155,6 +156,7 @@ constexpr int kStampWorkgroups = 4096, kStampWords = 8;
 #ifdef TGEMM_STAMPS
 hipError_t stamps_read(unsigned long long* host, int64_t words);
 hipError_t stamps_clear();
+unsigned long long* stamps_table();  // device address of the table on the current device
 #endif
 
 }  // namespace tgemm

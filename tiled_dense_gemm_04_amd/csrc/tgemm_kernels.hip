@@ -23,49 +23,11 @@
 namespace tgemm {
 namespace {
 
-// Per-workgroup timestamps, compiled in only for the instrumented build (TGEMM_STAMPS) and
-// empty otherwise. Words per workgroup: wall clock (s_memrealtime, 100 MHz) at kernel
-// start, main-loop start, main-loop end and after every wave's stores completed; shader
-// clock ticks (s_memtime, which counts at the current shader clock) from kernel start to
-// main-loop end; main-loop iterations; threads per workgroup; 1 (written). Ticks divided
-// by wall time is the shader clock the workgroup ran at.
 #ifdef TGEMM_STAMPS
 __device__ unsigned long long g_stamps[kStampWorkgroups * kStampWords];
-struct WgClock {
-  unsigned long long rt0, ct0, rt1, rt2, ct2;
-  __device__ void start() {
-    rt0 = __builtin_amdgcn_s_memrealtime();
-    ct0 = __builtin_amdgcn_s_memtime();
-  }
-  __device__ void loop_begin() { rt1 = __builtin_amdgcn_s_memrealtime(); }
-  __device__ void loop_end() {
-    rt2 = __builtin_amdgcn_s_memrealtime();
-    ct2 = __builtin_amdgcn_s_memtime();
-  }
-  // Called by every thread of the workgroup, at its very end.
-  __device__ void finish(int iterations) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kStampWorkgroups) {
-      unsigned long long* o = &g_stamps[(size_t)blockIdx.x * kStampWords];
-      o[0] = rt0;
-      o[1] = rt1;
-      o[2] = rt2;
-      o[3] = __builtin_amdgcn_s_memrealtime();
-      o[4] = ct2 - ct0;
-      o[5] = (unsigned long long)iterations;
-      o[6] = blockDim.x;
-      o[7] = 1;
-    }
-  }
-};
+#define TG_STAMP_TABLE g_stamps
 #else
-struct WgClock {
-  __device__ void start() {}
-  __device__ void loop_begin() {}
-  __device__ void loop_end() {}
-  __device__ void finish(int) {}
-};
+#define TG_STAMP_TABLE nullptr
 #endif
 
 
@@ -268,7 +230,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
       }
     }
   }
-  clk.finish(nk);
+  clk.finish(nk, TG_STAMP_TABLE);
 }
 
 // ------------------------------------------------------------------------------------
@@ -511,7 +473,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
       }
     }
   }
-  clk.finish(nk);
+  clk.finish(nk, TG_STAMP_TABLE);
 }
 
 // ------------------------------------------------------------------------------------
@@ -751,7 +713,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
     __syncthreads();
     const int last = *(const TG_LDS int*)smem;
     if (!last) {
-      clk.finish(nloc);
+      clk.finish(nloc, TG_STAMP_TABLE);
       return;
     }
 #pragma unroll
@@ -827,7 +789,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
     const int m = wm * WTM + r, n = wn * WTN + 8 * c;
     if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
   }
-  clk.finish(nloc);
+  clk.finish(nloc, TG_STAMP_TABLE);
 }
 
 
@@ -971,7 +933,7 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe(int iters, float* ou
 #pragma unroll
   for (int j = 0; j < kProbeMfmaPerIter; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
   out[tid] = sum;
-  clk.finish(iters);
+  clk.finish(iters, TG_STAMP_TABLE);
 }
 
 // C[i, j] = +0 for i < M, j < N (the empty sum when K == 0).
@@ -1097,6 +1059,11 @@ hipError_t stamps_read(unsigned long long* host, int64_t words) {
   return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_stamps), (size_t)words * sizeof(unsigned long long), 0,
                              hipMemcpyDeviceToHost);
 }
+unsigned long long* stamps_table() {
+  void* p = nullptr;
+  return hipGetSymbolAddress(&p, HIP_SYMBOL(g_stamps)) == hipSuccess ? static_cast<unsigned long long*>(p) : nullptr;
+}
+
 hipError_t stamps_clear() {
   static const unsigned long long zeros[kStampWorkgroups * kStampWords] = {};
   return hipMemcpyToSymbol(HIP_SYMBOL(g_stamps), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);

@@ -43,6 +43,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+FP8_PEAK_TFLOPS = 256 * 8192 * 2.4e9 / 1e12   # dense fp8 MFMA peak (AMD: ~5.0 PFLOP/s)
+HBM_PEAK_GBS = 8000.0
 REALTIME_HZ = 100e6          # s_memrealtime
 CACHE_BYTES = 288 << 20      # cold sets must exceed this in total (Infinity Cache: 256 MiB)
 NUM_XCD = 8
@@ -283,6 +285,106 @@ def measure_grouped(torch, tg, w, stream, with_torch=True):
     return res
 
 
+def measure_fp8(torch, tg, w, stream, with_torch=True):
+    """One fp8 workload. Block-scaled GEMM (w.linear False): the default config and every
+    other fp8 config, hot. Linear step (w.linear True): the 1 x 128 quantizer alone
+    (against HBM bandwidth), the GEMM on the quantized x, and quantizer + GEMM together.
+    Context: torch._scaled_mm (hipBLASLt fp8, one scale per tensor) where it runs."""
+    M, N, K = w.M, w.N, w.K
+    KB = -(-K // 128)
+
+    def tf(us):
+        return w.flop / (us * 1e-6) / 1e12
+
+    res = {"workload": w.name, "M": M, "N": N, "K": K, "relu": w.relu, "flop": w.flop, "linear": w.linear}
+    if w.linear:
+        x, Wc, SW = w.inputs()
+        xd, wd, swd = torch.from_numpy(x).cuda(), torch.from_numpy(Wc).cuda(), torch.from_numpy(SW).cuda()
+        xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        sx = torch.empty((M, KB), dtype=torch.float32, device="cuda")
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        q = timed_trials(torch, stream, lambda i: tg.quant_fp8_block(xd, 1, xq, sx, stream=stream))
+        qbytes = 2 * M * K + M * K + 4 * M * KB
+        res["quant"] = {**q, "bytes": qbytes, "gbs": qbytes / (q["median_us"] * 1e-6) / 1e9}
+        res["quant"]["pct_of_hbm"] = 100 * res["quant"]["gbs"] / HBM_PEAK_GBS
+        a, sa, b, sb = xq, sx, wd, swd
+        lin = timed_trials(torch, stream, lambda i: (tg.quant_fp8_block(xd, 1, xq, sx, stream=stream),
+                                                     tg.gemm_fp8_block(xq, sx, wd, swd, c, relu=w.relu,
+                                                                       stream=stream)))
+        res["linear_total"] = {**lin, "tflops": tf(lin["median_us"])}
+        log(f"{w.name}: quant {q['median_us']:.2f} us ({res['quant']['gbs']:.0f} GB/s), "
+            f"quant + gemm {lin['median_us']:.2f} us")
+    else:
+        A, SA, B, SB = w.inputs()
+        a, sa = torch.from_numpy(A).cuda(), torch.from_numpy(SA).cuda()
+        b, sb = torch.from_numpy(B).cuda(), torch.from_numpy(SB).cuda()
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    cfg = tg.tgemm_fp8_select_config(M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), c.data_ptr(),
+                                     c.stride(0))
+    res["config"] = tg.tgemm_fp8_config_desc(cfg)["name"] if cfg >= 0 else "generic"
+    h = timed_trials(torch, stream, lambda i: tg.gemm_fp8_block(a, sa, b, sb, c, relu=w.relu, stream=stream))
+    res["hot"] = {**h, "tflops": tf(h["median_us"]), "pct_of_peak": 100 * tf(h["median_us"]) / FP8_PEAK_TFLOPS}
+    log(f"{w.name}: gemm_fp8_block {h['median_us']:.2f} us ({res['hot']['tflops']:.1f} TFLOP/s) [{res['config']}]")
+    if cfg >= 0:
+        S = tg.stamps_lib()
+        timed_trials(torch, stream, lambda i: tg.gemm_fp8_block(a, sa, b, sb, c, relu=w.relu, stream=stream,
+                                                                library=S), trials=1, warm=3)
+        d = tg.tgemm_fp8_config_desc(cfg)
+        res["phases"] = phases(tg.tgemm_stamps_read(-(-M // d["block_m"]) * -(-N // d["block_n"])))
+        if res["phases"]:
+            ph = res["phases"]
+            log(f"{w.name}: phases prologue {ph['prologue_us']:.2f} loop {ph['loop_us']:.2f} "
+                f"epilogue {ph['epilogue_us']:.2f} us, clock {ph['shader_clock_ghz']:.3f} GHz, "
+                f"{ph['ns_per_iteration']:.0f} ns per k-tile")
+    res["per_config"] = {}
+    for idx in range(tg.tgemm_fp8_num_configs()):
+        if idx == cfg:
+            continue
+        t = timed_trials(torch, stream, lambda i, idx=idx: tg.gemm_fp8_block(a, sa, b, sb, c, relu=w.relu,
+                                                                             stream=stream, cfg=idx), trials=5)
+        res["per_config"][tg.tgemm_fp8_config_desc(idx)["name"]] = t["median_us"]
+    if with_torch and not w.linear:
+        try:
+            f8 = torch.float8_e4m3fn
+            a8, bt8 = a.view(f8), b.view(f8).t()
+            one = torch.ones((), dtype=torch.float32, device="cuda")
+            with torch.cuda.stream(stream):
+                th = timed_trials(torch, stream, lambda i: torch._scaled_mm(a8, bt8, one, one, out_dtype=torch.float16))
+            res["torch_scaled_mm"] = {**th, "tflops": tf(th["median_us"]), "note": "context only; one scale per tensor"}
+        except Exception as e:  # not every torch build runs fp8 GEMMs on this device
+            res["torch_scaled_mm"] = {"error": f"{type(e).__name__}: {e}"[:160]}
+    torch.cuda.empty_cache()
+    return res
+
+
+def fp8_markdown(fp8) -> str:
+    L = ["", f"fp8 (E4M3) block-scaled path (gemm_fp8_block; peak = dense fp8 MFMA {FP8_PEAK_TFLOPS:.1f} TFLOP/s):",
+         "", "| workload | config | hot us (min-max) | TFLOP/s | % fp8 peak | other configs us | "
+         "quant_fp8_block us (GB/s, % of 8 TB/s) | quant + GEMM us | torch._scaled_mm us (context) |",
+         "|---|---|---|---|---|---|---|---|---|"]
+    for r in fp8:
+        h = r["hot"]
+        others = ", ".join(f"{k} {v:.2f}" for k, v in r.get("per_config", {}).items()) or "-"
+        q = r.get("quant")
+        qs = f"{q['median_us']:.2f} ({q['gbs']:.0f}, {q['pct_of_hbm']:.1f} %)" if q else "-"
+        lt = f"{r['linear_total']['median_us']:.2f}" if "linear_total" in r else "-"
+        ts = r.get("torch_scaled_mm")
+        tss = "-" if not ts else (f"{ts['median_us']:.2f}" if "median_us" in ts else ts["error"])
+        L.append(f"| {r['workload']} ({r['M']}x{r['N']}x{r['K']}) | {r['config']} | {h['median_us']:.2f} "
+                 f"({h['min_us']:.2f}-{h['max_us']:.2f}) | {h['tflops']:.1f} | {h['pct_of_peak']:.1f} | {others} | "
+                 f"{qs} | {lt} | {tss} |")
+    L += ["", "Phases of gemm_fp8_block (instrumented build, means over workgroups):", "",
+          "| workload | workgroups | prologue us | main loop us (max) | epilogue us | launch span us | "
+          "ns per k-tile (128 k) | shader clock GHz |", "|---|---|---|---|---|---|---|---|"]
+    for r in fp8:
+        ph = r.get("phases")
+        if ph:
+            L.append(f"| {r['workload']} | {ph['workgroups']} | {ph['prologue_us']:.2f} | {ph['loop_us']:.2f} "
+                     f"({ph['loop_us_max']:.2f}) | {ph['epilogue_us']:.2f} | {ph['span_us']:.2f} | "
+                     f"{ph['ns_per_iteration']:.0f} | {ph['shader_clock_ghz']:.3f} |")
+    return "\n".join(L) + "\n"
+
+
 def markdown(results, probe, host, grouped=None) -> str:
     L = []
     L.append(f"Device: {host['device']}; {host['library']}; torch {host['torch']}.")
@@ -380,11 +482,15 @@ def main():
     grouped = [measure_grouped(torch, tg, gw, stream, with_torch=not args.no_torch)
                for gw in W.GROUPED_WORKLOADS.values()
                if not args.workloads or gw.name in set(args.workloads.split(","))]
-    md = markdown(results, probe, host, grouped)
+    fp8 = [measure_fp8(torch, tg, fw, stream, with_torch=not args.no_torch)
+           for fw in W.FP8_WORKLOADS.values()
+           if not args.workloads or fw.name in set(args.workloads.split(","))]
+    md = markdown(results, probe, host, grouped) + (fp8_markdown(fp8) if fp8 else "")
     print(md)
     if args.json:
         with open(args.json, "w") as f:
-            json.dump({"host": host, "probe": probe, "results": results, "grouped": grouped}, f, indent=1)
+            json.dump({"host": host, "probe": probe, "results": results, "grouped": grouped, "fp8": fp8}, f,
+                      indent=1)
     if args.md:
         with open(args.md, "w") as f:
             f.write(md)
