@@ -70,7 +70,7 @@ SHAPES = [(256, 256, 128), (300, 264, 1008), (520, 392, 272), (1, 8, 16), (257, 
 ODD = [(17, 23, 29), (65, 63, 129), (1, 1, 1), (130, 7, 250), (40, 200, 100)]
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, tg.FP8_GENERIC])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, tg.FP8_GENERIC])
 def test_each_config(cfg):
     if cfg != tg.FP8_GENERIC and cfg >= tg.tgemm_fp8_num_configs():
         pytest.skip("config not in table")

@@ -331,7 +331,7 @@ def test_fp8_config_table():
 def test_fp8_select():
     s = tg.tgemm_fp8_select_config
     assert s(4096, 4096, 4096) == 0                       # 256 x 256 tiles
-    assert s(16384, 512, 4096) == 2                       # 256 x 128 tiles fill the GPU
+    assert s(16384, 512, 4096) == 3                       # 256 x 128 tiles fill the GPU
     assert s(1024, 1024, 1024) == 1                       # 128 x 128
     assert s(0, 8, 16) == tg.SELECT_NOOP and s(8, 8, 0) == tg.SELECT_ZERO_FILL
     # generic kernel: K or ld not a multiple of 16, N or ldc not a multiple of 8, unaligned

@@ -221,7 +221,9 @@ const tgemm::Fp8Config& fp8_row(int idx) {
   return tgemm::fp8_config_table(&n)[idx];
 }
 constexpr int kFp8Generic = TGEMM_FP8_GENERIC;  // the generic kernel (-102)
-constexpr int kFp8Cfg256 = 0, kFp8Cfg128 = 1, kFp8Cfg256x128 = 2;
+// 0: 256 x 256; 1: 128 x 128; 2: 256 x 128 (single fragment set, kept for the sweep);
+// 3: 256 x 128 with double-buffered fragments (92 us against 103 us for 2 at 4096^3).
+constexpr int kFp8Cfg256 = 0, kFp8Cfg128 = 1, kFp8Cfg256x128 = 3;
 
 int fp8_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const float* SA,
                  const void* B, int64_t ldb, const float* SB, const void* C, int64_t ldc) {

@@ -100,9 +100,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
 // wait for this thread's copies of tile kt, barrier (everyone's have landed), MFMAs +
 // folds of tile kt, barrier (every wave is done with the slot), copies of tile
 // kt+STAGES into it (past the last tile: empty ranges, zeros, never read).
+// DB (double-buffered fragments, STAGES >= 3): every fragment of a k-tile (A, B and the
+// scales) is read into registers at once, one k-tile ahead: iteration kt waits for tile
+// kt+1, passes one barrier (after which the slot of tile kt, read in the iteration
+// before, is free), refills that slot with tile kt+STAGES, reads tile kt+1's fragments
+// into the second register set and runs tile kt's MFMAs and folds from the first. Reads
+// of the next tile then overlap the MFMAs of this one; this needs a wave tile small
+// enough for two fragment sets (64 x 64).
 // Requirements (checked by the host): A, B 16-byte aligned, lda, ldb, K multiples of 16;
 // C 16-byte aligned, ldc and N multiples of 8; (BM - 1) * KB * 4 < 2^31.
-template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD>
+template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD, bool DB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g) {
   WgClock clk;
   clk.start();
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile of 16 x 16 MFMA tiles");
   static_assert(kFp8Block % WTN == 0, "a wave's columns lie in one scale block of B");
   static_assert(SB_WAVE < NW && BN / kFp8Block <= 64, "a spare wave fetches the scales of B");
-  static_assert(STAGES >= 2 && PT * STAGES < 64, "ring depth / vmcnt budget");
+  static_assert(STAGES >= (DB ? 3 : 2) && PT * STAGES < 64, "ring depth / vmcnt budget");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const a_lds = smem;
@@ -194,40 +201,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
 
   // Operands go in as (B fragment, A fragment): a lane's result holds four consecutive
   // output columns (16 * fn + 4 * lkg ..) of one row (16 * fm + lrow) of the wave tile.
-  auto compute = [&](int slot) {
-    const char* const As = a_lds + slot * A_BYTES;
-    const char* const Bs = b_lds + slot * B_BYTES;
-    const TG_LDS float* const S = (const TG_LDS float*)(s_lds + slot * S_BYTES);
-    const float sb = S[sb_index];
-    float sc[FM];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) sc[fm] = S[wm * WTM + fm * 16 + lrow] * sb;
-    int8v fb[FN];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
-    const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    // Software pipeline over the wave tile's FM x FN MFMA tiles, in order t = fm * FN + fn:
-    // MFMA t writes result register t % 3, and the block sum of MFMA t-2 (issued two MFMAs
-    // earlier, so complete) is folded into its accumulator right after, so no MFMA waits for
-    // a result and the folds run on the VALU under later MFMAs. The A fragment of row fm+1
-    // is read at the start of row fm (double-buffered).
-    constexpr int T = FM * FN;
-    int8v fa[2];
-    float4v p[3];
-    fa[0] = cat_frag(opa.frag(As, 0, 0), opa.frag(As, 0, 1));
-#pragma unroll
-    for (int t = 0; t < T + 2; ++t) {
-      if (t < T) {
-        const int fm = t / FN, fn = t % FN;
-        if (fn == 0 && fm + 1 < FM) fa[(fm + 1) & 1] = cat_frag(opa.frag(As, fm + 1, 0), opa.frag(As, fm + 1, 1));
-        p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa[fm & 1], zero, 0, 0, 0, 0, 0, 0);
-      }
-      if (t >= 2) {
-        const int u = t - 2;
-        acc[u / FN][u % FN] += sc[u / FN] * p[u % 3];
-      }
-    }
-    // Keep that order: one MFMA, then the four FMAs of the fold two MFMAs back.
+  // MFMA t (t = fm * FN + fn) writes result register t % 3, and the block sum of MFMA t-2
+  // (issued two MFMAs earlier, so complete) is folded into its accumulator right after,
+  // so no MFMA waits for a result and the folds run on the VALU under later MFMAs.
+  constexpr int T = FM * FN;
+  const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto fold_order = [&]() {  // keep that order: one MFMA, then the fold two MFMAs back
 #pragma unroll
     for (int t = 0; t < T + 2; ++t) {
       if (t < T) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -235,18 +214,102 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     }
   };
 
+  if constexpr (!DB) {
+    auto compute = [&](int slot) {
+      const char* const As = a_lds + slot * A_BYTES;
+      const char* const Bs = b_lds + slot * B_BYTES;
+      const TG_LDS float* const S = (const TG_LDS float*)(s_lds + slot * S_BYTES);
+      const float sb = S[sb_index];
+      float sc[FM];
 #pragma unroll
-  for (int t = 0; t < STAGES; ++t) copy_tile(t);
-  clk.loop_begin();
-  for (int kt = 0; kt < nk; ++kt) {
+      for (int fm = 0; fm < FM; ++fm) sc[fm] = S[wm * WTM + fm * 16 + lrow] * sb;
+      int8v fb[FN];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
+      // The A fragment of row fm+1 is read at the start of row fm (double-buffered).
+      int8v fa[2];
+      float4v p[3];
+      fa[0] = cat_frag(opa.frag(As, 0, 0), opa.frag(As, 0, 1));
+#pragma unroll
+      for (int t = 0; t < T + 2; ++t) {
+        if (t < T) {
+          const int fm = t / FN, fn = t % FN;
+          if (fn == 0 && fm + 1 < FM) fa[(fm + 1) & 1] = cat_frag(opa.frag(As, fm + 1, 0), opa.frag(As, fm + 1, 1));
+          p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa[fm & 1], zero, 0, 0, 0, 0, 0, 0);
+        }
+        if (t >= 2) {
+          const int u = t - 2;
+          acc[u / FN][u % FN] += sc[u / FN] * p[u % 3];
+        }
+      }
+      fold_order();
+    };
+
+#pragma unroll
+    for (int t = 0; t < STAGES; ++t) copy_tile(t);
+    clk.loop_begin();
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<PT * (STAGES - 1)>();
+      lds_barrier();
+      compute(kt % STAGES);
+      lds_barrier();
+      copy_tile(kt + STAGES);
+    }
+    wait_vmcnt<0>();
+    clk.loop_end();
+  } else {
+    struct Frags {
+      int8v a[FM], b[FN];
+      float sa[FM], sb;
+    };
+    auto read_frags = [&](int slot, Frags& f) {
+      const char* const As = a_lds + slot * A_BYTES;
+      const char* const Bs = b_lds + slot * B_BYTES;
+      const TG_LDS float* const S = (const TG_LDS float*)(s_lds + slot * S_BYTES);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) f.b[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) f.a[fm] = cat_frag(opa.frag(As, fm, 0), opa.frag(As, fm, 1));
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) f.sa[fm] = S[wm * WTM + fm * 16 + lrow];
+      f.sb = S[sb_index];
+    };
+    auto mma_frags = [&](const Frags& f) {
+      float4v p[3];
+#pragma unroll
+      for (int t = 0; t < T + 2; ++t) {
+        if (t < T)
+          p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[t % FN], f.a[t / FN], zero, 0, 0, 0, 0, 0, 0);
+        if (t >= 2) {
+          const int u = t - 2;
+          acc[u / FN][u % FN] += (f.sa[u / FN] * f.sb) * p[u % 3];
+        }
+      }
+    };
+
+#pragma unroll
+    for (int t = 0; t < STAGES; ++t) copy_tile(t);
     wait_vmcnt<PT * (STAGES - 1)>();
     lds_barrier();
-    compute(kt % STAGES);
-    lds_barrier();
-    copy_tile(kt + STAGES);
+    Frags f0, f1;
+    read_frags(0, f0);
+    clk.loop_begin();
+    auto iteration = [&](int kt, const Frags& cur, Frags& nxt) {
+      wait_vmcnt<PT * (STAGES - 2)>();    // this thread's copies of tile kt+1 have landed
+      lds_barrier();                      // everyone's have; every wave is done with tile kt
+      copy_tile(kt + STAGES);             // into tile kt's slot (past the end: zeros)
+      read_frags((kt + 1) % STAGES, nxt); // past the last tile: a settled slot, unused
+      mma_frags(cur);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      iteration(kt, f0, f1);
+      iteration(kt + 1, f1, f0);
+    }
+    if (kt < nk) iteration(kt, f0, f1);
+    wait_vmcnt<0>();
+    clk.loop_end();
   }
-  wait_vmcnt<0>();
-  clk.loop_end();
 
   // Epilogue: ReLU in float32, round to fp16, stage the wave's WTM x WTN sub-tile in its
   // own LDS region (the ring is free once every wave passes the barrier) and write it back
@@ -435,11 +498,11 @@ __global__ __launch_bounds__(256) void quant_fp8_tiles(QuantArgs q) {
   if (t == 0) q.S[rb * q.KB + kb] = s;
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD>
+template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD, bool DB>
 hipError_t launch_fp8_cfg(const Fp8Args& g, hipStream_t s, int device) {
   constexpr int lds = fp8_lds_bytes<BM, BN, WM, WN, STAGES>();
   static_assert(lds <= 160 * 1024, "LDS");
-  auto kern = gemm_fp8_block_kernel<BM, BN, WM, WN, STAGES, PANEL, XCD>;
+  auto kern = gemm_fp8_block_kernel<BM, BN, WM, WN, STAGES, PANEL, XCD, DB>;
   static std::atomic<uint64_t> ready{0};
   const uint64_t bit = 1ull << (device & 63);
   if (!(ready.load(std::memory_order_acquire) & bit)) {
@@ -454,14 +517,16 @@ hipError_t launch_fp8_cfg(const Fp8Args& g, hipStream_t s, int device) {
 
 }  // namespace
 
-// fp8 configs: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD)
-#define TGEMM_FP8_CONFIGS(X)  \
-  X(256, 256, 2, 4, 2, 4, 1)  \
-  X(128, 128, 2, 2, 3, 4, 1)  \
-  X(256, 128, 4, 2, 3, 4, 1)
+// fp8 configs: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD, DB)
+#define TGEMM_FP8_CONFIGS(X)     \
+  X(256, 256, 2, 4, 2, 4, 1, 0)  \
+  X(128, 128, 2, 2, 3, 4, 1, 0)  \
+  X(256, 128, 4, 2, 3, 4, 1, 0)  \
+  X(256, 128, 4, 2, 3, 4, 1, 1)
 
-#define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X) {BM, BN, WM, WN, S, P, X, "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN},
-#define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X) launch_fp8_cfg<BM, BN, WM, WN, S, P, X>,
+#define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X, DB) \
+  {BM, BN, WM, WN, S, P, X, "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN "_db" #DB},
+#define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X, DB) launch_fp8_cfg<BM, BN, WM, WN, S, P, X, DB>,
 
 const Fp8Config* fp8_config_table(int* count) {
   static const Fp8Config table[] = {TGEMM_FP8_CONFIGS(TGEMM_FP8_ROW)};
