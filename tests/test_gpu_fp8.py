@@ -163,6 +163,34 @@ def test_quant_bitexact(block_rows):
             assert np.array_equal(q.cpu().numpy(), Qr), f"codes {R}x{K} block_rows={block_rows}"
 
 
+def test_quant_every_rounding_tie():
+    """A block whose maximum is 448 has scale 1, so x / s = x: rows holding every E4M3
+    midpoint (all exact in binary16) and its binary16 neighbours exercise every
+    round-to-nearest-even decision of the encoder, subnormals and the top binade included."""
+    torch = torch_cuda()
+    codes = np.arange(0x7F, dtype=np.uint8)
+    v = oracle.e4m3_decode(codes)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float16)
+    assert np.array_equal(mids.astype(np.float64), (v[:-1] + v[1:]) / 2)
+    vals = np.concatenate([mids, np.nextafter(mids, np.float16(0)), np.nextafter(mids, np.float16(1000)),
+                           v.astype(np.float16)]).astype(np.float16)
+    vals = np.concatenate([vals, -vals])
+    K = 128
+    rows = -(-len(vals) // (K - 1))
+    x = np.zeros((rows, K), np.float16)
+    x[:, 0] = np.float16(448.0)
+    flat = np.zeros(rows * (K - 1), np.float16)
+    flat[:len(vals)] = vals
+    x[:, 1:] = flat.reshape(rows, K - 1)
+    for block_rows in (1, 128):
+        Qr, Sr = oracle.quant_fp8(x, block_rows)
+        assert np.all(Sr == 1.0)
+        q, sc = tg.quant_fp8_block(to_dev(x), block_rows)
+        torch.cuda.synchronize()
+        assert np.array_equal(sc.cpu().numpy(), Sr)
+        assert np.array_equal(q.cpu().numpy(), Qr), f"block_rows={block_rows}"
+
+
 def test_fp8_linear_end_to_end():
     torch = torch_cuda()
     M, N, K = 257, 384, 1040

@@ -373,6 +373,8 @@ int quant_fp8_block(int64_t R, int64_t K, const void* X, int64_t ldx, int block_
   if (X == nullptr || Q == nullptr || scale == nullptr) return TGEMM_ENULL;
   if ((reinterpret_cast<uintptr_t>(X) & 1u) || (reinterpret_cast<uintptr_t>(scale) & 3u)) return TGEMM_EALIGN;
   const int64_t KB = tgemm::ceil_div(K, tgemm::kFp8Block);
+  // 1 x 128 blocks are numbered in 32 bits (2^32 blocks would be 1 TiB of input)
+  if (block_rows == 1 && R * KB >= ((int64_t)1 << 32)) return TGEMM_EINVAL_DIM;
   const int64_t groups = block_rows == 1 ? tgemm::ceil_div(R * KB, 16) : tgemm::ceil_div(R, 128) * KB;
   if (groups >= ((int64_t)1 << 31)) return TGEMM_EINVAL_DIM;
   int dev = -1;
