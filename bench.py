@@ -229,8 +229,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "libtgemm runs on one GPU; multi-GPU runs are not part of this "
-                                   "build (an output-row split needs no communication, see DESIGN.md)",
+        print(json.dumps({"error": "libtgemm runs on one GPU; there is no multi-GPU path (a GEMM split "
+                                   "by output rows needs no communication: one process per GPU, each "
+                                   "calling gemm_f16 on its own rows)",
                           "n_gpus": args.gpus}))
         return 2
 

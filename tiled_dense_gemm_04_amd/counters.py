@@ -20,7 +20,7 @@ Derived per launch (median over the GEMM dispatches):
 Writes profiles/traffic_<config>_<workload>.json (bench.py reports `roofline.traffic`
 from it while the kernel sources still hash the same) and a markdown summary.
 
-  python -m tiled_dense_gemm_04_amd.counters --out-dir gpurun_out/counters \\
+  python -m tiled_dense_gemm_04_amd.counters --out-dir OUT/counters \\
       [--workloads a,b] [--md profiles/counters_all_workloads.md] [--measure-json m.json]
 """
 from __future__ import annotations
