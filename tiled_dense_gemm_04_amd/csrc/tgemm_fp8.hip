@@ -195,45 +195,68 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   // MFMA t (t = fm * FN + fn) writes result register t % 3, and the block sum of MFMA t-2
   // (issued two MFMAs earlier, so complete) is folded into its accumulator right after,
   // so no MFMA waits for a result and the folds run on the VALU under later MFMAs.
-  constexpr int T = FM * FN;
   const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto fold_order = [&]() {  // keep that order: one MFMA, then the fold two MFMAs back
-#pragma unroll
-    for (int t = 0; t < T + 2; ++t) {
-      if (t < T) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (t >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
-  };
 
   if constexpr (!DB) {
-    auto compute = [&](int slot) {
+    // The last D rows of MFMA tiles of k-tile kt are issued after the barrier that frees
+    // its slot (their operands are already in registers): they keep the MFMA pipe busy
+    // while the wave waits for k-tile kt+1 and reads its first fragments, and their folds
+    // run after that barrier. The A fragment of row fm+PF is read at the start of row fm
+    // (a ring of PF+1 fragments; PF >= D leaves the deferred rows' fragments in the ring).
+    // sched_barrier(0) around each MFMA and each fold keeps exactly this order.
+    constexpr int D = FM >= 4 ? 3 : FM - 1;
+    constexpr int PF = D > 2 ? D : 2;
+    constexpr int TM = (FM - D) * FN;
+    int8v fb[FN];
+    int8v fa[PF + 1];
+    float sc[FM];
+    float4v ptail[D > 0 ? D * FN : 1];
+    float sctail[D > 0 ? D : 1];
+    auto main_part = [&](int slot, bool fold_prev) {
       const char* const As = a_lds + slot * A_BYTES;
       const char* const Bs = b_lds + slot * B_BYTES;
       const TG_LDS float* const S = (const TG_LDS float*)(s_lds + slot * S_BYTES);
       const float sb = S[sb_index];
-      float sc[FM];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) sc[fm] = S[wm * WTM + fm * 16 + lrow] * sb;
-      int8v fb[FN];
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
-      // The A fragment of row fm+1 is read at the start of row fm (double-buffered).
-      int8v fa[2];
-      float4v p[3];
-      fa[0] = cat_frag(opa.frag(As, 0, 0), opa.frag(As, 0, 1));
 #pragma unroll
-      for (int t = 0; t < T + 2; ++t) {
-        if (t < T) {
+      for (int r = 0; r < PF; ++r) fa[r] = cat_frag(opa.frag(As, r, 0), opa.frag(As, r, 1));
+      if (D > 0 && fold_prev) {  // the previous k-tile's deferred rows
+#pragma unroll
+        for (int r = 0; r < D; ++r)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) acc[FM - D + r][fn] += sctail[r] * ptail[r * FN + fn];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float4v p[3];
+#pragma unroll
+      for (int t = 0; t < TM + 2; ++t) {
+        if (t < TM) {
           const int fm = t / FN, fn = t % FN;
-          if (fn == 0 && fm + 1 < FM) fa[(fm + 1) & 1] = cat_frag(opa.frag(As, fm + 1, 0), opa.frag(As, fm + 1, 1));
-          p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa[fm & 1], zero, 0, 0, 0, 0, 0, 0);
+          if (fn == 0 && fm + PF < FM) fa[(fm + PF) % (PF + 1)] = cat_frag(opa.frag(As, fm + PF, 0), opa.frag(As, fm + PF, 1));
+          __builtin_amdgcn_sched_barrier(0);
+          p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa[fm % (PF + 1)], zero, 0, 0, 0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (t >= 2) {
           const int u = t - 2;
           acc[u / FN][u % FN] += sc[u / FN] * p[u % 3];
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      fold_order();
+    };
+    auto tail_part = [&]() {
+#pragma unroll
+      for (int r = 0; r < D; ++r) {
+        const int fm = FM - D + r;
+        sctail[r] = sc[fm];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          ptail[r * FN + fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[fn], fa[fm % (PF + 1)], zero, 0, 0, 0, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
 
 #pragma unroll
@@ -241,10 +264,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     clk.loop_begin();
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<PT * (STAGES - 1)>();
-      lds_barrier();
-      compute(kt % STAGES);
-      lds_barrier();
-      copy_tile(kt + STAGES);
+      lds_barrier();           // tile kt landed everywhere
+      main_part(kt % STAGES, kt > 0);
+      lds_barrier();           // every wave is done reading tile kt's slot
+      copy_tile(kt + STAGES);  // refill it (past the end: empty ranges, zeros)
+      if (D > 0) tail_part();
+    }
+    if (D > 0) {
+#pragma unroll
+      for (int r = 0; r < D; ++r)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[FM - D + r][fn] += sctail[r] * ptail[r * FN + fn];
     }
     wait_vmcnt<0>();
     clk.loop_end();
@@ -265,6 +295,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
       for (int fm = 0; fm < FM; ++fm) f.sa[fm] = S[wm * WTM + fm * 16 + lrow];
       f.sb = S[sb_index];
     };
+    constexpr int T = FM * FN;
     auto mma_frags = [&](const Frags& f) {
       float4v p[3];
 #pragma unroll
