@@ -358,7 +358,7 @@ int tgemm_fp8_config_desc(int idx, tgemm_config_info* out) {
   out->xcd_remap = c.xcd_remap;
   out->generic = 0;
   out->layouts = 1 << 1;  // A as given (M x K), B transposed (N x K)
-  out->lds_bytes = c.stages * ((c.bm + c.bn) * tgemm::kFp8Block + 256 * c.waves_m * c.waves_n);
+  out->lds_bytes = c.lds_bytes;
   std::strncpy(out->name, c.name, sizeof(out->name) - 1);
   return TGEMM_OK;
 }

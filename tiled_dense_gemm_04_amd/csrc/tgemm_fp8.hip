@@ -19,8 +19,11 @@
 //     buffer->LDS copies, range-checked edges and swizzle. A lane's 32-byte fp8 fragment is
 //     two 16-byte reads (k bytes 16g..16g+15 and 64+16g..64+16g+15 for lane group g); A
 //     and B use the same k order, which is all the dot product needs;
-//   * the per-row scales of A (and the per-column-block scales of B) ride the same
-//     buffer->LDS copies, one dword per lane, so every wait counts copies exactly;
+//   * the per-row scales of A ride the same buffer->LDS copies, one dword per lane per
+//     k-tile, so every wait counts copies exactly; each copy carries one slice of a group
+//     of G k-tiles' scales, so that G consecutive lanes read G consecutive floats of one
+//     row (a 1 x 128 block's scales sit KB floats apart in memory, one per row). B's block
+//     scales, one per wave and k-tile, come through the scalar path;
 //   * XCD-aware, panel-ordered tile order as in the binary16 kernels.
 #include "tgemm_device.h"
 
@@ -84,10 +87,9 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
 // Block-scaled GEMM, fast path. BM x BN tile, WM x WN waves (wave tile WTM x WTN of 16 x 16
 // MFMA tiles), k-tile = one 128-wide scale block, STAGES-deep LDS ring.
 // Per k-tile every thread issues PT copies: its share of the A and B tiles (16 bytes each)
-// and one dword of scales: waves whose 64 lanes cover rows of A fetch SA[row, kt]; the
-// first wave past the rows fetches SB[jb, kt] for the tile's column blocks; any other
-// wave fetches nothing (an out-of-range offset writes zeros to its own scratch dwords).
-// Schedule (tile t in slot t % STAGES): copies of tiles 0 .. STAGES-1; then for each kt:
+// and one dword of A row scales (a slice of a later scale group; waves with no lanes in a
+// slice write zeros to a spare 256 bytes). The first scale group is fetched before any
+// tile. Schedule (tile t in slot t % STAGES): copies of tiles 0 .. STAGES-1; then for each kt:
 // wait for this thread's copies of tile kt, barrier (everyone's have landed), MFMAs +
 // folds of tile kt, barrier (every wave is done with the slot), copies of tile
 // kt+STAGES into it (past the last tile: empty ranges, zeros, never read).
@@ -100,6 +102,13 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
 // enough for two fragment sets (64 x 64).
 // Requirements (checked by the host): A, B 16-byte aligned, lda, ldb, K multiples of 16;
 // C 16-byte aligned, ldc and N multiples of 8; (BM - 1) * KB * 4 < 2^31.
+// k-tiles per group of A row scales: 8 where three groups fit the LDS beside the operand
+// ring, else 4.
+template <int BM, int BN, int STAGES>
+constexpr int fp8_scale_group() {
+  return STAGES * (BM + BN) * kFp8Block + 3 * BM * 8 * 4 + 256 <= 160 * 1024 ? 8 : 4;
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD, bool DB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g) {
   WgClock clk;
@@ -110,14 +119,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   using OpA = PpOperand<BM, kF8Kh, 16, true, NW>;
   using OpB = PpOperand<BN, kF8Kh, 16, true, NW>;
   constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
-  constexpr int S_BYTES = 256 * NW;  // one dword per lane of every wave
+  constexpr int G = fp8_scale_group<BM, BN, STAGES>();  // k-tiles per A-scale group
+  constexpr int SG_BYTES = BM * G * 4;                   // one group: [BM rows][G]
+  constexpr int NG0 = BM * G / (64 * NW);                // copies per wave for group 0
   constexpr int PT = OpA::LD + OpB::LD + 1;
-  constexpr int SB_WAVE = BM / 64;  // the wave that fetches the scales of B
   static_assert(BM % 128 == 0 && BN % 128 == 0, "operand tiles of whole 128-row LDS extents");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile of 16 x 16 MFMA tiles");
   static_assert(kFp8Block % WTN == 0, "a wave's columns lie in one scale block of B");
-  static_assert(SB_WAVE < NW && BN / kFp8Block <= 64, "a spare wave fetches the scales of B");
-  static_assert(STAGES >= (DB ? 3 : 2) && PT * STAGES < 64, "ring depth / vmcnt budget");
+  static_assert(BM <= 64 * NW && (BM * G) % (64 * NW) == 0 && BM % G == 0, "scale copy shape");
+  static_assert(G >= STAGES, "a group slot is refilled only after its last k-tile is read");
+  static_assert(STAGES >= (DB ? 3 : 2) && PT * STAGES + NG0 < 64, "ring depth / vmcnt budget");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const a_lds = smem;
@@ -140,33 +151,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   opa.init_copies((const _Float16*)g.A, g.lda / 2, row0, mvalid, kin_last / 2, wave, lane);
   opb.init_copies((const _Float16*)g.B, g.ldb / 2, col0, nvalid, kin_last / 2, wave, lane);
 
-  // Scale copies of this wave: base (k-tile 0), per-lane offset, range.
-  const float* s_base;
-  uint32_t s_off, s_rng;
-  if (wave * 64 < BM) {
-    const int r = wave * 64 + lane;
-    s_base = g.SA + (int64_t)row0 * g.KB;
-    s_off = r < BM ? (uint32_t)(r * g.KB * 4) : kOob;
-    s_rng = (uint32_t)(((int64_t)(mvalid - 1) * g.KB + 1) * 4);
-  } else if (wave == SB_WAVE) {
-    const int nb_valid = (nvalid + kFp8Block - 1) / kFp8Block;
-    s_base = g.SB + (int64_t)(col0 / kFp8Block) * g.KB;
-    s_off = lane < BN / kFp8Block ? (uint32_t)(lane * g.KB * 4) : kOob;
-    s_rng = (uint32_t)(((int64_t)(nb_valid - 1) * g.KB + 1) * 4);
-  } else {
-    s_base = g.SA;
-    s_off = kOob;
-    s_rng = 0;
-  }
+  // A row scales go to LDS in groups of G k-tiles, [BM rows][G] floats per group, in a
+  // ring of three group slots. Group 0 is fetched before the loop; every k-tile copy t then
+  // fetches slice t % G (BM / G rows) of group t / G + 1, so each copy is one dword per
+  // lane, G consecutive lanes read G consecutive floats of one row, and the group is
+  // complete (and its slot free) well before its first k-tile.
+  const float* const sa_base = g.SA + (int64_t)row0 * g.KB;
+  const int si = wave * 64 + lane;  // this lane's element of a slice
+  const uint32_t s_off = si < BM ? (uint32_t)(((si / G) * g.KB + si % G) * 4) : kOob;
+  // B block scales: one per wave per k-tile, read through the scalar path. (Waves whose
+  // columns all lie past N read the last block row: their results are dropped.)
+  const int sb_blk = min((col0 + (wave % WN) * WTN) / kFp8Block, (g.N - 1) / kFp8Block);
+  const float* const sb_row = g.SB + (int64_t)sb_blk * g.KB;
 
   const uint32_t a_lds0 = lds_addr(a_lds) + wave * 1024;
   const uint32_t b_lds0 = lds_addr(b_lds) + wave * 1024;
-  const uint32_t s_lds0 = lds_addr(s_lds) + wave * 256;
+  // Waves with no lanes in a slice write their (zero) copy to a spare 256 bytes.
+  const bool s_real = wave * 64 < BM;
+  const uint32_t s_lds0 = s_real ? lds_addr(s_lds) + wave * 256 : lds_addr(s_lds) + 3 * SG_BYTES;
+  const uint32_t s_step = s_real ? 1u : 0u;  // branch-free in the loop
   auto copy_tile = [&](int t) {
     const int4v ra = opa.rsrc(t, nk, nk);
     const int4v rb = opb.rsrc(t, nk, nk);
-    const int tt = t < nk ? t : nk - 1;
-    const int4v rs = make_rsrc(s_base + tt, t < nk ? s_rng : 0u);
     const int slot = t % STAGES;
     const bool last = t == nk - 1;
 #pragma unroll
@@ -175,14 +181,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
 #pragma unroll
     for (int j = 0; j < OpB::LD; ++j)
       dma_to_lds(rb, b_lds0 + slot * B_BYTES + j * NW * 1024, last ? opb.off_last[j] : opb.off[j]);
-    dma_dword_to_lds(rs, s_lds0 + slot * S_BYTES, s_off);
+    {
+      // Written without conditionals: a uniform branch here splits the loop body and
+      // costs the register allocator dearly.
+      const int grp = t / G + 1, part = t % G;
+      const int r0 = part * (BM / G), k0 = grp * G;
+      const int rl = max(mvalid - r0, 0), kl = max(g.KB - k0, 0);
+      const uint32_t rng = (uint32_t)(max((rl - 1) * g.KB + kl, 0) * 4 * min(kl, 1));
+      const int4v rs = make_rsrc(sa_base + (int64_t)r0 * g.KB + min(k0, nk - 1), rng);
+      dma_dword_to_lds(rs, s_lds0 + s_step * ((grp % 3) * SG_BYTES + part * BM * 4), s_off);
+    }
   };
+  auto sa_lds = [&](int t) { return (const TG_LDS float*)(s_lds + ((t / G) % 3) * SG_BYTES) + t % G; };
+  // Group 0, before the first operand copies: NG0 copies per wave over the whole group.
+  {
+    const int4v rs = make_rsrc(sa_base, (uint32_t)(((int64_t)(mvalid - 1) * g.KB + g.KB) * 4));
+#pragma unroll
+    for (int j = 0; j < NG0; ++j) {
+      const int i = (wave * NG0 + j) * 64 + lane;
+      dma_dword_to_lds(rs, lds_addr(s_lds) + (wave * NG0 + j) * 256, (uint32_t)(((i / G) * g.KB + i % G) * 4));
+    }
+  }
 
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane % 16, lkg = lane / 16;
   opa.init_frags(wm * WTM, lane);
   opb.init_frags(wn * WTN, lane);
-  const int sb_index = SB_WAVE * 64 + (wn * WTN) / kFp8Block;
 
   float4v acc[FM][FN];
 #pragma unroll
@@ -212,13 +236,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     float sc[FM];
     float4v ptail[D > 0 ? D * FN : 1];
     float sctail[D > 0 ? D : 1];
-    auto main_part = [&](int slot, bool fold_prev) {
+    auto main_part = [&](int kt, float sb) {
+      const int slot = kt % STAGES;
+      const bool fold_prev = kt > 0;
       const char* const As = a_lds + slot * A_BYTES;
       const char* const Bs = b_lds + slot * B_BYTES;
-      const TG_LDS float* const S = (const TG_LDS float*)(s_lds + slot * S_BYTES);
-      const float sb = S[sb_index];
+      const TG_LDS float* const S = sa_lds(kt);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) sc[fm] = S[wm * WTM + fm * 16 + lrow] * sb;
+      for (int fm = 0; fm < FM; ++fm) sc[fm] = S[(wm * WTM + fm * 16 + lrow) * G] * sb;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
 #pragma unroll
@@ -263,9 +288,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     for (int t = 0; t < STAGES; ++t) copy_tile(t);
     clk.loop_begin();
     for (int kt = 0; kt < nk; ++kt) {
+      const float sb = sb_row[kt];
       wait_vmcnt<PT * (STAGES - 1)>();
       lds_barrier();           // tile kt landed everywhere
-      main_part(kt % STAGES, kt > 0);
+      main_part(kt, sb);
       lds_barrier();           // every wave is done reading tile kt's slot
       copy_tile(kt + STAGES);  // refill it (past the end: empty ranges, zeros)
       if (D > 0) tail_part();
@@ -283,17 +309,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
       int8v a[FM], b[FN];
       float sa[FM], sb;
     };
-    auto read_frags = [&](int slot, Frags& f) {
+    auto read_frags = [&](int kt, Frags& f) {
+      const int slot = kt % STAGES;
       const char* const As = a_lds + slot * A_BYTES;
       const char* const Bs = b_lds + slot * B_BYTES;
-      const TG_LDS float* const S = (const TG_LDS float*)(s_lds + slot * S_BYTES);
+      const TG_LDS float* const S = sa_lds(kt);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) f.b[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) f.a[fm] = cat_frag(opa.frag(As, fm, 0), opa.frag(As, fm, 1));
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) f.sa[fm] = S[wm * WTM + fm * 16 + lrow];
-      f.sb = S[sb_index];
+      for (int fm = 0; fm < FM; ++fm) f.sa[fm] = S[(wm * WTM + fm * 16 + lrow) * G];
+      f.sb = sb_row[min(kt, nk - 1)];
     };
     constexpr int T = FM * FN;
     auto mma_frags = [&](const Frags& f) {
@@ -320,7 +347,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
       wait_vmcnt<PT * (STAGES - 2)>();    // this thread's copies of tile kt+1 have landed
       lds_barrier();                      // everyone's have; every wave is done with tile kt
       copy_tile(kt + STAGES);             // into tile kt's slot (past the end: zeros)
-      read_frags((kt + 1) % STAGES, nxt); // past the last tile: a settled slot, unused
+      read_frags(kt + 1, nxt);            // past the last tile: a settled slot, unused
       mma_frags(cur);
     };
     int kt = 0;
@@ -377,7 +404,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 constexpr int fp8_lds_bytes() {
-  return STAGES * ((BM + BN) * kFp8Block + 256 * WM * WN);
+  return STAGES * (BM + BN) * kFp8Block + 3 * BM * fp8_scale_group<BM, BN, STAGES>() * 4 + 256;
 }
 
 // ------------------------------------------------------------------------------------
@@ -567,7 +594,7 @@ hipError_t launch_fp8_cfg(const Fp8Args& g, hipStream_t s, int device) {
   X(256, 128, 4, 2, 3, 4, 1, 1)
 
 #define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X, DB) \
-  {BM, BN, WM, WN, S, P, X, "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN "_db" #DB},
+  {BM, BN, WM, WN, S, P, X, fp8_lds_bytes<BM, BN, WM, WN, S>(), "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN "_db" #DB},
 #define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X, DB) launch_fp8_cfg<BM, BN, WM, WN, S, P, X, DB>,
 
 const Fp8Config* fp8_config_table(int* count) {

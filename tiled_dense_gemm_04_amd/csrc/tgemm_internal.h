@@ -121,6 +121,7 @@ struct Fp8Args {
 // fp8 tile configs (index order is tooling ABI: gemm_fp8_block_cfg, sweeps).
 struct Fp8Config {
   int bm, bn, waves_m, waves_n, stages, panel, xcd_remap;
+  int lds_bytes;  // dynamic LDS of one workgroup
   const char* name;
 };
 const Fp8Config* fp8_config_table(int* count);
