@@ -320,11 +320,10 @@ def test_fp8_config_table():
         assert c["block_k"] == 128 and c["generic"] == 0 and c["layouts"] == 2
         assert c["block_m"] % 128 == 0 and c["block_n"] % 128 == 0
         waves = c["waves_m"] * c["waves_n"]
-        # operand ring + three groups of A row scales (8 k-tiles each where they fit, else 4)
-        # + a spare 256 bytes for copies with nothing to fetch
+        # operand ring + three groups of A row scales (4 k-tiles each) + a spare 256 bytes
+        # for copies with nothing to fetch
         ring = c["stages"] * (c["block_m"] + c["block_n"]) * 128
-        group = 8 if ring + 3 * c["block_m"] * 8 * 4 + 256 <= 160 * 1024 else 4
-        assert c["lds_bytes"] == ring + 3 * c["block_m"] * group * 4 + 256
+        assert c["lds_bytes"] == ring + 3 * c["block_m"] * 4 * 4 + 256
         assert c["lds_bytes"] <= 160 * 1024
         assert 128 % (c["block_n"] // c["waves_n"]) == 0   # a wave's columns in one scale block
         assert c["block_m"] <= 64 * waves                    # a slice of A scales: one copy per wave

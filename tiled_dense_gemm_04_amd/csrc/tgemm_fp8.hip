@@ -102,12 +102,9 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
 // enough for two fragment sets (64 x 64).
 // Requirements (checked by the host): A, B 16-byte aligned, lda, ldb, K multiples of 16;
 // C 16-byte aligned, ldc and N multiples of 8; (BM - 1) * KB * 4 < 2^31.
-// k-tiles per group of A row scales: 8 where three groups fit the LDS beside the operand
-// ring, else 4.
-template <int BM, int BN, int STAGES>
-constexpr int fp8_scale_group() {
-  return STAGES * (BM + BN) * kFp8Block + 3 * BM * 8 * 4 + 256 <= 160 * 1024 ? 8 : 4;
-}
+// k-tiles per group of A row scales (8 measured no faster on 256 x 256 tiles and slower
+// on 128 x 128 ones).
+constexpr int kScaleGroup = 4;
 
 template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD, bool DB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g) {
@@ -119,7 +116,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   using OpA = PpOperand<BM, kF8Kh, 16, true, NW>;
   using OpB = PpOperand<BN, kF8Kh, 16, true, NW>;
   constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
-  constexpr int G = fp8_scale_group<BM, BN, STAGES>();  // k-tiles per A-scale group
+  constexpr int G = kScaleGroup;                          // k-tiles per A-scale group
   constexpr int SG_BYTES = BM * G * 4;                   // one group: [BM rows][G]
   constexpr int NG0 = BM * G / (64 * NW);                // copies per wave for group 0
   constexpr int PT = OpA::LD + OpB::LD + 1;
@@ -404,7 +401,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 constexpr int fp8_lds_bytes() {
-  return STAGES * (BM + BN) * kFp8Block + 3 * BM * fp8_scale_group<BM, BN, STAGES>() * 4 + 256;
+  return STAGES * (BM + BN) * kFp8Block + 3 * BM * kScaleGroup * 4 + 256;
 }
 
 // ------------------------------------------------------------------------------------
