@@ -65,8 +65,11 @@ def _check(A, SA, B, SB, relu, cfg=None, what="", **pads):
     return c, rep
 
 
+# K spans 1 to 16 blocks of 128, with partial groups of 4 blocks of row scales (6, 7 and 9
+# blocks) and a single row with several groups (every other slice of row scales empty).
 SHAPES = [(256, 256, 128), (300, 264, 1008), (520, 392, 272), (1, 8, 16), (257, 136, 64),
-          (640, 1152, 1040), (33, 520, 2048), (1024, 256, 16), (129, 1000, 400)]
+          (640, 1152, 1040), (33, 520, 2048), (1024, 256, 16), (129, 1000, 400),
+          (1, 136, 1040), (96, 264, 704), (200, 136, 848)]
 ODD = [(17, 23, 29), (65, 63, 129), (1, 1, 1), (130, 7, 250), (40, 200, 100)]
 
 
