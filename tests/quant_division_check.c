@@ -5,8 +5,10 @@
  *     r = 1 / s;  y0 = x * r;  e = fma(-y0, s, x);  y = copysign(fma(e, r, y0), x)
  * (one IEEE division per block instead of one per element; Markstein's correction step;
  * copysign keeps the sign of a zero x, which the correction would turn into +0) gives the
- * same float32, bit for bit, as the IEEE quotient x / s. Prints the number of pairs checked
- * and of mismatches; exits 1 on any mismatch. Build: gcc -O2 -fopenmp -ffp-contract=off.
+ * same float32, bit for bit, as the IEEE quotient x / s; and that the scale itself,
+ *     s0 = amax * RN(1/448);  s = fma(fma(-s0, 448, amax), RN(1/448), s0)
+ * equals the IEEE quotient amax / 448 for every amax. Prints the number of pairs checked and
+ * of mismatches; exits 1 on any mismatch. Build: gcc -O2 -fopenmp -ffp-contract=off.
  */
 #include <math.h>
 #include <stdint.h>
@@ -27,6 +29,16 @@ int main(void) {
     for (int am = 1; am < 0x7C00; ++am) {
         const float amax = f16_value((uint16_t)am);
         const float s = amax / 448.0f;
+        {
+            const float inv448 = 1.0f / 448.0f;
+            const float s0 = amax * inv448;
+            const float s1 = fmaf(fmaf(-s0, 448.0f, amax), inv448, s0);
+            ++pairs;
+            if (bits(s1) != bits(s)) {
+                ++bad;
+                if (bad < 5) printf("scale mismatch amax=%a: %a vs %a\n", amax, s1, s);
+            }
+        }
         const float r = 1.0f / s;
         for (int xh = 0; xh <= am; ++xh)
             for (int sg = 0; sg < 2; ++sg) {

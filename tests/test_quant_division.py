@@ -1,8 +1,8 @@
 """The block quantizer divides by the block scale with one reciprocal per block and a
-corrected product per element (tgemm_fp8.hip, div_by_scale). quant_division_check.c
-replays that sequence on the CPU for every binary16 block maximum and every binary16 x
-with |x| <= amax (about 10^9 pairs) and checks it against IEEE float32 division bit for
-bit. No GPU."""
+corrected product per element (tgemm_fp8.hip, div_by_scale), and forms the scale amax / 448
+itself as a corrected product (block_scale). quant_division_check.c replays both sequences
+on the CPU for every binary16 block maximum and every binary16 x with |x| <= amax (about
+10^9 pairs) and checks them against IEEE float32 division bit for bit. No GPU."""
 import os
 import subprocess
 

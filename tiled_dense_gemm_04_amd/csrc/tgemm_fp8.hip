@@ -439,70 +439,79 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   return __builtin_copysignf(__builtin_fmaf(e, r, y0), x);
 }
 
+// A block's scale amax / 448 as the IEEE float32 division rounds it (1 for an all-zero
+// block), from RN(1/448) and one corrected product (Markstein's step again): equal to the
+// division for every binary16 amax, checked exhaustively on the CPU by the test suite.
+__device__ __forceinline__ float block_scale(float amax) {
+  constexpr float kInv448 = 1.0f / 448.0f;
+  const float s0 = amax * kInv448;
+  return amax > 0.0f ? __builtin_fmaf(__builtin_fmaf(-s0, 448.0f, amax), kInv448, s0) : 1.0f;
+}
+
 // ------------------------------------------------------------------------------------
 // Block quantizer, 1 x 128 blocks (activations): a group of 16 lanes per block, 8
-// elements per lane; a workgroup covers 16 * QNB consecutive blocks, group g taking blocks
-// g, g + 16, ... so that each of its QNB loads (issued before any arithmetic) covers 16
-// consecutive blocks across the workgroup. Scale s = amax / 448 in float32 (1 for an
-// all-zero block), codes E4M3(x / s) with x / s rounded as the IEEE float32 division. All 64 lanes of a
-// wave take part in the shuffles; lanes of groups past the last block skip their loads
-// and stores.
-constexpr int QNB = 1;
+// elements per lane, 16 consecutive blocks per workgroup. Scale s = amax / 448 in float32
+// (1 for an all-zero block), codes E4M3(x / s) with x / s rounded as the IEEE float32
+// division. All 64 lanes of a wave take part in the shuffles; lanes of groups past the
+// last block skip their loads and stores.
 template <bool VEC>
 __global__ __launch_bounds__(256) void quant_fp8_rows(QuantArgs q) {
   const int sub = threadIdx.x % 16;
   const uint32_t KB = (uint32_t)q.KB;
   const uint32_t nblk = (uint32_t)q.R * KB;  // < 2^32 (checked by the host)
-  const uint32_t base = blockIdx.x * 16 * QNB + threadIdx.x / 16;
-  float x[QNB][8];
-#pragma unroll
-  for (int i = 0; i < QNB; ++i) {
-    const uint32_t blk = base + 16 * i;
-    const bool active = blk < nblk;
-    const uint32_t rw = active ? blk / KB : 0;
-    const int64_t row = rw;
-    const int k = (int)(active ? blk - rw * KB : 0) * kFp8Block + 8 * sub;
-    if (VEC) {
-      half8 h = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (active && k < q.K) h = *(const half8*)(q.X + row * q.ldx + k);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = (float)h[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = (active && k + e < q.K) ? (float)q.X[row * q.ldx + k + e] : 0.0f;
+  // This workgroup's first block, decoded once (uniform: a scalar division); a thread's
+  // block is 0 .. 15 blocks further, at most one row further when KB >= 16.
+  const uint32_t wg0 = blockIdx.x * 16;
+  const uint32_t row0 = wg0 / KB, kb0 = wg0 - row0 * KB;
+  const uint32_t g = threadIdx.x / 16;
+  const uint32_t blk = wg0 + g;
+  uint32_t kb = kb0 + g, rw = row0;
+  if (KB >= 16) {
+    const bool wrap = kb >= KB;
+    kb -= wrap ? KB : 0u;
+    rw += wrap ? 1u : 0u;
+  } else {
+    while (kb >= KB) {
+      kb -= KB;
+      ++rw;
     }
   }
+  const bool active = blk < nblk;
+  const int64_t row = active ? rw : 0;
+  const int k = (int)(active ? kb : 0) * kFp8Block + 8 * sub;
+  float x[8];
+  if (VEC) {
+    half8 h = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active && k < q.K) h = *(const half8*)(q.X + row * q.ldx + k);
 #pragma unroll
-  for (int i = 0; i < QNB; ++i) {
-    const uint32_t blk = base + 16 * i;
-    float m = 0.0f;
+    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[i][e]));
-#pragma unroll
-    for (int w = 1; w < 16; w <<= 1) m = fmaxf(m, __shfl_xor(m, w, 16));
-    const float s = m > 0.0f ? m / 448.0f : 1.0f;
-    const float r = 1.0f / s;
-    if (blk >= nblk) continue;
-    const uint32_t rw = blk / KB;
-    const int64_t row = rw;
-    const int kb = (int)(blk - rw * KB);
-    const int k = kb * kFp8Block + 8 * sub;
-    if (VEC) {
-      if (k < q.K) {
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = div_by_scale(x[i][e], s, r);
-        const uint32_t lo = e4m3_pack2<true>(y[2], y[3], e4m3_pack2<false>(y[0], y[1], 0u));
-        const uint32_t hi = e4m3_pack2<true>(y[6], y[7], e4m3_pack2<false>(y[4], y[5], 0u));
-        *(uint2v*)(q.Q + row * q.ldq + k) = (uint2v){lo, hi};
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k + e < q.K) q.Q[row * q.ldq + k + e] = (uint8_t)e4m3_pack2<false>(div_by_scale(x[i][e], s, r), 0.0f, 0u);
-    }
-    if (sub == 0) q.S[row * q.KB + kb] = s;
+    for (int e = 0; e < 8; ++e) x[e] = (active && k + e < q.K) ? (float)q.X[row * q.ldx + k + e] : 0.0f;
   }
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+  for (int w = 1; w < 16; w <<= 1) m = fmaxf(m, __shfl_xor(m, w, 16));
+  const float s = block_scale(m);
+  const float r = 1.0f / s;
+  if (!active) return;
+  if (VEC) {
+    if (k < q.K) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = div_by_scale(x[e], s, r);
+      const uint32_t lo = e4m3_pack2<true>(y[2], y[3], e4m3_pack2<false>(y[0], y[1], 0u));
+      const uint32_t hi = e4m3_pack2<true>(y[6], y[7], e4m3_pack2<false>(y[4], y[5], 0u));
+      *(uint2v*)(q.Q + row * q.ldq + k) = (uint2v){lo, hi};
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k + e < q.K) q.Q[row * q.ldq + k + e] = (uint8_t)e4m3_pack2<false>(div_by_scale(x[e], s, r), 0.0f, 0u);
+  }
+  if (sub == 0) q.S[row * q.KB + kb] = s;
 }
 
 // Block quantizer, 128 x 128 blocks (weights): one workgroup of 256 threads per block,
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(256) void quant_fp8_tiles(QuantArgs q) {
   if ((t & 63) == 0) wmax[t >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float s = m > 0.0f ? m / 448.0f : 1.0f;
+  const float s = block_scale(m);
   const float rs = 1.0f / s;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -616,7 +625,7 @@ hipError_t launch_fp8_generic(const Fp8Args& g, hipStream_t s) {
 hipError_t launch_quant_fp8(const QuantArgs& q, bool vec, hipStream_t s) {
   if (q.block_rows == 1) {
     const int64_t blocks = (int64_t)q.R * q.KB;
-    const dim3 grid((unsigned)((blocks + 16 * QNB - 1) / (16 * QNB)));
+    const dim3 grid((unsigned)((blocks + 15) / 16));
     if (vec)
       hipLaunchKernelGGL(quant_fp8_rows<true>, grid, dim3(256), 0, s, q);
     else
