@@ -152,7 +152,10 @@ def _quant_inputs(R, K, seed):
 @pytest.mark.parametrize("block_rows", [1, 128])
 def test_quant_bitexact(block_rows):
     torch = torch_cuda()
-    for s, (R, K) in enumerate([(5, 300), (64, 4096), (129, 1000), (3, 8), (300, 256), (1, 128)]):
+    # rows of 32 or more blocks take two blocks per lane group (wrapping across rows,
+    # partial last workgroup and partial last block included): 4104, 5000 and 8200
+    for s, (R, K) in enumerate([(5, 300), (64, 4096), (129, 1000), (3, 8), (300, 256), (1, 128),
+                                (7, 4104), (33, 5000), (2, 8200)]):
         x = _quant_inputs(R, K, 800 + s)
         Qr, Sr = oracle.quant_fp8(x, block_rows)
         for pad in (0, 3):  # pad 3: odd row stride, element loads and stores
