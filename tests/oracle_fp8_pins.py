@@ -2,6 +2,8 @@
 
 Each pin takes an ``oracle.Oracle`` instance and raises AssertionError when the instance
 disagrees with something that does not come from the oracle:
+  * code points and roundings taken from the OCP 8-bit floating point specification's
+    definition of E4M3 (tests/golden/e4m3_points.txt);
   * torch's CPU float8_e4m3fn codec (an independent implementation of OCP E4M3) over all
     256 codes and on random float32 values below the saturation point;
   * ties-to-even at every midpoint between neighbouring E4M3 values (a property of the
@@ -15,11 +17,36 @@ disagrees with something that does not come from the oracle:
 """
 from __future__ import annotations
 
+import os
 from fractions import Fraction
 
 import numpy as np
 
 BLOCK = 128
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def pin_e4m3_golden(orc):
+    """Decode and encode the code points and roundings of tests/golden/e4m3_points.txt."""
+    n = 0
+    with open(os.path.join(GOLDEN, "e4m3_points.txt")) as f:
+        for line in f:
+            row = line.split("#", 1)[0].split()
+            if not row:
+                continue
+            kind, a, b = row
+            if kind == "decode":
+                got = float(orc.e4m3_decode(np.array([int(a, 16)], np.uint8))[0])
+                if b == "nan":
+                    assert got != got, (a, got)
+                else:
+                    assert Fraction(got) == Fraction(b), (a, got, b)
+                    assert np.signbit(got) == b.startswith("-"), (a, got, b)
+            else:
+                got = int(orc.e4m3_encode(np.array([float(Fraction(a))]))[0])
+                assert got == int(b, 16), (a, hex(got), b)
+            n += 1
+    assert n >= 30, n
 
 
 def _torch():
@@ -319,6 +346,7 @@ def pin_fp8_bound_entries(orc):
 
 
 FP8_PINS = [
+    pin_e4m3_golden,
     pin_e4m3_decode_all_codes,
     pin_e4m3_encode_roundtrip,
     pin_e4m3_encode_ties_even,
