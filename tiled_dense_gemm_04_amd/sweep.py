@@ -4,7 +4,7 @@ tgemm_api.cpp's choose_fast). With --split, time split-K instead: the 256 x 256 
 128 x 128 ping-pong configs at 1, 2, 4 and 8 splits per output tile on small-grid shapes
 (the evidence behind split_plan). Needs a GPU.
 
-  python -m tiled_dense_gemm_04_amd.sweep [--out results.json] [--iters 30]
+  python -m tiled_dense_gemm_04_amd.sweep [--out results.json] [--md out.md] [--torch] [--iters 30]
   python -m tiled_dense_gemm_04_amd.sweep --split [--md out.md]
 """
 from __future__ import annotations
@@ -93,7 +93,7 @@ def main():
     ap.add_argument("--torch", action="store_true",
                     help="also time torch.matmul (+ relu) on the same inputs, as context only")
     ap.add_argument("--split", action="store_true", help="split-K sweep on small-grid shapes")
-    ap.add_argument("--md", default=None, help="with --split: write the table here")
+    ap.add_argument("--md", default=None, help="write the table (markdown) here")
     args = ap.parse_args()
     if args.split:
         return split_sweep(args.md)
@@ -149,7 +149,37 @@ def main():
     if args.out:
         with open(args.out, "w") as f:
             json.dump(results, f, indent=1)
+    if args.md:
+        with open(args.md, "w") as f:
+            f.write(sweep_markdown(results, [cd["name"] for cd in cfgs], args, torch.cuda.get_device_name(0)))
     return 0
+
+
+def sweep_markdown(results, names, args, device) -> str:
+    """Configs as rows, workloads as columns, the fastest per column in bold."""
+    cmd = "python -m tiled_dense_gemm_04_amd.sweep" + (" --torch" if args.torch else "") + \
+        f" --iters {args.iters} --md gpurun_out/sweep.md"
+    L = ["# Config sweep, all measured workloads (one MI355X)", "",
+         f"Command (from the repository root): `{cmd}`", "",
+         f"Device: {device}. Every table config on every workload: {args.iters} timed launches after 5",
+         "warm-up, HIP events, microseconds per launch; **bold** is the fastest config per workload.",
+         "`torch.matmul` (+ `relu_`) is hipBLASLt on the same inputs, context only. Absolute times vary",
+         "by ~5-10 % between MI355X boxes (power and thermal state); compare within a column.", "",
+         "| config | " + " | ".join(r["workload"] for r in results) + " |",
+         "|---|" + "---|" * len(results)]
+    for n in names:
+        cells = []
+        for r in results:
+            t = r["times_us"].get(n)
+            cells.append("-" if t is None else (f"**{t:.2f}**" if n == r["best"] else f"{t:.2f}"))
+        L.append(f"| {n} | " + " | ".join(cells) + " |")
+    if any("torch_matmul_us" in r for r in results):
+        L.append("| torch.matmul(+relu) | " + " | ".join(f"{r['torch_matmul_us']:.2f}" if "torch_matmul_us" in r
+                                                        else "-" for r in results) + " |")
+    L += ["", "Default choice per workload (the config `gemm_f16` picks): " +
+          ", ".join(f"{r['workload']} -> {names[r['default_cfg']] if r['default_cfg'] >= 0 else 'generic'}"
+                    for r in results) + "."]
+    return "\n".join(L) + "\n"
 
 
 if __name__ == "__main__":
