@@ -333,9 +333,14 @@ def test_fp8_config_table():
 
 def test_fp8_select():
     s = tg.tgemm_fp8_select_config
-    assert s(4096, 4096, 4096) == 0                       # 256 x 256 tiles
-    assert s(16384, 512, 4096) == 3                       # 256 x 128 tiles fill the GPU
-    assert s(1024, 1024, 1024) == 1                       # 128 x 128
+    # rounds of 256 workgroups x the config's relative round cost (1, 0.75, 0.57)
+    assert s(4096, 4096, 4096) == 0                       # 256 x 256: one round
+    assert s(3072, 3072, 4096) == 0                       # 144 256 x 256 tiles beat two rounds of 256 x 128
+    assert s(16384, 512, 4096) == 3                       # one round of 256 x 128
+    assert s(2560, 2560, 4096) == 3
+    assert s(6144, 6144, 4096) == 0                       # 3 rounds against 5 x 0.75
+    assert s(1024, 1024, 1024) == 1                       # 128 x 128: one round
+    assert s(2048, 2048, 4096) == 1
     assert s(0, 8, 16) == tg.SELECT_NOOP and s(8, 8, 0) == tg.SELECT_ZERO_FILL
     # generic kernel: K or ld not a multiple of 16, N or ldc not a multiple of 8, unaligned
     assert s(256, 256, 100) == tg.FP8_GENERIC

@@ -251,12 +251,19 @@ bool fp8_fast_eligible(int64_t N, int64_t K, const void* A, int64_t lda, const v
          ldc % 8 == 0 && N % 8 == 0 && 256 * KB * 4 < ((int64_t)1 << 31);
 }
 
-// 256 x 256 tiles when they cover most compute units, else 256 x 128 when those do, else
-// 128 x 128.
+// Wave-quantized cost: one config's launch takes about ceil(tiles / 256) rounds of
+// workgroups (one per compute unit), each round costing about as long as its tile's work.
+// Relative round costs measured at K = 4096: 256 x 256 1, 256 x 128 0.75, 128 x 128 0.57
+// (e.g. 3072 x 3072: 144 tiles of 256 x 256 in one round, 56 us, beat 288 of 256 x 128 in
+// two, 76 us; 2048 x 4096: 256 tiles of 256 x 128 in one round, 42 us, beat 128 of
+// 256 x 256, 56 us).
 int fp8_choose(int64_t M, int64_t N) {
-  if (tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256) >= 160) return kFp8Cfg256;
-  if (tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 128) >= 160) return kFp8Cfg256x128;
-  return kFp8Cfg128;
+  const auto rounds = [](int64_t tiles) { return (double)tgemm::ceil_div(tiles, (int64_t)kNumCu); };
+  const double c256 = 1.00 * rounds(tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256));
+  const double c256x128 = 0.75 * rounds(tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 128));
+  const double c128 = 0.57 * rounds(tgemm::ceil_div(M, 128) * tgemm::ceil_div(N, 128));
+  if (c128 < c256x128 && c128 < c256) return kFp8Cfg128;
+  return c256x128 < c256 ? kFp8Cfg256x128 : kFp8Cfg256;
 }
 
 int fp8_select(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const float* SA, const void* B,
