@@ -165,6 +165,23 @@ def test_select_fast_vs_generic():
     assert s(4095, 3000, 1000, A16, 1000, A16, 3000, A16, 3000) > 0
 
 
+def test_select_by_rounds():
+    """Rounds of 256 workgroups: the smallest tile that fits one round, else 256 x 192 when
+    it needs no more rounds than 256 x 256."""
+    name = lambda M, N, K: tg.tgemm_config_desc(tg.tgemm_select_config(M, N, K, A16, K, A16, N, A16, N))["name"]
+    assert name(1024, 1024, 1024).startswith("p128x128")     # 64 tiles of 128 x 128
+    assert name(2048, 2048, 4096).startswith("p128x128")     # 256 tiles of 128 x 128
+    assert name(2560, 2560, 4096).startswith("m256x128")     # 200 tiles of 256 x 128
+    assert name(16384, 512, 4096).startswith("m256x128")     # 256 tiles of 256 x 128
+    assert name(3072, 3072, 4096).startswith("m256x192")     # 192 tiles of 256 x 192
+    assert name(4095, 3000, 1000).startswith("m256x192")     # 256 tiles of 256 x 192
+    assert name(3584, 3584, 2048).startswith("m256x256")     # 196 tiles of 256 x 256
+    assert name(4096, 4096, 4096).startswith("m256x256")     # 256 tiles of 256 x 256
+    assert name(6144, 6144, 4096).startswith("m256x192")     # 3 rounds either way
+    assert name(5120, 4096, 4096).startswith("m256x192")     # 2 rounds either way
+    assert name(8192, 8192, 8192).startswith("m256x256")     # 4 rounds against 6
+
+
 def test_gemm_rejects_invalid_before_hip():
     # invalid arguments are reported before any HIP call (works with no GPU present)
     assert tg.gemm_f16_raw(-1, 8, 8, A16, 8, A16, 8, A16, 8, 1, None) == tg.TGEMM_EINVAL_DIM

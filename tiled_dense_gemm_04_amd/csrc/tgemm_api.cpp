@@ -70,26 +70,27 @@ int64_t workgroups(const Config& c, int64_t M, int64_t N) {
 }
 
 // Config choice for a fast-eligible call (rows of the table in tgemm_kernels.hip:
-// 9 = 16x16x32 ping-pong 256x256, 16 = the same with 256x128 tiles, 15 = 128x128,
-// 7 = 4-wave pipelined 128x128 with BK 64). From the offline sweep on the measured
-// workloads: 256 x 256 ping-pong tiles win as soon as they cover most of the 256 compute
-// units (160+ tiles, e.g. 4095 x 3000 has 192); below that, 256 x 128 tiles when they
-// give about one workgroup per compute unit (16384 x 512: 67.9 us against 69.6 us), and
-// the 128 x 128 pipelined kernel for the smallest grids (1024^3: 11.3 us against 15.2 us
-// for the 128 x 128 ping-pong). Transposed operands take the ping-pong kernels only.
-// 18 = 256 x 192 tiles: when 256 x 256 tiles leave part of the GPU idle in their last
-// (only) wave and 256 x 192 tiles still fit in one wave (4095 x 3000: 192 tiles of
-// 256 x 256 against 256 of 256 x 192).
+// 9 = 16x16x32 ping-pong 256x256, 18 = the same with 256x192 tiles, 16 = 256x128,
+// 15 = 128x128, 7 = 4-wave pipelined 128x128 with BK 64). Counted in rounds of 256
+// workgroups (one per compute unit): when the grid fits one round, the smallest tile whose
+// tiles still fit one round (smaller tiles finish sooner: 1536^2 x 4096 42.5 us with
+// 128 x 128 against 53.1 us with 256 x 128; 3072^2 74.3 us with 256 x 192 against 102.8 us
+// for 128 x 128 in three rounds); beyond one round, 256 x 192 tiles if they need no more
+// rounds than 256 x 256 ones (6144^2 x 4096: 255 against 275 us), else 256 x 256.
+// Transposed operands take the ping-pong kernels only (15 instead of 7).
 constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15, kCfgMid = 16, kCfg192 = 18;
+constexpr int64_t kRound = 256;  // workgroups in flight at once: one per compute unit
 int choose_fast(int layout, int64_t M, int64_t N, int64_t K) {
   (void)K;
-  const int64_t t256 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 256);
-  const int64_t t192 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 192);
-  if (t256 >= 160 && t256 < 256 && t192 > t256 && t192 <= 256) return kCfg192;
-  if (t256 >= 160) return kCfgBig;
-  const int64_t t256x128 = tgemm::ceil_div(M, 256) * tgemm::ceil_div(N, 128);
-  if (t256x128 >= 200 && t256x128 <= 256) return kCfgMid;
-  return layout == 0 ? kCfgSmall : kCfgSmallT;
+  const int64_t tm = tgemm::ceil_div(M, 256);
+  const int64_t t256 = tm * tgemm::ceil_div(N, 256), t192 = tm * tgemm::ceil_div(N, 192);
+  const int64_t t256x128 = tm * tgemm::ceil_div(N, 128);
+  const int64_t t128 = tgemm::ceil_div(M, 128) * tgemm::ceil_div(N, 128);
+  if (t128 <= kRound) return layout == 0 ? kCfgSmall : kCfgSmallT;
+  if (t256x128 <= kRound) return kCfgMid;
+  if (t192 <= kRound) return kCfg192;
+  if (t256 <= kRound) return kCfgBig;
+  return tgemm::ceil_div(t192, kRound) <= tgemm::ceil_div(t256, kRound) ? kCfg192 : kCfgBig;
 }
 
 int select(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
