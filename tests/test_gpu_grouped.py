@@ -54,14 +54,19 @@ def test_grouped_random_shapes(gpu, ta, tb):
         assert_close(c.cpu().numpy().view(np.uint16), oracle.gemm(A, B, True), K, what=f"group {i} {shapes[i]}")
 
 
-def test_grouped_equals_single_launches_bitwise(gpu):
-    """Each GEMM of a group gives exactly the bits of the same config run on its own."""
+@pytest.mark.parametrize("shapes", [
+    [(1000, 1024, 512), (264, 392, 1000), (2048, 256, 128), (8, 8, 64), (520, 136, 264)],  # 119 tiles of 128^2
+    [(2048, 2048, 128), (520, 1000, 256)],                                                 # 296: 256^2 tiles
+], ids=["tiles128", "tiles256"])
+def test_grouped_equals_single_launches_bitwise(gpu, shapes):
+    """Each GEMM of a group gives exactly the bits of the same config run on its own. The
+    group takes 128 x 128 tiles when all of them fit one round of 256 workgroups, else
+    256 x 256."""
     torch = gpu
-    shapes = [(1000, 1024, 512), (264, 392, 1000), (2048, 256, 128), (8, 8, 64), (520, 136, 264)]
     ins = [W.make_inputs(M, N, K, "uniform", 1.0, seed=2100 + i) for i, (M, N, K) in enumerate(shapes)]
     probs = [(to_dev(A), to_dev(B)) for A, B in ins]
-    t256 = sum(-(-M // 256) * -(-N // 256) for M, N, K in shapes)
-    cfg_name = "m256x256x32_s4_w2x4_p4_x1" if t256 >= 160 else "m128x128x32_s4_w2x4_p4_x1"
+    t128 = sum(-(-M // 128) * -(-N // 128) for M, N, K in shapes)
+    cfg_name = "m128x128x32_s4_w2x4_p4_x1" if t128 <= 256 else "m256x256x32_s4_w2x4_p4_x1"
     idx = [c["name"] for c in tg.configs()].index(cfg_name)
     log(f"grouped vs single launches, config {cfg_name}")
     outs = tg.gemm_f16_grouped(probs, relu=False)

@@ -512,21 +512,22 @@ int gemm_f16_grouped(int trans_a, int trans_b, int count, const tgemm_gemm_desc*
   if (gemms == nullptr) return TGEMM_ENULL;
   const int layout = layout_of(trans_a, trans_b);
   // validate everything before enqueueing anything
-  int64_t t256 = 0;
+  int64_t t128 = 0;
   for (int i = 0; i < count; ++i) {
     const tgemm_gemm_desc& d = gemms[i];
     const int v = select(layout, d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc);
     if (v < 0 && v != kSelectNoop && v != kSelectZeroFill) return v;
     if (v >= 0 && fast_eligible(layout, d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc))
-      t256 += tgemm::ceil_div(d.M, 256) * tgemm::ceil_div(d.N, 256);
+      t128 += tgemm::ceil_div(d.M, 128) * tgemm::ceil_div(d.N, 128);
   }
   int dev = -1;
   const int dc = check_device(&dev);
   if (dc != TGEMM_OK) return dc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // one tile config for the whole group: 256 x 256 when the group's tiles cover most of
-  // the GPU, else 128 x 128
-  const int cfg = t256 >= 160 ? kCfgBig : kCfgSmallT;
+  // One tile config for the whole group, counted in rounds of 256 workgroups as in
+  // choose_fast: 128 x 128 tiles when all of them fit one round, else 256 x 256 (a round of
+  // 144 tiles of 256 x 256 beats 576 of 128 x 128 in three by about a third).
+  const int cfg = t128 <= kRound ? kCfgSmallT : kCfgBig;
   const tgemm::GroupedLauncher gl = tgemm::grouped_launcher(cfg);
   const Config& c = cfg_row(cfg);
   if (gl == nullptr) return TGEMM_ELAUNCH;
