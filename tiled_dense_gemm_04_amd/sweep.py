@@ -6,6 +6,10 @@ tgemm_api.cpp's choose_fast). With --split, time split-K instead: the 256 x 256 
 
   python -m tiled_dense_gemm_04_amd.sweep [--out results.json] [--md out.md] [--torch] [--iters 30]
   python -m tiled_dense_gemm_04_amd.sweep --split [--md out.md]
+  python -m tiled_dense_gemm_04_amd.sweep --choice [--md out.md]
+
+--choice checks the default config choice (fp16 choose_fast, fp8 fp8_choose) against the
+candidate configs on shapes from 1024^2 to 6144^2, timed with the measurement protocol.
 """
 from __future__ import annotations
 
@@ -33,6 +37,72 @@ def time_config(tg, torch, a, b, c, relu, cfg, iters, warmup=5):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters * 1e3  # us
+
+
+CHOICE_SHAPES = [(1024, 1024, 4096), (1536, 1536, 4096), (2048, 2048, 4096), (2560, 2560, 4096),
+                 (2048, 4096, 4096), (16384, 512, 4096), (3072, 3072, 4096), (3584, 3584, 2048),
+                 (4096, 2560, 2048), (4095, 3000, 1000), (4096, 3072, 1024), (3072, 4096, 4096),
+                 (5120, 4096, 4096), (6144, 6144, 4096)]
+CHOICE_F16 = ["p128x128x64_s2_w2x2_p4_x1", "m128x128x32_s4_w2x4_p4_x1", "m256x128x32_s4_w2x4_p4_x1",
+              "m128x256x32_s4_w2x4_p4_x1", "m256x192x32_s4_w2x4_p4_x1", "m256x256x32_s4_w2x4_p4_x1"]
+
+
+def choice_sweep(md_path=None):
+    """Time the candidate configs on CHOICE_SHAPES (fp16, then fp8 where the fast path
+    applies) and report the default choice's loss against the fastest."""
+    import torch
+
+    import tgemm_workloads as W
+    import tiled_dense_gemm_04_amd as tg
+    from tiled_dense_gemm_04_amd.measure import timed_trials
+
+    stream = torch.cuda.current_stream()
+    names = {c["name"]: i for i, c in enumerate(tg.configs())}
+    L = ["# Default config choice against the candidates (one MI355X)", "",
+         "Command (from the repository root): `python -m tiled_dense_gemm_04_amd.sweep --choice --md "
+         "gpurun_out/choice.md`", "",
+         f"Device: {torch.cuda.get_device_name(0)}. Each config: 10 warm-up calls and >= 50 ms of calls, then 5",
+         "trials of >= 20 ms (HIP events), median microseconds per call. * marks the config the library",
+         "picks by itself; the last column is its loss against the fastest candidate.", "",
+         "fp16 GEMM + ReLU (C = ReLU(A @ B), N(0,1) inputs):", "",
+         "| M x N x K | " + " | ".join(CHOICE_F16) + " | loss |", "|---|" + "---|" * (len(CHOICE_F16) + 1)]
+    for (M, N, K) in CHOICE_SHAPES:
+        A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=5)
+        a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        pick = tg.tgemm_config_desc(tg.tgemm_select_config(M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(),
+                                                           b.stride(0), c.data_ptr(), c.stride(0)))["name"]
+        t = {n: timed_trials(torch, stream, lambda i, n=n: tg.gemm_f16(a, b, c, cfg=names[n]), trials=5)["median_us"]
+             for n in CHOICE_F16}
+        best = min(t.values())
+        loss = f"{100 * (t[pick] / best - 1):.1f} %" if pick in t else "-"
+        L.append(f"| {M}x{N}x{K} | " + " | ".join(f"{v:.1f}{'*' if n == pick else ''}" for n, v in t.items())
+                 + f" | {loss} |")
+        print(L[-1], flush=True)
+        del a, b, c
+    nf8 = tg.tgemm_fp8_num_configs()
+    f8names = [tg.tgemm_fp8_config_desc(i)["name"] for i in range(nf8)]
+    L += ["", "fp8 block-scaled GEMM (E4M3 codes, 1 x 128 / 128 x 128 float32 scales):", "",
+          "| M x N x K | " + " | ".join(f8names) + " | loss |", "|---|" + "---|" * (nf8 + 1)]
+    for (M, N, K) in CHOICE_SHAPES:
+        if N % 8 or K % 16:
+            continue
+        A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=5)
+        a, sa, b, sb = (torch.from_numpy(x).cuda() for x in (A, SA, B, SB))
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        pick = tg.tgemm_fp8_select_config(M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
+                                          c.data_ptr(), c.stride(0))
+        t = [timed_trials(torch, stream, lambda i, k=k: tg.gemm_fp8_block(a, sa, b, sb, c, cfg=k), trials=5)["median_us"]
+             for k in range(nf8)]
+        L.append(f"| {M}x{N}x{K} | " + " | ".join(f"{v:.1f}{'*' if k == pick else ''}" for k, v in enumerate(t))
+                 + f" | {100 * (t[pick] / min(t) - 1):.1f} % |")
+        print(L[-1], flush=True)
+        del a, sa, b, sb, c
+    text = "\n".join(L) + "\n"
+    if md_path:
+        with open(md_path, "w") as f:
+            f.write(text)
+    return 0
 
 
 SPLIT_SHAPES = [(1024, 1024, 1024), (16384, 512, 4096), (512, 4096, 4096), (1024, 1024, 32768),
@@ -93,10 +163,13 @@ def main():
     ap.add_argument("--torch", action="store_true",
                     help="also time torch.matmul (+ relu) on the same inputs, as context only")
     ap.add_argument("--split", action="store_true", help="split-K sweep on small-grid shapes")
+    ap.add_argument("--choice", action="store_true", help="default config choice against the candidates")
     ap.add_argument("--md", default=None, help="write the table (markdown) here")
     args = ap.parse_args()
     if args.split:
         return split_sweep(args.md)
+    if args.choice:
+        return choice_sweep(args.md)
 
     import torch
 
