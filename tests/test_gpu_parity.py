@@ -117,6 +117,26 @@ def test_workload_full_size_sampled(name):
     assert not np.any((c & 0x7C00) == 0x7C00), "inf/NaN in output"
 
 
+# Shapes on which the default choice takes each tile config by its round count (256 x 192
+# in one round, 256 x 192 over three rounds, 256 x 128 in one round, 256 x 256 in one).
+CHOICE_SHAPES = [(3072, 3072, 4096, "m256x192"), (6144, 6144, 1024, "m256x192"),
+                 (2560, 2560, 2048, "m256x128"), (3584, 3584, 2048, "m256x256")]
+
+
+@pytest.mark.parametrize("M,N,K,prefix", CHOICE_SHAPES)
+def test_default_choice_shapes_sampled(M, N, K, prefix):
+    """The config the library picks on its own for mid-size and multi-round grids, against
+    the oracle on whole sampled rows and columns plus random entries."""
+    A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=77)
+    cfg = tg.tgemm_select_config(M, N, K)
+    log(f"default choice {M}x{N}x{K}: cfg {cfg}")
+    assert tg.tgemm_config_desc(cfg)["name"].startswith(prefix)
+    c = run(A, B, True)
+    rng = np.random.default_rng(M + N + K)
+    rows, cols = sample_entries(M, N, rng, n_rows=3, n_cols=3, n_rand=4096)
+    assert_close(c[rows, cols], oracle.gemm_entries(A, B, rows, cols, True), K, 1.0, f"{M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("name", ["plain_4096", "relu_tall_16384x512x4096", "relu_8192"])
 def test_workload_full_size_every_element(name):
     """The whole output of each full-size workload against the whole oracle matrix."""

@@ -211,14 +211,16 @@ def tgemm_config_desc(idx: int) -> dict:
     return info.as_dict()
 
 
-def tgemm_select_config(M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None) -> int:
+def tgemm_select_config(M, N, K, A=256, lda=None, B=256, ldb=None, C=256, ldc=None) -> int:
+    """Config index gemm_f16 would use for these arguments (the pointers are only checked
+    for null and alignment, never dereferenced: the defaults stand for aligned buffers)."""
     lda = max(1, K) if lda is None else lda
     ldb = max(1, N) if ldb is None else ldb
     ldc = max(1, N) if ldc is None else ldc
     return int(lib().tgemm_select_config(M, N, K, A, lda, B, ldb, C, ldc))
 
 
-def tgemm_select_config_ex(trans_a, trans_b, M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None) -> int:
+def tgemm_select_config_ex(trans_a, trans_b, M, N, K, A=256, lda=None, B=256, ldb=None, C=256, ldc=None) -> int:
     lda = max(1, M if trans_a else K) if lda is None else lda
     ldb = max(1, K if trans_b else N) if ldb is None else ldb
     ldc = max(1, N) if ldc is None else ldc
