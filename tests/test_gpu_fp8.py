@@ -215,6 +215,22 @@ def test_fp8_linear_end_to_end():
         tg.fp8_block_scaled_linear(xd, wd, swd, block=64)
 
 
+# ---------------------------------------------------------------- default choice by rounds
+@pytest.mark.parametrize("M,N,K,cfg", [(3072, 3072, 2048, 0), (2560, 2560, 2048, 3), (2048, 2048, 1024, 1)])
+def test_default_choice_shapes_sampled(M, N, K, cfg):
+    """The config the library picks by round count (256 x 256 in one round of 144 tiles,
+    256 x 128 in one round of 200, 128 x 128 in one round of 256), against the oracle on
+    sampled rows, columns and random entries."""
+    assert tg.tgemm_fp8_select_config(M, N, K) == cfg
+    A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=78)
+    log(f"fp8 default choice {M}x{N}x{K} cfg {cfg}")
+    c = _gemm(A, SA, B, SB, True)
+    rows, cols = sample_entries(M, N, np.random.default_rng(M + K), n_rows=3, n_cols=3, n_rand=4096)
+    rep = oracle.compare_fp8(c[rows, cols], oracle.gemm_fp8_entries(A, SA, B, SB, rows, cols, True),
+                             oracle.fp8_bound_entries(A, SA, B, SB, rows, cols))
+    assert rep["fails"] == 0, rep
+
+
 # ---------------------------------------------------------------- measured workloads
 @pytest.mark.parametrize("name", ["fp8_block_4096", "fp8_block_relu_8192"])
 def test_workload_sampled(name):
