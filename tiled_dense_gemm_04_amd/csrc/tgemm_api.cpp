@@ -77,8 +77,12 @@ int64_t workgroups(const Config& c, int64_t M, int64_t N) {
 // 128 x 128 against 53.1 us with 256 x 128; 3072^2 74.3 us with 256 x 192 against 102.8 us
 // for 128 x 128 in three rounds); beyond one round, 256 x 192 tiles if they need no more
 // rounds than 256 x 256 ones (6144^2 x 4096: 255 against 275 us), else 256 x 256.
-// Transposed operands take the ping-pong kernels only (15 instead of 7).
-constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15, kCfgMid = 16, kCfg192 = 18;
+// Transposed operands take the ping-pong kernels only (15 instead of 7). 14 = config 9
+// without the XCD remap, for A and B as given when all 256 x 256 tiles fit one round: the
+// hardware's round-robin dispatch then also gives each XCD a 4 x 8 block of tiles (one
+// tile-row of each of four panels), and measured 0.6-1.5 % faster at 4096^3 on three boxes;
+// over several rounds the remap keeps each XCD's tiles together and wins (8192^3: 1-1.5 %).
+constexpr int kCfgBig = 9, kCfgSmall = 7, kCfgSmallT = 15, kCfgMid = 16, kCfg192 = 18, kCfgBigOneRound = 14;
 constexpr int64_t kRound = 256;  // workgroups in flight at once: one per compute unit
 int choose_fast(int layout, int64_t M, int64_t N, int64_t K) {
   (void)K;
@@ -89,7 +93,7 @@ int choose_fast(int layout, int64_t M, int64_t N, int64_t K) {
   if (t128 <= kRound) return layout == 0 ? kCfgSmall : kCfgSmallT;
   if (t256x128 <= kRound) return kCfgMid;
   if (t192 <= kRound) return kCfg192;
-  if (t256 <= kRound) return kCfgBig;
+  if (t256 <= kRound) return layout == 0 ? kCfgBigOneRound : kCfgBig;
   return tgemm::ceil_div(t192, kRound) <= tgemm::ceil_div(t256, kRound) ? kCfg192 : kCfgBig;
 }
 

@@ -44,7 +44,8 @@ CHOICE_SHAPES = [(1024, 1024, 4096), (1536, 1536, 4096), (2048, 2048, 4096), (25
                  (4096, 2560, 2048), (4095, 3000, 1000), (4096, 3072, 1024), (3072, 4096, 4096),
                  (5120, 4096, 4096), (6144, 6144, 4096)]
 CHOICE_F16 = ["p128x128x64_s2_w2x2_p4_x1", "m128x128x32_s4_w2x4_p4_x1", "m256x128x32_s4_w2x4_p4_x1",
-              "m128x256x32_s4_w2x4_p4_x1", "m256x192x32_s4_w2x4_p4_x1", "m256x256x32_s4_w2x4_p4_x1"]
+              "m128x256x32_s4_w2x4_p4_x1", "m256x192x32_s4_w2x4_p4_x1", "m256x256x32_s4_w2x4_p4_x1",
+              "m256x256x32_s4_w2x4_p4_x0"]
 
 
 def choice_sweep(md_path=None):
