@@ -6,15 +6,19 @@ fp16 inputs drawn N(0,1) from seed 2, fp32 accumulate, fp16 out, row-major), inp
 already resident in HBM. W untimed warm-up steps, then exactly K timed steps bracketed
 by device synchronisation. Prints ONE JSON line on stdout; details go to stderr.
 
-From idle, the GPU raises its clocks over the first ~25 ms of load (about 200 calls at
-4096^3, each 10-30 % slower than the steady state); the default warm-up (400 calls,
-~45 ms) lies past that ramp, so the timed steps measure sustained throughput.
+From idle, the board's power control brings the clocks to their sustained level over the
+first few hundred calls (at 4096^3, calls 20-200 run 10-30 % slower than the steady state).
+Before the W counted warm-up steps, a settle phase therefore runs back-to-back calls for
+--settle-ms of wall time (default 300 ms), untimed, so that even a short run (W = 5) times
+the sustained state; the JSON line reports it as "settle" and names the clock state.
 
   value            = 2*M*N*K*steps / wall time of the timed steps, in TFLOP/s
   roofline.achieved = 2*M*N*K / mean kernel duration, from HIP events recorded on the
                      stream the kernels are launched on, against the dense fp16 MFMA peak
   cpu_baseline     = the CPU oracle (as it stands) timed on the host on a slab of rows of
-                     the same workload, in TFLOP/s, with the threads it used
+                     the same workload, in TFLOP/s: "cores" = the threads it used; also
+                     the host's CPU count and model, and the oracle on one thread over the
+                     1024^3 GEMM + ReLU (the pages' first example) for a per-core figure
 
 --workload also takes the fp8 block-scaled workloads (fp8_block_4096, fp8_block_relu_8192:
 one gemm_fp8_block call per step on pre-quantized E4M3 inputs; fp8_linear_4096: the 1 x 128
@@ -67,6 +71,39 @@ def load_traffic(workload: str, cfg_name: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def host_cpu() -> dict:
+    """The host the oracle runs on: logical CPUs, the ones this process may use, the model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"host_cpus": os.cpu_count(), "host_cpus_usable": usable, "cpu_model": model}
+
+
+def one_thread_1024():
+    """The oracle on one thread over relu_1024 (1024^3 GEMM + ReLU, N(0,1), seed 1): TFLOP/s."""
+    import oracle
+    import tgemm_workloads as W
+
+    w = W.by_name("relu_1024")
+    A, B = w.inputs()
+    t = time.perf_counter()
+    oracle.default().gemm(A, B, w.relu, nthreads=1)
+    dt = time.perf_counter() - t
+    eprint(f"cpu oracle, one thread, relu_1024: {dt:.2f} s ({w.flop / dt / 1e9:.2f} GFLOP/s)")
+    return {"workload": "relu_1024", "threads": 1, "seconds": round(dt, 3), "value": w.flop / dt / 1e12,
+            "unit": "TFLOP/s"}
+
+
 def cpu_baseline(A, B, relu, c_gpu_bits, target_s: float):
     """Time the oracle on the first R rows of the workload; R sized for ~target_s."""
     import numpy as np
@@ -98,6 +135,8 @@ def cpu_baseline(A, B, relu, c_gpu_bits, target_s: float):
         "kind": "oracle",
         "sample": f"first {rows} of {M} rows of the same workload (all N={N} columns, K={K}), "
                   f"{dt:.1f} s; GPU output on those rows vs oracle: {rep['fails']} tolerance failures",
+        **host_cpu(),
+        "per_core": one_thread_1024(),
     }
 
 
@@ -127,7 +166,26 @@ def cpu_baseline_fp8(A, SA, B, SB, relu, c_gpu_bits, target_s: float):
         "kind": "oracle",
         "sample": f"first {rows} of {M} rows of the same workload (all N={N} columns, K={K}), "
                   f"{dt:.1f} s; GPU output on those rows vs oracle: {rep['fails']} tolerance failures",
+        **host_cpu(),
     }
+
+
+def settle(step, torch, ms: float) -> dict:
+    """Untimed back-to-back calls for >= ms of wall time, so the clocks reach their
+    sustained level before the counted warm-up."""
+    torch.cuda.synchronize()
+    calls, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(16):
+            step()
+        calls += 16
+        torch.cuda.synchronize()
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "calls": calls}
+
+
+def clock_state(st: dict, warmup: int) -> str:
+    return (f"settled: {st['calls']} untimed back-to-back calls ({st['ms']} ms) before the {warmup} counted "
+            f"warm-up steps, so the timed steps run at the sustained clock")
 
 
 def bench_fp8(args, W, tg, torch, np) -> int:
@@ -157,7 +215,7 @@ def bench_fp8(args, W, tg, torch, np) -> int:
             tg.quant_fp8_block(xd, 1, a, sa, stream=stream)
         tg.gemm_fp8_block(a, sa, b, sb, c, relu=w.relu, stream=stream)
 
-    torch.cuda.synchronize()
+    st = settle(step, torch, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -191,6 +249,8 @@ def bench_fp8(args, W, tg, torch, np) -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "traffic": load_traffic(w.name, cfg_name), "kernel_us": round(step_ms * 1e3, 3),
                      "kernel_source_hash": kernel_source_hash()},
+        "settle": st,
+        "clock_state": clock_state(st, args.warmup),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and not w.linear:
@@ -210,6 +270,8 @@ def main() -> int:
     ap.add_argument("--cfg", type=int, default=None, help="force a config index (sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back calls for this long before the counted warm-up")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -265,7 +327,7 @@ def main() -> int:
     def step():
         tg.gemm_f16_ex(a, b, c, w.trans_a, w.trans_b, relu=w.relu, stream=stream, cfg=args.cfg)
 
-    torch.cuda.synchronize()
+    st = settle(step, torch, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -325,6 +387,8 @@ def main() -> int:
             "kernel_us": round(kern_ms * 1e3, 3),
             "kernel_source_hash": kernel_source_hash(),
         },
+        "settle": st,
+        "clock_state": clock_state(st, args.warmup),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

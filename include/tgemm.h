@@ -40,8 +40,7 @@ extern "C" {
 #define TGEMM_OK 0
 #define TGEMM_EINVAL_DIM (-1)   /* M, N or K negative, or larger than TGEMM_MAX_DIM        */
 #define TGEMM_EINVAL_LD (-2)    /* lda < max(1,K), ldb < max(1,N), ldc < max(1,N) (with    */
-                                /* transposed operands lda < max(1,M), ldb < max(1,K)), or */
-                                /* an ld larger than TGEMM_MAX_LD                          */
+                                /* transposed operands lda < max(1,M), ldb < max(1,K))     */
 #define TGEMM_ENULL (-3)        /* NULL pointer for an operand with a nonzero extent        */
 #define TGEMM_EDEVICE (-4)      /* current HIP device is not gfx950, or no device           */
 #define TGEMM_ELAUNCH (-5)      /* the kernel launch was rejected by the HIP runtime        */
@@ -51,7 +50,11 @@ extern "C" {
 #define TGEMM_EWORKSPACE (-8)   /* workspace smaller than tgemm_workspace_bytes requires    */
 
 #define TGEMM_MAX_DIM ((int64_t)1 << 31)  /* M, N, K must be < 2^31                        */
-#define TGEMM_MAX_LD ((int64_t)1 << 22)   /* lda, ldb, ldc must be <= 2^22 elements         */
+/* Any leading dimension at or above the row length is served. The fast kernels address
+ * a 256-row operand tile through a 32-bit buffer range, so lda and ldb above
+ * TGEMM_FAST_MAX_LD elements (binary16; bytes for fp8 codes: twice that) take the
+ * generic kernels, which index in 64 bits. ldc is not limited. */
+#define TGEMM_FAST_MAX_LD ((int64_t)1 << 22)
 
 /*
  * C = ReLU(A @ B) if relu != 0, else C = A @ B.
@@ -62,9 +65,10 @@ extern "C" {
  *               M x N elements are written, padding between rows is untouched.
  *   relu      : 0 = plain GEMM, any other value = fused ReLU.
  *   stream    : hipStream_t as void*, NULL for the default stream.
- * The fast path needs A, B, C 16-byte aligned, lda, ldb, ldc multiples of 8 and K, N
- * multiples of 8; other arguments take a slower generic kernel with the same results
- * (within the stated tolerance; both accumulate in float32).
+ * The fast path needs A, B, C 16-byte aligned, lda, ldb, ldc multiples of 8, lda and
+ * ldb at most TGEMM_FAST_MAX_LD, and K, N multiples of 8; other arguments take a slower
+ * generic kernel with the same results (within the stated tolerance; both accumulate in
+ * float32).
  * Returns TGEMM_OK or a negative TGEMM_E* code.
  */
 TGEMM_API int gemm_f16(int64_t M, int64_t N, int64_t K,
@@ -83,9 +87,9 @@ TGEMM_API int gemm_f16(int64_t M, int64_t N, int64_t K,
  *   trans_b == 0 : op(B) = B, stored K x N row-major, ldb >= max(1, N);
  *   trans_b != 0 : op(B) = B^T, B stored N x K row-major, ldb >= max(1, K).
  * Everything else as gemm_f16 (which is gemm_f16_ex(0, 0, ...)). The fast path needs A, B,
- * C 16-byte aligned, lda, ldb, ldc multiples of 8, N a multiple of 8 and each operand's
- * contiguous dimension (K for A and for B^T, M for A^T, N for B) a multiple of 8; other
- * arguments take the generic kernel. On the fast path the result is bit-for-bit the same
+ * C 16-byte aligned, lda, ldb, ldc multiples of 8, lda and ldb at most TGEMM_FAST_MAX_LD,
+ * N a multiple of 8 and each operand's contiguous dimension (K for A and for B^T, M for
+ * A^T, N for B) a multiple of 8; other arguments take the generic kernel. On the fast path the result is bit-for-bit the same
  * for all four layouts of the same logical operands.
  */
 TGEMM_API int gemm_f16_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
@@ -121,6 +125,14 @@ TGEMM_API int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_
                           const void* B, int64_t ldb,
                           void* C, int64_t ldc,
                           int relu, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * The workspace bytes gemm_f16_ws_cfg needs for config idx and split count splits over an
+ * M x N output: 0 when splits == 1, else a 4 KiB counter region plus splits fp32 partial
+ * tiles per output tile. TGEMM_EINVAL_CFG when gemm_f16_ws_cfg would reject idx or splits
+ * for this output, TGEMM_EINVAL_DIM for sizes outside [0, 2^31). Pure host logic.
+ */
+TGEMM_API int64_t tgemm_workspace_bytes_cfg(int idx, int splits, int64_t M, int64_t N);
 
 /*
  * Grouped GEMM: count independent GEMMs C_i = ReLU?(op(A_i) @ op(B_i)) with one operand
@@ -177,9 +189,9 @@ TGEMM_API const char* tgemm_version(void);
  * 128 products are summed by the fp8 matrix instructions (exact products; their block sum
  * may deviate from the exact one by up to about 2^-10 of the block's largest product) and
  * the scaled block sums are accumulated in float32 -- the per-block promotion the scaling
- * is for. The fast path needs A and B 16-byte aligned, lda, ldb and K multiples of 16, C
- * 16-byte aligned and ldc, N multiples of 8; other arguments take a generic kernel that
- * sums each block in float32. M == 0 or N == 0 is a no-op, K == 0 writes C = 0. Device
+ * is for. The fast path needs A and B 16-byte aligned, lda, ldb and K multiples of 16,
+ * lda and ldb at most 2 * TGEMM_FAST_MAX_LD bytes, C 16-byte aligned and ldc, N multiples
+ * of 8; other arguments take a generic kernel that sums each block in float32. M == 0 or N == 0 is a no-op, K == 0 writes C = 0. Device
  * pointers, ownership, streams and errors as for gemm_f16; scale_a and scale_b must be
  * 4-byte aligned (else TGEMM_EALIGN) and, when K > 0, non-NULL (else TGEMM_ENULL).
  */

@@ -120,6 +120,32 @@ def test_strided_operands():
     c, _ = _check(A, SA, B, SB, True, a_pad=8, what="lda = K + 8")
 
 
+def test_strides_past_fast_limit():
+    """Byte strides above 2^23 (past the fast kernels' 32-bit buffer ranges) are served by
+    the generic kernel, against the oracle; the quantizer takes them with 64-bit indexing."""
+    torch = torch_cuda()
+    M, N, K = 20, 24, 272
+    A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=703)
+    big = (1 << 23) + 16
+    assert tg.tgemm_fp8_select_config(M, N, K, lda=big, ldb=big) == tg.FP8_GENERIC
+    log("fp8 lda = ldb = 2^23 + 16 bytes")
+    _check(A, SA, B, SB, True, a_pad=big - K, b_pad=big - K, what="lda = ldb = 2^23 + 16")
+    R, Kx = 6, 384
+    x = _quant_inputs(R, Kx, 804)
+    Qr, Sr = oracle.quant_fp8(x, 1)
+    ld = (1 << 22) + 8
+    xbuf = torch.zeros(((R - 1) * ld + Kx,), dtype=torch.float16, device="cuda")
+    qbuf = torch.zeros(((R - 1) * ld + Kx,), dtype=torch.uint8, device="cuda")
+    for i in range(R):
+        xbuf[i * ld:i * ld + Kx] = to_dev(x[i])
+    xd, qd = xbuf.as_strided((R, Kx), (ld, 1)), qbuf.as_strided((R, Kx), (ld, 1))
+    log("quant ldx = ldq = 2^22 + 8")
+    q, sc = tg.quant_fp8_block(xd, 1, q=qd)
+    torch.cuda.synchronize()
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), Sr.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), Qr)
+
+
 def test_zero_k_and_empty():
     torch = torch_cuda()
     a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")

@@ -107,6 +107,26 @@ def test_autograd_backward(gpu):
     assert_close(b.grad.cpu().numpy().view(np.uint16), dB_ref, M, what="dB = A^T @ dC")
 
 
+def test_autograd_broadcast_gradient(gpu):
+    """An upstream gradient that is a broadcast view (stride 0 along rows, as C.sum(0)
+    gives) is made dense before the backward GEMMs; dA and dB against the oracle."""
+    torch = gpu
+    M, N, K = 264, 136, 96
+    A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=44)
+    v, _ = W.make_inputs(1, 8, N, "normal", 1.0, seed=45)   # a 1 x N weight row
+    a = to_dev(A).requires_grad_(True)
+    b = to_dev(B).requires_grad_(True)
+    log("autograd with a broadcast upstream gradient")
+    c = tg.GemmFunction.apply(a, b)
+    (c.sum(0).float() * to_dev(v[0]).float()).sum().backward()   # dC = v broadcast over rows
+    torch.cuda.synchronize()
+    dC = np.repeat(v, M, axis=0)
+    dA_ref = oracle.gemm(dC, np.ascontiguousarray(B.T), False)
+    dB_ref = oracle.gemm(np.ascontiguousarray(A.T), dC, False)
+    assert_close(a.grad.cpu().numpy().view(np.uint16), dA_ref, N, what="dA, broadcast dC")
+    assert_close(b.grad.cpu().numpy().view(np.uint16), dB_ref, M, what="dB, broadcast dC")
+
+
 def test_matmul_views_match_explicit_layouts(gpu):
     torch = gpu
     M, N, K = 264, 136, 128

@@ -308,7 +308,7 @@ def test_k_zero_and_empty():
 
 
 def test_max_leading_dimension():
-    """lda at the documented maximum (2^22 elements): buffer ranges stay below 2^31 bytes."""
+    """lda at the fast kernels' limit (2^22 elements): buffer ranges stay below 2^31 bytes."""
     torch = torch_cuda()
     M, N, K = 3, 128, 64
     lda = 1 << 22
@@ -323,6 +323,45 @@ def test_max_leading_dimension():
         c = tg.gemm_f16(a, b, relu=False, cfg=cfg)
         torch.cuda.synchronize()
         assert_close(c.cpu().numpy().view(np.uint16), oracle.gemm(A, B, False), K)
+
+
+def _strided(X, ld, torch):
+    """Device view of the rows of X with row stride ld (elements)."""
+    R, C = X.shape
+    buf = torch.zeros(((R - 1) * ld + C,), dtype=torch.float16, device="cuda")
+    for i in range(R):
+        buf[i * ld:i * ld + C] = to_dev(X[i])
+    return buf.as_strided((R, C), (ld, 1))
+
+
+def test_leading_dimension_past_fast_limit():
+    """Row strides above 2^22 elements are served (by the generic kernel, 64-bit indexing),
+    in every layout, against the oracle; ldc is not limited at all."""
+    torch = torch_cuda()
+    M, N, K = 40, 72, 56
+    big = (1 << 22) + 8
+    A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=13)
+    for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+        a = _strided(A.T if ta else A, big, torch)
+        b = _strided(B.T if tb else B, big, torch)
+        assert tg.tgemm_select_config_ex(ta, tb, M, N, K, a.data_ptr(), big, b.data_ptr(), big,
+                                         256, N) == 0
+        log(f"lda = ldb = 2^22 + 8, layout ({ta}, {tb})")
+        c = tg.gemm_f16_ex(a, b, trans_a=bool(ta), trans_b=bool(tb), relu=True)
+        torch.cuda.synchronize()
+        assert_close(c.cpu().numpy().view(np.uint16), oracle.gemm(A, B, True), K, what=f"layout {ta}{tb}")
+    # a huge ldc with fast-path operands: only C's rows are far apart
+    Mc, Nc, Kc = 3, 256, 128
+    A2, B2 = W.make_inputs(Mc, Nc, Kc, "normal", 1.0, seed=14)
+    ldc = (1 << 23) + 64
+    cbuf = torch.full(((Mc - 1) * ldc + Nc,), float("nan"), dtype=torch.float16, device="cuda")
+    c = cbuf.as_strided((Mc, Nc), (ldc, 1))
+    assert tg.tgemm_select_config(Mc, Nc, Kc, 256, Kc, 256, Nc, 256, ldc) > 0
+    log("ldc = 2^23 + 64 on the fast path")
+    tg.gemm_f16(to_dev(A2), to_dev(B2), c, relu=False)
+    torch.cuda.synchronize()
+    assert_close(c.cpu().numpy().view(np.uint16), oracle.gemm(A2, B2, False), Kc, what="big ldc")
+    assert torch.isnan(cbuf[Nc:ldc]).all(), "padding between C rows was written"
 
 
 def test_pages_own_check():

@@ -36,7 +36,7 @@ def exported(path):
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 24, syms
+    assert len(syms) == 25, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -138,8 +138,15 @@ def test_select_rejects_bad_ld_null_align():
     assert s(8, 8, 8, A16, 7, A16, 8, A16, 8) == tg.TGEMM_EINVAL_LD
     assert s(8, 8, 8, A16, 8, A16, 7, A16, 8) == tg.TGEMM_EINVAL_LD
     assert s(8, 8, 8, A16, 8, A16, 8, A16, 7) == tg.TGEMM_EINVAL_LD
-    assert s(8, 8, 8, A16, (1 << 22) + 8, A16, 8, A16, 8) == tg.TGEMM_EINVAL_LD
-    assert s(8, 8, 8, A16, 1 << 22, A16, 8, A16, 8) >= 0
+    # any ld at or above the row length is valid: operand strides past the fast kernels'
+    # 32-bit buffer ranges take the generic kernel, ldc is not limited
+    assert s(8, 8, 8, A16, 1 << 22, A16, 8, A16, 8) > 0
+    assert s(8, 8, 8, A16, (1 << 22) + 8, A16, 8, A16, 8) == 0
+    assert s(8, 8, 8, A16, 8, A16, (1 << 22) + 8, A16, 8) == 0
+    assert s(8, 8, 8, A16, 1 << 40, A16, 1 << 40, A16, 8) == 0
+    assert s(8, 8, 8, A16, 8, A16, 8, A16, 1 << 40) > 0
+    assert tg.tgemm_select_config_ex(1, 1, 8, 8, 8, A16, (1 << 22) + 8, A16, 8, A16, 8) == 0
+    assert tg.tgemm_select_config_ex(1, 1, 8, 8, 8, A16, 8, A16, (1 << 22) + 8, A16, 8) == 0
     assert s(8, 8, 8, 0, 8, A16, 8, A16, 8) == tg.TGEMM_ENULL
     assert s(8, 8, 8, A16, 8, 0, 8, A16, 8) == tg.TGEMM_ENULL
     assert s(8, 8, 8, A16, 8, A16, 8, 0, 8) == tg.TGEMM_ENULL
@@ -366,6 +373,12 @@ def test_fp8_select():
     assert s(256, 256, 256, A=256 + 8) == tg.FP8_GENERIC
     assert s(256, 256, 256, C=256 + 2) == tg.FP8_GENERIC
     assert s(255, 256, 4000) == 1                         # ragged M and K (16 | K) stay fast
+    # any ld at or above K is valid: byte strides past 2^23 take the generic kernel
+    fast = s(256, 256, 256)
+    assert fast >= 0 and s(256, 256, 256, lda=1 << 23) == fast
+    assert s(256, 256, 256, lda=(1 << 23) + 16) == tg.FP8_GENERIC
+    assert s(256, 256, 256, ldb=(1 << 23) + 16) == tg.FP8_GENERIC
+    assert s(256, 256, 256, ldc=(1 << 40)) == fast
     # errors
     assert s(-1, 8, 8) == tg.TGEMM_EINVAL_DIM
     assert s(8, 8, 32, lda=16) == tg.TGEMM_EINVAL_LD
@@ -402,3 +415,29 @@ def test_fp8_quant_rejects_invalid_before_hip():
     assert q(8, 128, P + 1, 128, 1, P, 128, S, None) == tg.TGEMM_EALIGN
     assert q(8, 128, P, 128, 128, P, 128, S + 2, None) == tg.TGEMM_EALIGN
     assert q(0, 128, 0, 128, 1, 0, 128, 0, None) == tg.TGEMM_OK               # no-op
+    # no upper bound on the strides (the quantizer indexes in 64 bits): a huge ld is not an
+    # argument error, so the call goes on to the device check (no GPU here: TGEMM_EDEVICE)
+    assert q(8, 128, P, 1 << 40, 1, P, 1 << 40, S, None) in (tg.TGEMM_OK, tg.TGEMM_EDEVICE)
+
+
+def test_workspace_bytes_cfg():
+    """The per-config workspace query is the layout gemm_f16_ws_cfg checks against: 0 when
+    unsplit, else 4 KiB of counters plus splits fp32 partial tiles per output tile."""
+    q = tg.tgemm_workspace_bytes_cfg
+    for idx, c in enumerate(tg.configs()):
+        for M, N in ((1, 1), (520, 392), (1024, 1024)):
+            assert q(idx, 1, M, N) == 0
+            tiles = -(-M // c["block_m"]) * -(-N // c["block_n"])
+            splittable = not c["generic"] and c["layouts"] == 0xF and tiles <= 1024
+            for splits in (2, 8):
+                if splittable:
+                    assert q(idx, splits, M, N) == 4096 + tiles * splits * c["block_m"] * c["block_n"] * 4
+                else:
+                    with pytest.raises(tg.TgemmError):
+                        q(idx, splits, M, N)
+    with pytest.raises(tg.TgemmError):
+        q(tg.tgemm_num_configs(), 1, 8, 8)
+    with pytest.raises(tg.TgemmError):
+        q(0, 9, 8, 8)
+    with pytest.raises(tg.TgemmError):
+        q(0, 1, -1, 8)

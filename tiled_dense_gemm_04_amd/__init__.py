@@ -11,7 +11,8 @@ The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
 ``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``,
 ``tgemm_mfma_probe``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
 stream unless given), ``gemm_f16_ws_cfg`` (as ``cfg=``/``splits=``),
-``tgemm_workspace_bytes`` and ``tgemm_split_plan``; grouped GEMMs: ``gemm_f16_grouped``;
+``tgemm_workspace_bytes``, ``tgemm_workspace_bytes_cfg`` and ``tgemm_split_plan``; grouped
+GEMMs: ``gemm_f16_grouped``;
 the fp8 (E4M3) block-scaled path: ``gemm_fp8_block`` (``gemm_fp8_block_cfg`` as
 ``cfg=``), ``quant_fp8_block``, ``tgemm_fp8_num_configs``, ``tgemm_fp8_config_desc``,
 ``tgemm_fp8_select_config``, and ``fp8_block_scaled_linear`` (quantize x per 1 x 128
@@ -51,9 +52,11 @@ EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_
            "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups", "tgemm_mfma_probe",
            "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan",
            "gemm_f16_grouped", "gemm_fp8_block", "gemm_fp8_block_cfg", "quant_fp8_block",
-           "tgemm_fp8_num_configs", "tgemm_fp8_config_desc", "tgemm_fp8_select_config")
+           "tgemm_fp8_num_configs", "tgemm_fp8_config_desc", "tgemm_fp8_select_config",
+           "tgemm_workspace_bytes_cfg")
 # The extra symbols include/tgemm_stamps.h declares (instrumented build only).
 STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear")
+FAST_MAX_LD = 1 << 22        # TGEMM_FAST_MAX_LD
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
 PROBE_MFMA_PER_ITER = 16     # TGEMM_PROBE_MFMA_PER_ITER
 PROBE_FLOP_PER_MFMA = 2 * 16 * 16 * 32
@@ -128,6 +131,8 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.gemm_f16_ws_cfg.argtypes = [i32, i32, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p, i64, p]
     L.tgemm_workspace_bytes.restype = i64
     L.tgemm_workspace_bytes.argtypes = [i32, i32, i64, i64, i64]
+    L.tgemm_workspace_bytes_cfg.restype = i64
+    L.tgemm_workspace_bytes_cfg.argtypes = [i32, i32, i64, i64]
     L.gemm_f16_grouped.restype = i32
     L.gemm_f16_grouped.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, p]
     L.tgemm_split_plan.restype = i32
@@ -229,6 +234,15 @@ def tgemm_select_config_ex(trans_a, trans_b, M, N, K, A=256, lda=None, B=256, ld
 
 def tgemm_workspace_bytes(trans_a, trans_b, M, N, K) -> int:
     return int(lib().tgemm_workspace_bytes(int(trans_a), int(trans_b), M, N, K))
+
+
+def tgemm_workspace_bytes_cfg(idx, splits, M, N) -> int:
+    """Workspace bytes gemm_f16_ws_cfg needs for config idx with `splits` splits over an
+    M x N output (raises for a combination the library would reject)."""
+    n = int(lib().tgemm_workspace_bytes_cfg(int(idx), int(splits), M, N))
+    if n < 0:
+        raise TgemmError(n, f"tgemm_workspace_bytes_cfg[{idx}, {splits}]")
+    return n
 
 
 def tgemm_split_plan(trans_a, trans_b, M, N, K, A=256, lda=None, B=256, ldb=None, C=256, ldc=None):
@@ -403,9 +417,7 @@ def gemm_f16_ws(a, b, c=None, trans_a: bool = False, trans_b: bool = False, relu
             need = tgemm_split_plan(trans_a, trans_b, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb,
                                     c.data_ptr(), ldc)[2]
         else:
-            d = tgemm_config_desc(cfg)
-            tiles = -(-M // d["block_m"]) * -(-N // d["block_n"])
-            need = 4096 + tiles * splits * d["block_m"] * d["block_n"] * 4 if splits > 1 else 0
+            need = tgemm_workspace_bytes_cfg(cfg, splits, M, N)
         workspace = workspace_for(need, a.device, handle) if need else None
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -490,6 +502,16 @@ def matmul(a, b, relu: bool = False, out=None, stream=None):
     return gemm_f16_ws(sa, sb, out, ta, tb, relu, stream)
 
 
+def _dense_2d(x):
+    """x itself if it is a row- or column-major view the library can take (strides at
+    least the row or column length), else a contiguous copy: an upstream gradient may be
+    a broadcast view with stride 0 (e.g. from C.sum(0))."""
+    rows, cols = x.shape
+    row_major = (cols <= 1 or x.stride(1) == 1) and (rows <= 1 or x.stride(0) >= cols)
+    col_major = (rows <= 1 or x.stride(0) == 1) and (cols <= 1 or x.stride(1) >= rows)
+    return x if (row_major or col_major) else x.contiguous()
+
+
 def _autograd_function():
     import torch
 
@@ -506,7 +528,7 @@ def _autograd_function():
         @staticmethod
         def backward(ctx, dC):
             A, B = ctx.saved_tensors
-            dC = dC if dC.stride(-1) == 1 else dC.contiguous()
+            dC = _dense_2d(dC)
             dA = matmul(dC, B.t()) if ctx.needs_input_grad[0] else None
             dB = matmul(A.t(), dC) if ctx.needs_input_grad[1] else None
             return dA, dB

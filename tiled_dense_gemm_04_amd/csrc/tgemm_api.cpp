@@ -43,7 +43,6 @@ int validate(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t
   const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1, mmin = M > 1 ? M : 1;
   const int64_t amin = (layout & 2) ? mmin : kmin, bmin = (layout & 1) ? kmin : nmin;
   if (lda < amin || ldb < bmin || ldc < nmin) return TGEMM_EINVAL_LD;
-  if (lda > TGEMM_MAX_LD || ldb > TGEMM_MAX_LD || ldc > TGEMM_MAX_LD) return TGEMM_EINVAL_LD;
   const bool out_nonempty = M > 0 && N > 0;
   if (out_nonempty && C == nullptr) return TGEMM_ENULL;
   if (out_nonempty && K > 0 && (A == nullptr || B == nullptr)) return TGEMM_ENULL;
@@ -57,12 +56,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Can a fast (non-generic) config take these arguments? 16-byte chunks along each
 // operand's contiguous dimension (K for A as given and for B transposed, M for A
-// transposed, N for B as given) and along the rows of C.
+// transposed, N for B as given) and along the rows of C, and operand strides whose
+// 256-row tiles fit a 32-bit buffer range (the generic kernel indexes in 64 bits).
 bool fast_eligible(int layout, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                    const void* B, int64_t ldb, const void* C, int64_t ldc) {
   const int64_t a_contig = (layout & 2) ? M : K, b_contig = (layout & 1) ? K : N;
   return aligned16(A) && aligned16(B) && aligned16(C) && (lda % 8) == 0 && (ldb % 8) == 0 &&
-         (ldc % 8) == 0 && (a_contig % 8) == 0 && (b_contig % 8) == 0 && (N % 8) == 0;
+         (ldc % 8) == 0 && (a_contig % 8) == 0 && (b_contig % 8) == 0 && (N % 8) == 0 &&
+         lda <= TGEMM_FAST_MAX_LD && ldb <= TGEMM_FAST_MAX_LD;
 }
 
 int64_t workgroups(const Config& c, int64_t M, int64_t N) {
@@ -236,7 +237,6 @@ int fp8_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     return TGEMM_EINVAL_DIM;
   const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
   if (lda < kmin || ldb < kmin || ldc < nmin) return TGEMM_EINVAL_LD;
-  if (lda > TGEMM_MAX_LD || ldb > TGEMM_MAX_LD || ldc > TGEMM_MAX_LD) return TGEMM_EINVAL_LD;
   const bool out_nonempty = M > 0 && N > 0;
   if (out_nonempty && C == nullptr) return TGEMM_ENULL;
   if (out_nonempty && K > 0 && (A == nullptr || B == nullptr || SA == nullptr || SB == nullptr))
@@ -247,13 +247,15 @@ int fp8_validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   return TGEMM_OK;
 }
 
-// Fast configs need 16-byte operand rows in k (A, B), 16-byte output row segments (C), and
-// 32-bit scale offsets inside a 256-row tile.
+// Fast configs need 16-byte operand rows in k (A, B), 16-byte output row segments (C),
+// 32-bit scale offsets inside a 256-row tile, and operand strides whose 256-row tiles fit
+// a 32-bit buffer range (codes are one byte: twice the binary16 limit in elements).
 bool fp8_fast_eligible(int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                        const void* C, int64_t ldc) {
   const int64_t KB = tgemm::ceil_div(K, tgemm::kFp8Block);
   return aligned16(A) && aligned16(B) && aligned16(C) && lda % 16 == 0 && ldb % 16 == 0 && K % 16 == 0 &&
-         ldc % 8 == 0 && N % 8 == 0 && 256 * KB * 4 < ((int64_t)1 << 31);
+         ldc % 8 == 0 && N % 8 == 0 && 256 * KB * 4 < ((int64_t)1 << 31) && lda <= 2 * TGEMM_FAST_MAX_LD &&
+         ldb <= 2 * TGEMM_FAST_MAX_LD;
 }
 
 // Wave-quantized cost: one config's launch takes about ceil(tiles / 256) rounds of
@@ -380,7 +382,7 @@ int quant_fp8_block(int64_t R, int64_t K, const void* X, int64_t ldx, int block_
   if (R < 0 || K < 0 || R >= TGEMM_MAX_DIM || K >= TGEMM_MAX_DIM) return TGEMM_EINVAL_DIM;
   if (block_rows != 1 && block_rows != 128) return TGEMM_EINVAL_DIM;
   const int64_t kmin = K > 1 ? K : 1;
-  if (ldx < kmin || ldq < kmin || ldx > TGEMM_MAX_LD || ldq > TGEMM_MAX_LD) return TGEMM_EINVAL_LD;
+  if (ldx < kmin || ldq < kmin) return TGEMM_EINVAL_LD;
   if (R == 0 || K == 0) return TGEMM_OK;
   if (X == nullptr || Q == nullptr || scale == nullptr) return TGEMM_ENULL;
   if ((reinterpret_cast<uintptr_t>(X) & 1u) || (reinterpret_cast<uintptr_t>(scale) & 3u)) return TGEMM_EALIGN;
@@ -493,6 +495,14 @@ int gemm_f16_ws_cfg(int idx, int splits, int trans_a, int trans_b, int64_t M, in
   return run(idx, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, splits, workspace);
 }
 
+int64_t tgemm_workspace_bytes_cfg(int idx, int splits, int64_t M, int64_t N) {
+  if (idx < 0 || idx >= table_size() || splits < 1 || splits > kMaxSplits) return TGEMM_EINVAL_CFG;
+  if (M < 0 || N < 0 || M >= TGEMM_MAX_DIM || N >= TGEMM_MAX_DIM) return TGEMM_EINVAL_DIM;
+  const Config& c = cfg_row(idx);
+  if (splits > 1 && (!split_capable(c) || workgroups(c, M, N) > kMaxSplitTiles)) return TGEMM_EINVAL_CFG;
+  return ws_bytes(c, splits, M, N);
+}
+
 int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                 const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* workspace,
                 int64_t workspace_bytes, void* stream) {
@@ -596,7 +606,7 @@ const char* tgemm_strerror(int code) {
   switch (code) {
     case TGEMM_OK: return "success";
     case TGEMM_EINVAL_DIM: return "invalid dimension (negative, >= 2^31, or too many tiles)";
-    case TGEMM_EINVAL_LD: return "invalid leading dimension (below the stored row length or above 2^22)";
+    case TGEMM_EINVAL_LD: return "invalid leading dimension (below the stored row length)";
     case TGEMM_ENULL: return "null pointer for a non-empty operand";
     case TGEMM_EDEVICE: return "current HIP device is not gfx950 (MI355X) or is unavailable";
     case TGEMM_ELAUNCH: return "kernel launch failed";

@@ -41,6 +41,15 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
 
+// Stores of the output tile are non-temporal: C is written once and not read back by the
+// kernel, so it streams out instead of filling L2 with dirty lines that the end of the
+// kernel would have to write back (a 33.5 MB C from 256 workgroups: 6.2 us against 7.2 us
+// with ordinary stores, measured back to back on MI355X).
+template <typename V>
+__device__ __forceinline__ void store_c(_Float16* p, const V& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+}
+
 // Per-workgroup timestamps, compiled in only for the instrumented build (TGEMM_STAMPS) and
 // empty otherwise; finish() writes them to the table it is given (the library's one table,
 // defined next to the binary16 kernels and handed to the other kernels as an argument). Words per workgroup: wall clock (s_memrealtime, 100 MHz) at kernel

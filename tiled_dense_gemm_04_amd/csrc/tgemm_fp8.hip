@@ -400,7 +400,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     if (c >= CPR) continue;
     const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
     const int m = wm * WTM + r, n = wn * WTN + 8 * c;
-    if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
+    if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
   }
   clk.finish(nk, g.stamps);
 }

@@ -21,6 +21,7 @@
 #include <atomic>
 
 namespace tgemm {
+
 namespace {
 
 #ifdef TGEMM_STAMPS
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
           v3 = relu_f(v3);
         }
         half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        *(half4*)(crow + n) = h;
+        store_c(crow + n, h);
       }
     }
   }
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
           v3 = relu_f(v3);
         }
         half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        *(half4*)(crow + n) = h;
+        store_c(crow + n, h);
       }
     }
   }
@@ -787,7 +788,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
     if (c >= CPR) continue;
     const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
     const int m = wm * WTM + r, n = wn * WTN + 8 * c;
-    if (m < mvalid && n < nvalid) *(half8*)(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n) = x;
+    if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
   }
   clk.finish(nloc, TG_STAMP_TABLE);
 }
