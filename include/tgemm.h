@@ -135,6 +135,33 @@ TGEMM_API int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_
 TGEMM_API int64_t tgemm_workspace_bytes_cfg(int idx, int splits, int64_t M, int64_t N);
 
 /*
+ * gemm_f16_ws for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same operation,
+ * tile config and split plan, bit for bit the same results, but the split-K scratch (tile
+ * counters and fp32 partial tiles) is a static device array of the library instead of a
+ * caller workspace. The call allocates nothing and calls no allocating routine.
+ *   - The array holds TGEMM_STATIC_SCRATCH_BYTES bytes on every device the library runs
+ *     on, from the first use on that device until the process ends. A plan needing more
+ *     returns TGEMM_EWORKSPACE before anything is enqueued (the current split plans need
+ *     at most 4 KiB + 64 MiB: 256 partial tiles of 256 x 256 floats).
+ *   - The counters are zero when the library is loaded and every call leaves them at zero;
+ *     the partial tiles keep the last call's contents, which no later call reads before
+ *     writing.
+ *   - All calls on one device share the array: calls that may overlap in time on one
+ *     device (different streams, or different host threads) race and give wrong results.
+ *     Order them on one stream.
+ *   - The first call on a device looks the array's device address up
+ *     (hipGetSymbolAddress); make that first call outside graph capture.
+ * Arguments and return codes as gemm_f16_ex, plus TGEMM_EWORKSPACE as above.
+ */
+#define TGEMM_STATIC_SCRATCH_BYTES ((int64_t)4096 + ((int64_t)64 << 20))
+TGEMM_API int gemm_f16_ws_static(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                                 const void* A, int64_t lda,
+                                 const void* B, int64_t ldb,
+                                 void* C, int64_t ldc,
+                                 int relu, void* stream);
+
+/*
  * Grouped GEMM: count independent GEMMs C_i = ReLU?(op(A_i) @ op(B_i)) with one operand
  * layout and one ReLU flag for all, any sizes per GEMM (e.g. the experts of a
  * mixture-of-experts layer, each with its own number of rows: the "MoE GroupGEMM" planned

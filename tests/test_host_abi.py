@@ -36,7 +36,7 @@ def exported(path):
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 25, syms
+    assert len(syms) == 26, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -441,3 +441,14 @@ def test_workspace_bytes_cfg():
         q(0, 9, 8, 8)
     with pytest.raises(tg.TgemmError):
         q(0, 1, -1, 8)
+    # every split plan the library makes fits the static scratch of gemm_f16_ws_static
+    for M, N, K in ((512, 512, 16384), (2048, 2048, 131072), (128, 128, 1 << 20), (1024, 1024, 32768)):
+        assert tg.tgemm_split_plan(0, 0, M, N, K)[2] <= tg.STATIC_SCRATCH_BYTES
+
+
+def test_static_entry_rejects_before_hip():
+    s = tg.gemm_f16_ws_static_raw
+    assert s(0, 0, -1, 8, 8, 256, 8, 256, 8, 256, 8, 0, None) == tg.TGEMM_EINVAL_DIM
+    assert s(0, 0, 8, 8, 8, 256, 7, 256, 8, 256, 8, 0, None) == tg.TGEMM_EINVAL_LD
+    assert s(0, 0, 8, 8, 8, 0, 8, 256, 8, 256, 8, 0, None) == tg.TGEMM_ENULL
+    assert s(0, 0, 0, 8, 8, 0, 8, 0, 8, 0, 8, 0, None) == tg.TGEMM_OK

@@ -11,7 +11,8 @@ The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
 ``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``,
 ``tgemm_mfma_probe``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
 stream unless given), ``gemm_f16_ws_cfg`` (as ``cfg=``/``splits=``),
-``tgemm_workspace_bytes``, ``tgemm_workspace_bytes_cfg`` and ``tgemm_split_plan``; grouped
+``tgemm_workspace_bytes``, ``tgemm_workspace_bytes_cfg`` and ``tgemm_split_plan``, and
+``gemm_f16_ws_static`` (split-K scratch in a static device array: allocates nothing); grouped
 GEMMs: ``gemm_f16_grouped``;
 the fp8 (E4M3) block-scaled path: ``gemm_fp8_block`` (``gemm_fp8_block_cfg`` as
 ``cfg=``), ``quant_fp8_block``, ``tgemm_fp8_num_configs``, ``tgemm_fp8_config_desc``,
@@ -53,9 +54,10 @@ EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_
            "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan",
            "gemm_f16_grouped", "gemm_fp8_block", "gemm_fp8_block_cfg", "quant_fp8_block",
            "tgemm_fp8_num_configs", "tgemm_fp8_config_desc", "tgemm_fp8_select_config",
-           "tgemm_workspace_bytes_cfg")
+           "tgemm_workspace_bytes_cfg", "gemm_f16_ws_static")
 # The extra symbols include/tgemm_stamps.h declares (instrumented build only).
 STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear")
+STATIC_SCRATCH_BYTES = 4096 + (64 << 20)   # TGEMM_STATIC_SCRATCH_BYTES
 FAST_MAX_LD = 1 << 22        # TGEMM_FAST_MAX_LD
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
 PROBE_MFMA_PER_ITER = 16     # TGEMM_PROBE_MFMA_PER_ITER
@@ -133,6 +135,8 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.tgemm_workspace_bytes.argtypes = [i32, i32, i64, i64, i64]
     L.tgemm_workspace_bytes_cfg.restype = i64
     L.tgemm_workspace_bytes_cfg.argtypes = [i32, i32, i64, i64]
+    L.gemm_f16_ws_static.restype = i32
+    L.gemm_f16_ws_static.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p]
     L.gemm_f16_grouped.restype = i32
     L.gemm_f16_grouped.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, p]
     L.tgemm_split_plan.restype = i32
@@ -430,6 +434,38 @@ def gemm_f16_ws(a, b, c=None, trans_a: bool = False, trans_b: bool = False, relu
                                    b.data_ptr(), ldb, c.data_ptr(), ldc, int(relu), wptr, wbytes, handle)
     if rc != TGEMM_OK:
         raise TgemmError(rc, "gemm_f16_ws" if cfg is None else f"gemm_f16_ws_cfg[{cfg}, {splits}]")
+    return c
+
+
+def gemm_f16_ws_static_raw(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, library=None) -> int:
+    return (library or lib()).gemm_f16_ws_static(int(ta), int(tb), M, N, K, A, lda, B, ldb, C, ldc, int(relu),
+                                                 stream)
+
+
+def gemm_f16_ws_static(a, b, c=None, trans_a: bool = False, trans_b: bool = False, relu: bool = True,
+                       stream=None, library=None):
+    """gemm_f16_ws without a workspace (gemm_f16_ws_static): the split-K scratch is the
+    library's static device array, so the library allocates nothing. Calls on one device
+    must not overlap in time. ``c`` is allocated here only if not given."""
+    import torch
+    ra, ca, lda = _operand(a, "a")
+    rb, cb, ldb = _operand(b, "b")
+    M, K = (ca, ra) if trans_a else (ra, ca)
+    K2, N = (cb, rb) if trans_b else (rb, cb)
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: op(a) is {M}x{K}, op(b) is {K2}x{N}")
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    Mc, Nc, ldc = _operand(c, "c")
+    if (Mc, Nc) != (M, N):
+        raise ValueError(f"c has shape {tuple(c.shape)}, expected {(M, N)}")
+    if not (a.device == b.device == c.device):
+        raise ValueError("a, b and c must be on the same device")
+    with torch.cuda.device(a.device):
+        rc = gemm_f16_ws_static_raw(trans_a, trans_b, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb,
+                                    c.data_ptr(), ldc, relu, _stream_handle(stream, a.device), library)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "gemm_f16_ws_static")
     return c
 
 

@@ -12,6 +12,8 @@
 #endif
 #include "tgemm_internal.h"
 
+static_assert(TGEMM_STATIC_SCRATCH_BYTES == tgemm::kStaticScratchBytes,
+              "the header states the static scratch size the kernels' source defines");
 static_assert(TGEMM_PROBE_THREADS == tgemm::kProbeThreads &&
                   TGEMM_PROBE_MFMA_PER_ITER == tgemm::kProbeMfmaPerIter,
               "probe shape in the header matches the kernel");
@@ -501,6 +503,24 @@ int64_t tgemm_workspace_bytes_cfg(int idx, int splits, int64_t M, int64_t N) {
   const Config& c = cfg_row(idx);
   if (splits > 1 && (!split_capable(c) || workgroups(c, M, N) > kMaxSplitTiles)) return TGEMM_EINVAL_CFG;
   return ws_bytes(c, splits, M, N);
+}
+
+int gemm_f16_ws_static(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, void* C, int64_t ldc, int relu, void* stream) {
+  const int layout = layout_of(trans_a, trans_b);
+  const int cfg = select(layout, M, N, K, A, lda, B, ldb, C, ldc);
+  if (cfg == kSelectNoop) return TGEMM_OK;
+  if (cfg < 0 && cfg != kSelectZeroFill) return cfg;
+  if (cfg == kSelectZeroFill) return run(cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  const SplitPlan p = split_plan(layout, M, N, K, cfg);
+  if (p.splits == 1) return run(cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream);
+  if (ws_bytes(cfg_row(p.cfg), p.splits, M, N) > TGEMM_STATIC_SCRATCH_BYTES) return TGEMM_EWORKSPACE;
+  int dev = -1;
+  const int d = check_device(&dev);
+  if (d != TGEMM_OK) return d;
+  void* scratch = nullptr;
+  if (tgemm::static_scratch(dev, &scratch) != hipSuccess) return TGEMM_EDEVICE;
+  return run(p.cfg, layout, M, N, K, A, lda, B, ldb, C, ldc, relu, stream, p.splits, scratch);
 }
 
 int gemm_f16_ws(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

@@ -141,6 +141,12 @@ struct QuantArgs {
 // vec: X 16-byte aligned, Q 8-byte aligned, ldx, ldq and K multiples of 8.
 hipError_t launch_quant_fp8(const QuantArgs& q, bool vec, hipStream_t s);
 
+// Split-K scratch of the allocation-free entry point: a static device array of
+// kStaticScratchBytes per device (tile counters first, then partial tiles). Writes its
+// device address on the current device to *out (looked up once per device, then cached).
+constexpr int64_t kStaticScratchBytes = 4096 + ((int64_t)64 << 20);
+hipError_t static_scratch(int device, void** out);
+
 // Zero-fill of an M x N block with row stride ldc (the K == 0 case).
 hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s);
 

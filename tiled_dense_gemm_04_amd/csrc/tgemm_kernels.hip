@@ -22,6 +22,28 @@
 
 namespace tgemm {
 
+// Split-K scratch for callers that cannot allocate (gemm_f16_ws_static): the tile
+// counters (zero when the library is loaded on a device; every split launch leaves the
+// counters it used at zero) and the fp32 partial tiles. Host code must not pass this
+// name to a kernel (on the host it is only a stand-in for the device symbol): it uses
+// the device address static_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(int device, void** out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> addr[kMaxDev];
+  if (device < 0 || device >= kMaxDev) return hipErrorInvalidDevice;
+  void* p = addr[device].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[device].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 namespace {
 
 #ifdef TGEMM_STAMPS
