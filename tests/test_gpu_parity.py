@@ -35,7 +35,7 @@ SMALL = [(256, 256, 64), (512, 384, 192), (300, 264, 136), (1, 8, 8), (257, 136,
          (640, 1152, 1000), (33, 520, 520), (1024, 256, 24)]
 
 
-@pytest.mark.parametrize("idx", list(range(19)))
+@pytest.mark.parametrize("idx", list(range(32)))
 def test_small_shapes_each_config(idx):
     if idx >= tg.tgemm_num_configs():
         pytest.skip("config not in table")

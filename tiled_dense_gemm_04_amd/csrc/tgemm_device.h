@@ -204,6 +204,8 @@ struct PpOperand {
   static constexpr int UNITS = R * BK / 8;
   static constexpr int LD = UNITS / NT;              // copies per thread per k-tile
   static constexpr int KPM = 512 / MF;               // k per MFMA
+  static constexpr bool KMAJOR = KMAJ;
+  static constexpr int MFRAG = MF, BKV = BK, RV = R;
   static_assert(UNITS % NT == 0, "copies must split evenly over the threads");
   static_assert(KMAJ || (R * 2) % 256 == 0, "MN-major rows must span the 256-byte bank window");
 

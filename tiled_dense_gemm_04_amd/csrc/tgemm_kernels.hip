@@ -19,6 +19,8 @@
 #include "tgemm_device.h"
 
 #include <atomic>
+#include <type_traits>
+#include <utility>
 
 namespace tgemm {
 
@@ -853,6 +855,352 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong_grouped(GroupedArg
 }
 
 // ------------------------------------------------------------------------------------
+// Quad kernel: 4 waves, one per SIMD, each owning a (BM / WM) x (BN / WN) sub-tile (128 x
+// 128 for 256 x 256 tiles): 256 fp32 accumulators per lane and 16x16x32 MFMAs. Against the
+// ping-pong's eight 128 x 64 wave tiles it reads a third fewer bytes from LDS per FLOP
+// (every wave reads the A rows and B columns of its sub-tile once per k-tile), and LDS ->
+// register traffic is what costs this power-limited part its clock under load.
+//
+// One wave per SIMD keeps its own MFMA pipe busy, so the k-tile's NS = FM * FN MFMAs run
+// in a fixed order and every memory instruction has a fixed MFMA slot (QuadSchedule): the
+// MFMAs go in 8 blocks, (A half h, B quarter q) for h = 0, 1 and q = 0 .. 3, each block
+// FM/2 x FN/4 MFMAs with the A fragment changing slowest. Each fragment register is
+// reloaded with the next k-tile's data two slots after its last use in this one, which
+// leaves every read at least NS/2 - FM/2 - 2 slots (24 of 64 MFMAs, ~380 clocks for the
+// 128 x 128 wave tile) before its first use, with one register set and no unrolling. Reads
+// whose slot falls past the end of the k-tile are issued in slot 0 of the next one (they
+// belong to that k-tile). The one barrier per k-tile sits right before the first read of
+// the next tile: there every wave has finished reading this tile (its slot-0 reads have
+// long completed) and this wave's copies of the next tile have landed, so after it the next
+// tile may be read and this tile's ring slot takes the copies of tile t+STAGES, which go
+// out one every NS/PT slots until the next barrier (so the copy stream of one tile straddles
+// two iterations). Every iteration issues exactly PT copies (empty ranges past the last
+// tile), so one constant s_waitcnt vmcnt(PT * (STAGES - 2)) finds the next tile landed.
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, expanded at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// The same for I = LO .. HI-1.
+template <int LO, int HI, typename F>
+__device__ __forceinline__ void static_for_range(F&& f) {
+  static_for<HI - LO>([&](auto i) { f(std::integral_constant<int, LO + decltype(i)::value>{}); });
+}
+
+// Fragment reads of the quad kernel with their per-lane offsets precomputed (what
+// PpOperand::frag computes for k substep 0, hoisted out of the loop).
+template <typename Op, int NF>
+struct QuadFrags {
+  static constexpr bool KMAJ = Op::KMAJOR;
+  static constexpr int MF = Op::MFRAG, BKV = Op::BKV, RV = Op::RV;
+  uint32_t off[KMAJ ? 1 : NF][2];
+  __device__ void init(const Op& op) {
+    if constexpr (KMAJ) {
+      off[0][0] = op.fr_base + ((op.fr_k ^ op.fr_x) << 4);
+    } else {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int k = 4 * i + op.fr_k;
+          off[f][i] = k * RV * 2 + (((op.fr_x + (MF / 8) * f) ^ swz_b(k)) << 4) + op.fr_half;
+        }
+    }
+  }
+  __device__ half8 read(const char* S, int f) const {
+    if constexpr (KMAJ) {
+      return *(const TG_LDS half8*)(S + off[0][0] + f * MF * BKV * 2);
+    } else {
+      const short4v h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(S + off[f][0]));
+      const short4v h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(S + off[f][1]));
+      return __builtin_bit_cast(half8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+};
+
+template <int FM, int FN>
+struct QuadSchedule {
+  static constexpr int HM = FM / 2, QN = FN / 4, BLK = HM * QN, NS = FM * FN;
+  static_assert(FM % 2 == 0 && FN % 4 == 0, "A in halves, B in quarters");
+  // MFMA slot s -> (fm, fn)
+  __host__ __device__ static constexpr int fm_of(int s) { return (s / BLK / 4) * HM + (s % BLK) / QN; }
+  __host__ __device__ static constexpr int fn_of(int s) { return (s / BLK % 4) * QN + (s % BLK) % QN; }
+  // last slot reading A fragment j / B fragment f
+  __host__ __device__ static constexpr int last_a(int j) { return (4 * (j / HM) + 3) * BLK + (j % HM) * QN + QN - 1; }
+  __host__ __device__ static constexpr int last_b(int f) { return (4 + f / QN) * BLK + (HM - 1) * QN + f % QN; }
+  // slot after whose MFMA the reload is issued (>= NS: slot - NS of the next k-tile): GAP
+  // slots after the last use, so the load never overwrites a register an MFMA still in
+  // flight reads (which would cost hazard wait states)
+  static constexpr int GAP = 2;
+  __host__ __device__ static constexpr int read_a(int j) { return last_a(j) + GAP; }
+  __host__ __device__ static constexpr int read_b(int f) { return last_b(f) + GAP; }
+  // the barrier follows slot BAR: the last slot before the first read of the next tile
+  __host__ __device__ static constexpr int first_next_read() {
+    int m = 2 * NS;
+    for (int j = 0; j < FM; ++j) m = read_a(j) < m ? read_a(j) : m;
+    for (int f = 0; f < FN; ++f) m = read_b(f) < m ? read_b(f) : m;
+    return m;
+  }
+  static constexpr int BAR = first_next_read() - 1;
+  // LDS instructions issued after slot s's MFMA (reads of fragments reloaded there;
+  // IA / IB instructions per A / B fragment)
+  template <int IA, int IB>
+  __host__ __device__ static constexpr int reads_at(int s) {
+    int n = 0;
+    for (int j = 0; j < FM; ++j) n += (read_a(j) % NS == s) ? IA : 0;
+    for (int f = 0; f < FN; ++f) n += (read_b(f) % NS == s) ? IB : 0;
+    return n;
+  }
+  // The first MFMA of a k-tile needs fragments reloaded late in the previous one. An
+  // explicit wait after slot RETIRE, for all but the LDS instructions issued after the
+  // later of those two reloads, tells the compiler they have completed (it cannot track
+  // that many loads across the loop edge and would otherwise wait for every load issued
+  // at the end of the k-tile): RETIRE is a few slots before the end, and RETIRE_N counts
+  // the instructions issued after the later reload up to RETIRE.
+  __host__ __device__ static constexpr int first_reload() {
+    const int ra = read_a(fm_of(0)), rb = read_b(fn_of(0));
+    return ra > rb ? ra : rb;
+  }
+  static constexpr int RETIRE = NS - 9;
+  template <int IA, int IB>
+  __host__ __device__ static constexpr int retire_n() {
+    int n = 0;
+    for (int s = first_reload() + 1; s <= RETIRE; ++s) n += reads_at<IA, IB>(s);
+    return n;
+  }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, bool TA, bool TB>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_quad(GemmArgs g) {
+  WgClock clk;
+  clk.start();
+  constexpr int NW = WM * WN, MF = 16;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  using Q = QuadSchedule<FM, FN>;
+  constexpr int NS = Q::NS;
+  using OpA = PpOperand<pp_lds_extent(BM), BK, MF, !TA, NW>;
+  using OpB = PpOperand<pp_lds_extent(BN), BK, MF, TB, NW>;
+  constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
+  constexpr int PT = OpA::LD + OpB::LD;
+  constexpr int CSTEP = NS / PT;               // slots between copies
+  static_assert(NW == 4, "one wave per SIMD");
+  static_assert(BK == 32, "one 16x16x32 MFMA step per k-tile");
+  static_assert(NS % PT == 0 && Q::BAR >= 0 && Q::BAR < NS, "copy spacing and barrier slot");
+  static_assert(STAGES >= 3 && PT * (STAGES - 1) < 64, "ring depth and vmcnt budget");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const a_lds = smem;
+  char* const b_lds = smem + STAGES * A_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int64_t tm64, tn64;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
+  const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
+  const int nk = (g.K + BK - 1) / BK;
+  const int kin_last = g.K - (nk - 1) * BK;
+
+  OpA opa;
+  OpB opb;
+  opa.init_copies(g.A, g.lda, row0, mvalid, kin_last, wave, lane);
+  opb.init_copies(g.B, g.ldb, col0, nvalid, kin_last, wave, lane);
+  const uint32_t a_lds0 = lds_addr(a_lds) + wave * 1024;
+  const uint32_t b_lds0 = lds_addr(b_lds) + wave * 1024;
+
+  struct Dma {
+    int4v ra, rb;
+    uint32_t a_dst, b_dst;
+    bool last;
+  };
+  auto dma_setup = [&](int t) {
+    Dma d;
+    d.ra = opa.rsrc(t, nk, nk);
+    d.rb = opb.rsrc(t, nk, nk);
+    const int slot = t % STAGES;
+    d.a_dst = a_lds0 + slot * A_BYTES;
+    d.b_dst = b_lds0 + slot * B_BYTES;
+    d.last = t == nk - 1;
+    return d;
+  };
+  // The descriptors of tile u >= STAGES from running source pointers (no 64-bit multiply
+  // per k-tile); past the last tile the range is empty and the pointer is never used.
+  const char* pa_next = opa.base + (int64_t)STAGES * opa.step;
+  const char* pb_next = opb.base + (int64_t)STAGES * opb.step;
+  auto dma_next = [&](int u) {
+    Dma d;
+    d.ra = make_rsrc(pa_next, u < nk - 1 ? opa.rng_full : (u == nk - 1 ? opa.rng_last : 0u));
+    d.rb = make_rsrc(pb_next, u < nk - 1 ? opb.rng_full : (u == nk - 1 ? opb.rng_last : 0u));
+    pa_next += opa.step;
+    pb_next += opb.step;
+    const int slot = u % STAGES;
+    d.a_dst = a_lds0 + slot * A_BYTES;
+    d.b_dst = b_lds0 + slot * B_BYTES;
+    d.last = u == nk - 1;
+    return d;
+  };
+  auto dma_one = [&](const Dma& d, int j) {
+    if (j < OpA::LD)
+      dma_to_lds(d.ra, d.a_dst + j * NW * 1024, d.last ? opa.off_last[j] : opa.off[j]);
+    else
+      dma_to_lds(d.rb, d.b_dst + (j - OpA::LD) * NW * 1024, opb.off[j - OpA::LD]);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  opa.init_frags(wm * WTM, lane);
+  opb.init_frags(wn * WTN, lane);
+
+  half8 fa[FM], fb[FN];  // the wave's fragments: one set, each reloaded after its last use
+  // Per-lane byte offsets of every fragment inside a ring slot, computed once: a K-major
+  // operand needs one (fragment f sits f * MF rows further: an immediate offset), an
+  // MN-major one two per fragment (the transposed reads' swizzled chunks).
+  QuadFrags<OpA, FM> qa;
+  QuadFrags<OpB, FN> qb;
+  qa.init(opa);
+  qb.init(opb);
+  auto read_a = [&](int slot, int f) { fa[f] = qa.read(a_lds + slot * A_BYTES, f); };
+  auto read_b = [&](int slot, int f) { fb[f] = qb.read(b_lds + slot * B_BYTES, f); };
+
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  f4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Copies: copy c of tile t+STAGES goes out after slot BAR + 1 + c * CSTEP of iteration t
+  // (past NS: in the next iteration). The prologue issues tiles 0 .. STAGES-2 and the
+  // copies of tile STAGES-1 that iteration 0 would have issued in iteration -1.
+  constexpr int C_WRAP = (NS - (Q::BAR + 1) + CSTEP - 1) / CSTEP;  // copies before the wrap
+  static_assert(C_WRAP >= 1 && C_WRAP <= PT, "copy stream");
+#pragma unroll
+  for (int t = 0; t < STAGES; ++t) {
+    const Dma d = dma_setup(t);
+#pragma unroll
+    for (int j = 0; j < (t < STAGES - 1 ? PT : C_WRAP); ++j) dma_one(d, j);
+  }
+  wait_vmcnt<PT * (STAGES - 2) + C_WRAP>();
+  lds_barrier();
+#pragma unroll
+  for (int f = 0; f < FM; ++f) read_a(0, f);
+#pragma unroll
+  for (int f = 0; f < FN; ++f) read_b(0, f);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the loop starts with no load in flight
+
+  // Slots [LO, HI) of iteration t. `dc` holds the copies' descriptor: tile t-1+STAGES before
+  // the barrier, tile t+STAGES after it (set there).
+  Dma dc = dma_setup(STAGES - 1);
+  auto run_slots = [&](auto lo_c, auto hi_c, int t) {
+    constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+    const int slot = t % STAGES, nslot = (t + 1) % STAGES;
+    static_for_range<LO, HI>([&](auto sl_c) {
+      constexpr int sl = decltype(sl_c)::value;
+      constexpr int fm = Q::fm_of(sl), fn = Q::fn_of(sl);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // reloads: those past the end of the previous k-tile (this tile's data), and this
+      // slot's reloads with the next tile's data
+      static_for<FM>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        if constexpr (Q::read_a(j) >= NS && Q::read_a(j) - NS == sl) read_a(slot, j);
+        if constexpr (Q::read_a(j) == sl) read_a(nslot, j);
+      });
+      static_for<FN>([&](auto f_c) {
+        constexpr int f = decltype(f_c)::value;
+        if constexpr (Q::read_b(f) >= NS && Q::read_b(f) - NS == sl) read_b(slot, f);
+        if constexpr (Q::read_b(f) == sl) read_b(nslot, f);
+      });
+      static_for<PT>([&](auto c_c) {
+        constexpr int c = decltype(c_c)::value;
+        constexpr int at = Q::BAR + 1 + c * CSTEP;
+        if constexpr ((at >= NS && at - NS == sl) || at == sl) dma_one(dc, c);
+      });
+      if constexpr (sl == Q::RETIRE) {
+        constexpr int IA = QuadFrags<OpA, FM>::KMAJ ? 1 : 2, IB = QuadFrags<OpB, FN>::KMAJ ? 1 : 2;
+        constexpr int N = Q::template retire_n<IA, IB>();
+        static_assert(N >= 0 && N < 16, "lgkmcnt range");
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));  // lgkmcnt(N) only
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (sl == Q::BAR) {
+        __builtin_amdgcn_sched_barrier(0);
+        // this tile fully read by every wave; this wave's copies of the next tile landed
+        wait_vmcnt<PT * (STAGES - 2)>();
+        lds_barrier();
+        dc = dma_next(t + STAGES);
+      }
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using Zero = std::integral_constant<int, 0>;
+  using End = std::integral_constant<int, NS>;
+  clk.loop_begin();
+  for (int t = 0; t < nk; ++t) run_slots(Zero{}, End{}, t);
+  wait_vmcnt<0>();  // the copies past the last tile write zeros: drained before LDS is reused
+  clk.loop_end();
+
+  // Epilogue: ReLU and RNE in registers, each wave's WTM x WTN fp16 sub-tile staged in its
+  // own LDS region (rows of RB bytes, chunk c of row r at chunk c ^ (r / RPW) % SCPR with RPW
+  // rows per 256-byte bank window), then written back in 16-byte row segments.
+  constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
+  constexpr int RB = SCPR * 16, RPW = RB >= 256 ? 1 : 256 / RB;
+  static_assert(NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
+  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+  __syncthreads();
+  char* const stage = smem + wave * (WTM * RB);
+  const int lrow = lane % MF, lkg = lane / MF;
+  // The ReLU choice is made once for the whole tile (a per-value branch on the runtime
+  // flag costs registers at 256 accumulators).
+  auto stage_tile = [&](auto relu_tag) {
+    constexpr bool RELU = decltype(relu_tag)::value;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int mw = fm * MF + lrow;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int nw = fn * MF + 4 * lkg;
+        float v0 = acc[fm][fn][0], v1 = acc[fm][fn][1], v2 = acc[fm][fn][2], v3 = acc[fm][fn][3];
+        if constexpr (RELU) {
+          v0 = relu_f(v0);
+          v1 = relu_f(v1);
+          v2 = relu_f(v2);
+          v3 = relu_f(v3);
+        }
+        const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+        const int off = mw * RB + ((((nw >> 3) ^ ((mw / RPW) % SCPR))) << 4) + (nw & 7) * 2;
+        *(TG_LDS half4*)(stage + off) = h;
+      }
+    }
+  };
+  if (g.relu != 0)
+    stage_tile(std::true_type{});
+  else
+    stage_tile(std::false_type{});
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+  for (int i = 0; i < WTM * SCPR / 64; ++i) {
+    const int idx = i * 64 + lane;
+    const int r = idx / SCPR, c = idx % SCPR;
+    if (c >= CPR) continue;
+    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r / RPW) % SCPR)) << 4));
+    const int m = wm * WTM + r, n = wn * WTN + 8 * c;
+    if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
+  }
+  clk.finish(nk, TG_STAMP_TABLE);
+}
+
+// ------------------------------------------------------------------------------------
 // Generic kernel: 64 x 64 x 32 tile, 4 waves (2 x 2 of 32 x 32), element-wise predicated
 // loads (any 2-byte-aligned pointers, any strides and sizes, any operand layout). A is
 // staged as [m][k] and B transposed to [n][k] in LDS so both fragments are plain 16-byte
@@ -1047,6 +1395,39 @@ hipError_t launch_pp(const GemmArgs& g, hipStream_t s, int device) {
   return launch_pp_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, false, false>(g, s, device);
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, bool TA, bool TB>
+hipError_t launch_quad_layout(const GemmArgs& g, hipStream_t s, int device) {
+  constexpr int lds = pp_lds_bytes<BM, BN, BK, STAGES>();
+  auto kern = gemm_quad<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, TA, TB>;
+  static std::atomic<uint64_t> ready{0};
+  const uint64_t bit = 1ull << (device & 63);
+  if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  if (g.splits != 1) return hipErrorInvalidValue;
+  const int64_t nwg = (int64_t)g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * WM * WN), lds, s, g);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, bool ALL>
+hipError_t launch_quad(const GemmArgs& g, hipStream_t s, int device) {
+  if constexpr (ALL) {
+    switch (g.layout) {
+      case 1: return launch_quad_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, false, true>(g, s, device);
+      case 2: return launch_quad_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, true, false>(g, s, device);
+      case 3: return launch_quad_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, true, true>(g, s, device);
+      default: break;
+    }
+  } else {
+    if (g.layout != 0) return hipErrorInvalidValue;
+  }
+  return launch_quad_layout<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, false, false>(g, s, device);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD>
 hipError_t launch_pipe(const GemmArgs& g, hipStream_t s, int device) {
   constexpr int lds = STAGES * (BM * BK + BK * BN) * 2;
@@ -1135,6 +1516,11 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
   X(128, 256, 32, 2, 4, 4, 4, 1, 1)   \
   X(256, 192, 32, 2, 4, 4, 4, 1, 1)
 
+// Quad kernel instantiations (4 waves): X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD, ALL)
+#define TGEMM_QUAD_CONFIGS(X)         \
+  X(256, 256, 32, 2, 2, 4, 4, 0, 0)   \
+  X(256, 256, 32, 2, 2, 4, 4, 1, 0)
+
 #define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
   {BM, BN, BK, S, WM, WN, P, X, 0, 1, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
 #define TGEMM_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_fast<BM, BN, BK, WM, WN, S, P, X>,
@@ -1149,6 +1535,9 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
   {BM, BN, BK, S, WM, WN, P, X, 0, ALL ? 0xF : 1, "m" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
 #define TGEMM_PP1_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, ALL) launch_pp<BM, BN, BK, WM, WN, S, P, X, 16, ALL>,
 #define TGEMM_COUNT9(BM, BN, BK, WM, WN, S, P, X, ALL) 0,
+#define TGEMM_QUAD_ROW(BM, BN, BK, WM, WN, S, P, X, ALL) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, ALL ? 0xF : 1, "u" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_QUAD_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, ALL) launch_quad<BM, BN, BK, WM, WN, S, P, X, ALL>,
 
 // Function-local statics: host-only tables (the device pass parses these bodies, which
 // instantiates every kernel, but emits no host data).
@@ -1156,7 +1545,7 @@ const Config* config_table(int* count) {
   static const Config table[] = {
       {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, 0xF, "generic_64x64x32"},
       TGEMM_FAST_CONFIGS(TGEMM_ROW) TGEMM_PIPE_CONFIGS(TGEMM_PIPE_ROW) TGEMM_PP_CONFIGS(TGEMM_PP_ROW)
-          TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW)};
+          TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW) TGEMM_QUAD_CONFIGS(TGEMM_QUAD_ROW)};
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
 }
@@ -1180,10 +1569,12 @@ Launcher launcher(int idx) {
   static const Launcher table[] = {launch_generic, TGEMM_FAST_CONFIGS(TGEMM_LAUNCHER)
                                        TGEMM_PIPE_CONFIGS(TGEMM_PIPE_LAUNCHER)
                                            TGEMM_PP_CONFIGS(TGEMM_PP_LAUNCHER)
-                                               TGEMM_PP1_CONFIGS(TGEMM_PP1_LAUNCHER)};
+                                               TGEMM_PP1_CONFIGS(TGEMM_PP1_LAUNCHER)
+                                                   TGEMM_QUAD_CONFIGS(TGEMM_QUAD_LAUNCHER)};
   static_assert(sizeof(table) / sizeof(table[0]) ==
                     1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT) TGEMM_PIPE_CONFIGS(TGEMM_COUNT)
-                                           TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT9)}) /
+                                           TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT9)
+                                               TGEMM_QUAD_CONFIGS(TGEMM_COUNT9)}) /
                             sizeof(int),
                 "one launcher per config");
   return table[idx];
