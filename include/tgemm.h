@@ -252,6 +252,9 @@ typedef struct tgemm_config_info {
     int32_t generic;                   /* 1 = unaligned-capable generic kernel          */
     int32_t lds_bytes;                 /* dynamic LDS per workgroup                     */
     int32_t layouts;                   /* bit (2*trans_a + trans_b) set: layout accepted */
+    int32_t built;                     /* 1 = compiled into this library; 0 = a tooling  */
+                                       /* variant only the tooling build compiles (the   */
+                                       /* _cfg entry points refuse it here)              */
     char name[48];
 } tgemm_config_info;
 
@@ -320,19 +323,6 @@ TGEMM_API int tgemm_tile_of(int idx, int64_t M, int64_t N, int64_t wg,
 /* Number of workgroups config idx launches for an M x N output. */
 TGEMM_API int64_t tgemm_num_workgroups(int idx, int64_t M, int64_t N);
 
-/* ---- tooling: MFMA throughput probe (the measured compute ceiling of the board) ---- */
-
-/* Enqueues `blocks` workgroups of TGEMM_PROBE_THREADS threads (8 waves). Every wave
- * issues iters x TGEMM_PROBE_MFMA_PER_ITER independent 16x16x32 fp16 MFMAs (16384 FLOP
- * each) on pseudo-random register operands, with no memory traffic, then each thread
- * writes one float to out. out: caller-owned device memory of blocks * TGEMM_PROBE_THREADS
- * floats. FLOP per launch = blocks * TGEMM_PROBE_THREADS / 64 * iters *
- * TGEMM_PROBE_MFMA_PER_ITER * 16384. Returns TGEMM_OK, TGEMM_ENULL (out NULL),
- * TGEMM_EINVAL_DIM (blocks outside [1, 2^20] or iters outside [1, 2^24]), TGEMM_EDEVICE
- * or TGEMM_ELAUNCH. */
-#define TGEMM_PROBE_THREADS 512
-#define TGEMM_PROBE_MFMA_PER_ITER 16
-TGEMM_API int tgemm_mfma_probe(int blocks, int iters, void* out, void* stream);
 
 /* fp8 tooling: the fp8 tile configs (tgemm_config_info with block_k = 128 and layouts =
  * 2: A as given, B transposed), the config gemm_fp8_block would pick (scales not looked

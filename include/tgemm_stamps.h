@@ -1,7 +1,10 @@
 /*
- * tgemm_stamps.h -- extra entry points of libtgemm_stamps.so, the instrumented build of
- * libtgemm (same sources compiled with TGEMM_STAMPS; it also exports everything in
- * tgemm.h). Not part of the product library: libtgemm.so does not export these.
+ * tgemm_stamps.h -- extra entry points of libtgemm_stamps.so, the tooling build of libtgemm
+ * (same sources compiled with TGEMM_STAMPS and TGEMM_SWEEP_CONFIGS; it also exports
+ * everything in tgemm.h). Not part of the product library: libtgemm.so does not export
+ * these. Besides the stamps, this build compiles every row of the config table, including
+ * the variants the product leaves out (tgemm_config_info.built is 1 for all of them), for
+ * the offline sweep, and the MFMA throughput probe (the measured compute ceiling).
  *
  * In the instrumented build every workgroup of the GEMM kernels (all configs except the
  * generic one) and of the MFMA probe records, at its end, TGEMM_STAMP_WORDS 64-bit words
@@ -44,6 +47,20 @@ TGEMM_API int tgemm_stamps_read(uint64_t* host, int64_t words);
 /* Zeroes the table of the current device (synchronous). Returns TGEMM_OK or
  * TGEMM_ELAUNCH. */
 TGEMM_API int tgemm_stamps_clear(void);
+
+/* ---- MFMA throughput probe (the measured compute ceiling of the board) ---- */
+
+/* Enqueues `blocks` workgroups of TGEMM_PROBE_THREADS threads (8 waves). Every wave
+ * issues iters x TGEMM_PROBE_MFMA_PER_ITER independent 16x16x32 fp16 MFMAs (16384 FLOP
+ * each) on pseudo-random register operands, with no memory traffic, then each thread
+ * writes one float to out. out: caller-owned device memory of blocks * TGEMM_PROBE_THREADS
+ * floats. FLOP per launch = blocks * TGEMM_PROBE_THREADS / 64 * iters *
+ * TGEMM_PROBE_MFMA_PER_ITER * 16384. Returns TGEMM_OK, TGEMM_ENULL (out NULL),
+ * TGEMM_EINVAL_DIM (blocks outside [1, 2^20] or iters outside [1, 2^24]), TGEMM_EDEVICE
+ * or TGEMM_ELAUNCH. */
+#define TGEMM_PROBE_THREADS 512
+#define TGEMM_PROBE_MFMA_PER_ITER 16
+TGEMM_API int tgemm_mfma_probe(int blocks, int iters, void* out, void* stream);
 
 #ifdef __cplusplus
 }

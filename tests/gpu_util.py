@@ -20,16 +20,27 @@ def to_dev(x: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
 
 
+def library_for(cfg, fp8: bool = False):
+    """The build that compiles table row ``cfg``: the product library (None, the binding's
+    default) unless the row is a sweep-only variant, then the tooling build."""
+    if cfg is None or cfg < 0:
+        return None
+    desc = tg.tgemm_fp8_config_desc(cfg) if fp8 else tg.tgemm_config_desc(cfg)
+    return None if desc["built"] else tg.stamps_lib()
+
+
 def run(A: np.ndarray, B: np.ndarray, relu: bool, cfg=None, stream=None, trans_a=False,
         trans_b=False) -> np.ndarray:
     """fp16 numpy in (the logical op(A) M x K and op(B) K x N) -> fp16 output bits (uint16
     numpy) out. With trans_a / trans_b the operand goes to the library stored transposed
-    (a row-major copy of its transpose) through gemm_f16_ex."""
+    (a row-major copy of its transpose) through gemm_f16_ex. A sweep-only config runs on
+    the tooling build."""
     torch = torch_cuda()
     a = to_dev(A.T if trans_a else A)
     b = to_dev(B.T if trans_b else B)
     c = torch.full((A.shape[0], B.shape[1]), float("nan"), dtype=torch.float16, device="cuda")
-    tg.gemm_f16_ex(a, b, c, trans_a=trans_a, trans_b=trans_b, relu=relu, cfg=cfg, stream=stream)
+    tg.gemm_f16_ex(a, b, c, trans_a=trans_a, trans_b=trans_b, relu=relu, cfg=cfg, stream=stream,
+                   library=library_for(cfg))
     torch.cuda.synchronize()
     return c.cpu().numpy().view(np.uint16)
 

@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import tgemm_workloads as W
-from gpu_util import log, relu_bits, sample_entries, to_dev, torch_cuda
+from choice_table import smallest_exact_shape
+from gpu_util import library_for, log, relu_bits, sample_entries, to_dev, torch_cuda
 
 import tiled_dense_gemm_04_amd as tg
 
@@ -50,7 +51,7 @@ def _gemm(A, SA, B, SB, relu, cfg=None, a_pad=0, b_pad=0, c_pad=0):
     sa, sb = to_dev(SA), to_dev(SB)
     cbuf = torch.full((M, N + c_pad), float("nan"), dtype=torch.float16, device="cuda")
     c = cbuf[:, :N]
-    tg.gemm_fp8_block(a, sa, b, sb, c, relu=relu, cfg=cfg)
+    tg.gemm_fp8_block(a, sa, b, sb, c, relu=relu, cfg=cfg, library=library_for(cfg, fp8=True))
     torch.cuda.synchronize()
     if c_pad:  # padding between rows untouched
         assert torch.isnan(cbuf[:, N:]).all()
@@ -241,12 +242,16 @@ def test_fp8_linear_end_to_end():
         tg.fp8_block_scaled_linear(xd, wd, swd, block=64)
 
 
-# ---------------------------------------------------------------- default choice by rounds
-@pytest.mark.parametrize("M,N,K,cfg", [(3072, 3072, 2048, 0), (2560, 2560, 2048, 3), (2048, 2048, 1024, 1)])
-def test_default_choice_shapes_sampled(M, N, K, cfg):
-    """The config the library picks by round count (256 x 256 in one round of 144 tiles,
-    256 x 128 in one round of 200, 128 x 128 in one round of 256), against the oracle on
-    sampled rows, columns and random entries."""
+# ---------------------------------------------------------------- default choice
+@pytest.mark.parametrize("prefix", ["f256x256", "f128x128", "f256x128"])
+def test_default_choice_shapes_sampled(prefix):
+    """Each config the selector's table picks, on the smallest timed shape where it is the
+    table's choice (the library must pick it by itself), against the oracle on sampled
+    rows, columns and random entries."""
+    shape = smallest_exact_shape(prefix, [c["name"] for c in tg.fp8_configs()], kind="kFp8")
+    if shape is None:
+        pytest.skip(f"the selector's table picks no {prefix} config")
+    M, N, K, cfg = shape
     assert tg.tgemm_fp8_select_config(M, N, K) == cfg
     A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=78)
     log(f"fp8 default choice {M}x{N}x{K} cfg {cfg}")

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import tgemm_workloads as W
+from choice_table import smallest_exact_shape
 from gpu_util import assert_close, log, relu_bits, run, sample_entries, to_dev, torch_cuda
 
 import tiled_dense_gemm_04_amd as tg
@@ -27,8 +28,10 @@ def gpu():
     return torch
 
 
-def _fast_cfgs():
-    return [i for i, c in enumerate(tg.configs()) if not c["generic"]]
+def _fast_cfgs(all_builds=False):
+    """Fast config rows of the product library; with all_builds, also the sweep-only rows
+    (run on the tooling build through gpu_util.run)."""
+    return [i for i, c in enumerate(tg.configs()) if not c["generic"] and (c["built"] or all_builds)]
 
 
 SMALL = [(256, 256, 64), (512, 384, 192), (300, 264, 136), (1, 8, 8), (257, 136, 72),
@@ -70,7 +73,7 @@ def test_edge_sweep_default_selection():
 def test_edge_sweep_fast_configs_ragged():
     """Every fast config on shapes that leave ragged M, N and K tails inside one tile."""
     rng = np.random.default_rng(77)
-    for idx in _fast_cfgs():
+    for idx in _fast_cfgs(all_builds=True):
         for t in range(12):
             M = int(rng.choice(EDGE))
             N = int(rng.choice(EDGE8))
@@ -117,20 +120,23 @@ def test_workload_full_size_sampled(name):
     assert not np.any((c & 0x7C00) == 0x7C00), "inf/NaN in output"
 
 
-# Shapes on which the default choice takes each tile config by its round count (256 x 192
-# in one round, 256 x 192 over three rounds, 256 x 128 in one round, 256 x 256 in one).
-CHOICE_SHAPES = [(3072, 3072, 4096, "m256x192"), (6144, 6144, 1024, "m256x192"),
-                 (2560, 2560, 2048, "m256x128"), (3584, 3584, 2048, "m256x256")]
+# Every fast config the selector's table can pick, each on the smallest timed shape where it
+# is the table's choice: the library must pick it by itself there.
+CHOICE_PREFIXES = ["m256x192", "m256x128", "m256x256", "m128x128", "p128x128"]
 
 
-@pytest.mark.parametrize("M,N,K,prefix", CHOICE_SHAPES)
-def test_default_choice_shapes_sampled(M, N, K, prefix):
-    """The config the library picks on its own for mid-size and multi-round grids, against
-    the oracle on whole sampled rows and columns plus random entries."""
+@pytest.mark.parametrize("prefix", CHOICE_PREFIXES)
+def test_default_choice_shapes_sampled(prefix):
+    """The config the library picks on its own, at full size, against the oracle on whole
+    sampled rows and columns plus random entries."""
+    shape = smallest_exact_shape(prefix, [c["name"] for c in tg.configs()])
+    if shape is None:
+        pytest.skip(f"the selector's table picks no {prefix} config")
+    M, N, K, want = shape
     A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=77)
     cfg = tg.tgemm_select_config(M, N, K)
     log(f"default choice {M}x{N}x{K}: cfg {cfg}")
-    assert tg.tgemm_config_desc(cfg)["name"].startswith(prefix)
+    assert cfg == want
     c = run(A, B, True)
     rng = np.random.default_rng(M + N + K)
     rows, cols = sample_entries(M, N, rng, n_rows=3, n_cols=3, n_rand=4096)

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import tgemm_workloads as W
-from gpu_util import assert_close, log, to_dev, torch_cuda
+from gpu_util import assert_close, library_for, log, to_dev, torch_cuda
 
 import tiled_dense_gemm_04_amd as tg
 
@@ -34,7 +34,8 @@ def _run_ws(A, B, relu, cfg, splits, ta=False, tb=False, workspace=None):
     a = to_dev(A.T if ta else A)
     b = to_dev(B.T if tb else B)
     c = torch.full((A.shape[0], B.shape[1]), float("nan"), dtype=torch.float16, device="cuda")
-    tg.gemm_f16_ws(a, b, c, ta, tb, relu=relu, cfg=cfg, splits=splits, workspace=workspace)
+    tg.gemm_f16_ws(a, b, c, ta, tb, relu=relu, cfg=cfg, splits=splits, workspace=workspace,
+                   library=library_for(cfg))
     torch.cuda.synchronize()
     return c.cpu().numpy().view(np.uint16)
 

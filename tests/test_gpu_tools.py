@@ -26,7 +26,7 @@ def test_mfma_probe_runs_and_is_deterministic(gpu):
     torch = gpu
     blocks, iters = 16, 64
     outs = []
-    for library in (tg.lib(), tg.stamps_lib(), tg.lib()):
+    for library in (tg.stamps_lib(),) * 3:
         out = torch.full((blocks * tg.PROBE_THREADS,), float("nan"), dtype=torch.float32, device="cuda")
         log(f"probe blocks={blocks} iters={iters}")
         flop = tg.tgemm_mfma_probe(blocks, iters, out, library=library)
@@ -40,7 +40,7 @@ def test_mfma_probe_runs_and_is_deterministic(gpu):
 
 
 @pytest.mark.parametrize("cfg_name", ["m256x256x32_s4_w2x4_p4_x1", "p128x128x64_s2_w2x2_p4_x1",
-                                      "t256x256x64_s2_w2x4_p4_x1"])
+                                      "m256x192x32_s4_w2x4_p4_x1"])
 def test_stamps_build_same_result_and_sane_stamps(gpu, cfg_name):
     torch = gpu
     idx = [c["name"] for c in tg.configs()].index(cfg_name)

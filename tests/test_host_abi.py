@@ -1,12 +1,14 @@
 """libtgemm on the CPU: the C-ABI library loads and exports every symbol the header
 declares; argument validation, error codes, config selection and the workgroup -> tile
 map are checked without any GPU work (every call here returns before touching HIP)."""
+import ctypes
 import os
 import re
 
 import pytest
 
 import tiled_dense_gemm_04_amd as tg
+from choice_table import expected_choice, parse_choice_table
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -36,7 +38,7 @@ def exported(path):
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 26, syms
+    assert len(syms) == 25, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -69,8 +71,8 @@ def test_instrumented_build_exports():
 
 def test_probe_argument_checks():
     """Rejected before any HIP call; the shape constants match the header."""
-    L = tg.lib()
-    text = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    L = tg.stamps_lib()
+    text = open(os.path.join(ROOT, "include", "tgemm_stamps.h")).read()
     assert f"#define TGEMM_PROBE_THREADS {tg.PROBE_THREADS}" in text
     assert f"#define TGEMM_PROBE_MFMA_PER_ITER {tg.PROBE_MFMA_PER_ITER}" in text
     assert L.tgemm_mfma_probe(1, 1, None, None) == tg.TGEMM_ENULL
@@ -96,7 +98,7 @@ def test_config_table():
     n = tg.tgemm_num_configs()
     assert n >= 2
     # the per-config GPU tests are parametrized over these counts
-    assert n <= 19
+    assert n <= 32
     assert sum(c["layouts"] == 0xF for c in tg.configs()) <= 6
     cfgs = tg.configs()
     assert cfgs[0]["generic"] == 1
@@ -117,6 +119,43 @@ def test_config_table():
         tg.tgemm_config_desc(n)
     with pytest.raises(tg.TgemmError):
         tg.tgemm_config_desc(-1)
+
+
+def config_list_prod_flags():
+    """PROD column of every row of csrc/tgemm_configs.h, in table order (fp16, then fp8)."""
+    text = open(os.path.join(ROOT, "tiled_dense_gemm_04_amd", "csrc", "tgemm_configs.h")).read()
+    lists = {}
+    for m in re.finditer(r"#define (TGEMM_\w+_CONFIGS)\(X\)((?:[^\n]*\\\n)*[^\n]*)", text):
+        lists[m.group(1)] = [int(r.split(",")[-1]) for r in re.findall(r"X\(([^)]*)\)", m.group(2))]
+    f16 = [1] + sum((lists[k] for k in ("TGEMM_FAST_CONFIGS", "TGEMM_PIPE_CONFIGS", "TGEMM_PP_CONFIGS",
+                                         "TGEMM_PP1_CONFIGS", "TGEMM_QUAD_CONFIGS")), [])
+    return f16, lists["TGEMM_FP8_CONFIGS"]
+
+
+def test_built_flags_follow_config_lists():
+    """The product library compiles exactly the rows marked PROD (plus the generic kernel);
+    the tooling build compiles every row; both list the same rows under the same names."""
+    f16, f8 = config_list_prod_flags()
+    P, S = tg.lib(), tg.stamps_lib()
+
+    def desc(L, fn, i):
+        info = tg.ConfigInfo()
+        assert getattr(L, fn)(i, ctypes.byref(info)) == tg.TGEMM_OK
+        return info.as_dict()
+
+    assert P.tgemm_num_configs() == S.tgemm_num_configs() == len(f16)
+    assert P.tgemm_fp8_num_configs() == S.tgemm_fp8_num_configs() == len(f8)
+    for fn, flags in (("tgemm_config_desc", f16), ("tgemm_fp8_config_desc", f8)):
+        for i, prod in enumerate(flags):
+            p, s = desc(P, fn, i), desc(S, fn, i)
+            assert p["built"] == prod and s["built"] == 1, (fn, i)
+            assert {k: v for k, v in p.items() if k != "built"} == {k: v for k, v in s.items() if k != "built"}
+    # a row the product library does not compile is refused before any HIP call
+    off = f16.index(0)
+    assert tg.gemm_f16_cfg_raw(off, 256, 256, 256, A16, 256, A16, 256, A16, 256, 1, None) == tg.TGEMM_EINVAL_CFG
+    off8 = f8.index(0)
+    assert tg.gemm_fp8_block_cfg_raw(off8, 256, 256, 256, A16, 256, A16, A16, 256, A16, A16, 256, 0,
+                                     None) == tg.TGEMM_EINVAL_CFG
 
 
 A16 = 0x100000  # a fake, 16-byte-aligned address; select_config never dereferences
@@ -172,21 +211,52 @@ def test_select_fast_vs_generic():
     assert s(4095, 3000, 1000, A16, 1000, A16, 3000, A16, 3000) > 0
 
 
-def test_select_by_rounds():
-    """Rounds of 256 workgroups: the smallest tile that fits one round, else 256 x 192 when
-    it needs no more rounds than 256 x 256."""
-    name = lambda M, N, K: tg.tgemm_config_desc(tg.tgemm_select_config(M, N, K, A16, K, A16, N, A16, N))["name"]
-    assert name(1024, 1024, 1024).startswith("p128x128")     # 64 tiles of 128 x 128
-    assert name(2048, 2048, 4096).startswith("p128x128")     # 256 tiles of 128 x 128
-    assert name(2560, 2560, 4096).startswith("m256x128")     # 200 tiles of 256 x 128
-    assert name(16384, 512, 4096).startswith("m256x128")     # 256 tiles of 256 x 128
-    assert name(3072, 3072, 4096).startswith("m256x192")     # 192 tiles of 256 x 192
-    assert name(4095, 3000, 1000).startswith("m256x192")     # 256 tiles of 256 x 192
-    assert name(3584, 3584, 2048).startswith("m256x256")     # 196 tiles of 256 x 256
-    assert name(4096, 4096, 4096).startswith("m256x256")     # 256 tiles of 256 x 256
-    assert name(6144, 6144, 4096).startswith("m256x192")     # 3 rounds either way
-    assert name(5120, 4096, 4096).startswith("m256x192")     # 2 rounds either way
-    assert name(8192, 8192, 8192).startswith("m256x256")     # 4 rounds against 6
+def test_choice_table_names_product_configs():
+    """Every config the generated table names is compiled into the product library, is a
+    fast config, and takes the layout of its exact entries; the table covers the headline."""
+    cfgs = tg.configs()
+    t = parse_choice_table()
+    exact, model = t["kF16"]
+    assert model and exact
+    for cfg, coef in model:
+        assert cfgs[cfg]["built"] == 1 and cfgs[cfg]["generic"] == 0
+        assert all(v >= 0 for v in coef)
+    for (lay, M, N, K, cfg) in exact:
+        assert cfgs[cfg]["built"] == 1 and (cfgs[cfg]["layouts"] >> lay) & 1
+    assert any(e[:4] == (0, 4096, 4096, 4096) for e in exact)
+    f8 = tg.fp8_configs()
+    exact8, model8 = t["kFp8"]
+    assert model8 and exact8
+    for cfg, _ in model8:
+        assert f8[cfg]["built"] == 1
+    for e in exact8:
+        assert e[0] == 0 and f8[e[4]]["built"] == 1
+    # the tooling-only rows are listed (same indices in both builds) but not compiled here
+    assert any(c["built"] == 0 for c in cfgs) and any(c["built"] == 0 for c in f8)
+
+
+SELECT_SHAPES = [(1024, 1024, 1024), (2048, 2048, 4096), (2560, 2560, 4096), (16384, 512, 4096),
+                 (3072, 3072, 4096), (4095, 3000, 1000), (3584, 3584, 2048), (4096, 4096, 4096),
+                 (6144, 6144, 4096), (5120, 4096, 4096), (8192, 8192, 8192), (1000, 1000, 3000),
+                 (7000, 5000, 1536), (12288, 4096, 4096), (640, 20480, 2048), (2304, 2304, 6144)]
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2, 3])
+def test_select_follows_choice_table(layout):
+    """tgemm_select_config_ex returns the table's exact entry for a timed shape and the cost
+    model's argmin elsewhere (recomputed here from the parsed table)."""
+    cfgs = tg.configs()
+    exact, model = parse_choice_table()["kF16"]
+    ta, tb = layout >> 1, layout & 1
+    ok = lambda c: cfgs[c]["built"] and not cfgs[c]["generic"] and (cfgs[c]["layouts"] >> layout) & 1
+    tile_of = lambda c: (cfgs[c]["block_m"], cfgs[c]["block_n"])
+    shapes = SELECT_SHAPES + [e[1:4] for e in exact if e[0] == layout]
+    for (M, N, K) in shapes:
+        got = tg.tgemm_select_config_ex(ta, tb, M, N, K, A=A16, B=A16, C=A16)
+        # fast configs need 8-element chunks along each operand's contiguous dimension
+        eligible = ((M if ta else K) % 8 == 0 and (K if tb else N) % 8 == 0 and N % 8 == 0)
+        want = expected_choice(exact, model, layout, M, N, K, tile_of, ok) if eligible else 0
+        assert got == want, (layout, M, N, K, got, want)
 
 
 def test_gemm_rejects_invalid_before_hip():
@@ -357,14 +427,14 @@ def test_fp8_config_table():
 
 def test_fp8_select():
     s = tg.tgemm_fp8_select_config
-    # rounds of 256 workgroups x the config's relative round cost (1, 0.75, 0.57)
-    assert s(4096, 4096, 4096) == 0                       # 256 x 256: one round
-    assert s(3072, 3072, 4096) == 0                       # 144 256 x 256 tiles beat two rounds of 256 x 128
-    assert s(16384, 512, 4096) == 3                       # one round of 256 x 128
-    assert s(2560, 2560, 4096) == 3
-    assert s(6144, 6144, 4096) == 0                       # 3 rounds against 5 x 0.75
-    assert s(1024, 1024, 1024) == 1                       # 128 x 128: one round
-    assert s(2048, 2048, 4096) == 1
+    f8 = tg.fp8_configs()
+    exact, model = parse_choice_table()["kFp8"]
+    ok = lambda c: f8[c]["built"] == 1
+    tile_of = lambda c: (f8[c]["block_m"], f8[c]["block_n"])
+    for (M, N, K) in SELECT_SHAPES + [e[1:4] for e in exact]:
+        if N % 8 or K % 16:
+            continue
+        assert s(M, N, K) == expected_choice(exact, model, 0, M, N, K, tile_of, ok), (M, N, K)
     assert s(0, 8, 16) == tg.SELECT_NOOP and s(8, 8, 0) == tg.SELECT_ZERO_FILL
     # generic kernel: K or ld not a multiple of 16, N or ldc not a multiple of 8, unaligned
     assert s(256, 256, 100) == tg.FP8_GENERIC
@@ -372,7 +442,7 @@ def test_fp8_select():
     assert s(256, 252, 256) == tg.FP8_GENERIC
     assert s(256, 256, 256, A=256 + 8) == tg.FP8_GENERIC
     assert s(256, 256, 256, C=256 + 2) == tg.FP8_GENERIC
-    assert s(255, 256, 4000) == 1                         # ragged M and K (16 | K) stay fast
+    assert s(255, 256, 4000) >= 0                         # ragged M and K (16 | K) stay fast
     # any ld at or above K is valid: byte strides past 2^23 take the generic kernel
     fast = s(256, 256, 256)
     assert fast >= 0 and s(256, 256, 256, lda=1 << 23) == fast

@@ -8,8 +8,7 @@ missing or cannot be loaded, every call raises.
 The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
 ``gemm_f16_cfg``, ``gemm_f16_ex_cfg`` (as ``cfg=``), ``tgemm_strerror``, ``tgemm_version``,
 ``tgemm_num_configs``, ``tgemm_config_desc``, ``tgemm_select_config``,
-``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``,
-``tgemm_mfma_probe``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
+``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
 stream unless given), ``gemm_f16_ws_cfg`` (as ``cfg=``/``splits=``),
 ``tgemm_workspace_bytes``, ``tgemm_workspace_bytes_cfg`` and ``tgemm_split_plan``, and
 ``gemm_f16_ws_static`` (split-K scratch in a static device array: allocates nothing); grouped
@@ -19,9 +18,11 @@ the fp8 (E4M3) block-scaled path: ``gemm_fp8_block`` (``gemm_fp8_block_cfg`` as
 ``tgemm_fp8_select_config``, and ``fp8_block_scaled_linear`` (quantize x per 1 x 128
 block, then the block-scaled GEMM against an fp8 weight). ``matmul`` takes row- or
 column-major operand views and picks the layout; ``GemmFunction`` is the autograd wrapper (backward: dA = dC B^T, dB = A^T dC
-through gemm_f16_ex). The instrumented
-twin ``libtgemm_stamps.so`` (``stamps_lib()``, measurement tools only) adds
-``tgemm_stamps_capacity``, ``tgemm_stamps_read`` and ``tgemm_stamps_clear``
+through gemm_f16_ex). The tooling
+twin ``libtgemm_stamps.so`` (``stamps_lib()``, measurement tools only) compiles every config
+row (the sweep-only variants too; ``built`` in a config description says whether the
+library at hand has the row) and adds ``tgemm_stamps_capacity``, ``tgemm_stamps_read``,
+``tgemm_stamps_clear`` and the MFMA throughput probe ``tgemm_mfma_probe``
 (``include/tgemm_stamps.h``).
 """
 from __future__ import annotations
@@ -50,13 +51,13 @@ FP8_BLOCK = 128
 # Every symbol include/tgemm.h declares.
 EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_strerror",
            "tgemm_version", "tgemm_num_configs", "tgemm_config_desc", "tgemm_select_config",
-           "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups", "tgemm_mfma_probe",
+           "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups",
            "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan",
            "gemm_f16_grouped", "gemm_fp8_block", "gemm_fp8_block_cfg", "quant_fp8_block",
            "tgemm_fp8_num_configs", "tgemm_fp8_config_desc", "tgemm_fp8_select_config",
            "tgemm_workspace_bytes_cfg", "gemm_f16_ws_static")
-# The extra symbols include/tgemm_stamps.h declares (instrumented build only).
-STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear")
+# The extra symbols include/tgemm_stamps.h declares (tooling build only).
+STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear", "tgemm_mfma_probe")
 STATIC_SCRATCH_BYTES = 4096 + (64 << 20)   # TGEMM_STATIC_SCRATCH_BYTES
 FAST_MAX_LD = 1 << 22        # TGEMM_FAST_MAX_LD
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
@@ -76,7 +77,7 @@ class ConfigInfo(ctypes.Structure):
                 ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("panel", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("generic", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("layouts", ctypes.c_int32), ("name", ctypes.c_char * 48)]
+                ("layouts", ctypes.c_int32), ("built", ctypes.c_int32), ("name", ctypes.c_char * 48)]
 
     def as_dict(self) -> dict:
         d = {f: getattr(self, f) for f, _ in self._fields_ if f != "name"}
@@ -125,8 +126,6 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.tgemm_tile_of.argtypes = [i32, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.tgemm_num_workgroups.restype = i64
     L.tgemm_num_workgroups.argtypes = [i32, i64, i64]
-    L.tgemm_mfma_probe.restype = i32
-    L.tgemm_mfma_probe.argtypes = [i32, i32, p, p]
     L.gemm_f16_ws.restype = i32
     L.gemm_f16_ws.argtypes = [i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, i32, p, i64, p]
     L.gemm_f16_ws_cfg.restype = i32
@@ -161,6 +160,8 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
         L.tgemm_stamps_read.argtypes = [ctypes.POINTER(ctypes.c_uint64), i64]
         L.tgemm_stamps_clear.restype = i32
         L.tgemm_stamps_clear.argtypes = []
+        L.tgemm_mfma_probe.restype = i32
+        L.tgemm_mfma_probe.argtypes = [i32, i32, p, p]
     return L
 
 
@@ -275,15 +276,16 @@ def tgemm_num_workgroups(idx: int, M: int, N: int) -> int:
 
 
 def tgemm_mfma_probe(blocks: int, iters: int, out, stream=None, library=None) -> int:
-    """Enqueue the MFMA throughput probe; out is a float32 device tensor of at least
-    blocks * PROBE_THREADS elements. Returns the FLOP the launch performs."""
+    """Enqueue the MFMA throughput probe of the tooling build (libtgemm_stamps.so); out is a
+    float32 device tensor of at least blocks * PROBE_THREADS elements. Returns the FLOP the
+    launch performs."""
     import torch
     if out.dtype != torch.float32 or not out.is_cuda or out.numel() < blocks * PROBE_THREADS:
         raise ValueError("out must be a float32 device tensor of blocks * PROBE_THREADS elements")
     handle = torch.cuda.current_stream(out.device).cuda_stream if stream is None else (
         stream if isinstance(stream, int) else stream.cuda_stream)
     with torch.cuda.device(out.device):
-        rc = (library or lib()).tgemm_mfma_probe(int(blocks), int(iters), out.data_ptr(), handle)
+        rc = (library or stamps_lib()).tgemm_mfma_probe(int(blocks), int(iters), out.data_ptr(), handle)
     if rc != TGEMM_OK:
         raise TgemmError(rc, "tgemm_mfma_probe")
     return blocks * (PROBE_THREADS // 64) * iters * PROBE_MFMA_PER_ITER * PROBE_FLOP_PER_MFMA

@@ -1,6 +1,7 @@
 """Build libtgemm.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and its
-instrumented twin libtgemm_stamps.so (the same sources with per-workgroup timestamps,
-used only by the measurement tools).
+tooling twin libtgemm_stamps.so (the same sources with per-workgroup timestamps, every
+config row of tgemm_configs.h compiled, including the sweep-only variants, and the MFMA
+throughput probe; used only by the measurement tools).
 
 Usage: python -m tiled_dense_gemm_04_amd.build   (always recompiles both)
 """
@@ -43,7 +44,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=None, stamps: bool = False) -> str:
     target = STAMPS_LIBRARY if stamps else LIBRARY
     tmp = target + ".tmp"
-    flags = list(extra_flags or []) + (["-DTGEMM_STAMPS"] if stamps else [])
+    flags = list(extra_flags or []) + (["-DTGEMM_STAMPS", "-DTGEMM_SWEEP_CONFIGS"] if stamps else [])
     cmd = [hipcc()] + HIPCC_FLAGS + flags + ["-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)

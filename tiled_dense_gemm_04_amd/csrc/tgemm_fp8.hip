@@ -25,6 +25,7 @@
 //     row (a 1 x 128 block's scales sit KB floats apart in memory, one per row). B's block
 //     scales, one per wave and k-tile, come through the scalar path;
 //   * XCD-aware, panel-ordered tile order as in the binary16 kernels.
+#include "tgemm_configs.h"
 #include "tgemm_device.h"
 
 #include <atomic>
@@ -611,16 +612,14 @@ hipError_t launch_fp8_cfg(const Fp8Args& g, hipStream_t s, int device) {
 
 }  // namespace
 
-// fp8 configs: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD, DB)
-#define TGEMM_FP8_CONFIGS(X)     \
-  X(256, 256, 2, 4, 2, 4, 1, 0)  \
-  X(128, 128, 2, 2, 3, 4, 1, 0)  \
-  X(256, 128, 4, 2, 3, 4, 1, 0)  \
-  X(256, 128, 4, 2, 3, 4, 1, 1)
+static hipError_t launch_fp8_unbuilt(const Fp8Args&, hipStream_t, int) { return hipErrorNotSupported; }
 
-#define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X, DB) \
-  {BM, BN, WM, WN, S, P, X, fp8_lds_bytes<BM, BN, WM, WN, S>(), "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN "_db" #DB},
-#define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X, DB) launch_fp8_cfg<BM, BN, WM, WN, S, P, X, DB>,
+// The fp8 rows of tgemm_configs.h: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD, DB, PROD)
+#define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X, DB, PROD)                                          \
+  {BM, BN, WM, WN, S, P, X, fp8_lds_bytes<BM, BN, WM, WN, S>(), TGEMM_BUILT(PROD),               \
+   "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN "_db" #DB},
+#define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X, DB, PROD) \
+  TGEMM_IF_BUILT(PROD, (launch_fp8_cfg<BM, BN, WM, WN, S, P, X, DB>), launch_fp8_unbuilt),
 
 const Fp8Config* fp8_config_table(int* count) {
   static const Fp8Config table[] = {TGEMM_FP8_CONFIGS(TGEMM_FP8_ROW)};

@@ -23,6 +23,7 @@ struct Config {
   int xcd_remap;        // keep consecutive logical tiles on one XCD
   int generic;          // unaligned-capable generic kernel
   int layouts;          // bit (2 * trans_a + trans_b) set: the config takes that layout
+  int built;            // 1 = this build compiles the kernel (see tgemm_configs.h)
   const char* name;
 };
 
@@ -122,6 +123,7 @@ struct Fp8Args {
 struct Fp8Config {
   int bm, bn, waves_m, waves_n, stages, panel, xcd_remap;
   int lds_bytes;  // dynamic LDS of one workgroup
+  int built;      // 1 = this build compiles the kernel (see tgemm_configs.h)
   const char* name;
 };
 const Fp8Config* fp8_config_table(int* count);
@@ -150,11 +152,13 @@ hipError_t static_scratch(int device, void** out);
 // Zero-fill of an M x N block with row stride ldc (the K == 0 case).
 hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s);
 
-// MFMA throughput probe (tooling): `blocks` workgroups of 8 waves, each wave issuing
-// iters x 16 independent 16x16x32 fp16 MFMAs; one float per thread goes to out
+// MFMA throughput probe (tooling build only): `blocks` workgroups of 8 waves, each wave
+// issuing iters x 16 independent 16x16x32 fp16 MFMAs; one float per thread goes to out
 // (blocks * 512 floats).
 constexpr int kProbeThreads = 512, kProbeMfmaPerIter = 16;
+#ifdef TGEMM_STAMPS
 hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s);
+#endif
 
 // Workgroup timestamps of the instrumented build (TGEMM_STAMPS): kStampWords words per
 // workgroup for the first kStampWorkgroups workgroups of every launch (later launches

@@ -16,6 +16,7 @@
 //   * 32x32x16 fp16 MFMAs accumulate in fp32; operands are fed as (B^T, A^T) so that each
 //     lane ends up holding four consecutive output columns, stored as one 8-byte write;
 //   * the workgroup order is XCD-aware and panel-ordered (tile_of in tgemm_internal.h).
+#include "tgemm_configs.h"
 #include "tgemm_device.h"
 
 #include <atomic>
@@ -1259,6 +1260,7 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g) {
   }
 }
 
+#ifdef TGEMM_STAMPS
 // MFMA throughput probe (tooling, not part of the GEMM): every wave keeps 16 independent
 // 16x16x32 accumulators and issues them back to back, `iters` rounds, on register operands
 // filled with pseudo-random binary16 values (random sign and mantissa, magnitudes 2^-2 to
@@ -1306,6 +1308,8 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe(int iters, float* ou
   out[tid] = sum;
   clk.finish(iters, TG_STAMP_TABLE);
 }
+
+#endif  // TGEMM_STAMPS
 
 // C[i, j] = +0 for i < M, j < N (the empty sum when K == 0).
 __global__ __launch_bounds__(256) void zero_fill(_Float16* C, int M, int N, int64_t ldc) {
@@ -1453,12 +1457,12 @@ hipError_t launch_generic(const GemmArgs& g, hipStream_t s, int) {
 
 }  // namespace
 
+#ifdef TGEMM_STAMPS
 hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s) {
   hipLaunchKernelGGL(mfma_probe, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters, out);
   return hipGetLastError();
 }
 
-#ifdef TGEMM_STAMPS
 hipError_t stamps_read(unsigned long long* host, int64_t words) {
   return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_stamps), (size_t)words * sizeof(unsigned long long), 0,
                              hipMemcpyDeviceToHost);
@@ -1483,67 +1487,41 @@ hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t 
   return hipGetLastError();
 }
 
-// The config table: one X-macro list drives both the table rows and the kernel
-// instantiations, so a row always describes the kernel it launches.
-//   X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP)
-#define TGEMM_FAST_CONFIGS(X)      \
-  X(256, 256, 64, 2, 4, 2, 4, 1)   \
-  X(128, 128, 64, 2, 2, 2, 4, 1)
+// The config table: the X-macro lists of tgemm_configs.h drive both the table rows and the
+// kernel instantiations, so a row always describes the kernel it launches. Rows this build
+// does not compile keep their place in the table, marked not built, with a launcher that
+// refuses (the host never calls it: it checks `built` first).
+static hipError_t launch_unbuilt(const GemmArgs&, hipStream_t, int) { return hipErrorNotSupported; }
 
-// Pipelined kernel instantiations: X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP)
-#define TGEMM_PIPE_CONFIGS(X)      \
-  X(256, 256, 32, 2, 4, 4, 4, 1)   \
-  X(256, 256, 32, 2, 2, 4, 4, 1)   \
-  X(128, 128, 32, 2, 2, 4, 4, 1)   \
-  X(256, 128, 32, 2, 2, 4, 4, 1)   \
-  X(128, 128, 64, 2, 2, 2, 4, 1)
-
-// Ping-pong kernel instantiations (8 waves): X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD)
-#define TGEMM_PP_CONFIGS(X)        \
-  X(256, 256, 32, 2, 4, 4, 4, 1)
-// Ping-pong with 16x16x32 MFMAs (the default for large grids), with variants of the
-// wave grid, ring depth and workgroup order kept for the sweep. Last column: 1 = also
-// instantiated for transposed operands (all four layouts).
-#define TGEMM_PP1_CONFIGS(X)          \
-  X(256, 256, 32, 2, 4, 4, 4, 1, 1)   \
-  X(256, 256, 32, 4, 2, 4, 4, 1, 0)   \
-  X(256, 256, 32, 2, 4, 5, 4, 1, 0)   \
-  X(256, 256, 32, 2, 4, 4, 8, 1, 0)   \
-  X(256, 256, 32, 2, 4, 4, 2, 1, 0)   \
-  X(256, 256, 32, 2, 4, 4, 4, 0, 0)   \
-  X(128, 128, 32, 2, 4, 4, 4, 1, 1)   \
-  X(256, 128, 32, 2, 4, 4, 4, 1, 1)   \
-  X(128, 256, 32, 2, 4, 4, 4, 1, 1)   \
-  X(256, 192, 32, 2, 4, 4, 4, 1, 1)
-
-// Quad kernel instantiations (4 waves): X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD, ALL)
-#define TGEMM_QUAD_CONFIGS(X)         \
-  X(256, 256, 32, 2, 2, 4, 4, 0, 0)   \
-  X(256, 256, 32, 2, 2, 4, 4, 1, 0)
-
-#define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, 1, "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
-#define TGEMM_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_fast<BM, BN, BK, WM, WN, S, P, X>,
-#define TGEMM_COUNT(BM, BN, BK, WM, WN, S, P, X) 0,
-#define TGEMM_PIPE_ROW(BM, BN, BK, WM, WN, S, P, X) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, 1, "p" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
-#define TGEMM_PIPE_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pipe<BM, BN, BK, WM, WN, S, P, X>,
-#define TGEMM_PP_ROW(BM, BN, BK, WM, WN, S, P, X) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, 1, "q" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
-#define TGEMM_PP_LAUNCHER(BM, BN, BK, WM, WN, S, P, X) launch_pp<BM, BN, BK, WM, WN, S, P, X, 32, false>,
-#define TGEMM_PP1_ROW(BM, BN, BK, WM, WN, S, P, X, ALL) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, ALL ? 0xF : 1, "m" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
-#define TGEMM_PP1_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, ALL) launch_pp<BM, BN, BK, WM, WN, S, P, X, 16, ALL>,
-#define TGEMM_COUNT9(BM, BN, BK, WM, WN, S, P, X, ALL) 0,
-#define TGEMM_QUAD_ROW(BM, BN, BK, WM, WN, S, P, X, ALL) \
-  {BM, BN, BK, S, WM, WN, P, X, 0, ALL ? 0xF : 1, "u" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
-#define TGEMM_QUAD_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, ALL) launch_quad<BM, BN, BK, WM, WN, S, P, X, ALL>,
+#define TGEMM_ROW(BM, BN, BK, WM, WN, S, P, X, PROD) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, 1, TGEMM_BUILT(PROD), "t" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, PROD) \
+  TGEMM_IF_BUILT(PROD, (launch_fast<BM, BN, BK, WM, WN, S, P, X>), launch_unbuilt),
+#define TGEMM_COUNT(...) 0,
+#define TGEMM_PIPE_ROW(BM, BN, BK, WM, WN, S, P, X, PROD) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, 1, TGEMM_BUILT(PROD), "p" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PIPE_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, PROD) \
+  TGEMM_IF_BUILT(PROD, (launch_pipe<BM, BN, BK, WM, WN, S, P, X>), launch_unbuilt),
+#define TGEMM_PP_ROW(BM, BN, BK, WM, WN, S, P, X, PROD) \
+  {BM, BN, BK, S, WM, WN, P, X, 0, 1, TGEMM_BUILT(PROD), "q" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PP_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, PROD) \
+  TGEMM_IF_BUILT(PROD, (launch_pp<BM, BN, BK, WM, WN, S, P, X, 32, false>), launch_unbuilt),
+#define TGEMM_PP1_ROW(BM, BN, BK, WM, WN, S, P, X, ALL, PROD)                                                 \
+  {BM, BN, BK, S, WM, WN, P, X, 0, ALL ? 0xF : 1, TGEMM_BUILT(PROD),                                        \
+   "m" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_PP1_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, ALL, PROD) \
+  TGEMM_IF_BUILT(PROD, (launch_pp<BM, BN, BK, WM, WN, S, P, X, 16, ALL>), launch_unbuilt),
+#define TGEMM_QUAD_ROW(BM, BN, BK, WM, WN, S, P, X, ALL, PROD)                                                \
+  {BM, BN, BK, S, WM, WN, P, X, 0, ALL ? 0xF : 1, TGEMM_BUILT(PROD),                                        \
+   "u" #BM "x" #BN "x" #BK "_s" #S "_w" #WM "x" #WN "_p" #P "_x" #X},
+#define TGEMM_QUAD_LAUNCHER(BM, BN, BK, WM, WN, S, P, X, ALL, PROD) \
+  TGEMM_IF_BUILT(PROD, (launch_quad<BM, BN, BK, WM, WN, S, P, X, ALL>), launch_unbuilt),
 
 // Function-local statics: host-only tables (the device pass parses these bodies, which
 // instantiates every kernel, but emits no host data).
 const Config* config_table(int* count) {
   static const Config table[] = {
-      {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, 0xF, "generic_64x64x32"},
+      {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, 0xF, 1, "generic_64x64x32"},
       TGEMM_FAST_CONFIGS(TGEMM_ROW) TGEMM_PIPE_CONFIGS(TGEMM_PIPE_ROW) TGEMM_PP_CONFIGS(TGEMM_PP_ROW)
           TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW) TGEMM_QUAD_CONFIGS(TGEMM_QUAD_ROW)};
   *count = (int)(sizeof(table) / sizeof(table[0]));
@@ -1573,8 +1551,8 @@ Launcher launcher(int idx) {
                                                    TGEMM_QUAD_CONFIGS(TGEMM_QUAD_LAUNCHER)};
   static_assert(sizeof(table) / sizeof(table[0]) ==
                     1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT) TGEMM_PIPE_CONFIGS(TGEMM_COUNT)
-                                           TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT9)
-                                               TGEMM_QUAD_CONFIGS(TGEMM_COUNT9)}) /
+                                           TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT)
+                                               TGEMM_QUAD_CONFIGS(TGEMM_COUNT)}) /
                             sizeof(int),
                 "one launcher per config");
   return table[idx];

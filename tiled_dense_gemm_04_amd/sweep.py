@@ -7,9 +7,19 @@ tgemm_api.cpp's choose_fast). With --split, time split-K instead: the 256 x 256 
   python -m tiled_dense_gemm_04_amd.sweep [--out results.json] [--md out.md] [--torch] [--iters 30]
   python -m tiled_dense_gemm_04_amd.sweep --split [--md out.md]
   python -m tiled_dense_gemm_04_amd.sweep --choice [--md out.md]
+  python -m tiled_dense_gemm_04_amd.sweep --write-table csrc/tgemm_choice.inc [--md out.md]
+  python -m tiled_dense_gemm_04_amd.sweep --refit results.json --write-table tgemm_choice.inc
 
 --choice checks the default config choice (fp16 choose_fast, fp8 fp8_choose) against the
 candidate configs on shapes from 1024^2 to 6144^2, timed with the measurement protocol.
+
+--write-table times every product config (those the product library compiles) on
+TABLE_SHAPES and the measured workloads, fits the per-config cost model of the selector
+(predicted microseconds a*R + b*R*k + c*O + d*k*O, R = ceil(tiles / 256), O = tiles / 256,
+k = K / 1024; non-negative least squares on relative error), and writes the selector's
+table (exact shapes with their fastest config, then the model coefficients) as C++ for
+tgemm_api.cpp to include. The timings go to <table>.json beside it; --refit rewrites the
+table from such a file without a GPU.
 """
 from __future__ import annotations
 
@@ -156,6 +166,197 @@ def split_sweep(md_path=None):
     return 0
 
 
+# Shapes the selector's cost model is fitted on (A and B as given): grid sizes from under
+# one round of 256 workgroups to several, K from 512 to 8192.
+TABLE_SHAPES = [
+    (1024, 1024, 4096), (1536, 1536, 4096), (2048, 2048, 4096), (2560, 2560, 4096), (2048, 4096, 4096),
+    (16384, 512, 4096), (3072, 3072, 4096), (3072, 4096, 4096), (4096, 4096, 4096), (5120, 4096, 4096),
+    (6144, 6144, 4096), (4096, 8192, 4096), (8192, 8192, 4096),
+    (3584, 3584, 2048), (4096, 2560, 2048), (2048, 2048, 2048), (6144, 4096, 2048), (8192, 8192, 2048),
+    (4095, 3000, 1000), (4096, 3072, 1024), (1024, 1024, 1024), (2048, 2048, 1024), (4096, 4096, 1024),
+    (8192, 8192, 1024), (1024, 1024, 8192), (2048, 2048, 8192), (4096, 4096, 8192), (8192, 8192, 8192),
+    (4096, 4096, 512), (8192, 8192, 512), (2560, 5120, 2048), (5120, 5120, 1024),
+]
+ROUND = 256  # workgroups in flight at once: one per compute unit
+
+
+def model_features(tiles: int, K: int):
+    R = -(-tiles // ROUND)
+    O = tiles / ROUND
+    k = K / 1024.0
+    return [R, R * k, O, k * O]
+
+
+def fit_model(rows):
+    """rows: [(tiles, K, us)]. Non-negative coefficients (a, b, c, d) minimising the
+    relative error of a*R + b*R*k + c*O + d*k*O against us."""
+    import numpy as np
+    from scipy.optimize import nnls
+
+    X = np.array([model_features(t, K) for t, K, _ in rows], dtype=np.float64)
+    y = np.array([us for _, _, us in rows], dtype=np.float64)
+    coef, _ = nnls(X / y[:, None], np.ones_like(y))
+    return [float(v) for v in coef]
+
+
+def predict(coef, tiles, K):
+    return sum(c * f for c, f in zip(coef, model_features(tiles, K)))
+
+
+def table_sweep(out_inc, md_path=None, refit=None):
+    """Time (or reload) the product configs on TABLE_SHAPES and the workloads, fit the cost
+    model and write the selector's table."""
+    if refit:
+        with open(refit) as f:
+            data = json.load(f)
+    else:
+        data = measure_table()
+        with open(os.path.splitext(out_inc)[0] + ".json", "w") as f:
+            json.dump(data, f, indent=1)
+    text_inc, text_md = render_table(data)
+    with open(out_inc, "w") as f:
+        f.write(text_inc)
+    if md_path:
+        with open(md_path, "w") as f:
+            f.write(text_md)
+    print(text_md)
+    return 0
+
+
+def measure_table():
+    import torch
+
+    import tgemm_workloads as W
+    import tiled_dense_gemm_04_amd as tg
+    from tiled_dense_gemm_04_amd.measure import timed_trials
+
+    stream = torch.cuda.current_stream()
+    cfgs = tg.configs()
+    f16 = [i for i, c in enumerate(cfgs) if c["built"] and not c["generic"]]
+    cases = [(0, M, N, K) for (M, N, K) in TABLE_SHAPES]
+    for w in list(W.WORKLOADS.values()) + list(W.LAYOUT_WORKLOADS.values()) + list(W.SPLIT_WORKLOADS.values()):
+        case = (2 * int(w.trans_a) + int(w.trans_b), w.M, w.N, w.K)
+        if case not in cases:
+            cases.append(case)
+    data = {"device": torch.cuda.get_device_name(0), "round": ROUND,
+            "f16": {"configs": {str(i): cfgs[i]["name"] for i in f16}, "cases": []},
+            "fp8": {"configs": {}, "cases": []}}
+    for (layout, M, N, K) in cases:
+        ta, tb = bool(layout & 2), bool(layout & 1)
+        A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=5)
+        a = torch.from_numpy(A.T.copy() if ta else A).cuda()
+        b = torch.from_numpy(B.T.copy() if tb else B).cuda()
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        times = {}
+        for i in f16:
+            if not (cfgs[i]["layouts"] >> layout) & 1:
+                continue
+            times[str(i)] = round(timed_trials(
+                torch, stream, lambda j, i=i: tg.gemm_f16_ex(a, b, c, trans_a=ta, trans_b=tb, cfg=i),
+                trials=5, warm_ms=30.0)["median_us"], 2)
+        best = min(times, key=times.get)
+        data["f16"]["cases"].append({"layout": layout, "M": M, "N": N, "K": K, "us": times})
+        print(f"f16 layout {layout} {M}x{N}x{K}: " + ", ".join(f"{k}:{v}" for k, v in times.items())
+              + f" -> best {best}", flush=True)
+        del a, b, c
+        torch.cuda.empty_cache()
+    nf8 = tg.tgemm_fp8_num_configs()
+    f8 = [i for i in range(nf8) if tg.tgemm_fp8_config_desc(i)["built"]]
+    data["fp8"]["configs"] = {str(i): tg.tgemm_fp8_config_desc(i)["name"] for i in f8}
+    f8cases = [(M, N, K) for (M, N, K) in TABLE_SHAPES if N % 8 == 0 and K % 16 == 0]
+    for w in W.FP8_WORKLOADS.values():
+        if (w.M, w.N, w.K) not in f8cases:
+            f8cases.append((w.M, w.N, w.K))
+    for (M, N, K) in f8cases:
+        A, SA, B, SB = W.make_fp8_inputs(M, N, K, seed=5)
+        a, sa, b, sb = (torch.from_numpy(x).cuda() for x in (A, SA, B, SB))
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        times = {str(i): round(timed_trials(
+            torch, stream, lambda j, i=i: tg.gemm_fp8_block(a, sa, b, sb, c, cfg=i),
+            trials=5, warm_ms=30.0)["median_us"], 2) for i in f8}
+        data["fp8"]["cases"].append({"layout": 0, "M": M, "N": N, "K": K, "us": times})
+        print(f"fp8 {M}x{N}x{K}: " + ", ".join(f"{k}:{v}" for k, v in times.items()), flush=True)
+        del a, sa, b, sb, c
+        torch.cuda.empty_cache()
+    return data
+
+
+def _tiles(name: str, M: int, N: int) -> int:
+    """Workgroups of a config from its name (kind letter, then BMxBNxBK)."""
+    bm, bn = (int(v) for v in name[1:].split("_")[0].split("x")[:2])
+    return -(-M // bm) * -(-N // bn)
+
+
+def render_table(data):
+    """(C++ table, markdown report) from measured timings."""
+    L_inc = ["// tgemm_choice.inc -- the config selector's table, generated by",
+             "// `python -m tiled_dense_gemm_04_amd.sweep --write-table` from timings on "
+             f"{data['device']}; do not edit by hand.",
+             "// Exact entries: every shape the sweep timed, with its fastest product config.",
+             "// Model entries: per product config, microseconds ~ a*R + b*R*k + c*O + d*k*O with",
+             f"// R = ceil(tiles / {data['round']}), O = tiles / {data['round']}, k = K / 1024 (tiles = the config's",
+             "// workgroup count); non-negative least squares on relative error over the timed",
+             "// shapes with A and B as given."]
+    L_md = ["# Config selector table: timings, fitted cost model, choice quality (one MI355X)", "",
+            "Command (from the repository root): `python -m tiled_dense_gemm_04_amd.sweep --write-table "
+            "tiled_dense_gemm_04_amd/csrc/tgemm_choice.inc --md gpurun_out/config_choice.md`", "",
+            f"Device: {data['device']}. Every product config on every shape: 10 warm-up calls and >= 30 ms",
+            "of calls, then 5 trials of >= 20 ms (HIP events), median microseconds per call. The",
+            "selector takes an exact entry when the shape was timed, else the cost model's argmin;",
+            "`held-out loss` is the loss of the model's pick when that shape is left out of the fit",
+            "(the model alone, as for a shape the sweep never saw).", ""]
+    for kind, label in (("f16", "fp16 GEMM (+ ReLU), N(0,1) inputs"),
+                        ("fp8", "fp8 block-scaled GEMM (E4M3 codes, 1 x 128 / 128 x 128 scales)")):
+        d = data[kind]
+        names = d["configs"]
+        ids = sorted(names, key=int)
+        cases = d["cases"]
+        fit_rows = {i: [(_tiles(names[i], c["M"], c["N"]), c["K"], c["us"][i]) for c in cases
+                        if c["layout"] == 0 and i in c["us"]] for i in ids}
+        coefs = {i: fit_model(fit_rows[i]) for i in ids}
+        prefix = "kF16" if kind == "f16" else "kFp8"
+        L_inc += ["", f"static const ChoiceExact {prefix}Exact[] = {{"]
+        for c in cases:
+            best = min(c["us"], key=c["us"].get)
+            L_inc.append(f"    {{{c['layout']}, {c['M']}, {c['N']}, {c['K']}, {best}}},")
+        L_inc += ["};", f"static const ChoiceModel {prefix}Model[] = {{"]
+        for i in ids:
+            a, b, cc, dd = coefs[i]
+            L_inc.append(f"    {{{i}, {a:.6g}, {b:.6g}, {cc:.6g}, {dd:.6g}}},  // {names[i]}")
+        L_inc.append("};")
+        # report
+        L_md += [f"## {label}", "",
+                 "| layout | M x N x K | " + " | ".join(names[i] for i in ids)
+                 + " | fastest | model pick | held-out pick | held-out loss |",
+                 "|---|---|" + "---|" * (len(ids) + 4)]
+        losses = []
+        for n, c in enumerate(cases):
+            best = min(c["us"], key=c["us"].get)
+            avail = [i for i in ids if i in c["us"]]
+            pick = min(avail, key=lambda i: predict(coefs[i], _tiles(names[i], c["M"], c["N"]), c["K"]))
+            held = {i: fit_model([r for m, r in enumerate(
+                [(_tiles(names[i], x["M"], x["N"]), x["K"], x["us"].get(i)) for x in cases]) if m != n
+                and cases[m]["layout"] == 0 and r[2] is not None]) for i in avail}
+            hpick = min(avail, key=lambda i: predict(held[i], _tiles(names[i], c["M"], c["N"]), c["K"]))
+            loss = 100 * (c["us"][hpick] / c["us"][best] - 1)
+            losses.append(loss)
+            L_md.append(f"| {c['layout']} | {c['M']}x{c['N']}x{c['K']} | "
+                        + " | ".join(("**%.1f**" if i == best else "%.1f") % c["us"][i] if i in c["us"] else "-"
+                                     for i in ids)
+                        + f" | {names[best]} | {names[pick]} | {names[hpick]} | {loss:.1f} % |")
+        L_md += ["", "Fitted coefficients (microseconds):", "",
+                 "| config | a (per round) | b (per round per 1024 of K) | c (per round's worth of tiles) | d (per round's worth of tiles per 1024 of K) | median abs. rel. error |",
+                 "|---|---|---|---|---|---|"]
+        for i in ids:
+            errs = sorted(abs(predict(coefs[i], t, K) / us - 1) for t, K, us in fit_rows[i])
+            med = errs[len(errs) // 2] if errs else float("nan")
+            L_md.append(f"| {names[i]} | " + " | ".join(f"{v:.3f}" for v in coefs[i]) + f" | {100 * med:.1f} % |")
+        losses.sort()
+        L_md += ["", f"Held-out loss over {len(losses)} shapes: median {losses[len(losses) // 2]:.1f} %, "
+                 f"mean {sum(losses) / len(losses):.1f} %, max {losses[-1]:.1f} %.", ""]
+    return "\n".join(L_inc) + "\n", "\n".join(L_md) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=None)
@@ -166,7 +367,13 @@ def main():
     ap.add_argument("--split", action="store_true", help="split-K sweep on small-grid shapes")
     ap.add_argument("--choice", action="store_true", help="default config choice against the candidates")
     ap.add_argument("--md", default=None, help="write the table (markdown) here")
+    ap.add_argument("--write-table", default=None, metavar="INC",
+                    help="time the product configs, fit the selector's cost model, write its table here")
+    ap.add_argument("--refit", default=None, metavar="JSON",
+                    help="with --write-table: refit from saved timings instead of timing (no GPU)")
     args = ap.parse_args()
+    if args.write_table:
+        return table_sweep(args.write_table, args.md, args.refit)
     if args.split:
         return split_sweep(args.md)
     if args.choice:
