@@ -50,8 +50,10 @@ def eprint(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the device code and the config lists (not the host-side selector), so
+    profiles taken on a kernel stay valid while only the host logic changes."""
     h = hashlib.sha256()
-    for f in ("tgemm_kernels.hip", "tgemm_device.h", "tgemm_fp8.hip", "tgemm_internal.h", "tgemm_api.cpp"):
+    for f in ("tgemm_kernels.hip", "tgemm_device.h", "tgemm_fp8.hip", "tgemm_internal.h", "tgemm_configs.h"):
         with open(os.path.join(ROOT, "tiled_dense_gemm_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -35,15 +35,22 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 
 
-def time_config(tg, torch, a, b, c, relu, cfg, iters, warmup=5):
+def time_config(tg, torch, a, b, c, relu, cfg, iters, warmup=5, trans_a=False, trans_b=False):
+    """Microseconds per launch of table config cfg: on the product library when it compiles
+    the row, else on the tooling build (sweep-only variants)."""
     stream = torch.cuda.current_stream()
+    library = None if tg.tgemm_config_desc(cfg)["built"] else tg.stamps_lib()
+
+    def call():
+        tg.gemm_f16_ex(a, b, c, trans_a, trans_b, relu=relu, cfg=cfg, library=library)
+
     for _ in range(warmup):
-        tg.gemm_f16(a, b, c, relu=relu, cfg=cfg)
+        call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(iters):
-        tg.gemm_f16(a, b, c, relu=relu, cfg=cfg)
+        call()
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters * 1e3  # us
@@ -71,7 +78,7 @@ def choice_sweep(md_path=None):
     names = {c["name"]: i for i, c in enumerate(tg.configs())}
     L = ["# Default config choice against the candidates (one MI355X)", "",
          "Command (from the repository root): `python -m tiled_dense_gemm_04_amd.sweep --choice --md "
-         "gpurun_out/choice.md`", "",
+         "out/choice.md`", "",
          f"Device: {torch.cuda.get_device_name(0)}. Each config: 10 warm-up calls and >= 50 ms of calls, then 5",
          "trials of >= 20 ms (HIP events), median microseconds per call. * marks the config the library",
          "picks by itself; the last column is its loss against the fastest candidate.", "",
@@ -299,7 +306,7 @@ def render_table(data):
              "// shapes with A and B as given."]
     L_md = ["# Config selector table: timings, fitted cost model, choice quality (one MI355X)", "",
             "Command (from the repository root): `python -m tiled_dense_gemm_04_amd.sweep --write-table "
-            "tiled_dense_gemm_04_amd/csrc/tgemm_choice.inc --md gpurun_out/config_choice.md`", "",
+            "tiled_dense_gemm_04_amd/csrc/tgemm_choice.inc --md out/config_choice.md`", "",
             f"Device: {data['device']}. Every product config on every shape: 10 warm-up calls and >= 30 ms",
             "of calls, then 5 trials of >= 20 ms (HIP events), median microseconds per call. The",
             "selector takes an exact entry when the shape was timed, else the cost model's argmin;",
@@ -432,20 +439,25 @@ def main():
             json.dump(results, f, indent=1)
     if args.md:
         with open(args.md, "w") as f:
-            f.write(sweep_markdown(results, [cd["name"] for cd in cfgs], args, torch.cuda.get_device_name(0)))
+            f.write(sweep_markdown(results, cfgs, args, torch.cuda.get_device_name(0)))
     return 0
 
 
-def sweep_markdown(results, names, args, device) -> str:
+def sweep_markdown(results, cfgs, args, device) -> str:
     """Configs as rows, workloads as columns, the fastest per column in bold."""
+    from bench import kernel_source_hash
+
+    names = [cd["name"] for cd in cfgs]
     cmd = "python -m tiled_dense_gemm_04_amd.sweep" + (" --torch" if args.torch else "") + \
-        f" --iters {args.iters} --md gpurun_out/sweep.md"
+        f" --iters {args.iters} --md out/sweep.md"
     L = ["# Config sweep, all measured workloads (one MI355X)", "",
          f"Command (from the repository root): `{cmd}`", "",
          f"Device: {device}. Every table config on every workload: {args.iters} timed launches after 5",
          "warm-up, HIP events, microseconds per launch; **bold** is the fastest config per workload.",
          "`torch.matmul` (+ `relu_`) is hipBLASLt on the same inputs, context only. Absolute times vary",
-         "by ~5-10 % between MI355X boxes (power and thermal state); compare within a column.", "",
+         "by ~5-10 % between MI355X boxes (power and thermal state); compare within a column.",
+         "Configs marked (t) are sweep-only variants, timed on the tooling build (libtgemm_stamps.so);",
+         f"the rest run on the product library. Kernel source hash {kernel_source_hash()}.", "",
          "| config | " + " | ".join(r["workload"] for r in results) + " |",
          "|---|" + "---|" * len(results)]
     for n in names:
@@ -453,7 +465,7 @@ def sweep_markdown(results, names, args, device) -> str:
         for r in results:
             t = r["times_us"].get(n)
             cells.append("-" if t is None else (f"**{t:.2f}**" if n == r["best"] else f"{t:.2f}"))
-        L.append(f"| {n} | " + " | ".join(cells) + " |")
+        L.append(f"| {n}{'' if cfgs[names.index(n)]['built'] else ' (t)'} | " + " | ".join(cells) + " |")
     if any("torch_matmul_us" in r for r in results):
         L.append("| torch.matmul(+relu) | " + " | ".join(f"{r['torch_matmul_us']:.2f}" if "torch_matmul_us" in r
                                                         else "-" for r in results) + " |")
