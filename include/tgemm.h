@@ -38,7 +38,8 @@ extern "C" {
 #endif
 
 #define TGEMM_OK 0
-#define TGEMM_EINVAL_DIM (-1)   /* M, N or K negative, or larger than TGEMM_MAX_DIM        */
+#define TGEMM_EINVAL_DIM (-1)   /* M, N or K negative, or larger than TGEMM_MAX_DIM, or an  */
+                                /* output that needs 2^31 or more workgroups in one launch */
 #define TGEMM_EINVAL_LD (-2)    /* lda < max(1,K), ldb < max(1,N), ldc < max(1,N) (with    */
                                 /* transposed operands lda < max(1,M), ldb < max(1,K))     */
 #define TGEMM_ENULL (-3)        /* NULL pointer for an operand with a nonzero extent        */
