@@ -33,6 +33,7 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG_DIR, "libtgemm.so")
 STAMPS_LIBRARY = os.path.join(PKG_DIR, "libtgemm_stamps.so")
+DEBUGFILL_LIBRARY = os.path.join(PKG_DIR, "libtgemm_debugfill.so")
 
 TGEMM_OK = 0
 TGEMM_EINVAL_DIM = -1
@@ -166,11 +167,25 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libtgemm.so (raises if it has not been built)."""
+    """The loaded libtgemm.so (raises if it has not been built). The environment variable
+    TGEMM_LIBRARY names another build with the same ABI to load instead (for instance
+    libtgemm_debugfill.so, to run a whole test suite on the NaN-poisoning build)."""
     global _lib
     if _lib is None:
-        _lib = _load(LIBRARY, stamps=False)
+        _lib = _load(os.environ.get("TGEMM_LIBRARY") or LIBRARY, stamps=False)
     return _lib
+
+
+_debugfill_lib = None
+
+
+def debugfill_lib() -> ctypes.CDLL:
+    """The debugging build libtgemm_debugfill.so (TGEMM_DEBUG_FILL: LDS copy destinations
+    are NaN-poisoned before every copy); same ABI as libtgemm.so."""
+    global _debugfill_lib
+    if _debugfill_lib is None:
+        _debugfill_lib = _load(DEBUGFILL_LIBRARY, stamps=False)
+    return _debugfill_lib
 
 
 def stamps_lib() -> ctypes.CDLL:

@@ -1,7 +1,9 @@
-"""Build libtgemm.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and its
-tooling twin libtgemm_stamps.so (the same sources with per-workgroup timestamps, every
-config row of tgemm_configs.h compiled, including the sweep-only variants, and the MFMA
-throughput probe; used only by the measurement tools).
+"""Build libtgemm.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and two twins
+from the same sources: the tooling build libtgemm_stamps.so (per-workgroup timestamps,
+every config row of tgemm_configs.h compiled, including the sweep-only variants, and the
+MFMA throughput probe; used only by the measurement tools) and the debugging build
+libtgemm_debugfill.so (TGEMM_DEBUG_FILL: every LDS copy destination is overwritten with
+NaN bytes before the copy is issued; used only by its GPU test).
 
 Usage: python -m tiled_dense_gemm_04_amd.build   (always recompiles both)
 """
@@ -17,6 +19,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libtgemm.so")
 STAMPS_LIBRARY = os.path.join(PKG, "libtgemm_stamps.so")
+DEBUGFILL_LIBRARY = os.path.join(PKG, "libtgemm_debugfill.so")
+VARIANTS = {
+    "product": (LIBRARY, []),
+    "stamps": (STAMPS_LIBRARY, ["-DTGEMM_STAMPS", "-DTGEMM_SWEEP_CONFIGS"]),
+    "debugfill": (DEBUGFILL_LIBRARY, ["-DTGEMM_DEBUG_FILL"]),
+}
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "tgemm_kernels.hip"), os.path.join(CSRC, "tgemm_fp8.hip"),
@@ -41,10 +49,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtgemm)")
 
 
-def build(verbose: bool = False, extra_flags=None, stamps: bool = False) -> str:
-    target = STAMPS_LIBRARY if stamps else LIBRARY
+def build(verbose: bool = False, extra_flags=None, stamps: bool = False, variant: str | None = None) -> str:
+    target, vflags = VARIANTS[variant or ("stamps" if stamps else "product")]
     tmp = target + ".tmp"
-    flags = list(extra_flags or []) + (["-DTGEMM_STAMPS", "-DTGEMM_SWEEP_CONFIGS"] if stamps else [])
+    flags = list(extra_flags or []) + vflags
     cmd = [hipcc()] + HIPCC_FLAGS + flags + ["-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -61,11 +69,11 @@ def build(verbose: bool = False, extra_flags=None, stamps: bool = False) -> str:
 
 
 def build_all(verbose: bool = False):
-    """Both libraries, compiled in parallel."""
+    """All three libraries, compiled in parallel."""
     from concurrent.futures import ThreadPoolExecutor
 
-    with ThreadPoolExecutor(2) as ex:
-        futs = [ex.submit(build, verbose, None, st) for st in (False, True)]
+    with ThreadPoolExecutor(len(VARIANTS)) as ex:
+        futs = [ex.submit(build, verbose, None, False, v) for v in VARIANTS]
         return [f.result() for f in futs]
 
 

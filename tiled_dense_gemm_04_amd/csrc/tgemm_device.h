@@ -118,7 +118,27 @@ __device__ __forceinline__ int4v make_rsrc(const void* base, uint32_t range_byte
 // indexing, no messages), so clobbering it is safe here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// TGEMM_DEBUG_FILL (a debugging build, never the product): every copy first overwrites its
+// destination with all-ones bytes (a NaN as binary16, as an E4M3 code and as float32) and
+// waits for that write, then issues the copy. A read of a slot before its copy has landed
+// (a missing wait or barrier), or after the next copy into it was issued (a slot reused too
+// early), then sees NaN, which reaches the output.
+#ifdef TGEMM_DEBUG_FILL
+__device__ __forceinline__ void debug_poison(uint32_t lds_base, int bytes_per_lane) {
+  const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const uint32_t a = lds_base + lane * (uint32_t)bytes_per_lane;
+  const int4v ones = {-1, -1, -1, -1};
+  if (bytes_per_lane == 16)
+    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(a), "v"(ones) : "memory");
+  else
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(a), "v"(-1) : "memory");
+}
+#endif
+
 __device__ __forceinline__ void dma_to_lds(const int4v& rsrc, uint32_t lds_base, uint32_t voffset) {
+#ifdef TGEMM_DEBUG_FILL
+  debug_poison(lds_base, 16);
+#endif
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"

@@ -45,6 +45,9 @@ constexpr int kF8Kh = kFp8Block / 2;  // k-tile width in binary16 units (the LDS
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_dword_to_lds(const int4v& rsrc, uint32_t lds_base, uint32_t voffset) {
+#ifdef TGEMM_DEBUG_FILL
+  debug_poison(lds_base, 4);
+#endif
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
