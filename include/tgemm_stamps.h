@@ -4,7 +4,8 @@
  * everything in tgemm.h). Not part of the product library: libtgemm.so does not export
  * these. Besides the stamps, this build compiles every row of the config table, including
  * the variants the product leaves out (tgemm_config_info.built is 1 for all of them), for
- * the offline sweep, and the MFMA throughput probe (the measured compute ceiling).
+ * the offline sweep, the MFMA throughput probe (the measured compute ceiling) and the LDS
+ * access probe (bank-conflict cycles of any lane address pattern).
  *
  * In the instrumented build every workgroup of the GEMM kernels (all configs except the
  * generic one) and of the MFMA probe records, at its end, TGEMM_STAMP_WORDS 64-bit words
@@ -61,6 +62,29 @@ TGEMM_API int tgemm_stamps_clear(void);
 #define TGEMM_PROBE_THREADS 512
 #define TGEMM_PROBE_MFMA_PER_ITER 16
 TGEMM_API int tgemm_mfma_probe(int blocks, int iters, void* out, void* stream);
+
+/* ---- LDS access probe (calibrates the host-side LDS bank model) ---- */
+
+/* Enqueues `blocks` workgroups of one wave (64 lanes) each with a 64 KiB LDS block. Every
+ * wave runs `iters` rounds; a round issues ni instructions of kind op (TGEMM_LDS_*) and
+ * waits for them; instruction j of a round is issued by the lanes whose bit is set in
+ * active[j] and accesses byte address addrs[j * 64 + lane] of the (uninitialised) block.
+ * addrs: host memory, ni * 64 int32, each in [0, 65536 - width] and a multiple of the
+ * access width (4, 8 or 16 bytes; 8 for TGEMM_LDS_READ_TR16_B64), checked for every lane;
+ * active: host memory, ni lane masks. out: caller-owned
+ * device memory of `blocks` floats. Returns TGEMM_OK, TGEMM_ENULL, TGEMM_EINVAL_DIM (op,
+ * ni outside [1, 8], iters outside [1, 2^20], blocks outside [1, 2^16], or an address out
+ * of range or misaligned; checked before anything is enqueued), TGEMM_EDEVICE or
+ * TGEMM_ELAUNCH. */
+#define TGEMM_LDS_READ_B32 0
+#define TGEMM_LDS_READ_B64 1
+#define TGEMM_LDS_READ_B128 2
+#define TGEMM_LDS_WRITE_B32 3
+#define TGEMM_LDS_WRITE_B64 4
+#define TGEMM_LDS_WRITE_B128 5
+#define TGEMM_LDS_READ_TR16_B64 6
+TGEMM_API int tgemm_lds_probe(int op, const int32_t* addrs, const uint64_t* active, int ni, int iters,
+                              int blocks, void* out, void* stream);
 
 #ifdef __cplusplus
 }

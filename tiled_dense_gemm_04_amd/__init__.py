@@ -22,8 +22,8 @@ through gemm_f16_ex). The tooling
 twin ``libtgemm_stamps.so`` (``stamps_lib()``, measurement tools only) compiles every config
 row (the sweep-only variants too; ``built`` in a config description says whether the
 library at hand has the row) and adds ``tgemm_stamps_capacity``, ``tgemm_stamps_read``,
-``tgemm_stamps_clear`` and the MFMA throughput probe ``tgemm_mfma_probe``
-(``include/tgemm_stamps.h``).
+``tgemm_stamps_clear``, the MFMA throughput probe ``tgemm_mfma_probe`` and the LDS access
+probe ``tgemm_lds_probe`` (``include/tgemm_stamps.h``).
 """
 from __future__ import annotations
 
@@ -58,7 +58,11 @@ EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_
            "tgemm_fp8_num_configs", "tgemm_fp8_config_desc", "tgemm_fp8_select_config",
            "tgemm_workspace_bytes_cfg", "gemm_f16_ws_static")
 # The extra symbols include/tgemm_stamps.h declares (tooling build only).
-STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear", "tgemm_mfma_probe")
+STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear", "tgemm_mfma_probe",
+                  "tgemm_lds_probe")
+# LDS probe instruction kinds (TGEMM_LDS_*) and their access widths in bytes.
+LDS_OPS = {"read_b32": (0, 4), "read_b64": (1, 8), "read_b128": (2, 16), "write_b32": (3, 4),
+           "write_b64": (4, 8), "write_b128": (5, 16), "read_tr16_b64": (6, 8)}
 STATIC_SCRATCH_BYTES = 4096 + (64 << 20)   # TGEMM_STATIC_SCRATCH_BYTES
 FAST_MAX_LD = 1 << 22        # TGEMM_FAST_MAX_LD
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
@@ -163,6 +167,9 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
         L.tgemm_stamps_clear.argtypes = []
         L.tgemm_mfma_probe.restype = i32
         L.tgemm_mfma_probe.argtypes = [i32, i32, p, p]
+        L.tgemm_lds_probe.restype = i32
+        L.tgemm_lds_probe.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_uint64), i32, i32,
+                                      i32, p, p]
     return L
 
 
@@ -304,6 +311,29 @@ def tgemm_mfma_probe(blocks: int, iters: int, out, stream=None, library=None) ->
     if rc != TGEMM_OK:
         raise TgemmError(rc, "tgemm_mfma_probe")
     return blocks * (PROBE_THREADS // 64) * iters * PROBE_MFMA_PER_ITER * PROBE_FLOP_PER_MFMA
+
+
+def tgemm_lds_probe(op: str, addrs, active=None, iters: int = 1000, blocks: int = 256, out=None, stream=None):
+    """Enqueue the tooling build's LDS access probe: instruction kind ``op`` (a key of
+    LDS_OPS), addrs an (ni, 64) array of byte addresses (ni <= 8), active an optional list
+    of ni 64-bit lane masks (default: all lanes). Returns the float32 device tensor the
+    workgroups write."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(np.asarray(addrs, dtype=np.int32).reshape(-1, 64))
+    ni = a.shape[0]
+    m = np.asarray(active if active is not None else [(1 << 64) - 1] * ni, dtype=np.uint64)
+    if out is None:
+        out = torch.empty(blocks, dtype=torch.float32, device="cuda")
+    handle = torch.cuda.current_stream(out.device).cuda_stream if stream is None else (
+        stream if isinstance(stream, int) else stream.cuda_stream)
+    with torch.cuda.device(out.device):
+        rc = stamps_lib().tgemm_lds_probe(LDS_OPS[op][0], a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                          m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ni, int(iters),
+                                          int(blocks), out.data_ptr(), handle)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "tgemm_lds_probe")
+    return out
 
 
 def tgemm_stamps_read(workgroups: int):

@@ -310,5 +310,91 @@ struct PpOperand {
 };
 
 
+// ------------------------------------------------------------------------------------
+// Epilogue of the 16x16 MFMA kernels: a wave's WTM x WTN tile of float32 accumulators
+// (tile (fm, fn) holds, in lane l, row 16 fm + l % 16 and columns 16 fn + 4 (l / 16) .. +3)
+// goes through the wave's own LDS region and out to C as 16-byte row segments.
+//
+// Staging: ReLU (optional) in float32 and rounding to fp16 in registers; then the tiles are
+// taken in pairs (t0, t1) = (2q, 2q + 1) in (fm, fn) order, and v_permlane16_swap swaps
+// lanes 16-31 of t0 with lanes 0-15 of t1 (and 48-63 with 32-47): afterwards the lanes with
+// an even l / 16 hold 8 consecutive columns of one row of t0, the others 8 of t1, and each
+// lane writes them with one ds_write_b128. Writes move 128 bytes per cycle in 8-lane passes
+// (8 rows of one tile, one 16-byte chunk each); staged row r, 16-byte chunk c sits at chunk
+// c ^ ((r / RPW) % SWZ), RPW rows per 128 bytes, so the 8 rows of a pass fall on 8
+// distinct chunk slots: no bank conflicts (writing 8 bytes per lane straight from the
+// accumulator layout takes 16-lane passes of 16 rows, at best 2-way conflicted, and twice
+// the write cycles). Rows are padded to SCPR (a power of two) chunks.
+// Store: lane i of read round j takes staged row (64 j + i) / SCPR, chunk (64 j + i) %
+// SCPR (ds_read_b128; conflict-free: a 16-lane read pass covers 256 bytes of whole rows),
+// skipping chunks past WTN / 8, and stores it unless it lies past M or N (N and ldc are
+// multiples of 8 on these paths, so a chunk is wholly inside the matrix or outside).
+template <int WTM, int WTN>
+struct StagedTile {
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  static constexpr int CPR = WTN / 8;
+  static constexpr int SCPR = CPR <= 4 ? 4 : (CPR <= 8 ? 8 : (CPR <= 16 ? 16 : 32));
+  static constexpr int RB = SCPR * 16;  // bytes per staged row
+  static constexpr int BYTES = WTM * RB;
+  static constexpr int RPW = RB >= 128 ? 1 : 128 / RB;
+  static constexpr int SWZ = SCPR < 8 ? SCPR : 8;
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0 && (FM * FN) % 2 == 0, "pairs of 16 x 16 tiles");
+  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-read shape");
+
+  __device__ static int chunk_at(int r, int c) { return c ^ ((r / RPW) % SWZ); }
+
+  template <bool RELU, typename Acc>
+  __device__ static uint32_t pack2(const Acc& a, int e) {
+    float x = a[e], y = a[e + 1];
+    if (RELU) {
+      x = relu_f(x);
+      y = relu_f(y);
+    }
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    const half2v h = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+
+  // acc: FM x FN accumulators of 4 floats (any indexable 4-vector type).
+  template <bool RELU, typename Acc>
+  __device__ static void stage(char* region, const Acc (&acc)[FM][FN], int lane) {
+    const int lrow = lane & 15, lkg = lane >> 4;
+    const bool second = (lkg & 1) != 0;
+#pragma unroll
+    for (int q = 0; q < FM * FN / 2; ++q) {
+      const int t0 = 2 * q, t1 = 2 * q + 1;
+      const auto s0 = __builtin_amdgcn_permlane16_swap(pack2<RELU>(acc[t0 / FN][t0 % FN], 0),
+                                                       pack2<RELU>(acc[t1 / FN][t1 % FN], 0), false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(pack2<RELU>(acc[t0 / FN][t0 % FN], 2),
+                                                       pack2<RELU>(acc[t1 / FN][t1 % FN], 2), false, false);
+      const int4v v = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+      const int row = (second ? t1 / FN : t0 / FN) * 16 + lrow;
+      const int c = (second ? t1 % FN : t0 % FN) * 2 + (lkg >> 1);
+      *(TG_LDS int4v*)(region + row * RB + (chunk_at(row, c) << 4)) = v;
+    }
+  }
+
+  // Rows past mvalid or chunks past nvalid (counted from the wave tile's origin) are not
+  // stored; C points at the wave tile's first element.
+  __device__ static void store(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < WTM * SCPR / 64; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx / SCPR, c = idx % SCPR;
+      if (c >= CPR) continue;
+      const half8 x = *(const TG_LDS half8*)(region + r * RB + (chunk_at(r, c) << 4));
+      if (r < mvalid && 8 * c < nvalid) store_c(C + (int64_t)r * ldc + 8 * c, x);
+    }
+  }
+
+  // The rows read back were written by other lanes of the same wave: keep the compiler
+  // from moving the reads above the writes (LDS runs one wave's instructions in order).
+  __device__ static void wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+};
+
 }  // namespace
 }  // namespace tgemm

@@ -157,7 +157,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   // ring of three group slots. Group 0 is fetched before the loop; every k-tile copy t then
   // fetches slice t % G (BM / G rows) of group t / G + 1, so each copy is one dword per
   // lane, G consecutive lanes read G consecutive floats of one row, and the group is
-  // complete (and its slot free) well before its first k-tile.
+  // complete (and its slot free) well before its first k-tile. The loop reads one scale per
+  // MFMA row with ds_read_b32; rows r and r + 8 share a bank of the 32 such a read serves
+  // per cycle (2-way conflicts, 2 extra LDS cycles per read). Conflict-free layouts were
+  // measured slower: [16-row block][G][16] (one 64-lane copy per block, the copies then
+  // touch 4 bytes per lane instead of 16) by 0.4 %, and aligned ds_read_b64 pairs plus a
+  // select by 1.1-1.8 %: the LDS is not the limit here, the instruction stream is.
   const float* const sa_base = g.SA + (int64_t)row0 * g.KB;
   const int si = wave * 64 + lane;  // this lane's element of a slice
   const uint32_t s_off = si < BM ? (uint32_t)(((si / G) * g.KB + si % G) * 4) : kOob;
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   }
 
   const int wm = wave / WN, wn = wave % WN;
-  const int lrow = lane % 16, lkg = lane / 16;
+  const int lrow = lane % 16;  // the MFMA row of this lane in a 16 x 16 tile
   opa.init_frags(wm * WTM, lane);
   opb.init_frags(wn * WTN, lane);
 
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     for (int j = 0; j < FN; ++j) acc[i][j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
   // Operands go in as (B fragment, A fragment): a lane's result holds four consecutive
-  // output columns (16 * fn + 4 * lkg ..) of one row (16 * fm + lrow) of the wave tile.
+  // output columns (16 * fn + 4 * (lane / 16) ..) of one row (16 * fm + lrow) of the wave tile.
   // MFMA t (t = fm * FN + fn) writes result register t % 3, and the block sum of MFMA t-2
   // (issued two MFMAs earlier, so complete) is folded into its accumulator right after,
   // so no MFMA waits for a result and the folds run on the VALU under later MFMAs.
@@ -369,43 +374,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
 
   // Epilogue: ReLU in float32, round to fp16, stage the wave's WTM x WTN sub-tile in its
   // own LDS region (the ring is free once every wave passes the barrier) and write it back
-  // as 16-byte row segments. Staged row r, chunk c sits at chunk c ^ ((r / 2) % SCPR).
-  constexpr int CPR = WTN / 8, SCPR = CPR <= 4 ? 4 : (CPR <= 8 ? 8 : 16);
-  constexpr int RB = SCPR * 16;
-  static_assert(SCPR >= CPR && NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "staged tile fits in the ring");
-  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+  // as 16-byte row segments (StagedTile).
+  using ST = StagedTile<WTM, WTN>;
+  static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "staged tile fits in the ring");
   __syncthreads();
-  char* const stage = smem + wave * (WTM * RB);
-  const bool relu = g.relu != 0;
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int mw = fm * 16 + lrow;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int nw = fn * 16 + 4 * lkg;
-      float v0 = acc[fm][fn][0], v1 = acc[fm][fn][1], v2 = acc[fm][fn][2], v3 = acc[fm][fn][3];
-      if (relu) {
-        v0 = relu_f(v0);
-        v1 = relu_f(v1);
-        v2 = relu_f(v2);
-        v3 = relu_f(v3);
-      }
-      const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-      *(TG_LDS half4*)(stage + mw * RB + (((nw >> 3) ^ ((mw >> 1) % SCPR)) << 4) + (nw & 7) * 2) = h;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-  for (int i = 0; i < WTM * SCPR / 64; ++i) {
-    const int idx = i * 64 + lane;
-    const int r = idx / SCPR, c = idx % SCPR;
-    if (c >= CPR) continue;
-    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
-    const int m = wm * WTM + r, n = wn * WTN + 8 * c;
-    if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
-  }
+  char* const stage = smem + wave * ST::BYTES;
+  if (g.relu != 0)
+    ST::template stage<true>(stage, acc, lane);
+  else
+    ST::template stage<false>(stage, acc, lane);
+  ST::wave_fence();
+  ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
+            nvalid - wn * WTN);
   clk.finish(nk, g.stamps);
 }
 

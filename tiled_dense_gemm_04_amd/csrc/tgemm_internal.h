@@ -160,6 +160,20 @@ constexpr int kProbeThreads = 512, kProbeMfmaPerIter = 16;
 hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s);
 #endif
 
+// LDS access probe (tooling build only): instruction kinds (ds_read_b32, ds_read_b64,
+// ds_read_b128, ds_write_b32, ds_write_b64, ds_write_b128, ds_read_b64_tr_b16), up to
+// kLdsProbeSlots instructions per round, byte addresses inside a kLdsProbeBytes block.
+constexpr int kLdsProbeOps = 7, kLdsProbeSlots = 8, kLdsProbeBytes = 65536;
+struct LdsProbeArgs {
+  int32_t addr[kLdsProbeSlots][64];
+  uint64_t active[kLdsProbeSlots];  // lanes that issue instruction j
+  int ni, iters;
+  float* out;
+};
+#ifdef TGEMM_STAMPS
+hipError_t launch_lds_probe(int op, int blocks, const LdsProbeArgs& p, hipStream_t s);
+#endif
+
 // Workgroup timestamps of the instrumented build (TGEMM_STAMPS): kStampWords words per
 // workgroup for the first kStampWorkgroups workgroups of every launch (later launches
 // overwrite earlier ones).

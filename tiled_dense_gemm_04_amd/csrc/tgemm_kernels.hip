@@ -765,55 +765,65 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   // every copy, including the empty-range ones past the last tile, has landed once all
   // waves pass the barrier below) and writes it back row by row, 16 bytes per lane and
   // WTN / 8 lanes per row, so each store covers whole 16-byte-aligned row segments instead
-  // of 8-byte pieces of MF rows. Staged row r, 16-byte chunk c sits at chunk
-  // c ^ ((r / 2) % (WTN / 8)): conflict-free LDS writes for the 16x16 layout (2-way for
-  // 32x32) and conflict-free row reads. N and ldc are multiples of 8 on this path, so a
-  // chunk is either wholly inside the matrix or wholly outside.
-  // Staged rows are padded to a power-of-two number of 16-byte chunks (SCPR); chunks past
-  // the wave's WTN / 8 are never written or stored.
-  constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
-  constexpr int RB = SCPR * 16;
-  static_assert(SCPR >= CPR && WTN % 8 == 0, "staged row shape");
-  static_assert(NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
-  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
-  __syncthreads();
-  char* const stage = smem + wave * (WTM * RB);
-  const bool relu = g.relu != 0;
+  // of 8-byte pieces of MF rows. The 16x16 layout uses StagedTile (conflict-free 16-byte
+  // staging writes after a lane swap); the 32x32 one (a sweep-only config) writes 8-byte
+  // pieces at chunk c ^ ((r / 2) % SCPR) of staged row r. N and ldc are multiples of 8 on
+  // this path, so a chunk is either wholly inside the matrix or wholly outside.
+  if constexpr (MF == 16) {
+    using ST = StagedTile<WTM, WTN>;
+    static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
+    __syncthreads();
+    char* const stage = smem + wave * ST::BYTES;
+    if (g.relu != 0)
+      ST::template stage<true>(stage, acc, lane);
+    else
+      ST::template stage<false>(stage, acc, lane);
+    ST::wave_fence();
+    ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
+              nvalid - wn * WTN);
+  } else {
+    constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
+    constexpr int RB = SCPR * 16;
+    static_assert(SCPR >= CPR && WTN % 8 == 0, "staged row shape");
+    static_assert(NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
+    static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+    __syncthreads();
+    char* const stage = smem + wave * (WTM * RB);
+    const bool relu = g.relu != 0;
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int mw = fm * MF + lrow;
+    for (int fm = 0; fm < FM; ++fm) {
+      const int mw = fm * MF + lrow;
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
+      for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
-      for (int g4 = 0; g4 < NACC / 4; ++g4) {
-        const int nw = fn * MF + 8 * g4 + 4 * lkg;
-        float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
-        float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
-        if (relu) {
-          v0 = relu_f(v0);
-          v1 = relu_f(v1);
-          v2 = relu_f(v2);
-          v3 = relu_f(v3);
+        for (int g4 = 0; g4 < NACC / 4; ++g4) {
+          const int nw = fn * MF + 8 * g4 + 4 * lkg;
+          float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
+          float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
+          if (relu) {
+            v0 = relu_f(v0);
+            v1 = relu_f(v1);
+            v2 = relu_f(v2);
+            v3 = relu_f(v3);
+          }
+          const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+          const int off = mw * RB + ((((nw >> 3) ^ ((mw >> 1) % SCPR))) << 4) + (nw & 7) * 2;
+          *(TG_LDS half4*)(stage + off) = h;
         }
-        const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        const int off = mw * RB + ((((nw >> 3) ^ ((mw >> 1) % SCPR))) << 4) + (nw & 7) * 2;
-        *(TG_LDS half4*)(stage + off) = h;
       }
     }
-  }
-  // The rows read back below were written by other lanes of this wave: keep the compiler
-  // from moving the reads above the writes (LDS executes one wave's instructions in order).
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
-  for (int i = 0; i < WTM * SCPR / 64; ++i) {
-    const int idx = i * 64 + lane;
-    const int r = idx / SCPR, c = idx % SCPR;
-    if (c >= CPR) continue;
-    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
-    const int m = wm * WTM + r, n = wn * WTN + 8 * c;
-    if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
+    for (int i = 0; i < WTM * SCPR / 64; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx / SCPR, c = idx % SCPR;
+      if (c >= CPR) continue;
+      const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
+      const int m = wm * WTM + r, n = wn * WTN + 8 * c;
+      if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
+    }
   }
   clk.finish(nloc, TG_STAMP_TABLE);
 }
@@ -1150,54 +1160,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_quad(GemmArgs g) {
   clk.loop_end();
 
   // Epilogue: ReLU and RNE in registers, each wave's WTM x WTN fp16 sub-tile staged in its
-  // own LDS region (rows of RB bytes, chunk c of row r at chunk c ^ (r / RPW) % SCPR with RPW
-  // rows per 256-byte bank window), then written back in 16-byte row segments.
-  constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
-  constexpr int RB = SCPR * 16, RPW = RB >= 256 ? 1 : 256 / RB;
-  static_assert(NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
-  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+  // own LDS region and written back in 16-byte row segments (StagedTile).
+  using ST = StagedTile<WTM, WTN>;
+  static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
   __syncthreads();
-  char* const stage = smem + wave * (WTM * RB);
-  const int lrow = lane % MF, lkg = lane / MF;
+  char* const stage = smem + wave * ST::BYTES;
   // The ReLU choice is made once for the whole tile (a per-value branch on the runtime
   // flag costs registers at 256 accumulators).
-  auto stage_tile = [&](auto relu_tag) {
-    constexpr bool RELU = decltype(relu_tag)::value;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int mw = fm * MF + lrow;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int nw = fn * MF + 4 * lkg;
-        float v0 = acc[fm][fn][0], v1 = acc[fm][fn][1], v2 = acc[fm][fn][2], v3 = acc[fm][fn][3];
-        if constexpr (RELU) {
-          v0 = relu_f(v0);
-          v1 = relu_f(v1);
-          v2 = relu_f(v2);
-          v3 = relu_f(v3);
-        }
-        const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        const int off = mw * RB + ((((nw >> 3) ^ ((mw / RPW) % SCPR))) << 4) + (nw & 7) * 2;
-        *(TG_LDS half4*)(stage + off) = h;
-      }
-    }
-  };
   if (g.relu != 0)
-    stage_tile(std::true_type{});
+    ST::template stage<true>(stage, acc, lane);
   else
-    stage_tile(std::false_type{});
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-  for (int i = 0; i < WTM * SCPR / 64; ++i) {
-    const int idx = i * 64 + lane;
-    const int r = idx / SCPR, c = idx % SCPR;
-    if (c >= CPR) continue;
-    const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r / RPW) % SCPR)) << 4));
-    const int m = wm * WTM + r, n = wn * WTN + 8 * c;
-    if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
-  }
+    ST::template stage<false>(stage, acc, lane);
+  ST::wave_fence();
+  ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
+            nvalid - wn * WTN);
   clk.finish(nk, TG_STAMP_TABLE);
 }
 
@@ -1307,6 +1283,59 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe(int iters, float* ou
   for (int j = 0; j < kProbeMfmaPerIter; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
   out[tid] = sum;
   clk.finish(iters, TG_STAMP_TABLE);
+}
+
+// LDS access probe (tooling): one wave per workgroup issues `iters` rounds of p.ni LDS
+// instructions of kind OP, instruction j of a round at byte address p.addr[j][lane] of a
+// 64 KiB dynamic LDS block by the lanes set in p.active[j], then waits for them. Run under
+// the SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS counters, it gives the bank-conflict cycles of
+// any lane address pattern (the calibration of the host-side bank model). The block is
+// not initialised (only the access pattern matters). The host checks every address
+// against the block and the access width before launching.
+typedef int int2v __attribute__((ext_vector_type(2)));
+
+template <int OP>
+__global__ __launch_bounds__(64) void lds_probe(LdsProbeArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char lds_block[];
+  const int lane = threadIdx.x;
+  const uint32_t base = lds_addr(lds_block);
+  uint32_t a[kLdsProbeSlots];
+#pragma unroll
+  for (int j = 0; j < kLdsProbeSlots; ++j) a[j] = base + (uint32_t)p.addr[j][lane];
+  const int4v w4 = {lane, lane + 1, lane + 2, lane + 3};
+  for (int it = 0; it < p.iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kLdsProbeSlots; ++j) {
+      if (j >= p.ni) break;
+      if (!((p.active[j] >> lane) & 1)) continue;
+      if (OP == 0) {
+        int v;
+        asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(a[j]) : "memory");
+        asm volatile("" : : "v"(v));
+      } else if (OP == 1) {
+        int2v v;
+        asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(a[j]) : "memory");
+        asm volatile("" : : "v"(v));
+      } else if (OP == 2) {
+        int4v v;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a[j]) : "memory");
+        asm volatile("" : : "v"(v));
+      } else if (OP == 3) {
+        asm volatile("ds_write_b32 %0, %1" : : "v"(a[j]), "v"(w4[0]) : "memory");
+      } else if (OP == 4) {
+        const int2v w2 = {w4[0], w4[1]};
+        asm volatile("ds_write_b64 %0, %1" : : "v"(a[j]), "v"(w2) : "memory");
+      } else if (OP == 5) {
+        asm volatile("ds_write_b128 %0, %1" : : "v"(a[j]), "v"(w4) : "memory");
+      } else {
+        int2v v;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a[j]) : "memory");
+        asm volatile("" : : "v"(v));
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  }
+  if (lane == 0) p.out[blockIdx.x] = (float)p.iters;
 }
 
 #endif  // TGEMM_STAMPS
@@ -1458,6 +1487,15 @@ hipError_t launch_generic(const GemmArgs& g, hipStream_t s, int) {
 }  // namespace
 
 #ifdef TGEMM_STAMPS
+hipError_t launch_lds_probe(int op, int blocks, const LdsProbeArgs& p, hipStream_t s) {
+  typedef void (*K)(LdsProbeArgs);
+  static const K kernels[kLdsProbeOps] = {lds_probe<0>, lds_probe<1>, lds_probe<2>, lds_probe<3>,
+                                          lds_probe<4>, lds_probe<5>, lds_probe<6>};
+  if (op < 0 || op >= kLdsProbeOps) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kernels[op], dim3((unsigned)blocks), dim3(64), kLdsProbeBytes, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s) {
   hipLaunchKernelGGL(mfma_probe, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters, out);
   return hipGetLastError();

@@ -1,0 +1,319 @@
+"""LDS access patterns: the lane addresses of the LDS instructions the kernels issue, written
+out from the kernels' address arithmetic (csrc/tgemm_device.h PpOperand::frag, the ping-pong
+epilogue in csrc/tgemm_kernels.hip, the fp8 fragment and scale reads in csrc/tgemm_fp8.hip),
+plus synthetic calibration patterns. Used by the LDS probe tool (ldsprobe.py), which times
+each pattern's bank conflicts on the GPU, and by the host-side bank model test.
+
+A pattern is a dict: name, op (a key of LDS_OPS), addrs (int array (ni, 64), byte
+addresses), active (ni lane masks), and for kernel patterns the kernel, the config, the
+phase ("loop": issued once per k-tile, "epilogue": once per output tile) and the number of
+waves of a workgroup that issue it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ALL = (1 << 64) - 1
+LANES = np.arange(64)
+
+
+def _pat(name, op, addrs, active=None, **kw):
+    a = np.asarray(addrs, dtype=np.int64).reshape(-1, 64)
+    act = list(active) if active is not None else [ALL] * a.shape[0]
+    return dict(name=name, op=op, addrs=a.astype(np.int32), active=act, **kw)
+
+
+def _mask(bits):
+    m = 0
+    for lane, on in enumerate(bits):
+        if on:
+            m |= 1 << lane
+    return m
+
+
+# ------------------------------------------------------------------ the bank model
+# LDS of gfx950 as the probe measures it (every pattern in ldspatterns reproduced exactly):
+# a wave's access is served in a fixed number of passes; in each pass the lanes of that pass
+# touch banks of 4 bytes, and a pass takes as many cycles as the largest number of
+# distinct 4-byte words that fall on one bank (the same word read by several lanes is one
+# access). Reads move 256 bytes per cycle (64 banks), except ds_read_b32 (128, 32 banks);
+# writes move 128 bytes per cycle (32 banks). Passes hold consecutive lanes, except for
+# ds_read_b128, whose four 16-lane passes are: lanes 0-31 or 32-63, and within them the
+# 4-lane groups whose index (bits 2-4 of the lane) has even or odd parity. Empty passes
+# still take their cycle.
+WIDTH = {"read_b32": 4, "read_b64": 8, "read_b128": 16, "read_tr16_b64": 8, "write_b32": 4, "write_b64": 8,
+         "write_b128": 16}
+BYTES_PER_CYCLE = {"read_b32": 128, "read_b64": 256, "read_b128": 256, "read_tr16_b64": 256, "write_b32": 128,
+                   "write_b64": 128, "write_b128": 128}
+
+
+def pass_of(op, lane):
+    if op == "read_b128":
+        return 2 * (lane >> 5) + (bin((lane >> 2) & 7).count("1") & 1)
+    return lane // (BYTES_PER_CYCLE[op] // WIDTH[op])
+
+
+def bank_cycles(op, addrs, active=ALL):
+    """(conflict cycles, busy cycles) of one wave-wide LDS instruction: `addrs` the 64 lane
+    byte addresses, `active` the lane mask."""
+    w, nb = WIDTH[op], BYTES_PER_CYCLE[op] // 4
+    passes = {}
+    for lane in range(64):
+        if (active >> lane) & 1:
+            passes.setdefault(pass_of(op, lane), []).append(int(addrs[lane]))
+    conflict = 0
+    for lane_addrs in passes.values():
+        words = {}
+        for a in lane_addrs:
+            for k in range(w // 4):
+                dw = a // 4 + k
+                words.setdefault(dw % nb, set()).add(dw)
+        conflict += max(len(v) for v in words.values()) - 1
+    return conflict, 64 * w // BYTES_PER_CYCLE[op] + conflict
+
+
+def pattern_cycles(p):
+    """(conflict, busy) cycles of a pattern (summed over its instructions)."""
+    c = b = 0
+    for j in range(p["addrs"].shape[0]):
+        cc, bb = bank_cycles(p["op"], p["addrs"][j], p["active"][j])
+        c += cc
+        b += bb
+    return c, b
+
+
+# ------------------------------------------------------------------ swizzles (kernel copies)
+def swz_a_mf(r, bk):
+    """K-major 16x16 fragment rows: (r / 2) mod (BK / 8)."""
+    return (r >> 1) & (bk // 8 - 1)
+
+
+def swz_b(k):
+    """MN-major rows: 4 (k mod 4) xor 2 ((k / 8) mod 2)."""
+    return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1))
+
+
+# ------------------------------------------------------------------ ping-pong fp16 kernel
+def kmajor_frag(wbase, f, bk=32, mf=16, ks=0):
+    """PpOperand<R, BK, MF, K-major>::frag: one ds_read_b128 per lane."""
+    lrow, lkg = LANES % mf, LANES // mf
+    kpm = 512 // mf
+    chunk = (kpm // 8) * ks + lkg
+    return (wbase + lrow) * bk * 2 + f * mf * bk * 2 + ((chunk ^ swz_a_mf(lrow, bk)) << 4)
+
+
+def mnmajor_frag(wbase, f, R, mf=16, ks=0):
+    """PpOperand<R, BK, MF, MN-major>::frag: two ds_read_b64_tr_b16 per lane (i = 0, 1)."""
+    bg, bj, bq = LANES >> 4, (LANES >> 2) & 3, LANES & 3
+    fr_k = (8 * (bg >> 1) if mf == 32 else 8 * bg) + bj
+    fr_x = wbase // 8 + (2 * (bg & 1) if mf == 32 else 0) + (bq >> 1)
+    fr_half = (bq & 1) * 8
+    kpm = 512 // mf
+    out = []
+    for i in range(2):
+        k = kpm * ks + 4 * i + fr_k
+        out.append(k * R * 2 + (((fr_x + (mf // 8) * f) ^ swz_b(k)) << 4) + fr_half)
+    return out
+
+
+def lds_extent(r):
+    return (r + 127) // 128 * 128
+
+
+def pingpong_patterns(bm, bn, wm=2, wn=4, bk=32, mf=16, layout=0):
+    """Every LDS instruction one workgroup of the 16x16x32 ping-pong kernel issues per
+    k-tile (fragment reads) and per output tile (epilogue staging), for operand layout
+    `layout` = 2 trans_a + trans_b (A K-major unless trans_a; B MN-major unless trans_b)."""
+    assert mf == 16 and bk == 32
+    wtm, wtn = bm // wm, bn // wn
+    fm_n, fn_n = wtm // mf, wtn // mf
+    cfg = f"pp{bm}x{bn}"
+    pats = []
+    a_kmaj, b_kmaj = not (layout & 2), bool(layout & 1)
+    ra, rb = lds_extent(bm), lds_extent(bn)
+    for w in range(wm * wn):
+        wmi, wni = w // wn, w % wn
+        for f in range(fm_n):
+            if a_kmaj:
+                pats.append(_pat(f"{cfg} A frag w{w} f{f}", "read_b128", kmajor_frag(wmi * wtm, f),
+                                 kernel=cfg, phase="loop"))
+            else:
+                for i, ad in enumerate(mnmajor_frag(wmi * wtm, f, ra)):
+                    pats.append(_pat(f"{cfg} A^T frag w{w} f{f} r{i}", "read_tr16_b64", ad, kernel=cfg,
+                                     phase="loop"))
+        for f in range(fn_n):
+            if b_kmaj:
+                pats.append(_pat(f"{cfg} B^T frag w{w} f{f}", "read_b128", kmajor_frag(wni * wtn, f),
+                                 kernel=cfg, phase="loop"))
+            else:
+                for i, ad in enumerate(mnmajor_frag(wni * wtn, f, rb)):
+                    pats.append(_pat(f"{cfg} B frag w{w} f{f} r{i}", "read_tr16_b64", ad, kernel=cfg,
+                                     phase="loop"))
+        pats += epilogue_patterns(cfg, w, wtm, wtn, mf)
+    return pats
+
+
+def staged_shape(wtm, wtn):
+    """StagedTile's row shape: (chunks per row, padded chunks per row, row bytes, rows per
+    128 bytes, swizzle period)."""
+    cpr = wtn // 8
+    scpr = 4 if cpr <= 4 else 8 if cpr <= 8 else 16 if cpr <= 16 else 32
+    rb = scpr * 16
+    return cpr, scpr, rb, (1 if rb >= 128 else 128 // rb), min(scpr, 8)
+
+
+def epilogue_patterns(cfg, w, wtm, wtn, mf=16):
+    """StagedTile (csrc/tgemm_device.h): after the lane swap of each pair of 16 x 16 tiles
+    (t0, t1), lane l writes 8 columns of row 16 fm + l % 16 of tile t0 (l / 16 even) or t1
+    (odd) with one ds_write_b128 at chunk c ^ ((r / RPW) % SWZ); then the row reads
+    (ds_read_b128; lanes past the row's CPR chunks inactive). Each wave stages into its own
+    region; addresses here are relative to that region."""
+    assert mf == 16
+    cpr, scpr, rb, rpw, swz = staged_shape(wtm, wtn)
+    fm_n, fn_n = wtm // 16, wtn // 16
+    lrow, lkg = LANES % 16, LANES // 16
+    pats = []
+    for q in range(fm_n * fn_n // 2):
+        t = 2 * q + (lkg & 1)
+        row = (t // fn_n) * 16 + lrow
+        c = (t % fn_n) * 2 + (lkg >> 1)
+        off = row * rb + ((c ^ ((row // rpw) % swz)) << 4)
+        pats.append(_pat(f"{cfg} epi write w{w} q{q}", "write_b128", off, kernel=cfg, phase="epilogue"))
+    for i in range(wtm * scpr // 64):
+        idx = i * 64 + LANES
+        r, c = idx // scpr, idx % scpr
+        off = r * rb + ((c ^ ((r // rpw) % swz)) << 4)
+        act = _mask(c < cpr)
+        pats.append(_pat(f"{cfg} epi read w{w} i{i}", "read_b128", np.where(c < cpr, off, 0), [act],
+                         kernel=cfg, phase="epilogue"))
+    return pats
+
+
+def epilogue_patterns_b64(cfg, w, wtm, wtn, mf=16):
+    """The staging StagedTile replaced (kept as the probe's reference): every lane wrote its
+    4 accumulator columns (ds_write_b64) at chunk (c ^ ((r / 2) % SCPR)) of staged row r,
+    and the rows were read back with the same swizzle."""
+    cpr, scpr, rb, _, _ = staged_shape(wtm, wtn)
+    lrow, lkg = LANES % mf, LANES // mf
+    pats = []
+    for fm in range(wtm // mf):
+        mw = fm * mf + lrow
+        for fn in range(wtn // mf):
+            nw = fn * mf + 4 * lkg
+            off = mw * rb + (((nw >> 3) ^ ((mw >> 1) % scpr)) << 4) + (nw & 7) * 2
+            pats.append(_pat(f"{cfg} old epi write w{w} fm{fm} fn{fn}", "write_b64", off, kernel=cfg,
+                             phase="epilogue_old"))
+    for i in range(wtm * scpr // 64):
+        idx = i * 64 + LANES
+        r, c = idx // scpr, idx % scpr
+        off = r * rb + ((c ^ ((r >> 1) % scpr)) << 4)
+        pats.append(_pat(f"{cfg} old epi read w{w} i{i}", "read_b128", np.where(c < cpr, off, 0), [_mask(c < cpr)],
+                         kernel=cfg, phase="epilogue_old"))
+    return pats
+
+
+# ------------------------------------------------------------------ fp8 block-scaled kernel
+def fp8_patterns(bm, bn, wm, wn, group=4):
+    """Per k-tile LDS accesses of the fp8 kernel: A and B fragments (K-major rows of 128 bytes,
+    two ds_read_b128 per 32-byte fragment), the A row scales ([BM][G] floats, one ds_read_b32
+    per MFMA row; each of the G k-tiles of a group weighs 1 / G), and the epilogue staging
+    (StagedTile)."""
+    wtm, wtn = bm // wm, bn // wn
+    cfg = f"fp8_{bm}x{bn}"
+    pats = []
+    for w in range(wm * wn):
+        wmi, wni = w // wn, w % wn
+        for f in range(wtm // 16):
+            for ks in range(2):
+                pats.append(_pat(f"{cfg} A frag w{w} f{f} k{ks}", "read_b128",
+                                 kmajor_frag(wmi * wtm, f, bk=64, ks=ks), kernel=cfg, phase="loop"))
+            row = wmi * wtm + f * 16 + LANES % 16
+            for k in range(group):  # k-tile k of a group of [BM][G] floats
+                pats.append(_pat(f"{cfg} A scale w{w} f{f} k{k}", "read_b32", (row * group + k) * 4,
+                                 kernel=cfg, phase="loop", weight=1.0 / group))
+        for f in range(wtn // 16):
+            for ks in range(2):
+                pats.append(_pat(f"{cfg} B frag w{w} f{f} k{ks}", "read_b128",
+                                 kmajor_frag(wni * wtn, f, bk=64, ks=ks), kernel=cfg, phase="loop"))
+        pats += epilogue_patterns(cfg, w, wtm, wtn)
+    return pats
+
+
+def kernel_patterns():
+    """The configs the measured workloads run: 256 x 256, 256 x 192, 256 x 128 and 128 x 128
+    ping-pong (A and B as given), and the fp8 256 x 256 kernel."""
+    out = []
+    for bm, bn in ((256, 256), (256, 192), (256, 128), (128, 128)):
+        out += pingpong_patterns(bm, bn)
+        wtm, wtn = bm // 2, bn // 4
+        for w in range(8):
+            out += epilogue_patterns_b64(f"pp{bm}x{bn}", w, wtm, wtn)
+    out += fp8_patterns(256, 256, 2, 4)
+    for w in range(8):
+        out += epilogue_patterns_b64("fp8_256x256", w, 128, 64)
+    return out
+
+
+def kernel_rate(patterns, kernel, k_tiles, old=False):
+    """Bank-conflict cycles per LDS-busy cycle (the SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+    rate) of one workgroup of `kernel` over `k_tiles` k-tiles: loop patterns count once per
+    k-tile (times their weight), epilogue patterns once. old=True takes the replaced
+    epilogue staging instead of StagedTile."""
+    epi = "epilogue_old" if old else "epilogue"
+    conflict = busy = 0.0
+    for p in patterns:
+        if p["kernel"] != kernel:
+            continue
+        if p["phase"] == "loop":
+            n = k_tiles * p.get("weight", 1.0)
+        elif p["phase"] == epi:
+            n = 1
+        else:
+            continue
+        c, b = pattern_cycles(p)
+        conflict += c * n
+        busy += b * n
+    return conflict / busy
+
+
+# ------------------------------------------------------------------ calibration patterns
+def calibration_patterns():
+    """Synthetic patterns that separate hypotheses about how the LDS serves a wave: the
+    linear pattern of each width; for every lane j, the linear pattern with lane j moved
+    onto lane 0's banks (another row), which conflicts only if lanes 0 and j are served in
+    the same cycle; all lanes on one bank; all lanes on one address (broadcast); and
+    strided patterns."""
+    pats = []
+    widths = {"read_b32": 4, "read_b64": 8, "read_b128": 16, "read_tr16_b64": 8, "write_b32": 4,
+              "write_b64": 8, "write_b128": 16}
+    for op, w in widths.items():
+        lin = LANES * w
+        pats.append(_pat(f"cal {op} linear", op, lin))
+        if op in ("read_b32", "read_b64", "read_b128", "read_tr16_b64"):
+            for j in range(1, 64):
+                a = lin.copy()
+                a[j] = 8192  # bank of byte 0 (8192 mod 256 = 0), another address
+                pats.append(_pat(f"cal {op} pair 0-{j}", op, a))
+        if op == "read_b128":
+            # only lanes a and b active, on the same banks at different addresses: a
+            # conflict means the two are served in the same cycle
+            for a in (0, 1, 4, 8, 16, 24, 32):
+                for b in range(a + 1, 64):
+                    ad = np.zeros(64, dtype=np.int64)
+                    ad[b] = 8192
+                    pats.append(_pat(f"cal {op} only {a},{b}", op, ad, [(1 << a) | (1 << b)]))
+            # eight groups of 8 lanes, each on one 128-byte half (bit g of `halves`: upper) of
+            # the 256-byte bank window, every group in its own rows
+            for halves in range(256):
+                g = LANES // 8
+                ad = 1024 * g + 128 * ((halves >> g) & 1) + 16 * (LANES % 8)
+                pats.append(_pat(f"cal {op} halves {halves:08b}", op, ad))
+        pats.append(_pat(f"cal {op} one bank", op, LANES * 256))
+        pats.append(_pat(f"cal {op} one address", op, np.zeros(64, dtype=np.int64)))
+        for stride in (2, 4, 8):
+            pats.append(_pat(f"cal {op} stride {stride}x", op, LANES * w * stride))
+    return pats
+
+
+def all_patterns():
+    return calibration_patterns() + kernel_patterns()
