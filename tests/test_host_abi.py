@@ -105,15 +105,22 @@ def test_config_table():
     for c in cfgs[1:]:
         assert c["generic"] == 0
         assert c["lds_bytes"] <= 160 * 1024
-        # operand tiles sit in LDS at a multiple of 128 rows / columns (192 -> 256)
-        bm_l = -(-c["block_m"] // 128) * 128
-        bn_l = -(-c["block_n"] // 128) * 128
-        assert c["lds_bytes"] == c["stages"] * (bm_l + bn_l) * c["block_k"] * 2
+        # operand tiles sit in LDS at their own extent when it is a multiple of 128 or 192,
+        # else rounded up to a multiple of 128
+        ext = lambda r: r if r % 128 == 0 or r == 192 else -(-r // 128) * 128
+        bm_l, bn_l = ext(c["block_m"]), ext(c["block_n"])
+        ring = c["stages"] * (bm_l + bn_l) * c["block_k"] * 2
+        # the epilogue stages each wave's tile in rows of a power of two (>= 4) of 16-byte chunks
+        cpr = c["block_n"] // c["waves_n"] // 8
+        scpr = next(p for p in (4, 8, 16, 32) if p >= cpr)
+        staged = c["waves_m"] * c["waves_n"] * (c["block_m"] // c["waves_m"]) * scpr * 16
+        assert c["lds_bytes"] == max(ring, staged), c
         assert c["block_m"] % (16 * c["waves_m"]) == 0 and c["block_n"] % (16 * c["waves_n"]) == 0
         assert c["block_n"] >= 128 and c["block_k"] in (16, 32, 64, 128)
         threads = 64 * c["waves_m"] * c["waves_n"]
-        assert (bm_l * c["block_k"] // 8) % threads == 0
-        assert (c["block_k"] * bn_l // 8) % threads == 0
+        # 16-byte copies split evenly over the threads, or with one extra copy for half of them
+        for ext_units in (bm_l * c["block_k"] // 8, c["block_k"] * bn_l // 8):
+            assert ext_units % threads in (0, threads // 2)
         assert c["name"][1:].startswith("%dx%dx%d" % (c["block_m"], c["block_n"], c["block_k"]))
     with pytest.raises(tg.TgemmError):
         tg.tgemm_config_desc(n)
@@ -522,3 +529,21 @@ def test_static_entry_rejects_before_hip():
     assert s(0, 0, 8, 8, 8, 256, 7, 256, 8, 256, 8, 0, None) == tg.TGEMM_EINVAL_LD
     assert s(0, 0, 8, 8, 8, 0, 8, 256, 8, 256, 8, 0, None) == tg.TGEMM_ENULL
     assert s(0, 0, 0, 8, 8, 0, 8, 0, 8, 0, 8, 0, None) == tg.TGEMM_OK
+
+
+def test_product_kernels_use_no_scratch():
+    """The product build records every kernel's resources (kernel_resources.txt, from the
+    compiler's resource remarks) and refuses kernels that use scratch memory or spill: a
+    register array moved to scratch puts memory loads and full waits into the copy stream."""
+    from tiled_dense_gemm_04_amd import build as B
+    if not os.path.exists(B.RESOURCES):
+        pytest.skip("library built before the resource report existed")
+    text = open(B.RESOURCES).read()
+    rows = [ln for ln in text.splitlines() if ln.strip()]
+    assert any("gemm_pingpong" in r for r in rows) and any("gemm_fp8_block_kernel" in r for r in rows)
+    for r in rows:
+        assert "ScratchSize [bytes/lane]=0 " in r and "VGPRs Spill=0" in r and "SGPRs Spill=0" in r, r
+    # the parser itself, on a made-up remark pair
+    res = B.kernel_resources("x.hip:1:1: remark: Function Name: k [-Rpass-analysis=kernel-resource-usage]\n"
+                             "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 20 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert B.check_resources(res) == ["k"]

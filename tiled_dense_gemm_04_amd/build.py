@@ -10,6 +10,7 @@ Usage: python -m tiled_dense_gemm_04_amd.build   (always recompiles both)
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -49,21 +50,66 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtgemm)")
 
 
+RESOURCES = os.path.join(PKG, "kernel_resources.txt")
+
+
+def kernel_resources(remarks: str) -> dict:
+    """{kernel: {field: value}} from the compiler's kernel-resource-usage remarks."""
+    out, name = {}, None
+    for ln in remarks.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            out[name] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][\w \[\]/]*?): (\S+) \[-Rpass-analysis", ln)
+        if m and name:
+            out[name][m.group(1).strip()] = m.group(2)
+    return out
+
+
+def check_resources(res: dict) -> list:
+    """Kernels that use scratch memory or spill: a missed unroll or a spill in a hot loop
+    turns register arrays into scratch loads and serializes the copy stream."""
+    bad = []
+    for k, f in res.items():
+        if f.get("ScratchSize [bytes/lane]", "0") != "0" or f.get("VGPRs Spill", "0") != "0" or \
+                f.get("SGPRs Spill", "0") != "0":
+            bad.append(k)
+    return bad
+
+
 def build(verbose: bool = False, extra_flags=None, stamps: bool = False, variant: str | None = None) -> str:
-    target, vflags = VARIANTS[variant or ("stamps" if stamps else "product")]
+    """Compile one variant. The product build also records every kernel's registers,
+    scratch and LDS (kernel_resources.txt) and fails if any kernel uses scratch memory."""
+    variant = variant or ("stamps" if stamps else "product")
+    target, vflags = VARIANTS[variant]
     tmp = target + ".tmp"
     flags = list(extra_flags or []) + vflags
+    if variant == "product":
+        flags.append("-Rpass-analysis=kernel-resource-usage")
     cmd = [hipcc()] + HIPCC_FLAGS + flags + ["-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless.
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln]
+    out = r.stdout + r.stderr
+    msgs = [ln for ln in out.splitlines() if noise not in ln and "-Rpass-analysis" not in ln and
+            not re.match(r"^\s*(\d+ \|.*|\|\s*\^)$", ln)]
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+    if variant == "product":
+        res = kernel_resources(out)
+        with open(RESOURCES, "w") as f:
+            for k in sorted(res):
+                f.write(k + " " + " ".join(f"{a}={b}" for a, b in res[k].items()) + "\n")
+        bad = check_resources(res)
+        if bad:
+            os.remove(tmp)
+            raise RuntimeError("kernels use scratch memory or spill registers:\n" + "\n".join(bad))
     os.replace(tmp, target)
     return target
 

@@ -184,6 +184,12 @@ __host__ __device__ constexpr int swz_a_mf(int r) {
 // group, XOR by 2*((k/8)%2) separates rows k and k+8: in both patterns the 16 (row,
 // chunk) pairs land on 16 distinct 16-byte slots of the bank window.
 __host__ __device__ constexpr int swz_b(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
+// MN-major rows of 384 bytes (192 columns): row k starts 128 bytes further into the bank
+// window than row k - 1, so the window position of a chunk depends on k % 2 as well. XOR by
+// 2 ((k / 2) % 2) + 4 ((k / 8) % 2) spreads the 16 (row, chunk) pairs of a 16x16
+// transposed read over 16 distinct 16-byte slots (checked with the host-side bank model)
+// and keeps every chunk inside its row (only bits 1 and 2 of the chunk index change).
+__host__ __device__ constexpr int swz_b384(int k) { return 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1); }
 
 // ------------------------------------------------------------------------------------
 // Operand staging of the ping-pong kernel. An operand tile spans R output rows (A, R = BM)
@@ -206,28 +212,50 @@ __host__ __device__ constexpr int swz_b(int k) { return (4 * (k & 3)) ^ (2 * ((k
 // MN-major: the m/n chunks past the edge). The contiguous dimension is a multiple of 8 on
 // this path, so a chunk is wholly inside or wholly outside.
 // LDS extent (rows or columns) used for an operand tile of R rows or columns: R itself
-// when R is a multiple of 128 (MN-major rows then span whole 256-byte bank windows and the
-// copies split evenly), else R rounded up to 128 (e.g. 192 -> 256: the extra rows or
-// columns are out-of-range copies that only write zeros, and no fragment reads them).
-__host__ __device__ constexpr int pp_lds_extent(int R) { return (R + 127) / 128 * 128; }
+// when R is a multiple of 128 (MN-major rows then span whole 256-byte bank windows) or
+// R = 192 (384-byte MN-major rows, swizzled by swz_b384), else R rounded up to 128 (the
+// extra rows or columns are out-of-range copies that only write zeros, and no fragment
+// reads them).
+__host__ __device__ constexpr int pp_lds_extent(int R) { return R % 128 == 0 || R == 192 ? R : (R + 127) / 128 * 128; }
 
 template <int BM, int BN, int BK, int STAGES>
 __host__ __device__ constexpr int pp_lds_bytes() {
   return STAGES * (pp_lds_extent(BM) + pp_lds_extent(BN)) * BK * 2;
 }
 
+// Bytes of the epilogue's staged tiles (StagedTile: WTM rows of SCPR 16-byte chunks per wave)
+// and the dynamic LDS of a ping-pong launch: the larger of the operand ring and the staging,
+// which reuses the ring once the last k-tile is read.
+__host__ __device__ constexpr int staged_bytes(int nw, int wtm, int wtn) {
+  return nw * wtm * 16 * (wtn / 8 <= 4 ? 4 : wtn / 8 <= 8 ? 8 : wtn / 8 <= 16 ? 16 : 32);
+}
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+__host__ __device__ constexpr int pp_launch_lds_bytes() {
+  return pp_lds_bytes<BM, BN, BK, STAGES>() > staged_bytes(WM * WN, BM / WM, BN / WN)
+             ? pp_lds_bytes<BM, BN, BK, STAGES>()
+             : staged_bytes(WM * WN, BM / WM, BN / WN);
+}
+
+// Copies: unit u = (i * NW + wave) * 64 + lane for copy i of a thread. When the units do
+// not split evenly over the threads (R = 192: 768 units for 512 threads), every wave makes
+// LD_ALL copies and the first half of the waves one more (LD in all); LD_OF(g) is the count
+// of wave group g (waves [4g, 4g + 4) of an 8-wave workgroup), a compile-time constant in
+// the code of each group, so the copy waits stay exact.
 template <int R, int BK, int MF, bool KMAJ, int NW>
 struct PpOperand {
   static constexpr int NT = 64 * NW;
   static constexpr int BYTES = R * BK * 2;
   static constexpr int CPR = KMAJ ? BK / 8 : R / 8;  // 16-byte chunks per LDS row
   static constexpr int UNITS = R * BK / 8;
-  static constexpr int LD = UNITS / NT;              // copies per thread per k-tile
+  static constexpr int LD_ALL = UNITS / NT;          // copies every thread makes per k-tile
+  static constexpr int REM = UNITS % NT;             // units of the extra copy (first half of the waves)
+  static constexpr int LD = LD_ALL + (REM ? 1 : 0);  // copies of a thread of the first half
   static constexpr int KPM = 512 / MF;               // k per MFMA
   static constexpr bool KMAJOR = KMAJ;
   static constexpr int MFRAG = MF, BKV = BK, RV = R;
-  static_assert(UNITS % NT == 0, "copies must split evenly over the threads");
-  static_assert(KMAJ || (R * 2) % 256 == 0, "MN-major rows must span the 256-byte bank window");
+  static_assert(REM == 0 || REM * 2 == NT, "copies split evenly, or the extra copy over half the waves");
+  static_assert(KMAJ || (R * 2) % 256 == 0 || R == 192, "MN-major rows: whole 256-byte bank windows, or 384 bytes");
+  __host__ __device__ static constexpr int LD_OF(int group) { return LD_ALL + (REM && group == 0 ? 1 : 0); }
 
   const char* base;  // the tile's first element at k-tile 0
   int64_t step;      // bytes from one k-tile to the next
@@ -235,7 +263,9 @@ struct PpOperand {
   uint32_t off[LD], off_last[LD];
   int fr_base, fr_x, fr_k, fr_half;  // this lane's fragment-read constants
 
-  __device__ static int swz(int row) { return KMAJ ? swz_a_mf<BK, MF>(row) : swz_b(row); }
+  __device__ static int swz(int row) {
+    return KMAJ ? swz_a_mf<BK, MF>(row) : ((R * 2) % 256 == 0 ? swz_b(row) : swz_b384(row));
+  }
 
   // X, ld: operand base and row stride (elements); r0: the tile's first m or n; rvalid:
   // its m or n extent inside the matrix; kin_last: k values in the last k-tile.
@@ -250,6 +280,8 @@ struct PpOperand {
     rng_last = (uint32_t)(last < kMaxRange ? last : kMaxRange);
 #pragma unroll
     for (int i = 0; i < LD; ++i) {
+      // (for the extra copy of a wave of the second half u is past the tile: computed, never
+      // issued)
       const int u = (i * NW + wave) * 64 + lane;
       const int row = u / CPR;
       const int c = (u % CPR) ^ swz(row);
@@ -301,7 +333,7 @@ struct PpOperand {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int k = KPM * ks + 4 * i + fr_k;
-        const int off = k * R * 2 + (((fr_x + (MF / 8) * f) ^ swz_b(k)) << 4) + fr_half;
+        const int off = k * R * 2 + (((fr_x + (MF / 8) * f) ^ swz(k)) << 4) + fr_half;
         h[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS short4v*)(S + off));
       }
       return __builtin_bit_cast(half8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));

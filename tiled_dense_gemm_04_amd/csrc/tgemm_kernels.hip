@@ -546,7 +546,10 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   using OpA = PpOperand<pp_lds_extent(BM), BK, MF, !TA, NW>;
   using OpB = PpOperand<pp_lds_extent(BN), BK, MF, TB, NW>;
   constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
-  constexpr int PT = OpA::LD + OpB::LD;
+  // copies per thread and k-tile of wave group 0 and 1 (they differ when an operand's
+  // copies do not split evenly over the threads, as for 192-wide tiles)
+  constexpr int PT0 = OpA::LD_OF(0) + OpB::LD_OF(0), PT1 = OpA::LD_OF(1) + OpB::LD_OF(1);
+  constexpr int PT = PT0;  // the larger
   static_assert(NW == 8, "two groups of four waves");
   static_assert(WTM % MF == 0 && WTN % MF == 0 && KS >= 1, "wave tile must be a multiple of the MFMA");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tiles start on swizzle periods");
@@ -602,15 +605,21 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
     d.last = kt == nk - 1;
     return d;
   };
-  auto copy_tile = [&](int t) {
+  // Copies of wave group G (a compile-time constant in each group's code).
+  // (always inlined: an out-of-line copy would take the operands' addresses and move their
+  // offset arrays to scratch memory)
+  auto copy_tile = [&](int t, auto group) __attribute__((always_inline)) {
+    constexpr int G = decltype(group)::value;
     const Dma d = dma_setup(t);
 #pragma unroll
-    for (int j = 0; j < OpA::LD; ++j)
+    for (int j = 0; j < OpA::LD_OF(G); ++j)
       dma_to_lds(d.ra, d.a_dst + j * NW * 1024, d.last ? opa.off_last[j] : opa.off[j]);
 #pragma unroll
-    for (int j = 0; j < OpB::LD; ++j)
+    for (int j = 0; j < OpB::LD_OF(G); ++j)
       dma_to_lds(d.rb, d.b_dst + j * NW * 1024, d.last ? opb.off_last[j] : opb.off[j]);
   };
+  using G0 = std::integral_constant<int, 0>;
+  using G1 = std::integral_constant<int, 1>;
 
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane % MF, lkg = lane / MF;
@@ -656,13 +665,14 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   };
 
   // Prologue: group 0 starts one copy ahead of group 1 (its next copy is in phase 2).
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t) copy_tile(t);
   if (grp == 0) {
-    copy_tile(STAGES - 1);
-    wait_vmcnt<PT * (STAGES - 1)>();
+#pragma unroll
+    for (int t = 0; t < STAGES; ++t) copy_tile(t, G0{});
+    wait_vmcnt<PT0 * (STAGES - 1)>();
   } else {
-    wait_vmcnt<PT * (STAGES - 2)>();
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t) copy_tile(t, G1{});
+    wait_vmcnt<PT1 * (STAGES - 2)>();
   }
   lds_barrier();
   if (grp == 0) read_tile(0);
@@ -675,11 +685,11 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       __builtin_amdgcn_sched_barrier(0);
       mma_tile();                    // phase 1: MFMAs of tile kt
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<PT * (STAGES - 2)>();
+      wait_vmcnt<PT0 * (STAGES - 2)>();
       lds_barrier();                 // B2: tile kt+1 landed everywhere; reads of tile kt done
       __builtin_amdgcn_sched_barrier(0);
       read_tile((kt + 1) % STAGES);  // phase 2 (past the last tile: a settled slot, unused)
-      copy_tile(kt + STAGES);
+      copy_tile(kt + STAGES, G0{});
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();                 // B1
     }
@@ -687,9 +697,9 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
     for (int kt = 0; kt < nloc; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
       read_tile(kt % STAGES);        // phase 1
-      copy_tile(kt + STAGES - 1);
+      copy_tile(kt + STAGES - 1, G1{});
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<PT * (STAGES - 2)>();
+      wait_vmcnt<PT1 * (STAGES - 2)>();
       lds_barrier();                 // B2
       __builtin_amdgcn_sched_barrier(0);
       mma_tile();                    // phase 2: MFMAs of tile kt
@@ -771,7 +781,9 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   // this path, so a chunk is either wholly inside the matrix or wholly outside.
   if constexpr (MF == 16) {
     using ST = StagedTile<WTM, WTN>;
-    static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
+    static_assert(NW * ST::BYTES == staged_bytes(NW, WTM, WTN) &&
+                      NW * ST::BYTES <= pp_launch_lds_bytes<BM, BN, BK, WM, WN, STAGES>(),
+                  "the staged tiles fit in the launch's LDS");
     __syncthreads();
     char* const stage = smem + wave * ST::BYTES;
     if (g.relu != 0)
@@ -918,7 +930,7 @@ struct QuadFrags {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int k = 4 * i + op.fr_k;
-          off[f][i] = k * RV * 2 + (((op.fr_x + (MF / 8) * f) ^ swz_b(k)) << 4) + op.fr_half;
+          off[f][i] = k * RV * 2 + (((op.fr_x + (MF / 8) * f) ^ Op::swz(k)) << 4) + op.fr_half;
         }
     }
   }
@@ -1370,7 +1382,7 @@ hipError_t launch_fast(const GemmArgs& g, hipStream_t s, int device) {
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA, bool TB>
 hipError_t launch_pp_layout(const GemmArgs& g, hipStream_t s, int device) {
-  constexpr int lds = pp_lds_bytes<BM, BN, BK, STAGES>();
+  constexpr int lds = pp_launch_lds_bytes<BM, BN, BK, WM, WN, STAGES>();
   auto kern = gemm_pingpong<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>;
   static std::atomic<uint64_t> ready{0};
   const uint64_t bit = 1ull << (device & 63);
@@ -1387,7 +1399,7 @@ hipError_t launch_pp_layout(const GemmArgs& g, hipStream_t s, int device) {
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int PANEL, int XCD, int MF, bool TA, bool TB>
 hipError_t launch_pp_grouped_layout(const GroupedArgs& ga, int64_t nwg, hipStream_t s, int device) {
-  constexpr int lds = pp_lds_bytes<BM, BN, BK, STAGES>();
+  constexpr int lds = pp_launch_lds_bytes<BM, BN, BK, WM, WN, STAGES>();
   auto kern = gemm_pingpong_grouped<BM, BN, BK, WM, WN, STAGES, PANEL, XCD, MF, TA, TB>;
   static std::atomic<uint64_t> ready{0};
   const uint64_t bit = 1ull << (device & 63);

@@ -102,6 +102,11 @@ def kmajor_frag(wbase, f, bk=32, mf=16, ks=0):
     return (wbase + lrow) * bk * 2 + f * mf * bk * 2 + ((chunk ^ swz_a_mf(lrow, bk)) << 4)
 
 
+def swz_b384(k):
+    """MN-major rows of 384 bytes: 2 ((k / 2) mod 2) + 4 ((k / 8) mod 2)."""
+    return 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1)
+
+
 def mnmajor_frag(wbase, f, R, mf=16, ks=0):
     """PpOperand<R, BK, MF, MN-major>::frag: two ds_read_b64_tr_b16 per lane (i = 0, 1)."""
     bg, bj, bq = LANES >> 4, (LANES >> 2) & 3, LANES & 3
@@ -112,12 +117,13 @@ def mnmajor_frag(wbase, f, R, mf=16, ks=0):
     out = []
     for i in range(2):
         k = kpm * ks + 4 * i + fr_k
-        out.append(k * R * 2 + (((fr_x + (mf // 8) * f) ^ swz_b(k)) << 4) + fr_half)
+        swz = swz_b(k) if (R * 2) % 256 == 0 else swz_b384(k)
+        out.append(k * R * 2 + (((fr_x + (mf // 8) * f) ^ swz) << 4) + fr_half)
     return out
 
 
 def lds_extent(r):
-    return (r + 127) // 128 * 128
+    return r if r % 128 == 0 or r == 192 else (r + 127) // 128 * 128
 
 
 def pingpong_patterns(bm, bn, wm=2, wn=4, bk=32, mf=16, layout=0):
