@@ -678,33 +678,39 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   if (grp == 0) read_tile(0);
 
   clk.loop_begin();
-  // sched_barrier(0) pins every phase: the compiler may not move MFMAs (register-only,
-  // so not ordered by s_barrier) from one phase into the other.
+  // One barrier per k-tile. Between barrier kt-1 and barrier kt, group 0 reads tile kt and
+  // copies its share of tile kt-1+STAGES, then issues the MFMAs of tile kt; group 1 issues
+  // the MFMAs of tile kt-1, then reads tile kt and copies its share of the same tile. The
+  // opposite order keeps the phases alternating on every SIMD (one wave reads while the
+  // other runs MFMAs) without a second barrier, and the barrier covers every LDS hazard:
+  // before it, each wave waits for its own copies of tile kt+1 (two tiles' copies may stay
+  // in flight), so after it tile kt+1 is complete for everyone; every read of the slot a
+  // copy refills (tile kt's, refilled with tile kt+STAGES after barrier kt) happens before
+  // barrier kt. sched_barrier(0) pins every phase: the compiler may not move MFMAs
+  // (register-only, so not ordered by s_barrier) across a phase boundary.
   if (grp == 0) {
     for (int kt = 0; kt < nloc; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
-      mma_tile();                    // phase 1: MFMAs of tile kt
+      mma_tile();                    // MFMAs of tile kt (fragments read before the barrier)
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<PT0 * (STAGES - 2)>();
-      lds_barrier();                 // B2: tile kt+1 landed everywhere; reads of tile kt done
+      lds_barrier();                 // tile kt+1 landed everywhere; reads of tile kt done
       __builtin_amdgcn_sched_barrier(0);
-      read_tile((kt + 1) % STAGES);  // phase 2 (past the last tile: a settled slot, unused)
+      read_tile((kt + 1) % STAGES);  // (past the last tile: a settled slot, unused)
       copy_tile(kt + STAGES, G0{});
       __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();                 // B1
     }
   } else {
     for (int kt = 0; kt < nloc; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
-      read_tile(kt % STAGES);        // phase 1
+      read_tile(kt % STAGES);
       copy_tile(kt + STAGES - 1, G1{});
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<PT1 * (STAGES - 2)>();
-      lds_barrier();                 // B2
+      lds_barrier();                 // tile kt+1 landed everywhere; reads of tile kt done
       __builtin_amdgcn_sched_barrier(0);
-      mma_tile();                    // phase 2: MFMAs of tile kt
+      mma_tile();                    // MFMAs of tile kt
       __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();                 // B1
     }
   }
   wait_vmcnt<0>();
