@@ -504,30 +504,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
 
 // ------------------------------------------------------------------------------------
 // Ping-pong kernel: 8 waves in two groups of 4 (waves 0-3 and 4-7), one wave of each
-// group per SIMD. Every iteration (one k-tile) has two phases separated by workgroup
-// barriers; in each phase one group only issues MFMAs (from registers) while the other
-// only moves data (LDS -> its fragment registers, and its share of the buffer->LDS
-// copies), then they swap. Each SIMD's MFMA pipe is fed by a wave that never waits on a
-// memory instruction, and LDS/TA stalls land on the partner wave.
+// group per SIMD. Every iteration (one k-tile) has two phases; in each phase one group
+// only issues MFMAs (from registers) while the other only moves data (LDS -> its fragment
+// registers, and its share of the buffer->LDS copies), then they swap. Each SIMD's MFMA
+// pipe is fed by a wave that never waits on a memory instruction, and LDS/TA stalls land
+// on the partner wave.
 //
-// Schedule (tile t lives in ring slot t % STAGES; PT copies per thread per tile):
+// Schedule (tile t lives in ring slot t % STAGES; PT0 / PT1 copies per thread per tile in
+// group 0 / 1):
 //   prologue: group 0 copies tiles 0 .. STAGES-1, group 1 tiles 0 .. STAGES-2; both wait
 //             for tile 0; barrier; group 0 reads tile 0.
-//   iteration kt, phase 1: group 0: MFMAs of tile kt.
-//                          group 1: reads tile kt; copies tile kt+STAGES-1.
-//             wait (tile kt+1 landed for this thread), barrier B2
-//             phase 2: group 0: reads tile kt+1; copies tile kt+STAGES.
-//                          group 1: MFMAs of tile kt.
-//             barrier B1
-// Slot safety: a copy of tile t+STAGES (group 0, phase 2 of kt = t) or t+STAGES-1 (group 1,
-// phase 1 of kt = t+1, i.e. into the slot of tile kt-1) only ever targets a slot whose
-// last reads finished before the preceding B2 (its readers were group 0 in phase 2 of
-// the iteration before and group 1 in phase 1 of the same iteration). Copies past the
-// last tile use an empty range, so every thread issues exactly PT copies per iteration
-// and at each B2 exactly STAGES-2 later tiles may still be in flight for every thread.
-// B1 (after this wave's LDS reads completed) holds the two groups exactly a phase apart;
-// every overwrite of a slot is already ordered after its last reads by B2 alone, so B1
-// only shapes the timing.
+//   iteration kt: group 0: MFMAs of tile kt; wait (tile kt+1 landed for this thread);
+//                          barrier; reads tile kt+1; copies tile kt+STAGES.
+//                 group 1: reads tile kt; copies tile kt+STAGES-1; wait (tile kt+1
+//                          landed for this thread); barrier; MFMAs of tile kt.
+// Between two barriers group 0 reads then runs MFMAs while group 1 runs MFMAs then reads:
+// the opposite order keeps the phases alternating without a barrier between them.
+// Slot safety: in iteration kt group 0 copies tile kt+STAGES after barrier kt, into the
+// slot of tile kt, whose last reads (group 1's, and group 0's in iteration kt-1) all come
+// before barrier kt; group 1 copies tile kt+STAGES-1 before barrier kt, into the slot of
+// tile kt-1, whose reads all come before barrier kt-1. Copies past the last tile use an
+// empty range, so every thread issues exactly its PT copies per iteration and at each
+// barrier exactly STAGES-2 later tiles may still be in flight for every thread.
 // MF selects the MFMA: 32 = v_mfma_f32_32x32x16_f16, 16 = v_mfma_f32_16x16x32_f16 (half
 // the accumulator traffic per FLOP, twice the instructions). TA / TB: A given transposed
 // (K x M, lda >= M) / B given transposed (N x K, ldb >= K).
