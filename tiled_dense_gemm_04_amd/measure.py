@@ -381,9 +381,12 @@ def measure_fp8(torch, tg, w, stream, with_torch=True):
     for idx in range(tg.tgemm_fp8_num_configs()):
         if idx == cfg:
             continue
-        t = timed_trials(torch, stream, lambda i, idx=idx: tg.gemm_fp8_block(a, sa, b, sb, c, relu=w.relu,
-                                                                             stream=stream, cfg=idx), trials=5)
-        res["per_config"][tg.tgemm_fp8_config_desc(idx)["name"]] = t["median_us"]
+        # configs left out of the product library run from the tooling build (marked "(t)")
+        d = tg.tgemm_fp8_config_desc(idx)
+        lib = None if d["built"] else tg.stamps_lib()
+        t = timed_trials(torch, stream, lambda i, idx=idx, lib=lib: tg.gemm_fp8_block(
+            a, sa, b, sb, c, relu=w.relu, stream=stream, cfg=idx, library=lib), trials=5)
+        res["per_config"][d["name"] + ("" if d["built"] else " (t)")] = t["median_us"]
     if with_torch and not w.linear:
         try:
             f8 = torch.float8_e4m3fn
