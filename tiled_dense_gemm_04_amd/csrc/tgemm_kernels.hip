@@ -686,6 +686,13 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   // copy refills (tile kt's, refilled with tile kt+STAGES after barrier kt) happens before
   // barrier kt. sched_barrier(0) pins every phase: the compiler may not move MFMAs
   // (register-only, so not ordered by s_barrier) across a phase boundary.
+  // Measured exception: 256 x 256 tiles with both operands k-contiguous run faster with a
+  // second barrier per k-tile, between the two phases (4096^3: 104.4 against 110.9 us,
+  // 8192^3: 793 against 859 us, one box). With either operand m- or n-contiguous the single
+  // barrier is as fast or up to 6 % faster, and so it is for smaller tiles in every layout
+  // (128 x 128 on 1024 x 1024 x 8192: 56.5 against 69.9 us). The extra barrier only adds
+  // ordering, so the slot argument above holds unchanged.
+  constexpr bool kMidBarrier = OpA::KMAJOR && OpB::KMAJOR && BM == 256 && BN == 256;
   if (grp == 0) {
     for (int kt = 0; kt < nloc; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
@@ -697,6 +704,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       read_tile((kt + 1) % STAGES);  // (past the last tile: a settled slot, unused)
       copy_tile(kt + STAGES, G0{});
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kMidBarrier) lds_barrier();
     }
   } else {
     for (int kt = 0; kt < nloc; ++kt) {
@@ -709,6 +717,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       __builtin_amdgcn_sched_barrier(0);
       mma_tile();                    // MFMAs of tile kt
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kMidBarrier) lds_barrier();
     }
   }
   wait_vmcnt<0>();
