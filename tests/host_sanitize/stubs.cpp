@@ -77,9 +77,10 @@ std::vector<tgemm::Config> build_table() {
 
 std::vector<tgemm::Fp8Config> build_fp8_table() {
   std::vector<tgemm::Fp8Config> t;
-  auto row = [&](int bm, int bn, int wm, int wn, int s, int p, int x, int db, int prod) {
+  auto row = [&](int bm, int bn, int wm, int wn, int s, int p, int x, int mode, int prod) {
     char buf[64];
-    std::snprintf(buf, sizeof buf, "f%dx%dx128_s%d_w%dx%d_db%d", bm, bn, s, wm, wn, db);
+    std::snprintf(buf, sizeof buf, "f%dx%dx128_s%d_w%dx%d%s", bm, bn, s, wm, wn,
+                  mode == 2 ? "_pp" : mode == 1 ? "_db1" : "_db0");
     t.push_back({bm, bn, wm, wn, s, p, x, 0, TGEMM_BUILT(prod), keep(buf)});
   };
 #define CALL_FP8(...) row(__VA_ARGS__);

@@ -74,7 +74,7 @@ SHAPES = [(256, 256, 128), (300, 264, 1008), (520, 392, 272), (1, 8, 16), (257, 
 ODD = [(17, 23, 29), (65, 63, 129), (1, 1, 1), (130, 7, 250), (40, 200, 100)]
 
 
-FP8_TABLE_CONFIGS = 4  # rows of the fp8 config table (tests/test_host_abi.py checks the count)
+FP8_TABLE_CONFIGS = 5  # rows of the fp8 config table (tests/test_host_abi.py checks the count)
 
 
 @pytest.mark.parametrize("cfg", list(range(FP8_TABLE_CONFIGS)) + [tg.FP8_GENERIC])

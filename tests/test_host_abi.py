@@ -416,7 +416,7 @@ def test_tile_map_keeps_xcd_tiles_together():
 # ---------------------------------------------------------------- fp8 block-scaled path
 def test_fp8_config_table():
     cfgs = tg.fp8_configs()
-    assert len(cfgs) == tg.tgemm_fp8_num_configs() == 4  # test_gpu_fp8.FP8_TABLE_CONFIGS
+    assert len(cfgs) == tg.tgemm_fp8_num_configs() == 5  # test_gpu_fp8.FP8_TABLE_CONFIGS
     for c in cfgs:
         assert c["block_k"] == 128 and c["generic"] == 0 and c["layouts"] == 2
         assert c["block_m"] % 128 == 0 and c["block_n"] % 128 == 0

@@ -68,10 +68,15 @@
   X(256, 256, 32, 2, 2, 4, 4, 0, 0, 0)   \
   X(256, 256, 32, 2, 2, 4, 4, 1, 0, 0)
 
-// fp8 block-scaled kernels: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP, DB, PROD)
-// (DB = 1: double-buffered fragments)                                          fp8 rows 0-3
+// fp8 block-scaled kernels: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP, MODE, PROD)
+// MODE 0: one group, single-buffered fragments (name suffix _db0); 1: one group,
+// double-buffered fragments (_db1); 2: two wave groups in ping-pong (_pp).  fp8 rows 0-4
 #define TGEMM_FP8_CONFIGS(X)             \
   X(256, 256, 2, 4, 2, 4, 1, 0, 1)       \
   X(128, 128, 2, 2, 3, 4, 1, 0, 1)       \
   X(256, 128, 4, 2, 3, 4, 1, 0, 0)       \
-  X(256, 128, 4, 2, 3, 4, 1, 1, 1)
+  X(256, 128, 4, 2, 3, 4, 1, 1, 1)       \
+  X(256, 256, 2, 4, 2, 4, 1, 2, 1)
+#define TGEMM_FP8_MODE_NAME_0 "_db0"
+#define TGEMM_FP8_MODE_NAME_1 "_db1"
+#define TGEMM_FP8_MODE_NAME_2 "_pp"

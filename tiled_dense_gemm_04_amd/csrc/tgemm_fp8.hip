@@ -389,6 +389,222 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   clk.finish(nk, g.stamps);
 }
 
+// ------------------------------------------------------------------------------------
+// Block-scaled GEMM, ping-pong variant: the binary16 ping-pong's split of the 8 waves into
+// two groups of 4 (one wave of each per SIMD), applied to the fp8 k-tile of one 128-wide
+// scale block. In every interval between two barriers one group issues MFMAs and folds,
+// from fragments already in its registers, while the other reads LDS.
+// The ring has two slots ((BM + BN) x 128 bytes each: three would not fit in LDS), so a
+// slot may only be refilled once both groups hold all of its fragments in registers: a
+// wave reads every A and B fragment of its 128 x 64 sub-tile (and the row scales) for a
+// k-tile in one go, 96 registers, and keeps them through its MFMAs.
+// Schedule (tile t in slot t % 2). Interval kt (between barrier kt-1 and barrier kt):
+//   group 0: reads tile kt; copies all of tile kt+1 (and a slice of a later scale group)
+//            into the other slot; MFMAs + folds of tile kt; waits for its copies;
+//   group 1: MFMAs + folds of tile kt-1; reads tile kt.
+// Slot safety: tile kt+1's copies go to the slot of tile kt-1, which both groups finished
+// reading before barrier kt-1 (group 1's MFMAs of tile kt-1 run from registers). Every
+// group-0 thread waits for all its copies before barrier kt, so after it tile kt+1 is
+// complete.
+// What bounds it (measured, 4096^3): the fold after each MFMA (4 FMAs per lane) does not
+// overlap the same wave's MFMAs, so a wave alone on its SIMD issues an MFMA + fold every
+// ~48 clocks against 32 for MFMAs alone, while two waves interleaving MFMAs + folds on one
+// SIMD reach ~35; and each 64-lane copy holds the issuing wave ~50 clocks, so group 0's
+// 17 copies per k-tile delay its MFMAs by ~900 clocks. Copies issued from group 1's MFMA
+// phase instead (one after every MFMA, every second, or only the B rows there) measured
+// 3-6 % slower. Against the single-group kernel this schedule is ~5 % faster at 4096^3
+// and 8192^3.
+// Scale groups as in gemm_fp8_block_kernel (G k-tiles per group, three group slots): the
+// copies of tile t carry slice t % G of group t / G + 1, one dword per group-0 lane.
+template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_pp_kernel(Fp8Args g) {
+  WgClock clk;
+  clk.start();
+  constexpr int NW = WM * WN, NC = NW / 2;  // NC waves (group 0) issue the copies
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  using OpA = PpOperand<BM, kF8Kh, 16, true, NC>;
+  using OpB = PpOperand<BN, kF8Kh, 16, true, NC>;
+  constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
+  constexpr int G = kScaleGroup;
+  constexpr int SG_BYTES = BM * G * 4;
+  constexpr int NG0 = BM * G / (64 * NC);     // copies per group-0 wave for scale group 0
+  constexpr int NCOPY = OpA::LD + OpB::LD + 1;  // copies per group-0 thread per k-tile
+  static_assert(NW == 8 && WM == 2 && STAGES == 2, "two groups of four waves (rows of wave tiles), two slots");
+  static_assert(OpA::REM == 0 && OpB::REM == 0, "copies split evenly over group 0");
+  static_assert(BM == 64 * NC, "one scale dword per group-0 lane per k-tile");
+  static_assert(kFp8Block % WTN == 0 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+  static_assert(G >= 2, "a scale group slot is refilled only after its last k-tile is read");
+  static_assert(NCOPY + NG0 < 64, "vmcnt budget");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const a_lds = smem;
+  char* const b_lds = smem + STAGES * A_BYTES;
+  char* const s_lds = b_lds + STAGES * B_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / NC;
+  const int cw = wave % NC;  // this wave's share of the copies (group 0 issues them)
+
+  int64_t tm64, tn64;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
+  const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
+  const int nk = g.KB;
+  const int kin_last = g.K - (nk - 1) * kFp8Block;
+
+  OpA opa;
+  OpB opb;
+  opa.init_copies((const _Float16*)g.A, g.lda / 2, row0, mvalid, kin_last / 2, cw, lane);
+  opb.init_copies((const _Float16*)g.B, g.ldb / 2, col0, nvalid, kin_last / 2, cw, lane);
+
+  const float* const sa_base = g.SA + (int64_t)row0 * g.KB;
+  const int si = cw * 64 + lane;  // this lane's element of a scale slice
+  const uint32_t s_off = (uint32_t)(((si / G) * g.KB + si % G) * 4);
+  const int sb_blk = min((col0 + (wave % WN) * WTN) / kFp8Block, (g.N - 1) / kFp8Block);
+  const float* const sb_row = g.SB + (int64_t)sb_blk * g.KB;
+
+  const uint32_t a_lds0 = lds_addr(a_lds) + cw * 1024;
+  const uint32_t b_lds0 = lds_addr(b_lds) + cw * 1024;
+  const uint32_t s_lds0 = lds_addr(s_lds) + cw * 256;
+  // Copy j of a thread sits RSTEP rows after copy 0, a multiple of the swizzle period, so
+  // its offset is copy 0's plus j * RSTEP rows. An out-of-range offset (kOob, a k chunk
+  // past K) stays out of range and below 2^32: the fast path takes lda, ldb <= 2^23 bytes,
+  // so (LD - 1) * RSTEP rows <= 7 * 2^28 bytes < 2^31. Two registers per operand instead
+  // of 2 * LD keep the ping-pong's 96 fragment registers from spilling.
+  constexpr int RSTEP = NC * 64 / OpA::CPR;
+  static_assert(OpA::CPR == OpB::CPR && RSTEP % 16 == 0, "copy rows step by whole swizzle periods");
+  static_assert((OpA::LD - 1) * RSTEP <= 8 * 32 && (OpB::LD - 1) * RSTEP <= 8 * 32, "offset headroom below 2^32");
+  const uint32_t a_rstep = (uint32_t)RSTEP * (uint32_t)g.lda, b_rstep = (uint32_t)RSTEP * (uint32_t)g.ldb;
+  const uint32_t a_off = opa.off[0], a_off_last = opa.off_last[0];
+  const uint32_t b_off = opb.off[0], b_off_last = opb.off_last[0];
+  auto copy_tile = [&](int t) {
+    const int4v ra = opa.rsrc(t, nk, nk);
+    const int4v rb = opb.rsrc(t, nk, nk);
+    const int slot = t % STAGES;
+    const bool last = t == nk - 1;
+    const uint32_t ao = last ? a_off_last : a_off, bo = last ? b_off_last : b_off;
+#pragma unroll
+    for (int j = 0; j < OpA::LD; ++j) dma_to_lds(ra, a_lds0 + slot * A_BYTES + j * NC * 1024, ao + j * a_rstep);
+#pragma unroll
+    for (int j = 0; j < OpB::LD; ++j) dma_to_lds(rb, b_lds0 + slot * B_BYTES + j * NC * 1024, bo + j * b_rstep);
+    const int sgrp = t / G + 1, part = t % G;
+    const int r0 = part * (BM / G), k0 = sgrp * G;
+    const int rl = max(mvalid - r0, 0), kl = max(g.KB - k0, 0);
+    const uint32_t rng = (uint32_t)(max((rl - 1) * g.KB + kl, 0) * 4 * min(kl, 1));
+    const int4v rs = make_rsrc(sa_base + (int64_t)r0 * g.KB + min(k0, nk - 1), rng);
+    dma_dword_to_lds(rs, s_lds0 + (sgrp % 3) * SG_BYTES + part * BM * 4, s_off);
+  };
+  auto sa_lds = [&](int t) { return (const TG_LDS float*)(s_lds + ((t / G) % 3) * SG_BYTES) + t % G; };
+
+  const int wm = wave / WN, wn = wave % WN;
+  const int lrow = lane % 16;
+  opa.init_frags(wm * WTM, lane);
+  opb.init_frags(wn * WTN, lane);
+
+  float4v acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+  int8v fa[FM], fb[FN];
+  float sa[FM], sb = 0.0f;
+  // B's block scales through the scalar path (read-only in this kernel): a uniform value
+  // that an LDS-read wait covers, where a vector load would be waited on together with
+  // the copies in flight.
+  typedef __attribute__((address_space(4))) const float* ConstF32;
+  const ConstF32 sbp = (ConstF32)sb_row;
+  auto read_tile = [&](int kt) {
+    const int slot = kt % STAGES;
+    const char* const As = a_lds + slot * A_BYTES;
+    const char* const Bs = b_lds + slot * B_BYTES;
+    const TG_LDS float* const S = sa_lds(kt);
+    sb = sbp[kt];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) fa[fm] = cat_frag(opa.frag(As, fm, 0), opa.frag(As, fm, 1));
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sa[fm] = S[(wm * WTM + fm * 16 + lrow) * G];
+  };
+  // MFMA t (t = fm * FN + fn) writes result register t % 2; the block sum of MFMA t-1 is
+  // folded right after it (acc += sa * sb * P) while MFMA t runs. sched_barrier(0) keeps
+  // that order (left alone, the compiler folds each result right behind its own MFMA and
+  // waits for it).
+  const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto mma_tile = [&]() {
+    float4v p[2];
+#pragma unroll
+    for (int t = 0; t < FM * FN + 1; ++t) {
+      if (t < FM * FN) {
+        p[t % 2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[t % FN], fa[t / FN], zero, 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (t >= 1) {
+        const int u = t - 1;
+        acc[u / FN][u % FN] += (sa[u / FN] * sb) * p[u % 2];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Prologue (group 0): scale group 0 and tile 0, waited for; then the first barrier.
+  if (grp == 0) {
+    const int4v rs = make_rsrc(sa_base, (uint32_t)(((int64_t)(mvalid - 1) * g.KB + g.KB) * 4));
+#pragma unroll
+    for (int j = 0; j < NG0; ++j) {
+      const int i = (cw * NG0 + j) * 64 + lane;
+      dma_dword_to_lds(rs, lds_addr(s_lds) + (cw * NG0 + j) * 256, (uint32_t)(((i / G) * g.KB + i % G) * 4));
+    }
+    copy_tile(0);
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  clk.loop_begin();
+  // sched_barrier(0) pins every phase (the MFMAs are register-only, so s_barrier alone
+  // would not keep the compiler from moving them across it).
+  if (grp == 0) {
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_tile(kt);
+      copy_tile(kt + 1);  // into the slot of tile kt-1 (past the last tile: empty ranges)
+      __builtin_amdgcn_sched_barrier(0);
+      mma_tile();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();
+      lds_barrier();      // (barrier kt) tile kt+1 landed everywhere; both groups hold tile kt
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_tile(kt);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();      // (barrier kt)
+      __builtin_amdgcn_sched_barrier(0);
+      mma_tile();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();
+  clk.loop_end();
+
+  using ST = StagedTile<WTM, WTN>;
+  static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "staged tile fits in the ring");
+  __syncthreads();
+  char* const stage = smem + wave * ST::BYTES;
+  if (g.relu != 0)
+    ST::template stage<true>(stage, acc, lane);
+  else
+    ST::template stage<false>(stage, acc, lane);
+  ST::wave_fence();
+  ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
+            nvalid - wn * WTN);
+  clk.finish(nk, g.stamps);
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES>
 constexpr int fp8_lds_bytes() {
   return STAGES * (BM + BN) * kFp8Block + 3 * BM * kScaleGroup * 4 + 256;
@@ -576,11 +792,16 @@ __global__ __launch_bounds__(256) void quant_fp8_tiles(QuantArgs q) {
   if (t == 0) q.S[rb * q.KB + kb] = s;
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD, bool DB>
+// MODE: 0 single-buffered fragments, 1 double-buffered (DB), 2 ping-pong.
+template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD, int MODE>
 hipError_t launch_fp8_cfg(const Fp8Args& g, hipStream_t s, int device) {
   constexpr int lds = fp8_lds_bytes<BM, BN, WM, WN, STAGES>();
   static_assert(lds <= 160 * 1024, "LDS");
-  auto kern = gemm_fp8_block_kernel<BM, BN, WM, WN, STAGES, PANEL, XCD, DB>;
+  void (*kern)(Fp8Args);
+  if constexpr (MODE == 2)
+    kern = gemm_fp8_pp_kernel<BM, BN, WM, WN, STAGES, PANEL, XCD>;
+  else
+    kern = gemm_fp8_block_kernel<BM, BN, WM, WN, STAGES, PANEL, XCD, MODE == 1>;
   static std::atomic<uint64_t> ready{0};
   const uint64_t bit = 1ull << (device & 63);
   if (!(ready.load(std::memory_order_acquire) & bit)) {
@@ -597,12 +818,12 @@ hipError_t launch_fp8_cfg(const Fp8Args& g, hipStream_t s, int device) {
 
 static hipError_t launch_fp8_unbuilt(const Fp8Args&, hipStream_t, int) { return hipErrorNotSupported; }
 
-// The fp8 rows of tgemm_configs.h: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD, DB, PROD)
-#define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X, DB, PROD)                                          \
+// The fp8 rows of tgemm_configs.h: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD, MODE, PROD)
+#define TGEMM_FP8_ROW(BM, BN, WM, WN, S, P, X, MODE, PROD)                                        \
   {BM, BN, WM, WN, S, P, X, fp8_lds_bytes<BM, BN, WM, WN, S>(), TGEMM_BUILT(PROD),               \
-   "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN "_db" #DB},
-#define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X, DB, PROD) \
-  TGEMM_IF_BUILT(PROD, (launch_fp8_cfg<BM, BN, WM, WN, S, P, X, DB>), launch_fp8_unbuilt),
+   "f" #BM "x" #BN "x128_s" #S "_w" #WM "x" #WN TGEMM_FP8_MODE_NAME_##MODE},
+#define TGEMM_FP8_LAUNCHER(BM, BN, WM, WN, S, P, X, MODE, PROD) \
+  TGEMM_IF_BUILT(PROD, (launch_fp8_cfg<BM, BN, WM, WN, S, P, X, MODE>), launch_fp8_unbuilt),
 
 const Fp8Config* fp8_config_table(int* count) {
   static const Fp8Config table[] = {TGEMM_FP8_CONFIGS(TGEMM_FP8_ROW)};
