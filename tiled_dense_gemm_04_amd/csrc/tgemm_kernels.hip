@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
           v3 = relu_f(v3);
         }
         half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        store_c(crow + n, h);
+        store_c<true>(crow + n, h);
       }
     }
   }
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
           v3 = relu_f(v3);
         }
         half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        store_c(crow + n, h);
+        store_c<false>(crow + n, h);
       }
     }
   }
@@ -805,7 +805,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       ST::template stage<false>(stage, acc, lane);
     ST::wave_fence();
     ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-              nvalid - wn * WTN);
+              nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
   } else {
     constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
     constexpr int RB = SCPR * 16;
@@ -847,7 +847,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       if (c >= CPR) continue;
       const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
       const int m = wm * WTM + r, n = wn * WTN + 8 * c;
-      if (m < mvalid && n < nvalid) store_c(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
+      if (m < mvalid && n < nvalid) store_c<true>(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
     }
   }
   clk.finish(nloc, TG_STAMP_TABLE);
@@ -1198,7 +1198,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_quad(GemmArgs g) {
     ST::template stage<false>(stage, acc, lane);
   ST::wave_fence();
   ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-            nvalid - wn * WTN);
+            nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
   clk.finish(nk, TG_STAMP_TABLE);
 }
 
