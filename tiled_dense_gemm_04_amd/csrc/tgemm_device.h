@@ -46,9 +46,11 @@ __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
 // kernel, so it streams out instead of leaving dirty lines in L2 for the end of the kernel
 // to write back (4096^3 + ReLU: 105.6 against 107.2 us, 8192^3: 810 against 823 us).
 // Ordinary stores where rows straddle lines (2 * ldc not a multiple of 128: the partial
-// lines at tile edges then merge in L2; 4095 x 3000 x 1000: 29.4 against 31.2 us) and for
-// 8-byte pieces (the pipelined kernel's epilogue; 1024^3: 10.5 against 11.4 us). Same box,
-// alternating, bit-identical.
+// lines at tile edges then merge in L2; 4095 x 3000 x 1000: 29.4 against 31.2 us). 8-byte
+// pieces written non-temporally lose even on aligned rows (the pipelined kernel's former
+// direct epilogue, 1024^3: 11.4 against 10.5 us with ordinary stores); every product
+// kernel now stages its tile and stores 16-byte chunks. Same box, alternating,
+// bit-identical.
 template <bool NT, typename V>
 __device__ __forceinline__ void store_c(_Float16* p, const V& v) {
   if constexpr (NT)
@@ -446,6 +448,74 @@ struct StagedTile {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+};
+
+// Epilogue of the 32x32 MFMA kernels: a wave's WTM x WTN tile of float32 accumulators
+// (tile (fm, fn) holds, in lane l, row 32 fm + l % 32 and columns 32 fn + 8 g + 4 (l / 32)
+// .. +3 for g = 0 .. 3) goes through the wave's own LDS region as 8-byte pieces, staged row
+// r's 16-byte chunk c at chunk c ^ ((r / 2) % SCPR) (rows padded to SCPR chunks, a power of
+// two), and out to C as 16-byte row segments read back by consecutive lanes. The 8-byte
+// writes of the 32 lanes of a row group are 2-way conflicted; the epilogue is a small part
+// of the kernels that use this layout (the pipelined kernel for the smallest grids, and a
+// sweep-only ping-pong variant). Stores as in StagedTile::store.
+template <int WTM, int WTN>
+struct StagedTile32 {
+  static constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
+  static constexpr int RB = SCPR * 16, BYTES = WTM * RB;
+  static_assert(SCPR >= CPR && WTN % 32 == 0 && WTM % 32 == 0, "staged row shape");
+  static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+
+  template <bool RELU, typename Acc>
+  __device__ static void stage(char* region, const Acc& acc, int lane) {
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    const int l32 = lane & 31, lhi = lane >> 5;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = fm * 32 + l32;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int n = fn * 32 + 8 * g4 + 4 * lhi;
+          float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
+          float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
+          if (RELU) {
+            v0 = relu_f(v0);
+            v1 = relu_f(v1);
+            v2 = relu_f(v2);
+            v3 = relu_f(v3);
+          }
+          const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+          *(TG_LDS half4*)(region + r * RB + (((n >> 3) ^ ((r >> 1) % SCPR)) << 4) + (n & 7) * 2) = h;
+        }
+      }
+    }
+  }
+
+  __device__ static void wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+
+  __device__ static void store(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid,
+                               bool nt) {
+    if (nt)
+      store_rows<true>(region, lane, C, ldc, mvalid, nvalid);
+    else
+      store_rows<false>(region, lane, C, ldc, mvalid, nvalid);
+  }
+  template <bool NT>
+  __device__ static void store_rows(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < WTM * SCPR / 64; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx / SCPR, c = idx % SCPR;
+      if (c >= CPR) continue;
+      const half8 x = *(const TG_LDS half8*)(region + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
+      if (r < mvalid && 8 * c < nvalid) store_c<NT>(C + (int64_t)r * ldc + 8 * c, x);
+    }
   }
 };
 

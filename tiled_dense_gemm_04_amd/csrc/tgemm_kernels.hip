@@ -474,31 +474,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
   wait_vmcnt<0>();
   clk.loop_end();
 
-  const bool relu = g.relu != 0;
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = wm * WTM + fm * 32 + l32;
-    if (m >= mvalid) continue;
-    _Float16* const crow = g.C + (int64_t)(row0 + m) * g.ldc + col0;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int n = wn * WTN + fn * 32 + 8 * g4 + 4 * lhi;
-        if (n >= nvalid) continue;
-        float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
-        float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
-        if (relu) {
-          v0 = relu_f(v0);
-          v1 = relu_f(v1);
-          v2 = relu_f(v2);
-          v3 = relu_f(v3);
-        }
-        half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        store_c<false>(crow + n, h);
-      }
-    }
-  }
+  // Epilogue: ReLU and RNE in registers, then each wave's sub-tile through its own LDS
+  // region (the ring is free once every wave passes the barrier) and out as 16-byte row
+  // segments (StagedTile32).
+  using ST = StagedTile32<WTM, WTN>;
+  static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
+  __syncthreads();
+  char* const stage = smem + wave * ST::BYTES;
+  if (g.relu != 0)
+    ST::template stage<true>(stage, acc, lane);
+  else
+    ST::template stage<false>(stage, acc, lane);
+  ST::wave_fence();
+  ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
+            nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
   clk.finish(nk, TG_STAMP_TABLE);
 }
 
@@ -789,9 +778,9 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   // waves pass the barrier below) and writes it back row by row, 16 bytes per lane and
   // WTN / 8 lanes per row, so each store covers whole 16-byte-aligned row segments instead
   // of 8-byte pieces of MF rows. The 16x16 layout uses StagedTile (conflict-free 16-byte
-  // staging writes after a lane swap); the 32x32 one (a sweep-only config) writes 8-byte
-  // pieces at chunk c ^ ((r / 2) % SCPR) of staged row r. N and ldc are multiples of 8 on
-  // this path, so a chunk is either wholly inside the matrix or wholly outside.
+  // staging writes after a lane swap); the 32x32 one (a sweep-only config) uses
+  // StagedTile32 (8-byte staging writes). N and ldc are multiples of 8 on this path, so a
+  // chunk is either wholly inside the matrix or wholly outside.
   if constexpr (MF == 16) {
     using ST = StagedTile<WTM, WTN>;
     static_assert(NW * ST::BYTES == staged_bytes(NW, WTM, WTN) &&
@@ -807,48 +796,17 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
     ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
               nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
   } else {
-    constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
-    constexpr int RB = SCPR * 16;
-    static_assert(SCPR >= CPR && WTN % 8 == 0, "staged row shape");
-    static_assert(NW * WTM * RB <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
-    static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+    using ST = StagedTile32<WTM, WTN>;
+    static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
     __syncthreads();
-    char* const stage = smem + wave * (WTM * RB);
-    const bool relu = g.relu != 0;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int mw = fm * MF + lrow;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-        for (int g4 = 0; g4 < NACC / 4; ++g4) {
-          const int nw = fn * MF + 8 * g4 + 4 * lkg;
-          float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
-          float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
-          if (relu) {
-            v0 = relu_f(v0);
-            v1 = relu_f(v1);
-            v2 = relu_f(v2);
-            v3 = relu_f(v3);
-          }
-          const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-          const int off = mw * RB + ((((nw >> 3) ^ ((mw >> 1) % SCPR))) << 4) + (nw & 7) * 2;
-          *(TG_LDS half4*)(stage + off) = h;
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-    for (int i = 0; i < WTM * SCPR / 64; ++i) {
-      const int idx = i * 64 + lane;
-      const int r = idx / SCPR, c = idx % SCPR;
-      if (c >= CPR) continue;
-      const half8 x = *(const TG_LDS half8*)(stage + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
-      const int m = wm * WTM + r, n = wn * WTN + 8 * c;
-      if (m < mvalid && n < nvalid) store_c<true>(g.C + (int64_t)(row0 + m) * g.ldc + col0 + n, x);
-    }
+    char* const stage = smem + wave * ST::BYTES;
+    if (g.relu != 0)
+      ST::template stage<true>(stage, acc, lane);
+    else
+      ST::template stage<false>(stage, acc, lane);
+    ST::wave_fence();
+    ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
+              nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
   }
   clk.finish(nloc, TG_STAMP_TABLE);
 }
