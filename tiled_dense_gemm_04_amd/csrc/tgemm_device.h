@@ -39,6 +39,21 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, expanded at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// The same for I = LO .. HI-1.
+template <int LO, int HI, typename F>
+__device__ __forceinline__ void static_for_range(F&& f) {
+  static_for<HI - LO>([&](auto i) { f(std::integral_constant<int, LO + decltype(i)::value>{}); });
+}
+
 __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
 
 // Stores of the output tile. Non-temporal (NT) where every row of C starts on a 128-byte

@@ -595,18 +595,37 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   // Copies of wave group G (a compile-time constant in each group's code).
   // (always inlined: an out-of-line copy would take the operands' addresses and move their
   // offset arrays to scratch memory)
-  auto copy_tile = [&](int t, auto group) __attribute__((always_inline)) {
-    constexpr int G = decltype(group)::value;
+  // Copies [LO, HI) of this thread's PT of tile t (A rows first, then B rows).
+  auto copy_part = [&](int t, auto group, auto lo_c, auto hi_c) __attribute__((always_inline)) {
+    constexpr int G = decltype(group)::value, LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+    constexpr int LA = OpA::LD_OF(G);
     const Dma d = dma_setup(t);
 #pragma unroll
-    for (int j = 0; j < OpA::LD_OF(G); ++j)
+    for (int j = LO; j < (HI < LA ? HI : LA); ++j)
       dma_to_lds(d.ra, d.a_dst + j * NW * 1024, d.last ? opa.off_last[j] : opa.off[j]);
 #pragma unroll
-    for (int j = 0; j < OpB::LD_OF(G); ++j)
-      dma_to_lds(d.rb, d.b_dst + j * NW * 1024, d.last ? opb.off_last[j] : opb.off[j]);
+    for (int j = (LO > LA ? LO : LA); j < HI; ++j)
+      dma_to_lds(d.rb, d.b_dst + (j - LA) * NW * 1024, d.last ? opb.off_last[j - LA] : opb.off[j - LA]);
   };
   using G0 = std::integral_constant<int, 0>;
   using G1 = std::integral_constant<int, 1>;
+  // CM of each thread's PT copies per k-tile go out from its MFMA phase, spread between
+  // the MFMAs, the rest from its memory phase. A copy holds the issuing wave ~60 clocks, so
+  // where the memory phase outlasts the other wave's MFMAs a copy can move: on 128 x 128
+  // tiles (8 MFMAs, ~130 clocks per MFMA phase) both copies move (512 x 4096 x 4096:
+  // 36.7 -> 34.6 us, 1536^2 x 1024: 12.3 -> 11.8 us, 2048^2 x 4096: 40.8 -> 39.7 us; one
+  // moved copy: no change; 1024^2 x 32768 with A transposed: 315.9 -> 273.2 us). Not with
+  // both operands k-contiguous, whose plain 16-byte fragment reads keep the memory phase
+  // short (1024^2 x 8192: 56.6 -> 60.8 us). On 256 x 128 and 256 x 192 tiles moving one or
+  // two measured 3-11 % slower, and 256 x 256 tiles are balanced as they are. Each tile's copies stay
+  // contiguous in issue order (group 0: memory part after barrier kt, MFMA part in the next
+  // MFMA phase; group 1: MFMA part after barrier kt-1, memory part before barrier kt), so
+  // the constant waits hold; only the prologue's waits change.
+  constexpr int CM = BM == 128 && BN == 128 && !(OpA::KMAJOR && OpB::KMAJOR) ? (PT0 < PT1 ? PT0 : PT1) : 0;
+  auto copy_tile = [&](int t, auto group) __attribute__((always_inline)) {
+    constexpr int G = decltype(group)::value, P = G == 0 ? PT0 : PT1;
+    copy_part(t, group, std::integral_constant<int, 0>{}, std::integral_constant<int, P - CM>{});
+  };
 
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane % MF, lkg = lane / MF;
@@ -650,16 +669,35 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
 #pragma unroll
     for (int m = 0; m < N_MFMA; ++m) mma_one(m);
   };
+  // The MFMAs of a tile with the CM MFMA-phase copies of tile t spread between them.
+  auto mma_tile_copy = [&](int t, auto group) __attribute__((always_inline)) {
+    constexpr int G = decltype(group)::value, P = G == 0 ? PT0 : PT1;
+    static_for<N_MFMA>([&](auto m_c) {
+      constexpr int m = decltype(m_c)::value;
+      mma_one(m);
+      static_for<CM>([&](auto c_c) {
+        constexpr int c = decltype(c_c)::value;
+        if constexpr ((c + 1) * N_MFMA / (CM + 1) == m + 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          copy_part(t, group, std::integral_constant<int, P - CM + c>{}, std::integral_constant<int, P - CM + c + 1>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    });
+  };
 
   // Prologue: group 0 starts one copy ahead of group 1 (its next copy is in phase 2).
   if (grp == 0) {
 #pragma unroll
-    for (int t = 0; t < STAGES; ++t) copy_tile(t, G0{});
-    wait_vmcnt<PT0 * (STAGES - 1)>();
+    for (int t = 0; t < STAGES - 1; ++t) copy_part(t, G0{}, std::integral_constant<int, 0>{}, std::integral_constant<int, PT0>{});
+    copy_tile(STAGES - 1, G0{});  // (its MFMA-phase copies go out in the first iteration)
+    wait_vmcnt<PT0 * (STAGES - 1) - CM>();
   } else {
 #pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t) copy_tile(t, G1{});
-    wait_vmcnt<PT1 * (STAGES - 2)>();
+    for (int t = 0; t < STAGES - 1; ++t) copy_part(t, G1{}, std::integral_constant<int, 0>{}, std::integral_constant<int, PT1>{});
+    // tile STAGES-1's MFMA-phase copies (those of the MFMAs of tile -1)
+    copy_part(STAGES - 1, G1{}, std::integral_constant<int, PT1 - CM>{}, std::integral_constant<int, PT1>{});
+    wait_vmcnt<PT1 * (STAGES - 2) + CM>();
   }
   lds_barrier();
   if (grp == 0) read_tile(0);
@@ -685,7 +723,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   if (grp == 0) {
     for (int kt = 0; kt < nloc; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
-      mma_tile();                    // MFMAs of tile kt (fragments read before the barrier)
+      mma_tile_copy(kt + STAGES - 1, G0{});  // MFMAs of tile kt (fragments read before the barrier)
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<PT0 * (STAGES - 2)>();
       lds_barrier();                 // tile kt+1 landed everywhere; reads of tile kt done
@@ -704,7 +742,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       wait_vmcnt<PT1 * (STAGES - 2)>();
       lds_barrier();                 // tile kt+1 landed everywhere; reads of tile kt done
       __builtin_amdgcn_sched_barrier(0);
-      mma_tile();                    // MFMAs of tile kt
+      mma_tile_copy(kt + STAGES, G1{});  // MFMAs of tile kt
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kMidBarrier) lds_barrier();
     }
@@ -870,21 +908,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pingpong_grouped(GroupedArg
 // out one every NS/PT slots until the next barrier (so the copy stream of one tile straddles
 // two iterations). Every iteration issues exactly PT copies (empty ranges past the last
 // tile), so one constant s_waitcnt vmcnt(PT * (STAGES - 2)) finds the next tile landed.
-// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1, expanded at compile time.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-// The same for I = LO .. HI-1.
-template <int LO, int HI, typename F>
-__device__ __forceinline__ void static_for_range(F&& f) {
-  static_for<HI - LO>([&](auto i) { f(std::integral_constant<int, LO + decltype(i)::value>{}); });
-}
-
 // Fragment reads of the quad kernel with their per-lane offsets precomputed (what
 // PpOperand::frag computes for k substep 0, hoisted out of the loop).
 template <typename Op, int NF>
