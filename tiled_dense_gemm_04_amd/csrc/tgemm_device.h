@@ -56,27 +56,18 @@ __device__ __forceinline__ void static_for_range(F&& f) {
 
 __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : 0.0f; }
 
-// Stores of the output tile. Non-temporal (NT) where every row of C starts on a 128-byte
-// line and the stores are whole 16-byte chunks: C is written once and not read back by the
-// kernel, so it streams out instead of leaving dirty lines in L2 for the end of the kernel
-// to write back (4096^3 + ReLU: 105.6 against 107.2 us, 8192^3: 810 against 823 us).
-// Ordinary stores where rows straddle lines (2 * ldc not a multiple of 128: the partial
-// lines at tile edges then merge in L2; 4095 x 3000 x 1000: 29.4 against 31.2 us). 8-byte
-// pieces written non-temporally lose even on aligned rows (the pipelined kernel's former
-// direct epilogue, 1024^3: 11.4 against 10.5 us with ordinary stores); every product
-// kernel now stages its tile and stores 16-byte chunks. Same box, alternating,
-// bit-identical.
-template <bool NT, typename V>
+// Stores of the output tile are non-temporal 16-byte chunks: C is written once and not read
+// back by the kernel, so it streams out instead of leaving dirty lines in L2 and the
+// Infinity Cache to be written back later (4096^3 + ReLU: 105.6 against 107.2 us with
+// ordinary stores, 8192^3: 810 against 823 us). Ordinary stores look faster where rows
+// straddle 128-byte lines (4095 x 3000 x 1000: 28.3 against 31.0 us) only while every call
+// rewrites the same C: with the buffers rotated past the caches the deferred write-backs
+// of the partial lines cost more (38.3 against 31.3 us). 8-byte pieces stream badly (the
+// pipelined kernel's former direct epilogue, 1024^3: 11.4 us), so every product kernel
+// stages its tile and stores whole 16-byte chunks (1024^3: 9.9 us).
+template <typename V>
 __device__ __forceinline__ void store_c(_Float16* p, const V& v) {
-  if constexpr (NT)
-    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
-  else
-    *reinterpret_cast<V*>(p) = v;
-}
-
-// Every row of the matrix C (leading dimension ldc) starts on a 128-byte line.
-__device__ __forceinline__ bool rows_line_aligned(const _Float16* C, int64_t ldc) {
-  return (((uintptr_t)C | (uintptr_t)(ldc * 2)) & 127) == 0;
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
 }
 
 // Per-workgroup timestamps, compiled in only for the instrumented build (TGEMM_STAMPS) and
@@ -436,24 +427,15 @@ struct StagedTile {
   }
 
   // Rows past mvalid or chunks past nvalid (counted from the wave tile's origin) are not
-  // stored; C points at the wave tile's first element. nt: non-temporal stores (store_c;
-  // the caller passes rows_line_aligned of the whole matrix).
-  __device__ static void store(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid,
-                               bool nt) {
-    if (nt)
-      store_rows<true>(region, lane, C, ldc, mvalid, nvalid);
-    else
-      store_rows<false>(region, lane, C, ldc, mvalid, nvalid);
-  }
-  template <bool NT>
-  __device__ static void store_rows(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid) {
+  // stored; C points at the wave tile's first element.
+  __device__ static void store(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid) {
 #pragma unroll
     for (int i = 0; i < WTM * SCPR / 64; ++i) {
       const int idx = i * 64 + lane;
       const int r = idx / SCPR, c = idx % SCPR;
       if (c >= CPR) continue;
       const half8 x = *(const TG_LDS half8*)(region + r * RB + (chunk_at(r, c) << 4));
-      if (r < mvalid && 8 * c < nvalid) store_c<NT>(C + (int64_t)r * ldc + 8 * c, x);
+      if (r < mvalid && 8 * c < nvalid) store_c(C + (int64_t)r * ldc + 8 * c, x);
     }
   }
 
@@ -473,7 +455,7 @@ struct StagedTile {
 // two), and out to C as 16-byte row segments read back by consecutive lanes. The 8-byte
 // writes of the 32 lanes of a row group are 2-way conflicted; the epilogue is a small part
 // of the kernels that use this layout (the pipelined kernel for the smallest grids, and a
-// sweep-only ping-pong variant). Stores as in StagedTile::store.
+// sweep-only ping-pong variant). Stores as in StagedTile::store (non-temporal).
 template <int WTM, int WTN>
 struct StagedTile32 {
   static constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
@@ -514,22 +496,14 @@ struct StagedTile32 {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   }
 
-  __device__ static void store(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid,
-                               bool nt) {
-    if (nt)
-      store_rows<true>(region, lane, C, ldc, mvalid, nvalid);
-    else
-      store_rows<false>(region, lane, C, ldc, mvalid, nvalid);
-  }
-  template <bool NT>
-  __device__ static void store_rows(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid) {
+  __device__ static void store(const char* region, int lane, _Float16* C, int64_t ldc, int mvalid, int nvalid) {
 #pragma unroll
     for (int i = 0; i < WTM * SCPR / 64; ++i) {
       const int idx = i * 64 + lane;
       const int r = idx / SCPR, c = idx % SCPR;
       if (c >= CPR) continue;
       const half8 x = *(const TG_LDS half8*)(region + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
-      if (r < mvalid && 8 * c < nvalid) store_c<NT>(C + (int64_t)r * ldc + 8 * c, x);
+      if (r < mvalid && 8 * c < nvalid) store_c(C + (int64_t)r * ldc + 8 * c, x);
     }
   }
 };

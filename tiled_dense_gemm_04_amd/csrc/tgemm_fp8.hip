@@ -385,7 +385,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
     ST::template stage<false>(stage, acc, lane);
   ST::wave_fence();
   ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-            nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
+            nvalid - wn * WTN);
   clk.finish(nk, g.stamps);
 }
 
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_pp_kernel(Fp8Args g) {
     ST::template stage<false>(stage, acc, lane);
   ST::wave_fence();
   ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-            nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
+            nvalid - wn * WTN);
   clk.finish(nk, g.stamps);
 }
 

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fast(GemmArgs g) {
           v3 = relu_f(v3);
         }
         half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-        store_c<true>(crow + n, h);
+        store_c(crow + n, h);
       }
     }
   }
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe(GemmArgs g) {
     ST::template stage<false>(stage, acc, lane);
   ST::wave_fence();
   ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-            nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
+            nvalid - wn * WTN);
   clk.finish(nk, TG_STAMP_TABLE);
 }
 
@@ -832,7 +832,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       ST::template stage<false>(stage, acc, lane);
     ST::wave_fence();
     ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-              nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
+              nvalid - wn * WTN);
   } else {
     using ST = StagedTile32<WTM, WTN>;
     static_assert(NW * ST::BYTES <= STAGES * (A_BYTES + B_BYTES), "the staged tile fits in the ring");
@@ -844,7 +844,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       ST::template stage<false>(stage, acc, lane);
     ST::wave_fence();
     ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-              nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
+              nvalid - wn * WTN);
   }
   clk.finish(nloc, TG_STAMP_TABLE);
 }
@@ -1179,7 +1179,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_quad(GemmArgs g) {
     ST::template stage<false>(stage, acc, lane);
   ST::wave_fence();
   ST::store(stage, lane, g.C + (int64_t)(row0 + wm * WTM) * g.ldc + col0 + wn * WTN, g.ldc, mvalid - wm * WTM,
-            nvalid - wn * WTN, rows_line_aligned(g.C, g.ldc));
+            nvalid - wn * WTN);
   clk.finish(nk, TG_STAMP_TABLE);
 }
 
