@@ -58,8 +58,8 @@
   X(256, 256, 32, 2, 4, 4, 2, 1, 0, 0)   \
   X(256, 256, 32, 2, 4, 4, 4, 0, 0, 1)   \
   X(128, 128, 32, 2, 4, 4, 4, 1, 1, 1)   \
-  X(256, 128, 32, 2, 4, 4, 4, 1, 1, 1)   \
-  X(128, 256, 32, 2, 4, 4, 4, 1, 1, 0)   \
+  X(256, 128, 32, 2, 4, 4, 4, 1, 1, 0)   \
+  X(128, 256, 32, 2, 4, 4, 4, 1, 1, 1)   \
   X(256, 192, 32, 2, 4, 4, 4, 1, 1, 1)
 
 // Quad kernel (4 waves of 128 x 128):
