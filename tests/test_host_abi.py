@@ -242,6 +242,31 @@ def test_choice_table_names_product_configs():
     assert any(c["built"] == 0 for c in cfgs) and any(c["built"] == 0 for c in f8)
 
 
+def test_every_product_config_is_reachable():
+    """The product library compiles no config that no call can reach: each compiled fast
+    config is the selector's pick for some shape (an exact entry of the table or the cost
+    model's argmin on a grid of shapes) or the split-K plan's config; the same for fp8."""
+    cfgs = tg.configs()
+    exact, _ = parse_choice_table()["kF16"]
+    reach = {e[4] for e in exact}
+    grid = [(M, N, K) for M in range(256, 16385, 768) for N in range(256, 16385, 768)
+            for K in (256, 1024, 4096, 16384)]
+    for layout in range(4):
+        ta, tb = layout >> 1, layout & 1
+        for (M, N, K) in grid:
+            reach.add(tg.tgemm_select_config_ex(ta, tb, M, N, K, A=A16, B=A16, C=A16))
+            reach.add(tg.tgemm_split_plan(ta, tb, M, N, K, A=A16, B=A16, C=A16)[0])
+    built = {i for i, c in enumerate(cfgs) if c["built"] and not c["generic"]}
+    assert built <= reach, [cfgs[i]["name"] for i in sorted(built - reach)]
+    f8 = tg.fp8_configs()
+    exact8, _ = parse_choice_table()["kFp8"]
+    reach8 = {e[4] for e in exact8}
+    for (M, N, K) in grid:
+        reach8.add(tg.tgemm_fp8_select_config(M, N, K, A=A16, B=A16, C=A16))
+    built8 = {i for i, c in enumerate(f8) if c["built"] and c["name"].startswith("f")}
+    assert built8 <= reach8, [f8[i]["name"] for i in sorted(built8 - reach8)]
+
+
 SELECT_SHAPES = [(1024, 1024, 1024), (2048, 2048, 4096), (2560, 2560, 4096), (16384, 512, 4096),
                  (3072, 3072, 4096), (4095, 3000, 1000), (3584, 3584, 2048), (4096, 4096, 4096),
                  (6144, 6144, 4096), (5120, 4096, 4096), (8192, 8192, 8192), (1000, 1000, 3000),
