@@ -72,6 +72,7 @@ std::vector<tgemm::Config> build_table() {
   TGEMM_PP_CONFIGS(CALL_PP)
   TGEMM_PP1_CONFIGS(CALL_PP1)
   TGEMM_QUAD_CONFIGS(CALL_QUAD)
+  TGEMM_PIPE2_CONFIGS(CALL_PIPE)
   return t;
 }
 

@@ -122,7 +122,7 @@ def test_workload_full_size_sampled(name):
 
 # Every fast config the selector's table can pick, each on the smallest timed shape where it
 # is the table's choice: the library must pick it by itself there.
-CHOICE_PREFIXES = ["m256x192", "m128x256", "m256x256", "m128x128", "p128x128"]
+CHOICE_PREFIXES = ["m256x192", "m128x256", "m256x256", "m128x128", "p128x128", "p64x128x64", "p64x128x32"]
 
 
 @pytest.mark.parametrize("prefix", CHOICE_PREFIXES)

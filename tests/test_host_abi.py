@@ -135,7 +135,7 @@ def config_list_prod_flags():
     for m in re.finditer(r"#define (TGEMM_\w+_CONFIGS)\(X\)((?:[^\n]*\\\n)*[^\n]*)", text):
         lists[m.group(1)] = [int(r.split(",")[-1]) for r in re.findall(r"X\(([^)]*)\)", m.group(2))]
     f16 = [1] + sum((lists[k] for k in ("TGEMM_FAST_CONFIGS", "TGEMM_PIPE_CONFIGS", "TGEMM_PP_CONFIGS",
-                                         "TGEMM_PP1_CONFIGS", "TGEMM_QUAD_CONFIGS")), [])
+                                         "TGEMM_PP1_CONFIGS", "TGEMM_QUAD_CONFIGS", "TGEMM_PIPE2_CONFIGS")), [])
     return f16, lists["TGEMM_FP8_CONFIGS"]
 
 

@@ -68,6 +68,14 @@
   X(256, 256, 32, 2, 2, 4, 4, 0, 0, 0)   \
   X(256, 256, 32, 2, 2, 4, 4, 1, 0, 0)
 
+// Single-group pipelined kernel on 64 x 128 tiles, for small output grids with long K
+// (twice the workgroups of 128 x 128 tiles). Listed after the quad rows so that every
+// earlier index keeps its meaning:
+//   X(BM, BN, BK, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP, PROD)            rows 21-22
+#define TGEMM_PIPE2_CONFIGS(X)        \
+  X(64, 128, 64, 2, 2, 3, 4, 1, 1)    \
+  X(64, 128, 32, 2, 2, 4, 4, 1, 1)
+
 // fp8 block-scaled kernels: X(BM, BN, WAVES_M, WAVES_N, STAGES, PANEL, XCD_REMAP, MODE, PROD)
 // MODE 0: one group, single-buffered fragments (name suffix _db0); 1: one group,
 // double-buffered fragments (_db1); 2: two wave groups in ping-pong (_pp).  fp8 rows 0-4

@@ -1567,7 +1567,8 @@ const Config* config_table(int* count) {
   static const Config table[] = {
       {GB_M, GB_N, GB_K, 1, 2, 2, 1, 0, 1, 0xF, 1, "generic_64x64x32"},
       TGEMM_FAST_CONFIGS(TGEMM_ROW) TGEMM_PIPE_CONFIGS(TGEMM_PIPE_ROW) TGEMM_PP_CONFIGS(TGEMM_PP_ROW)
-          TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW) TGEMM_QUAD_CONFIGS(TGEMM_QUAD_ROW)};
+          TGEMM_PP1_CONFIGS(TGEMM_PP1_ROW) TGEMM_QUAD_CONFIGS(TGEMM_QUAD_ROW)
+              TGEMM_PIPE2_CONFIGS(TGEMM_PIPE_ROW)};
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
 }
@@ -1592,11 +1593,12 @@ Launcher launcher(int idx) {
                                        TGEMM_PIPE_CONFIGS(TGEMM_PIPE_LAUNCHER)
                                            TGEMM_PP_CONFIGS(TGEMM_PP_LAUNCHER)
                                                TGEMM_PP1_CONFIGS(TGEMM_PP1_LAUNCHER)
-                                                   TGEMM_QUAD_CONFIGS(TGEMM_QUAD_LAUNCHER)};
+                                                   TGEMM_QUAD_CONFIGS(TGEMM_QUAD_LAUNCHER)
+                                                       TGEMM_PIPE2_CONFIGS(TGEMM_PIPE_LAUNCHER)};
   static_assert(sizeof(table) / sizeof(table[0]) ==
                     1 + sizeof((int[]){TGEMM_FAST_CONFIGS(TGEMM_COUNT) TGEMM_PIPE_CONFIGS(TGEMM_COUNT)
                                            TGEMM_PP_CONFIGS(TGEMM_COUNT) TGEMM_PP1_CONFIGS(TGEMM_COUNT)
-                                               TGEMM_QUAD_CONFIGS(TGEMM_COUNT)}) /
+                                               TGEMM_QUAD_CONFIGS(TGEMM_COUNT) TGEMM_PIPE2_CONFIGS(TGEMM_COUNT)}) /
                             sizeof(int),
                 "one launcher per config");
   return table[idx];

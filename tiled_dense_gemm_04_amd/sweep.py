@@ -60,7 +60,7 @@ CHOICE_SHAPES = [(1024, 1024, 4096), (1536, 1536, 4096), (2048, 2048, 4096), (25
                  (2048, 4096, 4096), (16384, 512, 4096), (3072, 3072, 4096), (3584, 3584, 2048),
                  (4096, 2560, 2048), (4095, 3000, 1000), (4096, 3072, 1024), (3072, 4096, 4096),
                  (5120, 4096, 4096), (6144, 6144, 4096)]
-CHOICE_F16 = ["p128x128x64_s2_w2x2_p4_x1", "m128x128x32_s4_w2x4_p4_x1", "m256x128x32_s4_w2x4_p4_x1",
+CHOICE_F16 = ["p64x128x64_s3_w2x2_p4_x1", "p64x128x32_s4_w2x2_p4_x1", "p128x128x64_s2_w2x2_p4_x1", "m128x128x32_s4_w2x4_p4_x1", "m256x128x32_s4_w2x4_p4_x1",
               "m128x256x32_s4_w2x4_p4_x1", "m256x192x32_s4_w2x4_p4_x1", "m256x256x32_s4_w2x4_p4_x1",
               "m256x256x32_s4_w2x4_p4_x0"]
 
@@ -123,8 +123,9 @@ def choice_sweep(md_path=None):
     return 0
 
 
-SPLIT_SHAPES = [(1024, 1024, 1024), (16384, 512, 4096), (512, 4096, 4096), (1024, 1024, 32768),
-                (512, 512, 16384), (2048, 2048, 16384), (4096, 1024, 8192)]
+SPLIT_SHAPES = [(1024, 1024, 1024), (16384, 512, 4096), (512, 4096, 4096), (1024, 1024, 4096),
+                (1024, 1024, 8192), (1024, 1024, 32768), (512, 512, 16384), (2048, 2048, 16384),
+                (4096, 1024, 8192)]
 
 
 def split_sweep(md_path=None):
@@ -183,6 +184,8 @@ TABLE_SHAPES = [
     (4095, 3000, 1000), (4096, 3072, 1024), (1024, 1024, 1024), (2048, 2048, 1024), (4096, 4096, 1024),
     (8192, 8192, 1024), (1024, 1024, 8192), (2048, 2048, 8192), (4096, 4096, 8192), (8192, 8192, 8192),
     (4096, 4096, 512), (8192, 8192, 512), (2560, 5120, 2048), (5120, 5120, 1024),
+    (1024, 2048, 4096), (2048, 1024, 2048), (2048, 2048, 16384), (4096, 1024, 8192), (1024, 1024, 16384),
+    (3072, 2048, 8192),
 ]
 ROUND = 256  # workgroups in flight at once: one per compute unit
 
