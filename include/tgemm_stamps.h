@@ -63,6 +63,31 @@ TGEMM_API int tgemm_stamps_clear(void);
 #define TGEMM_PROBE_MFMA_PER_ITER 16
 TGEMM_API int tgemm_mfma_probe(int blocks, int iters, void* out, void* stream);
 
+/* The same probe with a choice of operands and MFMA shape. Every mode does the same FLOP
+ * per launch as tgemm_mfma_probe (FLOP = blocks * TGEMM_PROBE_THREADS / 64 * iters *
+ * TGEMM_PROBE_MFMA_PER_ITER * 16384):
+ *   TGEMM_PROBE_SYNTHETIC   the pseudo-random register operands of tgemm_mfma_probe,
+ *                           16x16x32 MFMAs (operands may be NULL);
+ *   TGEMM_PROBE_OPERANDS    operands loaded once from `operands`, 16x16x32 MFMAs;
+ *   TGEMM_PROBE_OPERANDS_32 operands from `operands`, 32x32x16 MFMAs (8 accumulators of
+ *                           16 floats, half as many MFMAs of twice the FLOP);
+ *   TGEMM_PROBE_LDS_READS   operands from `operands`, 16x16x32 MFMAs, plus per wave and
+ *                           round 6 conflict-free ds_read_b128 from a 64 KiB LDS copy of
+ *                           the same values (the read rate of the 256 x 256 ping-pong
+ *                           GEMM), whose results are the next round's operands.
+ * operands: device memory of TGEMM_PROBE_THREADS * 64 binary16 values (64 KiB), 16-byte
+ * aligned; thread t of every workgroup takes values [64 t, 64 t + 64). Their magnitudes
+ * and signs set how much the multipliers toggle, so the power the probe draws. Returns
+ * TGEMM_OK, TGEMM_ENULL (out NULL, or operands NULL for a mode that reads them),
+ * TGEMM_EALIGN (operands not 16-byte aligned), TGEMM_EINVAL_DIM (mode unknown, blocks
+ * outside [1, 2^20] or iters outside [1, 2^24]), TGEMM_EDEVICE or TGEMM_ELAUNCH. */
+#define TGEMM_PROBE_SYNTHETIC 0
+#define TGEMM_PROBE_OPERANDS 1
+#define TGEMM_PROBE_OPERANDS_32 2
+#define TGEMM_PROBE_LDS_READS 3
+TGEMM_API int tgemm_mfma_probe_ex(int mode, int blocks, int iters, const void* operands, void* out,
+                                  void* stream);
+
 /* ---- LDS access probe (calibrates the host-side LDS bank model) ---- */
 
 /* Enqueues `blocks` workgroups of one wave (64 lanes) each with a 64 KiB LDS block. Every

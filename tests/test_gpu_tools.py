@@ -39,6 +39,34 @@ def test_mfma_probe_runs_and_is_deterministic(gpu):
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("mode", ["operands", "operands_32x32", "lds_reads"])
+def test_mfma_probe_modes_exact_on_ones(gpu, mode):
+    """With every operand 1.0 each accumulator element gains k (32 or 16) per round, exactly
+    in float32 at these counts, so every thread's sum is 2048 per round in each mode (16
+    accumulators x 4 elements x 32, or 8 x 16 x 16); N(0,1) operands give finite,
+    repeatable sums."""
+    torch = gpu
+    blocks, iters = 8, 40
+    ones = torch.ones(tg.PROBE_THREADS * 64, dtype=torch.float16, device="cuda")
+    out = torch.full((blocks * tg.PROBE_THREADS,), float("nan"), dtype=torch.float32, device="cuda")
+    log(f"probe {mode} ones blocks={blocks} iters={iters}")
+    flop = tg.tgemm_mfma_probe_ex(mode, blocks, iters, out, operands=ones)
+    torch.cuda.synchronize()
+    assert flop == blocks * 8 * iters * 16 * 16384
+    assert torch.all(out == 2048.0 * iters), out.unique()[:8]
+    A, _ = W.make_inputs(tg.PROBE_THREADS, 1, 64, "normal", 1.0, seed=40)
+    ops = torch.from_numpy(A).cuda().contiguous()
+    got = []
+    for _ in range(2):
+        out.fill_(float("nan"))
+        tg.tgemm_mfma_probe_ex(mode, blocks, iters, out, operands=ops)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.all(np.isfinite(o)) and np.count_nonzero(o) > o.size // 2
+        got.append(o)
+    assert np.array_equal(got[0], got[1])
+
+
 @pytest.mark.parametrize("cfg_name", ["m256x256x32_s4_w2x4_p4_x1", "p128x128x64_s2_w2x2_p4_x1",
                                       "m256x192x32_s4_w2x4_p4_x1"])
 def test_stamps_build_same_result_and_sane_stamps(gpu, cfg_name):

@@ -80,6 +80,19 @@ def test_probe_argument_checks():
     assert L.tgemm_mfma_probe((1 << 20) + 1, 1, 16, None) == tg.TGEMM_EINVAL_DIM
     assert L.tgemm_mfma_probe(1, 0, 16, None) == tg.TGEMM_EINVAL_DIM
     assert L.tgemm_mfma_probe(1, (1 << 24) + 1, 16, None) == tg.TGEMM_EINVAL_DIM
+    for name, mode in tg.PROBE_MODES.items():
+        macro = {"synthetic": "SYNTHETIC", "operands": "OPERANDS", "operands_32x32": "OPERANDS_32",
+                 "lds_reads": "LDS_READS"}[name]
+        assert f"#define TGEMM_PROBE_{macro} {mode}" in text
+    P = L.tgemm_mfma_probe_ex
+    assert P(-1, 1, 1, 16, 16, None) == tg.TGEMM_EINVAL_DIM
+    assert P(len(tg.PROBE_MODES), 1, 1, 16, 16, None) == tg.TGEMM_EINVAL_DIM
+    assert P(0, 1, 1, None, None, None) == tg.TGEMM_ENULL
+    for mode in (1, 2, 3):
+        assert P(mode, 1, 1, None, 16, None) == tg.TGEMM_ENULL      # operands needed
+        assert P(mode, 1, 1, 24, 16, None) == tg.TGEMM_EALIGN       # 16-byte aligned operands
+        assert P(mode, 0, 1, 16, 16, None) == tg.TGEMM_EINVAL_DIM
+        assert P(mode, 1, (1 << 24) + 1, 16, 16, None) == tg.TGEMM_EINVAL_DIM
 
 
 def test_error_codes_match_header():

@@ -59,7 +59,7 @@ EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_
            "tgemm_workspace_bytes_cfg", "gemm_f16_ws_static")
 # The extra symbols include/tgemm_stamps.h declares (tooling build only).
 STAMPS_EXPORTS = ("tgemm_stamps_capacity", "tgemm_stamps_read", "tgemm_stamps_clear", "tgemm_mfma_probe",
-                  "tgemm_lds_probe")
+                  "tgemm_mfma_probe_ex", "tgemm_lds_probe")
 # LDS probe instruction kinds (TGEMM_LDS_*) and their access widths in bytes.
 LDS_OPS = {"read_b32": (0, 4), "read_b64": (1, 8), "read_b128": (2, 16), "write_b32": (3, 4),
            "write_b64": (4, 8), "write_b128": (5, 16), "read_tr16_b64": (6, 8)}
@@ -68,6 +68,8 @@ FAST_MAX_LD = 1 << 22        # TGEMM_FAST_MAX_LD
 PROBE_THREADS = 512          # TGEMM_PROBE_THREADS
 PROBE_MFMA_PER_ITER = 16     # TGEMM_PROBE_MFMA_PER_ITER
 PROBE_FLOP_PER_MFMA = 2 * 16 * 16 * 32
+# MFMA probe modes (TGEMM_PROBE_*): operand source and MFMA shape.
+PROBE_MODES = {"synthetic": 0, "operands": 1, "operands_32x32": 2, "lds_reads": 3}
 
 
 class TgemmError(RuntimeError):
@@ -167,6 +169,8 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
         L.tgemm_stamps_clear.argtypes = []
         L.tgemm_mfma_probe.restype = i32
         L.tgemm_mfma_probe.argtypes = [i32, i32, p, p]
+        L.tgemm_mfma_probe_ex.restype = i32
+        L.tgemm_mfma_probe_ex.argtypes = [i32, i32, i32, p, p, p]
         L.tgemm_lds_probe.restype = i32
         L.tgemm_lds_probe.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_uint64), i32, i32,
                                       i32, p, p]
@@ -310,6 +314,27 @@ def tgemm_mfma_probe(blocks: int, iters: int, out, stream=None, library=None) ->
         rc = (library or stamps_lib()).tgemm_mfma_probe(int(blocks), int(iters), out.data_ptr(), handle)
     if rc != TGEMM_OK:
         raise TgemmError(rc, "tgemm_mfma_probe")
+    return blocks * (PROBE_THREADS // 64) * iters * PROBE_MFMA_PER_ITER * PROBE_FLOP_PER_MFMA
+
+
+def tgemm_mfma_probe_ex(mode: str, blocks: int, iters: int, out, operands=None, stream=None, library=None) -> int:
+    """The MFMA probe with a choice of operands and MFMA shape (PROBE_MODES); operands is a
+    binary16 device tensor of PROBE_THREADS * 64 values for every mode but "synthetic".
+    Returns the FLOP the launch performs (the same for every mode)."""
+    import torch
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < blocks * PROBE_THREADS:
+        raise ValueError("out must be a float32 device tensor of blocks * PROBE_THREADS elements")
+    if operands is not None and (operands.dtype != torch.float16 or not operands.is_cuda or
+                                 operands.numel() < PROBE_THREADS * 64 or not operands.is_contiguous()):
+        raise ValueError("operands must be a contiguous float16 device tensor of PROBE_THREADS * 64 values")
+    handle = torch.cuda.current_stream(out.device).cuda_stream if stream is None else (
+        stream if isinstance(stream, int) else stream.cuda_stream)
+    with torch.cuda.device(out.device):
+        rc = (library or stamps_lib()).tgemm_mfma_probe_ex(PROBE_MODES[mode], int(blocks), int(iters),
+                                                           None if operands is None else operands.data_ptr(),
+                                                           out.data_ptr(), handle)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "tgemm_mfma_probe_ex")
     return blocks * (PROBE_THREADS // 64) * iters * PROBE_MFMA_PER_ITER * PROBE_FLOP_PER_MFMA
 
 

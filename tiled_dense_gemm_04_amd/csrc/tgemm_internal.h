@@ -153,11 +153,12 @@ hipError_t static_scratch(int device, void** out);
 hipError_t launch_zero_fill(_Float16* C, int M, int N, int64_t ldc, hipStream_t s);
 
 // MFMA throughput probe (tooling build only): `blocks` workgroups of 8 waves, each wave
-// issuing iters x 16 independent 16x16x32 fp16 MFMAs; one float per thread goes to out
-// (blocks * 512 floats).
-constexpr int kProbeThreads = 512, kProbeMfmaPerIter = 16;
+// issuing iters rounds of 16 x 16384 FLOP of independent fp16 MFMAs; one float per thread
+// goes to out (blocks * 512 floats). Modes: 0 synthetic operands, 1 operands from ops
+// (512 x 64 binary16 values), 2 as 1 with 32x32x16 MFMAs, 3 as 1 plus LDS fragment reads.
+constexpr int kProbeThreads = 512, kProbeMfmaPerIter = 16, kProbeModes = 4;
 #ifdef TGEMM_STAMPS
-hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s);
+hipError_t launch_mfma_probe(int mode, int blocks, int iters, const _Float16* ops, float* out, hipStream_t s);
 #endif
 
 // LDS access probe (tooling build only): instruction kinds (ds_read_b32, ds_read_b64,

@@ -1243,12 +1243,20 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g) {
 }
 
 #ifdef TGEMM_STAMPS
-// MFMA throughput probe (tooling, not part of the GEMM): every wave keeps 16 independent
-// 16x16x32 accumulators and issues them back to back, `iters` rounds, on register operands
-// filled with pseudo-random binary16 values (random sign and mantissa, magnitudes 2^-2 to
-// 2^1, so the multipliers toggle like they do on N(0,1) data). Each thread stores the sum
-// of its accumulators so the work stays live. Measures the MFMA rate this board sustains
-// at its power limit, with no memory traffic at all.
+// MFMA throughput probe (tooling, not part of the GEMM): every wave keeps independent
+// accumulators and issues MFMAs on them back to back, `iters` rounds of kProbeMfmaPerIter x
+// 16384 FLOP, with no memory traffic to speak of. Each thread then stores the sum of its
+// accumulators so the work stays live. Measures the MFMA rate this board sustains at its
+// power limit. The operands decide how much the multipliers toggle, and so the power:
+//   MODE 0: register operands filled with pseudo-random binary16 values (random sign and
+//           mantissa, magnitudes 2^-2 to 2^1), 16x16x32 MFMAs, 16 accumulators;
+//   MODE 1: operands loaded once from `ops` (64 binary16 values per thread, for instance
+//           samples of the workloads' N(0,1) inputs), 16x16x32 MFMAs;
+//   MODE 2: as MODE 1 with 32x32x16 MFMAs (8 accumulators of 16 floats: the same FLOP per
+//           round);
+//   MODE 3: as MODE 1 plus the LDS read rate of the 256 x 256 ping-pong kernel (per wave,
+//           6 ds_read_b128 per 16 MFMAs) from a 64 KiB block holding the same values; each
+//           round's reads are the next round's operands, so they stay live.
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
   x *= 0x7feb352du;
@@ -1258,35 +1266,98 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   return x;
 }
 
-__global__ __launch_bounds__(kProbeThreads) void mfma_probe(int iters, float* out) {
+template <int MODE>
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe(int iters, const _Float16* ops, float* out) {
   WgClock clk;
   clk.start();
   const uint32_t tid = blockIdx.x * kProbeThreads + threadIdx.x;
   half8 a[4], b[4];
+  if constexpr (MODE == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t ha = mix32(tid * 64u + 8u * i + e), hb = mix32(~(tid * 64u + 8u * i + e));
-      const uint16_t ba = (uint16_t)(((ha >> 31) << 15) | ((13u + ((ha >> 10) & 3u)) << 10) | (ha & 0x3FFu));
-      const uint16_t bb = (uint16_t)(((hb >> 31) << 15) | ((13u + ((hb >> 10) & 3u)) << 10) | (hb & 0x3FFu));
-      a[i][e] = __builtin_bit_cast(_Float16, ba);
-      b[i][e] = __builtin_bit_cast(_Float16, bb);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t ha = mix32(tid * 64u + 8u * i + e), hb = mix32(~(tid * 64u + 8u * i + e));
+        const uint16_t ba = (uint16_t)(((ha >> 31) << 15) | ((13u + ((ha >> 10) & 3u)) << 10) | (ha & 0x3FFu));
+        const uint16_t bb = (uint16_t)(((hb >> 31) << 15) | ((13u + ((hb >> 10) & 3u)) << 10) | (hb & 0x3FFu));
+        a[i][e] = __builtin_bit_cast(_Float16, ba);
+        b[i][e] = __builtin_bit_cast(_Float16, bb);
+      }
+  } else {
+    const half8* const src = reinterpret_cast<const half8*>(ops) + threadIdx.x * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = src[i];
+      b[i] = src[4 + i];
     }
-  typedef float float4v __attribute__((ext_vector_type(4)));
-  float4v acc[kProbeMfmaPerIter];
-#pragma unroll
-  for (int j = 0; j < kProbeMfmaPerIter; ++j) acc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-  clk.loop_begin();
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int j = 0; j < kProbeMfmaPerIter; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 3], a[j >> 2], acc[j], 0, 0, 0);
   }
-  clk.loop_end();
+  typedef float float4v __attribute__((ext_vector_type(4)));
   float sum = 0.0f;
+  if constexpr (MODE == 2) {
+    constexpr int NACC = kProbeMfmaPerIter / 2;
+    float16v acc[NACC];
 #pragma unroll
-  for (int j = 0; j < kProbeMfmaPerIter; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    for (int j = 0; j < NACC; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    clk.loop_begin();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < NACC; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j & 3], a[j >> 1 & 3], acc[j], 0, 0, 0);
+    }
+    clk.loop_end();
+#pragma unroll
+    for (int j = 0; j < NACC; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[j][r];
+  } else {
+    float4v acc[kProbeMfmaPerIter];
+#pragma unroll
+    for (int j = 0; j < kProbeMfmaPerIter; ++j) acc[j] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MODE == 3) {
+      // 64 KiB block: thread t's 64 values at bytes [128 t, 128 t + 128). Read j of a round
+      // takes one contiguous KiB (conflict-free), at an offset that moves every round.
+      __shared__ __attribute__((aligned(16))) char blk[kProbeThreads * 128];
+      half8* const mine = reinterpret_cast<half8*>(blk + threadIdx.x * 128);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mine[i] = a[i];
+        mine[4 + i] = b[i];
+      }
+      __syncthreads();
+      const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      clk.loop_begin();
+      for (int it = 0; it < iters; ++it) {
+        half8 na[3], nb[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const uint32_t base = ((wave * 6u + 2u * j + (uint32_t)it * 48u) & 63u) * 1024u + lane * 16u;
+          na[j] = *reinterpret_cast<const half8*>(blk + base);
+          nb[j] = *reinterpret_cast<const half8*>(blk + ((base + 1024u) & 0xFFFFu));
+        }
+#pragma unroll
+        for (int j = 0; j < kProbeMfmaPerIter; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 3], a[j >> 2], acc[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          a[j] = na[j];
+          b[j] = nb[j];
+        }
+      }
+      clk.loop_end();
+    } else {
+      clk.loop_begin();
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < kProbeMfmaPerIter; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 3], a[j >> 2], acc[j], 0, 0, 0);
+      }
+      clk.loop_end();
+    }
+#pragma unroll
+    for (int j = 0; j < kProbeMfmaPerIter; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  }
   out[tid] = sum;
   clk.finish(iters, TG_STAMP_TABLE);
 }
@@ -1502,8 +1573,11 @@ hipError_t launch_lds_probe(int op, int blocks, const LdsProbeArgs& p, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(mfma_probe, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters, out);
+hipError_t launch_mfma_probe(int mode, int blocks, int iters, const _Float16* ops, float* out, hipStream_t s) {
+  static void (*const kernels[kProbeModes])(int, const _Float16*, float*) = {mfma_probe<0>, mfma_probe<1>,
+                                                                             mfma_probe<2>, mfma_probe<3>};
+  if (mode < 0 || mode >= kProbeModes) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kernels[mode], dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters, ops, out);
   return hipGetLastError();
 }
 

@@ -15,8 +15,9 @@ For each workload, with the config gemm_f16 picks:
     gemm_f16_ws with its planned config and split count;
   * context: torch.matmul (hipBLASLt) (+ relu_ when the workload has ReLU) timed the
     same way. Context only; never a target.
-The MFMA ceiling is the library's MFMA probe (no memory traffic, pseudo-random
-operands) timed the same way, with its own clock from the stamps.
+The MFMA ceiling is the library's MFMA probe (no memory traffic, N(0,1) binary16
+operands) timed the same way, with its own clock from the stamps; its variants (synthetic
+operands, 32x32x16 MFMAs, the GEMM's LDS read rate added) are reported beside it.
 
 --ramp NAME instead records one event pair per call over a long back-to-back run of one
 workload (twice, 2 s idle in between) and prints the mean per-call time in windows of
@@ -195,12 +196,21 @@ def phases(stamps):
     }
 
 
-def measure_probe(torch, tg, stream, blocks=512, iters=2000):
+PROBE_VARIANTS = [
+    ("operands", "N(0,1) binary16 operands (the workloads' distribution), 16x16x32 MFMAs"),
+    ("synthetic", "pseudo-random register operands (random sign and mantissa, magnitudes 2^-2 to 2^1), 16x16x32"),
+    ("operands_32x32", "N(0,1) operands, 32x32x16 MFMAs (half as many, twice the FLOP each)"),
+    ("lds_reads", "N(0,1) operands, 16x16x32, plus the 256 x 256 GEMM's LDS read rate (6 ds_read_b128 "
+                  "per 16 MFMAs per wave)"),
+]
+
+
+def measure_probe(torch, tg, stream, mode="synthetic", operands=None, blocks=512, iters=2000):
     out = torch.empty(blocks * tg.PROBE_THREADS, dtype=torch.float32, device="cuda")
     flop = blocks * (tg.PROBE_THREADS // 64) * iters * tg.PROBE_MFMA_PER_ITER * tg.PROBE_FLOP_PER_MFMA
 
     def call(_i, library=None):
-        tg.tgemm_mfma_probe(blocks, iters, out, stream=stream, library=library)
+        tg.tgemm_mfma_probe_ex(mode, blocks, iters, out, operands=operands, stream=stream, library=library)
 
     t = timed_trials(torch, stream, call)
     S = tg.stamps_lib()
@@ -210,11 +220,21 @@ def measure_probe(torch, tg, stream, blocks=512, iters=2000):
     if not torch.isfinite(out).all():
         raise RuntimeError("MFMA probe produced non-finite values")
     tf = flop / (t["median_us"] * 1e-6) / 1e12
-    res = {"blocks": blocks, "iters": iters, "flop": flop, **t, "tflops": tf,
+    res = {"mode": mode, "blocks": blocks, "iters": iters, "flop": flop, **t, "tflops": tf,
            "pct_of_peak": 100 * tf / PEAK_TFLOPS, "phases": ph}
-    log(f"MFMA probe: {t['median_us']:.1f} us/launch, {tf:.1f} TFLOP/s ({100 * tf / PEAK_TFLOPS:.1f} % of "
+    log(f"MFMA probe ({mode}): {t['median_us']:.1f} us/launch, {tf:.1f} TFLOP/s ({100 * tf / PEAK_TFLOPS:.1f} % of "
         f"{PEAK_TFLOPS:.1f}); shader clock {ph['shader_clock_ghz'] if ph else float('nan'):.3f} GHz")
     return res
+
+
+def measure_probes(torch, tg, W, stream):
+    """Every probe variant; the one on N(0,1) operands is the ceiling the GEMMs are held to
+    (same data distribution as the workloads, no memory traffic)."""
+    A, _ = W.make_inputs(tg.PROBE_THREADS, 1, 64, "normal", 1.0, seed=40)
+    ops = torch.from_numpy(A).cuda().contiguous()
+    variants = [measure_probe(torch, tg, stream, mode, None if mode == "synthetic" else ops)
+                for mode, _ in PROBE_VARIANTS]
+    return {"ceiling": variants[0], "variants": variants}
 
 
 def measure_workload(torch, tg, W, w, stream, cold=True, with_torch=True, ceiling=None):
@@ -436,11 +456,22 @@ def markdown(results, probe, host, grouped=None) -> str:
     L.append(f"Device: {host['device']}; {host['library']}; torch {host['torch']}.")
     L.append("")
     if probe:
-        ph = probe.get("phases") or {}
-        L.append(f"MFMA ceiling (probe: {probe['blocks']} workgroups x 8 waves, {probe['iters']} rounds of 16 "
-                 f"independent 16x16x32 fp16 MFMAs, pseudo-random operands, no memory traffic): "
-                 f"**{probe['tflops']:.1f} TFLOP/s** = {probe['pct_of_peak']:.1f} % of {PEAK_TFLOPS:.1f}, "
+        c = probe["ceiling"]
+        ph = c.get("phases") or {}
+        L.append(f"MFMA ceiling (probe: {c['blocks']} workgroups x 8 waves, {c['iters']} rounds of 16 "
+                 f"independent 16x16x32 fp16 MFMAs, N(0,1) binary16 operands, no memory traffic): "
+                 f"**{c['tflops']:.1f} TFLOP/s** = {c['pct_of_peak']:.1f} % of {PEAK_TFLOPS:.1f}, "
                  f"shader clock {ph.get('shader_clock_ghz', float('nan')):.3f} GHz (s_memtime / s_memrealtime).")
+        L.append("")
+        L.append("Probe variants (same FLOP per launch; `tgemm_mfma_probe_ex` of the tooling build):")
+        L.append("")
+        L.append("| variant | TFLOP/s | % of peak | shader clock GHz |")
+        L.append("|---|---|---|---|")
+        desc = dict(PROBE_VARIANTS)
+        for v in probe["variants"]:
+            vph = v.get("phases") or {}
+            L.append(f"| {desc[v['mode']]} | {v['tflops']:.1f} | {v['pct_of_peak']:.1f} | "
+                     f"{vph.get('shader_clock_ghz', float('nan')):.3f} |")
         L.append("")
     L.append("| workload | config | hot us (min-max) | TFLOP/s | % peak | % MFMA ceiling | cold us | "
              "split-K (gemm_f16_ws) us | hipBLASLt us (context) |")
@@ -521,8 +552,8 @@ def main():
             with open(args.md, "w") as f:
                 f.write(md)
         return 0
-    probe = None if args.no_probe else measure_probe(torch, tg, stream)
-    ceiling = probe["tflops"] if probe else None
+    probe = None if args.no_probe else measure_probes(torch, tg, W, stream)
+    ceiling = probe["ceiling"]["tflops"] if probe else None
     results = [measure_workload(torch, tg, W, w, stream, cold=not args.no_cold, with_torch=not args.no_torch,
                                 ceiling=ceiling) for w in works]
     grouped = [measure_grouped(torch, tg, gw, stream, with_torch=not args.no_torch)
