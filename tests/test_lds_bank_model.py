@@ -6,8 +6,8 @@ calibration patterns plus every fragment read, scale read and epilogue staging a
 the kernels the measured workloads run, written out from the kernels' address arithmetic.
 The model must reproduce every one exactly. Kernel-level rates from the model are checked
 against the counter rates of whole GEMM launches, before and after the conflict-free
-epilogue staging (StagedTile), and the current kernels' accesses must be conflict-free
-except the fp8 kernel's scale reads (kept for speed)."""
+epilogue staging (StagedTile) and the fp8 kernel's swizzled scale layout (scale_pos), and
+every access of the current kernels must be conflict-free."""
 import json
 import os
 
@@ -60,22 +60,23 @@ def test_model_reproduces_kernel_conflict_rates(workload):
     assert abs(got - measured) < 0.1, (workload, got, measured)
 
 
-def test_current_kernels_conflict_free_but_fp8_scales():
-    """The fp16 kernels' fragment reads and every kernel's staging (StagedTile) are
-    conflict-free; the fp8 kernel's one-float scale reads stay 2-way conflicted on purpose
-    (the conflict-free layouts measured slower)."""
+def test_current_kernels_conflict_free():
+    """Every loop and epilogue access of the current kernels is conflict-free: the fp16
+    fragment reads, every kernel's staging (StagedTile) and the fp8 scale reads at scale_pos;
+    the fp8 scale reads in the earlier row-major layout were 2-way conflicted."""
     pats = LP.kernel_patterns()
     for p in pats:
-        if p["phase"] in ("loop", "epilogue") and "scale" not in p["name"]:
+        if p["phase"] in ("loop", "epilogue"):
             assert LP.pattern_cycles(p)[0] == 0, p["name"]
-        if "scale" in p["name"]:
+        if p["phase"] == "loop_old_scales":
             assert LP.pattern_cycles(p) == (2, 4), p["name"]
-    for kernel in ("pp256x256", "pp256x192", "pp256x128", "pp128x128"):
+    for kernel in ("pp256x256", "pp256x192", "pp256x128", "pp128x128", "fp8_256x256"):
         assert LP.kernel_rate(pats, kernel, 32) == 0.0
 
 
-# The same counter rates after the change (StagedTile epilogue), measured the same way.
-MEASURED_AFTER = {
+# The same counter rates with the StagedTile epilogue but the fp8 kernel's row-major scale
+# layout, measured the same way.
+MEASURED_STAGED = {
     "relu_4096": ("pp256x256", 128, 0.00),
     "relu_edge_4095x3000x1000": ("pp256x256", 32, 0.00),
     "relu_tall_16384x512x4096": ("pp256x128", 128, 0.00),
@@ -84,10 +85,10 @@ MEASURED_AFTER = {
 }
 
 
-@pytest.mark.parametrize("workload", sorted(MEASURED_AFTER))
-def test_model_reproduces_current_conflict_rates(workload):
-    kernel, k_tiles, measured = MEASURED_AFTER[workload]
-    got = 100 * LP.kernel_rate(LP.kernel_patterns(), kernel, k_tiles)
+@pytest.mark.parametrize("workload", sorted(MEASURED_STAGED))
+def test_model_reproduces_staged_epilogue_conflict_rates(workload):
+    kernel, k_tiles, measured = MEASURED_STAGED[workload]
+    got = 100 * LP.kernel_rate(LP.kernel_patterns(), kernel, k_tiles, old_scales=True)
     assert abs(got - measured) < 0.1, (workload, got, measured)
 
 

@@ -110,6 +110,14 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old) {
 // k-tiles per group of A row scales (8 measured no faster on 256 x 256 tiles and slower
 // on 128 x 128 ones).
 constexpr int kScaleGroup = 4;
+// Position of the scale of k-tile g (of its group) of tile row r in a [BM][G] group slot of
+// LDS: a row's G floats stay together (one 16-byte run, so a copy's lanes still fetch 16
+// contiguous bytes per row), swapped in pairs on rows whose bit 3 is set. The loop reads
+// one scale per MFMA row with ds_read_b32, the 16 rows r0 .. r0 + 15 of a 16 x 16 tile (r0
+// a multiple of 16), and such a read is served 32 banks per cycle: without the swap rows r
+// and r + 8 fall on one bank (2 extra cycles per read), with it all 16 rows fall on
+// distinct banks.
+__host__ __device__ constexpr int scale_pos(int r, int g) { return r * kScaleGroup + (g ^ ((r >> 3) & 1)); }
 
 template <int BM, int BN, int WM, int WN, int STAGES, int PANEL, int XCD, bool DB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g) {
@@ -157,15 +165,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
   // ring of three group slots. Group 0 is fetched before the loop; every k-tile copy t then
   // fetches slice t % G (BM / G rows) of group t / G + 1, so each copy is one dword per
   // lane, G consecutive lanes read G consecutive floats of one row, and the group is
-  // complete (and its slot free) well before its first k-tile. The loop reads one scale per
-  // MFMA row with ds_read_b32; rows r and r + 8 share a bank of the 32 such a read serves
-  // per cycle (2-way conflicts, 2 extra LDS cycles per read). Conflict-free layouts were
-  // measured slower: [16-row block][G][16] (one 64-lane copy per block, the copies then
-  // touch 4 bytes per lane instead of 16) by 0.4 %, and aligned ds_read_b64 pairs plus a
-  // select by 1.1-1.8 %: the LDS is not the limit here, the instruction stream is.
+  // complete (and its slot free) well before its first k-tile. Within a group slot the
+  // scales sit at scale_pos (pairs swapped on every other 8 rows), so the loop's one-float
+  // reads are conflict-free. (Two other conflict-free layouts measured slower: [16-row
+  // block][G][16], whose copies touch 4 bytes per lane instead of 16, by 0.4 %, and aligned
+  // ds_read_b64 pairs plus a select by 1.1-1.8 %.) Slices start on multiples of 16 rows, so
+  // lane si of a slice fetches the scale that position si of the slice holds: row si / G of
+  // the slice, k-tile (si % G) ^ ((si / G) >> 3 & 1).
+  static_assert((BM / G) % 16 == 0, "scale slices start on 16-row boundaries");
   const float* const sa_base = g.SA + (int64_t)row0 * g.KB;
   const int si = wave * 64 + lane;  // this lane's element of a slice
-  const uint32_t s_off = si < BM ? (uint32_t)(((si / G) * g.KB + si % G) * 4) : kOob;
+  const uint32_t s_off =
+      si < BM ? (uint32_t)(((si / G) * g.KB + ((si % G) ^ ((si / G) >> 3 & 1))) * 4) : kOob;
   // B block scales: one per wave per k-tile, read through the scalar path. (Waves whose
   // columns all lie past N read the last block row: their results are dropped.)
   const int sb_blk = min((col0 + (wave % WN) * WTN) / kFp8Block, (g.N - 1) / kFp8Block);
@@ -199,14 +210,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
       dma_dword_to_lds(rs, s_lds0 + s_step * ((grp % 3) * SG_BYTES + part * BM * 4), s_off);
     }
   };
-  auto sa_lds = [&](int t) { return (const TG_LDS float*)(s_lds + ((t / G) % 3) * SG_BYTES) + t % G; };
+  // A row scale of k-tile t for tile row r (scale_pos inside the group slot of t).
+  auto sa_at = [&](int t, int r) { return ((const TG_LDS float*)(s_lds + ((t / G) % 3) * SG_BYTES))[scale_pos(r, t % G)]; };
   // Group 0, before the first operand copies: NG0 copies per wave over the whole group.
   {
     const int4v rs = make_rsrc(sa_base, (uint32_t)(((int64_t)(mvalid - 1) * g.KB + g.KB) * 4));
 #pragma unroll
     for (int j = 0; j < NG0; ++j) {
-      const int i = (wave * NG0 + j) * 64 + lane;
-      dma_dword_to_lds(rs, lds_addr(s_lds) + (wave * NG0 + j) * 256, (uint32_t)(((i / G) * g.KB + i % G) * 4));
+      const int i = (wave * NG0 + j) * 64 + lane;  // position i of group 0's slot
+      dma_dword_to_lds(rs, lds_addr(s_lds) + (wave * NG0 + j) * 256,
+                       (uint32_t)(((i / G) * g.KB + ((i % G) ^ ((i / G) >> 3 & 1))) * 4));
     }
   }
 
@@ -248,9 +261,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
       const bool fold_prev = kt > 0;
       const char* const As = a_lds + slot * A_BYTES;
       const char* const Bs = b_lds + slot * B_BYTES;
-      const TG_LDS float* const S = sa_lds(kt);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) sc[fm] = S[(wm * WTM + fm * 16 + lrow) * G] * sb;
+      for (int fm = 0; fm < FM; ++fm) sc[fm] = sa_at(kt, wm * WTM + fm * 16 + lrow) * sb;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
 #pragma unroll
@@ -325,13 +337,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_block_kernel(Fp8Args g)
       const int slot = kt % STAGES;
       const char* const As = a_lds + slot * A_BYTES;
       const char* const Bs = b_lds + slot * B_BYTES;
-      const TG_LDS float* const S = sa_lds(kt);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) f.b[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) f.a[fm] = cat_frag(opa.frag(As, fm, 0), opa.frag(As, fm, 1));
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) f.sa[fm] = S[(wm * WTM + fm * 16 + lrow) * G];
+      for (int fm = 0; fm < FM; ++fm) f.sa[fm] = sa_at(kt, wm * WTM + fm * 16 + lrow);
       f.sb = sb_row[min(kt, nk - 1)];
     };
     constexpr int T = FM * FN;
@@ -462,7 +473,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_pp_kernel(Fp8Args g) {
 
   const float* const sa_base = g.SA + (int64_t)row0 * g.KB;
   const int si = cw * 64 + lane;  // this lane's element of a scale slice
-  const uint32_t s_off = (uint32_t)(((si / G) * g.KB + si % G) * 4);
+  static_assert((BM / G) % 16 == 0, "scale slices start on 16-row boundaries");
+  const uint32_t s_off = (uint32_t)(((si / G) * g.KB + ((si % G) ^ ((si / G) >> 3 & 1))) * 4);  // scale_pos
   const int sb_blk = min((col0 + (wave % WN) * WTN) / kFp8Block, (g.N - 1) / kFp8Block);
   const float* const sb_row = g.SB + (int64_t)sb_blk * g.KB;
 
@@ -497,7 +509,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_pp_kernel(Fp8Args g) {
     const int4v rs = make_rsrc(sa_base + (int64_t)r0 * g.KB + min(k0, nk - 1), rng);
     dma_dword_to_lds(rs, s_lds0 + (sgrp % 3) * SG_BYTES + part * BM * 4, s_off);
   };
-  auto sa_lds = [&](int t) { return (const TG_LDS float*)(s_lds + ((t / G) % 3) * SG_BYTES) + t % G; };
+  // A row scale of k-tile t for tile row r (scale_pos inside the group slot of t).
+  auto sa_at = [&](int t, int r) { return ((const TG_LDS float*)(s_lds + ((t / G) % 3) * SG_BYTES))[scale_pos(r, t % G)]; };
 
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane % 16;
@@ -521,14 +534,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_pp_kernel(Fp8Args g) {
     const int slot = kt % STAGES;
     const char* const As = a_lds + slot * A_BYTES;
     const char* const Bs = b_lds + slot * B_BYTES;
-    const TG_LDS float* const S = sa_lds(kt);
     sb = sbp[kt];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) fb[fn] = cat_frag(opb.frag(Bs, fn, 0), opb.frag(Bs, fn, 1));
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) fa[fm] = cat_frag(opa.frag(As, fm, 0), opa.frag(As, fm, 1));
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) sa[fm] = S[(wm * WTM + fm * 16 + lrow) * G];
+    for (int fm = 0; fm < FM; ++fm) sa[fm] = sa_at(kt, wm * WTM + fm * 16 + lrow);
   };
   // MFMA t (t = fm * FN + fn) writes result register t % 2; the block sum of MFMA t-1 is
   // folded right after it (acc += sa * sb * P) while MFMA t runs. sched_barrier(0) keeps
@@ -556,8 +568,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_pp_kernel(Fp8Args g) {
     const int4v rs = make_rsrc(sa_base, (uint32_t)(((int64_t)(mvalid - 1) * g.KB + g.KB) * 4));
 #pragma unroll
     for (int j = 0; j < NG0; ++j) {
-      const int i = (cw * NG0 + j) * 64 + lane;
-      dma_dword_to_lds(rs, lds_addr(s_lds) + (cw * NG0 + j) * 256, (uint32_t)(((i / G) * g.KB + i % G) * 4));
+      const int i = (cw * NG0 + j) * 64 + lane;  // position i of group 0's slot
+      dma_dword_to_lds(rs, lds_addr(s_lds) + (cw * NG0 + j) * 256,
+                       (uint32_t)(((i / G) * g.KB + ((i % G) ^ ((i / G) >> 3 & 1))) * 4));
     }
     copy_tile(0);
     wait_vmcnt<0>();

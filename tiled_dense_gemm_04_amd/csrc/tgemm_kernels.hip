@@ -628,7 +628,6 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   };
 
   const int wm = wave / WN, wn = wave % WN;
-  const int lrow = lane % MF, lkg = lane / MF;
   opa.init_frags(wm * WTM, lane);
   opb.init_frags(wn * WTN, lane);
 
@@ -665,10 +664,6 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
       acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[ks][fn], fa[ks][fm], acc[fm][fn], 0, 0, 0);
   };
   constexpr int N_MFMA = KS * FM * FN;
-  auto mma_tile = [&]() {
-#pragma unroll
-    for (int m = 0; m < N_MFMA; ++m) mma_one(m);
-  };
   // The MFMAs of a tile with the CM MFMA-phase copies of tile t spread between them.
   auto mma_tile_copy = [&](int t, auto group) __attribute__((always_inline)) {
     constexpr int G = decltype(group)::value, P = G == 0 ? PT0 : PT1;

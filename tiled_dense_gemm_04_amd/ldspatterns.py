@@ -219,10 +219,19 @@ def epilogue_patterns_b64(cfg, w, wtm, wtn, mf=16):
 
 
 # ------------------------------------------------------------------ fp8 block-scaled kernel
+def scale_pos(r, g, group=4, swapped=True):
+    """Float index of the scale of k-tile g of tile row r in a [BM][G] group slot (the
+    kernel's scale_pos: pairs swapped on rows whose bit 3 is set; swapped=False: the plain
+    row-major layout the kernel used before)."""
+    return r * group + (g ^ ((r >> 3) & 1) if swapped else g)
+
+
 def fp8_patterns(bm, bn, wm, wn, group=4):
     """Per k-tile LDS accesses of the fp8 kernel: A and B fragments (K-major rows of 128 bytes,
-    two ds_read_b128 per 32-byte fragment), the A row scales ([BM][G] floats, one ds_read_b32
-    per MFMA row; each of the G k-tiles of a group weighs 1 / G), and the epilogue staging
+    two ds_read_b128 per 32-byte fragment), the A row scales ([BM][G] floats at scale_pos,
+    one ds_read_b32 per MFMA row; each of the G k-tiles of a group weighs 1 / G; phase
+    "loop_old_scales" holds the same reads in the earlier row-major layout, which counts in
+    place of the current one for kernel_rate(old_scales=True)), and the epilogue staging
     (StagedTile)."""
     wtm, wtn = bm // wm, bn // wn
     cfg = f"fp8_{bm}x{bn}"
@@ -235,8 +244,11 @@ def fp8_patterns(bm, bn, wm, wn, group=4):
                                  kmajor_frag(wmi * wtm, f, bk=64, ks=ks), kernel=cfg, phase="loop"))
             row = wmi * wtm + f * 16 + LANES % 16
             for k in range(group):  # k-tile k of a group of [BM][G] floats
-                pats.append(_pat(f"{cfg} A scale w{w} f{f} k{k}", "read_b32", (row * group + k) * 4,
+                pats.append(_pat(f"{cfg} A scale w{w} f{f} k{k}", "read_b32", scale_pos(row, k, group) * 4,
                                  kernel=cfg, phase="loop", weight=1.0 / group))
+                pats.append(_pat(f"{cfg} A scale (row-major) w{w} f{f} k{k}", "read_b32",
+                                 scale_pos(row, k, group, swapped=False) * 4, kernel=cfg,
+                                 phase="loop_old_scales", weight=1.0 / group))
         for f in range(wtn // 16):
             for ks in range(2):
                 pats.append(_pat(f"{cfg} B frag w{w} f{f} k{ks}", "read_b128",
@@ -260,17 +272,21 @@ def kernel_patterns():
     return out
 
 
-def kernel_rate(patterns, kernel, k_tiles, old=False):
+def kernel_rate(patterns, kernel, k_tiles, old=False, old_scales=None):
     """Bank-conflict cycles per LDS-busy cycle (the SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
     rate) of one workgroup of `kernel` over `k_tiles` k-tiles: loop patterns count once per
     k-tile (times their weight), epilogue patterns once. old=True takes the replaced
-    epilogue staging instead of StagedTile."""
+    epilogue staging instead of StagedTile; old_scales (default: old) the fp8 kernel's
+    earlier row-major scale layout instead of scale_pos."""
     epi = "epilogue_old" if old else "epilogue"
+    old_scales = old if old_scales is None else old_scales
     conflict = busy = 0.0
     for p in patterns:
         if p["kernel"] != kernel:
             continue
-        if p["phase"] == "loop":
+        is_scale = "A scale" in p["name"]
+        if p["phase"] == "loop" and not (is_scale and old_scales) or \
+                p["phase"] == "loop_old_scales" and old_scales:
             n = k_tiles * p.get("weight", 1.0)
         elif p["phase"] == epi:
             n = 1
