@@ -585,3 +585,19 @@ def test_product_kernels_use_no_scratch():
     res = B.kernel_resources("x.hip:1:1: remark: Function Name: k [-Rpass-analysis=kernel-resource-usage]\n"
                              "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 20 [-Rpass-analysis=kernel-resource-usage]\n")
     assert B.check_resources(res) == ["k"]
+
+
+def test_choice_table_is_generated_from_committed_timings():
+    """The selector's table (csrc/tgemm_choice.inc) and its report (profiles/config_choice.md)
+    are exactly what `sweep.py --refit` makes of the committed sweep timings
+    (profiles/config_choice_timings.json) for the configs this build compiles: no hand
+    edits, and a config demoted to the tooling build drops out of both."""
+    import json
+    from tiled_dense_gemm_04_amd import sweep
+    with open(os.path.join(ROOT, "profiles", "config_choice_timings.json")) as f:
+        data = json.load(f)
+    inc, md = sweep.render_table(sweep.product_only(data))
+    with open(os.path.join(ROOT, "tiled_dense_gemm_04_amd", "csrc", "tgemm_choice.inc")) as f:
+        assert f.read() == inc
+    with open(os.path.join(ROOT, "profiles", "config_choice.md")) as f:
+        assert f.read() == md
