@@ -18,6 +18,9 @@ def parse_choice_table():
         model = [(int(m[0]), [float(v) for v in m[1:]])
                  for m in re.findall(r"\{(\d+), ([-\d.e+]+), ([-\d.e+]+), ([-\d.e+]+), ([-\d.e+]+)\}", mo)]
         out[prefix] = (exact, model)
+    sp = re.search(r"kSplitExact\[\] = \{(.*?)\};", text, re.S).group(1)
+    out["kSplit"] = [tuple(int(v) for v in m)
+                     for m in re.findall(r"\{(-?\d+), (\d+), (\d+), (\d+), (-?\d+), (\d+)\}", sp) if int(m[0]) >= 0]
     return out
 
 

@@ -234,6 +234,27 @@ def table_sweep(out_inc, md_path=None, refit=None):
     return 0
 
 
+# Split-K options the table sweep times (gemm_f16_ws_cfg): every split-capable product
+# config (all four layouts compiled) at 2, 4 and 8 splits, where the split launch stays
+# within one round of workgroups (tiles x splits <= 256, which also bounds the partial
+# tiles to what the allocation-free entry point's static scratch holds) and every split
+# keeps at least 64 k-tiles.
+SPLIT_COUNTS = (2, 4, 8)
+SPLIT_MIN_KTILES = 64
+
+
+def split_options(cfgs, built, M, N, K):
+    out = []
+    for i in built:
+        c = cfgs[i]
+        if c["layouts"] != 0xF:
+            continue
+        tiles = -(-M // c["block_m"]) * -(-N // c["block_n"])
+        nk = -(-K // c["block_k"])
+        out += [(i, s) for s in SPLIT_COUNTS if tiles * s <= ROUND and nk // s >= SPLIT_MIN_KTILES]
+    return out
+
+
 def product_only(data):
     """Saved timings restricted to the configs the product library compiles now (a config
     demoted to the tooling build since the timings were taken drops out of the exact
@@ -248,6 +269,8 @@ def product_only(data):
         for c in d["cases"]:
             c["us"] = {i: v for i, v in c["us"].items() if i in built[kind]}
         d["cases"] = [c for c in d["cases"] if c["us"]]
+    for c in data.get("split", {}).get("cases", []):
+        c["us"] = {k: v for k, v in c["us"].items() if k.split("x")[0] in built["f16"]}
     return data
 
 
@@ -268,7 +291,7 @@ def measure_table():
             cases.append(case)
     data = {"device": torch.cuda.get_device_name(0), "round": ROUND,
             "f16": {"configs": {str(i): cfgs[i]["name"] for i in f16}, "cases": []},
-            "fp8": {"configs": {}, "cases": []}}
+            "fp8": {"configs": {}, "cases": []}, "split": {"cases": []}}
     for (layout, M, N, K) in cases:
         ta, tb = bool(layout & 2), bool(layout & 1)
         A, B = W.make_inputs(M, N, K, "normal", 1.0, seed=5)
@@ -286,6 +309,18 @@ def measure_table():
         data["f16"]["cases"].append({"layout": layout, "M": M, "N": N, "K": K, "us": times})
         print(f"f16 layout {layout} {M}x{N}x{K}: " + ", ".join(f"{k}:{v}" for k, v in times.items())
               + f" -> best {best}", flush=True)
+        opts = split_options(cfgs, f16, M, N, K)
+        if opts:
+            ws = tg.workspace_for(max(tg.tgemm_workspace_bytes_cfg(i, s, M, N) for i, s in opts), a.device,
+                                  stream.cuda_stream)
+            stimes = {f"{i}x{s}": round(timed_trials(
+                torch, stream, lambda j, i=i, s=s: tg.gemm_f16_ws(a, b, c, trans_a=ta, trans_b=tb, cfg=i, splits=s,
+                                                                  workspace=ws),
+                trials=5, warm_ms=30.0)["median_us"], 2) for i, s in opts}
+            data["split"]["cases"].append({"layout": layout, "M": M, "N": N, "K": K, "us": stimes})
+            print(f"split layout {layout} {M}x{N}x{K}: " + ", ".join(f"{k}:{v}" for k, v in stimes.items()),
+                  flush=True)
+            del ws
         del a, b, c
         torch.cuda.empty_cache()
     nf8 = tg.tgemm_fp8_num_configs()
@@ -382,7 +417,44 @@ def render_table(data):
         losses.sort()
         L_md += ["", f"Held-out loss over {len(losses)} shapes: median {losses[len(losses) // 2]:.1f} %, "
                  f"mean {sum(losses) / len(losses):.1f} %, max {losses[-1]:.1f} %.", ""]
-    return "\n".join(L_inc) + "\n", "\n".join(L_md) + "\n"
+    inc_split, md_split = render_split(data)
+    return "\n".join(L_inc + inc_split) + "\n", "\n".join(L_md + md_split) + "\n"
+
+
+def render_split(data):
+    """The split-K part of the table: per timed shape with split options, the fastest of
+    the unsplit default (the f16 exact entry) and the timed splits, as (cfg, splits); cfg
+    -1 with 1 split means the unsplit default."""
+    names = data["f16"]["configs"]
+    unsplit = {(c["layout"], c["M"], c["N"], c["K"]): c["us"] for c in data["f16"]["cases"]}
+    inc = ["", "// Split-K plan (gemm_f16_ws): every shape the sweep timed split options on, with the",
+           "// fastest of the unsplit choice (cfg -1, 1 split) and the timed (cfg, splits).",
+           "static const SplitExact kSplitExact[] = {"]
+    md = ["## split-K plan (gemm_f16_ws), the same inputs", "",
+          "Options: every split-capable product config at 2, 4 and 8 splits with tiles x splits <= 256 and at",
+          "least 64 k-tiles per split. `unsplit` is the fastest config without splitting (the table's",
+          "choice for gemm_f16). Shapes not listed take the fixed rule in tgemm_api.cpp.", "",
+          "| layout | M x N x K | unsplit us | split options us | plan |", "|---|---|---|---|---|"]
+    rows = 0
+    for c in data.get("split", {}).get("cases", []):
+        key = (c["layout"], c["M"], c["N"], c["K"])
+        if not c["us"] or key not in unsplit:
+            continue
+        base = min(unsplit[key].values())
+        best = min(c["us"], key=c["us"].get)
+        cfg, splits = (int(best.split("x")[0]), int(best.split("x")[1])) if c["us"][best] < base else (-1, 1)
+        inc.append(f"    {{{c['layout']}, {c['M']}, {c['N']}, {c['K']}, {cfg}, {splits}}},")
+        opts = ", ".join(f"{names[k.split('x')[0]]} x{k.split('x')[1]}: " + ("**%.1f**" if k == best and cfg >= 0
+                                                                             else "%.1f") % v
+                         for k, v in c["us"].items())
+        plan = f"{names[str(cfg)]} x{splits}" if cfg >= 0 else "no split"
+        md.append(f"| {c['layout']} | {c['M']}x{c['N']}x{c['K']} | {base:.1f} | {opts} | {plan} |")
+        rows += 1
+    if rows == 0:  # (a C++ array needs an element)
+        inc.append("    {-1, 0, 0, 0, -1, 1},")
+    inc.append("};")
+    md.append("")
+    return inc, md
 
 
 def main():
