@@ -450,18 +450,39 @@ struct StagedTile {
 
 // Epilogue of the 32x32 MFMA kernels: a wave's WTM x WTN tile of float32 accumulators
 // (tile (fm, fn) holds, in lane l, row 32 fm + l % 32 and columns 32 fn + 8 g + 4 (l / 32)
-// .. +3 for g = 0 .. 3) goes through the wave's own LDS region as 8-byte pieces, staged row
-// r's 16-byte chunk c at chunk c ^ ((r / 2) % SCPR) (rows padded to SCPR chunks, a power of
-// two), and out to C as 16-byte row segments read back by consecutive lanes. The 8-byte
-// writes of the 32 lanes of a row group are 2-way conflicted; the epilogue is a small part
-// of the kernels that use this layout (the pipelined kernel for the smallest grids, and a
-// sweep-only ping-pong variant). Stores as in StagedTile::store (non-temporal).
+// .. +3 for g = 0 .. 3) goes through the wave's own LDS region and out to C as 16-byte row
+// segments read back by consecutive lanes, like StagedTile.
+// Staging: ReLU (optional) and rounding to fp16 in registers; then for each pair of column
+// groups (g, g + 1) = (2q, 2q + 1) of a tile, v_permlane32_swap swaps lanes 32-63 of group
+// 2q with lanes 0-31 of group 2q + 1. Afterwards lane l < 32 holds columns 16 q .. 16 q + 7
+// of row l and lane l >= 32 columns 16 q + 8 .. 16 q + 15 of row l - 32, and each lane
+// writes one 16-byte chunk (ds_write_b128). Staged row r, chunk c sits at chunk c ^ ((r /
+// RPW) % SWZ), RPW rows per 128 bytes, as in StagedTile: the 8 rows of an 8-lane write pass
+// fall on 8 distinct chunk slots, so the writes are conflict-free (8-byte writes straight
+// from the accumulator layout were 2-way conflicted). Rows are padded to SCPR chunks (a
+// power of two). Stores as in StagedTile::store (non-temporal).
 template <int WTM, int WTN>
 struct StagedTile32 {
   static constexpr int CPR = WTN / 8, SCPR = CPR <= 8 ? (CPR <= 4 ? 4 : 8) : (CPR <= 16 ? 16 : 32);
   static constexpr int RB = SCPR * 16, BYTES = WTM * RB;
+  static constexpr int RPW = RB >= 128 ? 1 : 128 / RB;
+  static constexpr int SWZ = SCPR < 8 ? SCPR : 8;
   static_assert(SCPR >= CPR && WTN % 32 == 0 && WTM % 32 == 0, "staged row shape");
   static_assert(64 % SCPR == 0 && (WTM * SCPR) % 64 == 0, "row-copy shape");
+
+  __device__ static int chunk_at(int r, int c) { return c ^ ((r / RPW) % SWZ); }
+
+  template <bool RELU, typename V>
+  __device__ static uint32_t pack2(const V& a, int e) {
+    float x = a[e], y = a[e + 1];
+    if (RELU) {
+      x = relu_f(x);
+      y = relu_f(y);
+    }
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    const half2v h = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, h);
+  }
 
   template <bool RELU, typename Acc>
   __device__ static void stage(char* region, const Acc& acc, int lane) {
@@ -473,18 +494,14 @@ struct StagedTile32 {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int n = fn * 32 + 8 * g4 + 4 * lhi;
-          float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
-          float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
-          if (RELU) {
-            v0 = relu_f(v0);
-            v1 = relu_f(v1);
-            v2 = relu_f(v2);
-            v3 = relu_f(v3);
-          }
-          const half4 h = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-          *(TG_LDS half4*)(region + r * RB + (((n >> 3) ^ ((r >> 1) % SCPR)) << 4) + (n & 7) * 2) = h;
+        for (int q = 0; q < 2; ++q) {
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pack2<RELU>(acc[fm][fn], 8 * q),
+                                                           pack2<RELU>(acc[fm][fn], 8 * q + 4), false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pack2<RELU>(acc[fm][fn], 8 * q + 2),
+                                                           pack2<RELU>(acc[fm][fn], 8 * q + 6), false, false);
+          const int4v v = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+          const int c = fn * 4 + 2 * q + lhi;
+          *(TG_LDS int4v*)(region + r * RB + (chunk_at(r, c) << 4)) = v;
         }
       }
     }
@@ -502,7 +519,7 @@ struct StagedTile32 {
       const int idx = i * 64 + lane;
       const int r = idx / SCPR, c = idx % SCPR;
       if (c >= CPR) continue;
-      const half8 x = *(const TG_LDS half8*)(region + r * RB + ((c ^ ((r >> 1) % SCPR)) << 4));
+      const half8 x = *(const TG_LDS half8*)(region + r * RB + (chunk_at(r, c) << 4));
       if (r < mvalid && 8 * c < nvalid) store_c(C + (int64_t)r * ldc + 8 * c, x);
     }
   }

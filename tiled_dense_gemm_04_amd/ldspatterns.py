@@ -218,6 +218,55 @@ def epilogue_patterns_b64(cfg, w, wtm, wtn, mf=16):
     return pats
 
 
+def epilogue_patterns32(cfg, w, wtm, wtn):
+    """StagedTile32 (the 32 x 32 MFMA kernels): after the lane swap of each pair of column
+    groups (2q, 2q + 1) of a 32 x 32 tile, lane l writes 8 columns of row 32 fm + l % 32
+    with one ds_write_b128 at chunk c ^ ((r / RPW) % SWZ), c = 4 fn + 2 q + l / 32; then
+    the row reads, as in StagedTile."""
+    cpr, scpr, rb, rpw, swz = staged_shape(wtm, wtn)
+    l32, lhi = LANES % 32, LANES // 32
+    pats = []
+    for fm in range(wtm // 32):
+        row = fm * 32 + l32
+        for fn in range(wtn // 32):
+            for q in range(2):
+                c = fn * 4 + 2 * q + lhi
+                off = row * rb + ((c ^ ((row // rpw) % swz)) << 4)
+                pats.append(_pat(f"{cfg} epi32 write w{w} fm{fm} fn{fn} q{q}", "write_b128", off, kernel=cfg,
+                                 phase="epilogue"))
+    for i in range(wtm * scpr // 64):
+        idx = i * 64 + LANES
+        r, c = idx // scpr, idx % scpr
+        off = r * rb + ((c ^ ((r // rpw) % swz)) << 4)
+        pats.append(_pat(f"{cfg} epi32 read w{w} i{i}", "read_b128", np.where(c < cpr, off, 0), [_mask(c < cpr)],
+                         kernel=cfg, phase="epilogue"))
+    return pats
+
+
+def epilogue_patterns32_b64(cfg, w, wtm, wtn):
+    """The 32 x 32 staging StagedTile32 replaced: every lane wrote its 4 columns of each
+    column group (ds_write_b64) at chunk ((n / 8) ^ ((r / 2) % SCPR)) of staged row r, and
+    the rows were read back with the same swizzle."""
+    cpr, scpr, rb, _, _ = staged_shape(wtm, wtn)
+    l32, lhi = LANES % 32, LANES // 32
+    pats = []
+    for fm in range(wtm // 32):
+        r = fm * 32 + l32
+        for fn in range(wtn // 32):
+            for g4 in range(4):
+                n = fn * 32 + 8 * g4 + 4 * lhi
+                off = r * rb + (((n >> 3) ^ ((r >> 1) % scpr)) << 4) + (n & 7) * 2
+                pats.append(_pat(f"{cfg} old epi32 write w{w} fm{fm} fn{fn} g{g4}", "write_b64", off, kernel=cfg,
+                                 phase="epilogue_old"))
+    for i in range(wtm * scpr // 64):
+        idx = i * 64 + LANES
+        r, c = idx // scpr, idx % scpr
+        off = r * rb + ((c ^ ((r >> 1) % scpr)) << 4)
+        pats.append(_pat(f"{cfg} old epi32 read w{w} i{i}", "read_b128", np.where(c < cpr, off, 0),
+                         [_mask(c < cpr)], kernel=cfg, phase="epilogue_old"))
+    return pats
+
+
 # ------------------------------------------------------------------ fp8 block-scaled kernel
 def scale_pos(r, g, group=4, swapped=True):
     """Float index of the scale of k-tile g of tile row r in a [BM][G] group slot (the
@@ -260,7 +309,8 @@ def fp8_patterns(bm, bn, wm, wn, group=4):
 def kernel_patterns():
     """The ping-pong configs of the measured workloads and the selector: 256 x 256, 256 x 192,
     128 x 256, 128 x 128 and the earlier 256 x 128 (A and B as given), and the fp8 256 x 256
-    kernel. (The single-group pipelined kernels of the smallest grids are not modelled.)"""
+    kernel, and the epilogues of the single-group pipelined kernels of the smallest grids
+    (their main loops are not modelled)."""
     out = []
     for bm, bn in ((256, 256), (256, 192), (256, 128), (128, 256), (128, 128)):
         out += pingpong_patterns(bm, bn)
@@ -270,6 +320,10 @@ def kernel_patterns():
     out += fp8_patterns(256, 256, 2, 4)
     for w in range(8):
         out += epilogue_patterns_b64("fp8_256x256", w, 128, 64)
+    # epilogues of the single-group pipelined kernels (4 waves of 64 x 64 and 32 x 64)
+    for name, wtm, wtn in (("pipe128x128", 64, 64), ("pipe64x128", 32, 64)):
+        for w in range(4):
+            out += epilogue_patterns32(name, w, wtm, wtn) + epilogue_patterns32_b64(name, w, wtm, wtn)
     return out
 
 
