@@ -321,6 +321,14 @@ TGEMM_API int gemm_f16_cfg(int idx, int64_t M, int64_t N, int64_t K,
 TGEMM_API int tgemm_tile_of(int idx, int64_t M, int64_t N, int64_t wg,
                   int64_t* tile_m, int64_t* tile_n);
 
+/* The same map for a split-K launch of config idx with `splits` splits per tile
+ * (tiles x splits workgroups; splits = 1 gives tgemm_tile_of's map): writes the tile
+ * and the split (0 .. splits - 1) workgroup wg computes. Returns TGEMM_OK,
+ * TGEMM_EINVAL_CFG (idx out of range, splits outside 1 .. 8, or splits > 1 for a config
+ * that cannot split), TGEMM_ENULL, or TGEMM_EINVAL_DIM if wg is outside the launch. */
+TGEMM_API int tgemm_split_tile_of(int idx, int64_t M, int64_t N, int splits, int64_t wg,
+                        int64_t* tile_m, int64_t* tile_n, int* split);
+
 /* Number of workgroups config idx launches for an M x N output. */
 TGEMM_API int64_t tgemm_num_workgroups(int idx, int64_t M, int64_t N);
 

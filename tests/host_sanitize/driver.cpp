@@ -279,6 +279,31 @@ void fuzz_f16(int iters) {
         int64_t a, b;
         CHECK(tgemm_tile_of(c0, M, N, nwg, &a, &b) == TGEMM_EINVAL_DIM, "tile_of past the grid");
       }
+      // the split-K map covers every (tile, split) once; splits = 1 is tile_of's map
+      const int sp = 1 + (int)(next() % 8);
+      int64_t a0, b0;
+      int s0;
+      const int src = tgemm_split_tile_of(c0, M, N, sp, 0, &a0, &b0, &s0);
+      CHECK(src == TGEMM_OK || (sp > 1 && src == TGEMM_EINVAL_CFG), "split_tile_of rc");
+      if (src == TGEMM_OK && nwg * sp <= 4096) {
+        static uint8_t seen[4096];
+        std::memset(seen, 0, sizeof seen);
+        const int64_t tn = cdiv(N, cfgs[c0].info.block_n);
+        for (int64_t wg = 0; wg < nwg * sp; ++wg) {
+          int64_t a = -1, b = -1, a1 = -1, b1 = -1;
+          int s = -1;
+          CHECK(tgemm_split_tile_of(c0, M, N, sp, wg, &a, &b, &s) == TGEMM_OK, "split_tile_of");
+          const int64_t cell = (a * tn + b) * sp + s;
+          CHECK(a >= 0 && b >= 0 && s >= 0 && s < sp && cell < nwg * sp && !seen[cell], "split map not a bijection");
+          seen[cell] = 1;
+          if (sp == 1) {
+            CHECK(tgemm_tile_of(c0, M, N, wg, &a1, &b1) == TGEMM_OK && a1 == a && b1 == b, "split map at 1 split");
+          }
+        }
+        CHECK(tgemm_split_tile_of(c0, M, N, sp, nwg * sp, &a0, &b0, &s0) == TGEMM_EINVAL_DIM, "split map past the grid");
+      }
+      CHECK(tgemm_split_tile_of(c0, M, N, 9, 0, &a0, &b0, &s0) == TGEMM_EINVAL_CFG, "split_tile_of splits > 8");
+      CHECK(tgemm_split_tile_of(c0, M, N, 1, 0, &a0, &b0, nullptr) == TGEMM_ENULL, "split_tile_of null");
     }
   }
 }

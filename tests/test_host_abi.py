@@ -38,7 +38,7 @@ def exported(path):
 
 def test_exports_every_header_symbol():
     syms = header_symbols()
-    assert len(syms) == 25, syms
+    assert len(syms) == 26, syms
     assert sorted(tg.EXPORTS) == syms
     L = tg.lib()
     for s in syms:
@@ -471,6 +471,44 @@ def test_tile_map_keeps_xcd_tiles_together():
         rows = {t[0] for t in tiles}
         cols = {t[1] for t in tiles}
         assert len(tiles) == 32 and len(rows) == 4 and len(cols) == 8, (x, rows, cols)
+
+
+@pytest.mark.parametrize("M,N,splits", [(1024, 1024, 4), (16384, 512, 2), (4096, 1024, 2), (2048, 2048, 3),
+                                          (1000, 520, 8), (256, 256, 5)])
+def test_split_tile_map(M, N, splits):
+    """The split-K map covers every (tile, split) once, equals tgemm_tile_of at one split,
+    and, with XCD-remapped configs, gives each XCD (hardware id % 8) one split only where
+    the splits divide the XCDs' equal shares."""
+    for idx in range(tg.tgemm_num_configs()):
+        c = tg.tgemm_config_desc(idx)
+        if c["generic"] or c["layouts"] != 0xF:  # the configs that cannot split
+            with pytest.raises(tg.TgemmError):
+                tg.tgemm_split_tile_of(idx, M, N, 2, 0)
+            continue
+        tiles = tg.tgemm_num_workgroups(idx, M, N)
+        got = [tg.tgemm_split_tile_of(idx, M, N, splits, wg) for wg in range(tiles * splits)]
+        assert len(set(got)) == tiles * splits
+        tn = -(-N // c["block_n"])
+        assert all(0 <= s < splits and 0 <= a * tn + b < tiles for a, b, s in got)
+        assert [t[:2] for t in (tg.tgemm_split_tile_of(idx, M, N, 1, wg) for wg in range(tiles))] == \
+            [tg.tgemm_tile_of(idx, M, N, wg) for wg in range(tiles)]
+        if c["xcd_remap"] and (tiles * splits) % 8 == 0 and tiles % ((tiles * splits) // 8) == 0:
+            for x in range(8):
+                assert len({s for wg, (_, _, s) in enumerate(got) if wg % 8 == x}) == 1, (idx, x)
+        with pytest.raises(tg.TgemmError):
+            tg.tgemm_split_tile_of(idx, M, N, splits, tiles * splits)
+
+
+def test_split_tile_map_shares_panels_per_xcd():
+    """16384 x 512 on 256^2 tiles in two splits (256 workgroups): each XCD runs one split
+    (half of k) of 32 tiles, both tile columns of 16 tile rows, so each A row panel's half
+    of k is fetched into one L2."""
+    idx = next(i for i, c in enumerate(tg.configs()) if c["name"] == "m256x256x32_s4_w2x4_p4_x1")
+    for x in range(8):
+        got = [tg.tgemm_split_tile_of(idx, 16384, 512, 2, wg) for wg in range(x, 256, 8)]
+        tiles = {(a, b) for a, b, _ in got}
+        assert len(got) == 32 and len(tiles) == 32 and len({s for _, _, s in got}) == 1, (x, tiles)
+        assert len({a for a, _ in tiles}) == 16 and len({b for _, b in tiles}) == 2, (x, tiles)
 
 
 # ---------------------------------------------------------------- fp8 block-scaled path

@@ -8,7 +8,7 @@ missing or cannot be loaded, every call raises.
 The names mirror the C ABI: ``gemm_f16``, ``gemm_f16_ex`` (transposed operands),
 ``gemm_f16_cfg``, ``gemm_f16_ex_cfg`` (as ``cfg=``), ``tgemm_strerror``, ``tgemm_version``,
 ``tgemm_num_configs``, ``tgemm_config_desc``, ``tgemm_select_config``,
-``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_num_workgroups``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
+``tgemm_select_config_ex``, ``tgemm_tile_of``, ``tgemm_split_tile_of``, ``tgemm_num_workgroups``, and split-K: ``gemm_f16_ws`` (workspace managed here per device and
 stream unless given), ``gemm_f16_ws_cfg`` (as ``cfg=``/``splits=``),
 ``tgemm_workspace_bytes``, ``tgemm_workspace_bytes_cfg`` and ``tgemm_split_plan``, and
 ``gemm_f16_ws_static`` (split-K scratch in a static device array: allocates nothing); grouped
@@ -52,7 +52,7 @@ FP8_BLOCK = 128
 # Every symbol include/tgemm.h declares.
 EXPORTS = ("gemm_f16", "gemm_f16_ex", "gemm_f16_cfg", "gemm_f16_ex_cfg", "tgemm_strerror",
            "tgemm_version", "tgemm_num_configs", "tgemm_config_desc", "tgemm_select_config",
-           "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_num_workgroups",
+           "tgemm_select_config_ex", "tgemm_tile_of", "tgemm_split_tile_of", "tgemm_num_workgroups",
            "gemm_f16_ws", "gemm_f16_ws_cfg", "tgemm_workspace_bytes", "tgemm_split_plan",
            "gemm_f16_grouped", "gemm_fp8_block", "gemm_fp8_block_cfg", "quant_fp8_block",
            "tgemm_fp8_num_configs", "tgemm_fp8_config_desc", "tgemm_fp8_select_config",
@@ -131,6 +131,9 @@ def _load(path: str, stamps: bool) -> ctypes.CDLL:
     L.tgemm_select_config.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
     L.tgemm_tile_of.restype = i32
     L.tgemm_tile_of.argtypes = [i32, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.tgemm_split_tile_of.restype = i32
+    L.tgemm_split_tile_of.argtypes = [i32, i64, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                      ctypes.POINTER(i32)]
     L.tgemm_num_workgroups.restype = i64
     L.tgemm_num_workgroups.argtypes = [i32, i64, i64]
     L.gemm_f16_ws.restype = i32
@@ -295,6 +298,14 @@ def tgemm_tile_of(idx: int, M: int, N: int, wg: int):
     if rc != TGEMM_OK:
         raise TgemmError(rc, "tgemm_tile_of")
     return tm.value, tn.value
+
+
+def tgemm_split_tile_of(idx: int, M: int, N: int, splits: int, wg: int):
+    tm, tn, sp = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    rc = lib().tgemm_split_tile_of(idx, M, N, splits, wg, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(sp))
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "tgemm_split_tile_of")
+    return tm.value, tn.value, sp.value
 
 
 def tgemm_num_workgroups(idx: int, M: int, N: int) -> int:

@@ -41,15 +41,15 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 // panel-ordered block swizzle of "Writing High-Performance Kernels in TileLang, from
 // GEMM to MLA" (atlascloud.ai), section "Let's write a GEMM" (use_swizzle with a panel
 // size and column order), made XCD-aware for MI355X.
-__host__ __device__ inline void tile_of(int64_t wg, int64_t tiles_m, int64_t tiles_n, int panel,
-                                        int xcd_remap, int64_t* tm, int64_t* tn) {
-  const int64_t total = tiles_m * tiles_n;
-  int64_t t = wg;
-  if (xcd_remap && total >= kNumXcd) {
-    const int64_t q = total / kNumXcd, r = total % kNumXcd;
-    const int64_t x = wg % kNumXcd, j = wg / kNumXcd;
-    t = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
-  }
+__host__ __device__ inline int64_t xcd_logical_id(int64_t wg, int64_t total, int xcd_remap) {
+  if (!xcd_remap || total < kNumXcd) return wg;
+  const int64_t q = total / kNumXcd, r = total % kNumXcd;
+  const int64_t x = wg % kNumXcd, j = wg / kNumXcd;
+  return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+__host__ __device__ inline void panel_tile(int64_t t, int64_t tiles_m, int64_t tiles_n, int panel, int64_t* tm,
+                                           int64_t* tn) {
   if (panel < 1) panel = 1;
   const int64_t per_panel = (int64_t)panel * tiles_n;
   const int64_t p = t / per_panel;
@@ -58,6 +58,28 @@ __host__ __device__ inline void tile_of(int64_t wg, int64_t tiles_m, int64_t til
   if (rows > panel) rows = panel;
   *tm = p * panel + within % rows;
   *tn = within / rows;
+}
+
+__host__ __device__ inline void tile_of(int64_t wg, int64_t tiles_m, int64_t tiles_n, int panel,
+                                        int xcd_remap, int64_t* tm, int64_t* tn) {
+  panel_tile(xcd_logical_id(wg, tiles_m * tiles_n, xcd_remap), tiles_m, tiles_n, panel, tm, tn);
+}
+
+// Split-K launches run tiles * splits workgroups. Step 1 runs over all of them; logical id
+// t then names split t / tiles of the tile with panel index t % tiles (step 2). An XCD's
+// contiguous range of logical ids is thus, for the most part, one split (one k range) of a
+// compact block of panel-neighbouring tiles: its L2 holds the A rows and B columns those
+// tiles share over k / splits only, about sqrt(splits) times fewer bytes per XCD than
+// whole tiles with all their splits would need. The tile's linear index *tile_id numbers
+// its fixup counter and partial tiles. With splits = 1 this is tile_of.
+__host__ __device__ inline void split_tile_of(int64_t wg, int64_t tiles_m, int64_t tiles_n, int splits, int panel,
+                                              int xcd_remap, int64_t* tm, int64_t* tn, int64_t* tile_id,
+                                              int* split) {
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t t = xcd_logical_id(wg, tiles * splits, xcd_remap);
+  *split = (int)(t / tiles);
+  *tile_id = t - *split * tiles;
+  panel_tile(*tile_id, tiles_m, tiles_n, panel, tm, tn);
 }
 
 // Kernel arguments (passed by value).

@@ -553,12 +553,13 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // waves w and w+4 share SIMD w % 4
 
-  // Split-K (g.splits > 1): consecutive workgroup ids are the splits of one output tile;
-  // split s covers k-tiles [s * nk / splits, (s + 1) * nk / splits).
+  // Split-K (g.splits > 1): split s of a tile covers k-tiles [s * nk / splits,
+  // (s + 1) * nk / splits); an XCD runs mostly one split of a block of neighbouring tiles.
   const int splits = g.splits;
-  const int tile_id = wg / splits, split = wg - tile_id * splits;
-  int64_t tm64, tn64;
-  tile_of(tile_id, g.tiles_m, g.tiles_n, PANEL, XCD, &tm64, &tn64);
+  int64_t tm64, tn64, tile64;
+  int split;
+  split_tile_of(wg, g.tiles_m, g.tiles_n, splits, PANEL, XCD, &tm64, &tn64, &tile64, &split);
+  const int tile_id = (int)tile64;
   const int row0 = (int)tm64 * BM, col0 = (int)tn64 * BN;
   const int mvalid = min(BM, g.M - row0), nvalid = min(BN, g.N - col0);
   const int K = g.K;
@@ -812,7 +813,7 @@ __device__ __forceinline__ void pingpong_body(const GemmArgs& g, const int wg) {
   // WTN / 8 lanes per row, so each store covers whole 16-byte-aligned row segments instead
   // of 8-byte pieces of MF rows. The 16x16 layout uses StagedTile (conflict-free 16-byte
   // staging writes after a lane swap); the 32x32 one (a sweep-only config) uses
-  // StagedTile32 (8-byte staging writes). N and ldc are multiples of 8 on this path, so a
+  // StagedTile32 (the same after a 32-lane swap). N and ldc are multiples of 8 on this path, so a
   // chunk is either wholly inside the matrix or wholly outside.
   if constexpr (MF == 16) {
     using ST = StagedTile<WTM, WTN>;
