@@ -317,7 +317,8 @@ TGEMM_API int gemm_f16_cfg(int idx, int64_t M, int64_t N, int64_t K,
 /* Host replica of the device's workgroup -> output-tile map of config idx (the same
  * inline function the kernels run): for workgroup id wg of a launch over an M x N
  * output, writes the tile coordinates (*tile_m, *tile_n). Returns TGEMM_OK,
- * TGEMM_EINVAL_CFG, or TGEMM_EINVAL_DIM if wg is outside the launch. */
+ * TGEMM_EINVAL_CFG, TGEMM_ENULL, or TGEMM_EINVAL_DIM if wg is outside the launch or M
+ * or N is outside 1 .. TGEMM_MAX_DIM - 1. */
 TGEMM_API int tgemm_tile_of(int idx, int64_t M, int64_t N, int64_t wg,
                   int64_t* tile_m, int64_t* tile_n);
 
@@ -325,11 +326,12 @@ TGEMM_API int tgemm_tile_of(int idx, int64_t M, int64_t N, int64_t wg,
  * (tiles x splits workgroups; splits = 1 gives tgemm_tile_of's map): writes the tile
  * and the split (0 .. splits - 1) workgroup wg computes. Returns TGEMM_OK,
  * TGEMM_EINVAL_CFG (idx out of range, splits outside 1 .. 8, or splits > 1 for a config
- * that cannot split), TGEMM_ENULL, or TGEMM_EINVAL_DIM if wg is outside the launch. */
+ * that cannot split), TGEMM_ENULL, or TGEMM_EINVAL_DIM as for tgemm_tile_of. */
 TGEMM_API int tgemm_split_tile_of(int idx, int64_t M, int64_t N, int splits, int64_t wg,
                         int64_t* tile_m, int64_t* tile_n, int* split);
 
-/* Number of workgroups config idx launches for an M x N output. */
+/* Number of workgroups config idx launches for an M x N output (-1 for an idx out of
+ * range, or M or N outside 0 .. TGEMM_MAX_DIM - 1). */
 TGEMM_API int64_t tgemm_num_workgroups(int idx, int64_t M, int64_t N);
 
 

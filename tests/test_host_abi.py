@@ -499,6 +499,20 @@ def test_split_tile_map(M, N, splits):
             tg.tgemm_split_tile_of(idx, M, N, splits, tiles * splits)
 
 
+def test_tile_maps_refuse_dims_past_the_cap():
+    """M or N at TGEMM_MAX_DIM (2^31) is refused by the tile maps as by every entry point,
+    so the workgroup counts they compute stay far from int64 overflow."""
+    big = 1 << 31
+    for idx in range(tg.tgemm_num_configs()):
+        assert tg.tgemm_num_workgroups(idx, big, 8) == -1 and tg.tgemm_num_workgroups(idx, 8, big) == -1
+        assert tg.tgemm_num_workgroups(idx, big - 1, 8) > 0
+        for M, N in ((big, 8), (8, big), (big << 20, big << 20)):
+            with pytest.raises(tg.TgemmError):
+                tg.tgemm_tile_of(idx, M, N, 0)
+            with pytest.raises(tg.TgemmError):
+                tg.tgemm_split_tile_of(idx, M, N, 1, 0)
+
+
 def test_split_tile_map_shares_panels_per_xcd():
     """16384 x 512 on 256^2 tiles in two splits (256 workgroups): each XCD runs one split
     (half of k) of 32 tiles, both tile columns of 16 tile rows, so each A row panel's half
